@@ -1,0 +1,494 @@
+"""Plain fp64 CPU oracle for RoPE/YaRN + sink/sliding-window KV caching.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+module.  The product path (the HIP library and its Python binding) never
+imports or calls it, and this module imports nothing from the product path.
+
+Everything here is written for a reader to check against the pages by eye:
+no blocking, no fusion, no reordering beyond what each definition states.
+All floating point is numpy float64 unless a function says otherwise (the
+quantisers take their integer decisions in float32, the precision the
+kernels decide them in).
+
+Sources (cited by page title and section):
+  [RoPE]   "RoPE, scaling, sliding window, attention sinks" (mlinterviewnotes,
+           positional encoding and long context)
+  [GOSS]   "Inference & 128K Long Context" (GPT-OSS-Lite docs, inference)
+  [DYN]    "#2961 rope: --rope-scaling dynamic" (strata pull request)
+  [SINK]   "Attention Sink 与 Streaming KV Cache" (llm-glossary, attention-sink)
+  [VLLM]   "vLLM, from the inside out"
+
+Parity status: every function below is pinned by a CPU test against values
+the pages print, closed forms, invariants or brute force (tests/test_oracle_*.py);
+none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Configuration
+# --------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class RopeCfg:
+    """The rope parameters the pages use ([RoPE] notation section, "YaRN, precisely").
+
+    head_dim d_h, rotary_dim r <= d_h (leading slice, tail passes through),
+    rope_theta b, yarn_factor s (s <= 1 means plain RoPE), orig_max_pos L0,
+    beta_fast / beta_slow (defaults 32 / 1), extrapolation_factor (used in the
+    blend; the pages give no default, 1.0 is taken), neox pairing flag.
+    """
+
+    head_dim: int
+    rotary_dim: int
+    rope_theta: float = 10000.0
+    yarn_factor: float = 1.0
+    orig_max_pos: int = 4096
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+    extrapolation_factor: float = 1.0
+    neox: bool = True
+
+
+# --------------------------------------------------------------------------
+# Frequencies, YaRN band, mscale   ([RoPE] frequency definition; "YaRN, precisely")
+# --------------------------------------------------------------------------
+
+
+def plain_inv_freq(rotary_dim: int, base: float) -> np.ndarray:
+    """omega_i = 1 / b^(2i/r) for pair i = 0 .. r/2-1 ([RoPE] the inverse-frequency code)."""
+    i2 = np.arange(0, rotary_dim, 2, dtype=np.float64)
+    return 1.0 / (float(base) ** (i2 / rotary_dim))
+
+
+def yarn_correction_dim(num_rotations: float, rotary_dim: int, base: float, orig_max_pos: int) -> float:
+    """Pair index at which a pair turns `num_rotations` times within L0 ([RoPE] "YaRN, precisely")."""
+    return (rotary_dim * math.log(orig_max_pos / (num_rotations * 2 * math.pi))) / (2 * math.log(base))
+
+
+def yarn_correction_range(beta_fast, beta_slow, rotary_dim, base, orig_max_pos):
+    """(low, high): floor of d(beta_fast) and ceil of d(beta_slow), clamped to [0, r-1].
+
+    The body is not printed on the pages; this is the truncating reading the
+    worked script in [RoPE] ("See the YaRN band for your own config") uses.
+    """
+    low = math.floor(yarn_correction_dim(beta_fast, rotary_dim, base, orig_max_pos))
+    high = math.ceil(yarn_correction_dim(beta_slow, rotary_dim, base, orig_max_pos))
+    return max(low, 0), min(high, rotary_dim - 1)
+
+
+def yarn_ramp(low: float, high: float, n: int) -> np.ndarray:
+    """Linear ramp clamped to [0, 1], with the +0.001 singularity guard ([RoPE] "YaRN, precisely")."""
+    if low == high:
+        high += 0.001
+    x = (np.arange(n, dtype=np.float64) - low) / (high - low)
+    return np.clip(x, 0.0, 1.0)
+
+
+def yarn_mscale(scale: float) -> float:
+    """mu = 0.1 ln s + 1 for s > 1, else 1 ([RoPE] "YaRN, precisely")."""
+    if scale <= 1.0:
+        return 1.0
+    return 0.1 * math.log(scale) + 1.0
+
+
+def inv_freq(cfg: RopeCfg) -> np.ndarray:
+    """Per-pair angular frequency of the (possibly YaRN-scaled) rotation.
+
+    Plain RoPE when s <= 1.  Otherwise the extrapolated set 1/b^(2i/r) and
+    the interpolated set 1/(s b^(2i/r)) are blended by mask = (1 - ramp) *
+    extrapolation_factor: mask 1 keeps the original frequency (fast pairs,
+    below `low`), mask 0 divides it by s (slow pairs, above `high`)
+    ([RoPE] "YaRN, precisely", the _compute_inv_freq excerpt).
+    """
+    r, b = cfg.rotary_dim, float(cfg.rope_theta)
+    pos_freqs = b ** (np.arange(0, r, 2, dtype=np.float64) / r)
+    extrap = 1.0 / pos_freqs
+    s = float(cfg.yarn_factor)
+    if s <= 1.0:
+        return extrap
+    interp = 1.0 / (s * pos_freqs)
+    low, high = yarn_correction_range(cfg.beta_fast, cfg.beta_slow, r, b, cfg.orig_max_pos)
+    mask = (1.0 - yarn_ramp(low, high, r // 2)) * cfg.extrapolation_factor
+    return interp * (1.0 - mask) + extrap * mask
+
+
+def mscale(cfg: RopeCfg) -> float:
+    return yarn_mscale(cfg.yarn_factor)
+
+
+def build_table(cfg: RopeCfg, max_pos: int) -> np.ndarray:
+    """cos/sin table [max_pos, r]: cos(m w_i) * mu in the first r/2 columns, sin in the rest.
+
+    Angles are m * w_i in float64 ([RoPE] _compute_cos_sin_cache, scaled by
+    mscale as in the YaRN variant).  Returns float64; a device table is this
+    rounded once to float32.
+    """
+    w = inv_freq(cfg)
+    m = np.arange(max_pos, dtype=np.float64)
+    ang = np.outer(m, w)
+    mu = mscale(cfg)
+    return np.concatenate([np.cos(ang) * mu, np.sin(ang) * mu], axis=1)
+
+
+# --------------------------------------------------------------------------
+# Rotation   ([RoPE] the rotation excerpt and the NeoX / GPT-J pairing note)
+# --------------------------------------------------------------------------
+
+
+def pair_index(rotary_dim: int, neox: bool):
+    """(first, second) element index of each rotary pair.
+
+    NeoX pairs j with j + r/2; GPT-J pairs 2j with 2j + 1 ([RoPE] the
+    is_neox_style branch).
+    """
+    half = rotary_dim // 2
+    j = np.arange(half)
+    if neox:
+        return j, j + half
+    return 2 * j, 2 * j + 1
+
+
+def rope_apply(x: np.ndarray, positions: np.ndarray, table: np.ndarray, rotary_dim: int, neox: bool) -> np.ndarray:
+    """Rotate the leading r dims of x[..., d] by the table row of each position.
+
+    x has shape [N, ..., d]; positions has shape [N].  For each pair (a, c):
+    (a cos - c sin, c cos + a sin); dims r..d-1 pass through unchanged.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    half = rotary_dim // 2
+    rows = table[np.asarray(positions, dtype=np.int64)]
+    cos = rows[:, :half]
+    sin = rows[:, half:]
+    extra = x.ndim - 2
+    cos = cos.reshape(cos.shape[0], *([1] * extra), half)
+    sin = sin.reshape(sin.shape[0], *([1] * extra), half)
+    i1, i2 = pair_index(rotary_dim, neox)
+    out = x.copy()
+    a = x[..., i1]
+    c = x[..., i2]
+    out[..., i1] = a * cos - c * sin
+    out[..., i2] = c * cos + a * sin
+    return out
+
+
+def rotate_by_angle(x: np.ndarray, angles: np.ndarray, rotary_dim: int, neox: bool, gain: float = 1.0) -> np.ndarray:
+    """Rotate each pair i of rows x[n, d] by angles[n, i] and multiply the pair by `gain`."""
+    x = np.asarray(x, dtype=np.float64)
+    i1, i2 = pair_index(rotary_dim, neox)
+    c, s = np.cos(angles), np.sin(angles)
+    out = x.copy()
+    a = x[..., i1]
+    b = x[..., i2]
+    out[..., i1] = (a * c - b * s) * gain
+    out[..., i2] = (b * c + a * s) * gain
+    return out
+
+
+# --------------------------------------------------------------------------
+# Visible set   ([SINK] "可见集合与容量定义" and the C=6, S=2, T=10 table)
+# --------------------------------------------------------------------------
+
+
+def visible_positions(p: int, sinks: int, window: int) -> list[int]:
+    """Logical positions visible to the query at absolute position p.
+
+    sinks S, recent window W = C - S counting the current token.  A key j <= p
+    is visible iff j < S or p - j < W.  window == 0 means full causal attention.
+    """
+    if window == 0:
+        return list(range(p + 1))
+    return [j for j in range(p + 1) if j < sinks or p - j < window]
+
+
+# --------------------------------------------------------------------------
+# Quantisers (integer decisions taken in float32, as the kernels take them)
+# --------------------------------------------------------------------------
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (nearest, ties to even) via float32; returns float64 values."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = (u + 0x7FFF + lsb) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def round_f16(x: np.ndarray) -> np.ndarray:
+    """Round to IEEE half (nearest, ties to even); returns float64 values."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def quant_int8_rows(x: np.ndarray):
+    """Per-row symmetric int8: scale = max|x| / 127, code = clamp(rne(x / scale), -127, 127).
+
+    Decided in float32 (the row is rounded to float32 first).  An all-zero row
+    gets scale 0 and codes 0.  Returns (codes int8 [..., d], scale float32 [...]).
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint((x32 / safe[..., None]).astype(np.float32))
+    q = np.clip(q, -127, 127)
+    q = np.where(scale[..., None] > 0, q, 0)
+    return q.astype(np.int8), scale
+
+
+def dequant_int8_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    return codes.astype(np.float64) * scale.astype(np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------
+# Ring-buffer state   ([GOSS] "Windowed layers — ring buffer", "5.2 append", "5.3 get")
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class RingSeq:
+    """One sequence of a sink + ring cache: S sink slots then a W-slot ring.
+
+    Slot p holds the sink token at position p < S; non-sink tokens go to ring
+    index `head` (slot S + head).  seq_len counts tokens appended so far.
+    """
+
+    sinks: int
+    window: int
+    head: int = 0
+    count: int = 0
+    seq_len: int = 0
+    slot_pos: dict = field(default_factory=dict)  # slot -> position held (for tests)
+
+    def append(self, n_new: int) -> dict:
+        """Append positions seq_len .. seq_len+n_new-1; return {position: slot} of the writes kept.
+
+        A chunk holding k >= W non-sink tokens written into an empty ring
+        keeps its last W tokens in order and sets head 0, count W (the first
+        prompt write).  Otherwise each non-sink token is written at head, head
+        advances mod W and count saturates at W; only the last write to a slot
+        survives.
+        """
+        S, W = self.sinks, self.window
+        start = self.seq_len
+        positions = list(range(start, start + n_new))
+        writes: dict[int, int] = {}
+        nonsink = []
+        for p in positions:
+            if p < S:
+                writes[p] = p
+            else:
+                nonsink.append(p)
+        k = len(nonsink)
+        if k > 0 and self.count == 0 and k >= W:
+            for i, p in enumerate(nonsink[-W:]):
+                writes[p] = S + i
+            self.head = 0
+            self.count = W
+        else:
+            for p in nonsink:
+                writes[p] = S + self.head
+                self.head = (self.head + 1) % W
+                self.count = min(W, self.count + 1)
+        # drop writes overwritten later in the same chunk
+        last_for_slot = {}
+        for p in positions:
+            if p in writes:
+                last_for_slot[writes[p]] = p
+        kept = {p: s for s, p in last_for_slot.items()}
+        for s, p in last_for_slot.items():
+            self.slot_pos[s] = p
+        self.seq_len = start + n_new
+        return kept
+
+    def chronological_slots(self) -> list[int]:
+        """Sinks in order, then the ring from its oldest entry: (head - count) mod W onward."""
+        S, W = self.sinks, self.window
+        sinks = list(range(min(S, self.seq_len)))
+        first = (self.head - self.count) % W
+        ring = [S + (first + j) % W for j in range(self.count)]
+        return sinks + ring
+
+
+# --------------------------------------------------------------------------
+# Paged state   ([RoPE] the SlidingWindowSpec bound, the null-block freeing loop
+#               and the window edge; [VLLM] block tables of 16-token blocks)
+# --------------------------------------------------------------------------
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def sliding_window_max_blocks(window: int, block_size: int, extra: int = 0, in_flight: int = 0,
+                              max_model_len: int | None = None) -> int:
+    """Block bound of a windowed layer: cdiv(W - 1 + extra + in_flight, bs) + 1."""
+    num_tokens = window - 1 + extra + in_flight
+    if max_model_len is not None:
+        num_tokens = min(num_tokens, max_model_len)
+    return cdiv(num_tokens, block_size) + 1
+
+
+def paged_slot(block_table_row, p: int, block_size: int) -> tuple[int, int]:
+    """(physical block, offset) of logical position p: table[p // bs], p % bs."""
+    return int(block_table_row[p // block_size]), p % block_size
+
+
+def paged_free_expired(block_table_row: list[int], n_before: int, sinks: int, window: int,
+                       block_size: int) -> list[int]:
+    """Null the blocks that no present or future query can see; return freed ids.
+
+    The edge is e = max(0, n_before - W + 1) with n_before the tokens cached
+    before the call, so the call's first query (at position n_before) keeps
+    its whole window.  Blocks wholly below e that hold no sink are replaced by
+    -1, scanning backwards and stopping at the first null already present;
+    freed ids come out in that (descending) order.  W == 0 frees nothing.
+    """
+    if window == 0:
+        return []
+    edge = max(0, n_before - window + 1)
+    last_block = min(edge // block_size, len(block_table_row))
+    first_block = cdiv(sinks, block_size)
+    freed = []
+    for j in range(last_block - 1, first_block - 1, -1):
+        if block_table_row[j] == -1:
+            break
+        freed.append(block_table_row[j])
+        block_table_row[j] = -1
+    return freed
+
+
+# --------------------------------------------------------------------------
+# Attention   ([SINK] the runnable experiment; [GOSS] 4.4 GQA and 5.5 mask alignment)
+# --------------------------------------------------------------------------
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(q . K^T * scale) V for one query vector over the rows of K, V (float64)."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    s = (K @ q) * scale
+    s = s - np.max(s)
+    w = np.exp(s)
+    w = w / np.sum(w)
+    return w @ V
+
+
+def decode_attention(q: np.ndarray, k_by_pos, v_by_pos, n: int, sinks: int, window: int,
+                     n_kv_heads: int, scale: float | None = None) -> np.ndarray:
+    """Decode output for one sequence: q [Hq, d] at position n-1 over the visible keys.
+
+    k_by_pos(j) / v_by_pos(j) return the [Hkv, d] key / value rows at logical
+    position j.  Query head h reads KV head h // (Hq / Hkv) (repeat-free GQA).
+    """
+    Hq, d = q.shape
+    n_rep = Hq // n_kv_heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    vis = visible_positions(n - 1, sinks, window)
+    K = np.stack([np.asarray(k_by_pos(j), dtype=np.float64) for j in vis])  # [nv, Hkv, d]
+    V = np.stack([np.asarray(v_by_pos(j), dtype=np.float64) for j in vis])
+    out = np.empty((Hq, d), dtype=np.float64)
+    for h in range(Hq):
+        g = h // n_rep
+        out[h] = attend(q[h], K[:, g, :], V[:, g, :], scale)
+    return out
+
+
+def prefill_attention(q: np.ndarray, k_by_pos, v_by_pos, pos0: int, sinks: int, window: int,
+                      n_kv_heads: int, scale: float | None = None) -> np.ndarray:
+    """Chunk of T queries at positions pos0 .. pos0+T-1; q [T, Hq, d].
+
+    Query t sits at absolute position pos0 + t (the idx_q = arange(T_q) + (T_k - T_q)
+    alignment of [GOSS] 5.5) and sees visible_positions(pos0 + t).
+    """
+    T, Hq, d = q.shape
+    out = np.empty((T, Hq, d), dtype=np.float64)
+    for t in range(T):
+        out[t] = decode_attention(q[t], k_by_pos, v_by_pos, pos0 + t + 1, sinks, window, n_kv_heads, scale)
+    return out
+
+
+def dense_sink_attention(q, k, v, capacity: int, sinks: int):
+    """Dense masked form over a whole sequence: q, k, v [t, d] (the [SINK] experiment's dense path).
+
+    The mask comes from the capacity form: query p sees all of 0..p while
+    p < C, else the S sinks and the last C - S positions.
+    """
+    t, d = q.shape
+    scores = (q @ k.T) / math.sqrt(d)
+    mask = np.zeros((t, t), dtype=bool)
+    for p in range(t):
+        if p < capacity:
+            mask[p, : p + 1] = True
+        else:
+            recent = capacity - sinks
+            mask[p, :sinks] = True
+            mask[p, max(sinks, p - recent + 1): p + 1] = True
+    scores = np.where(mask, scores, -np.inf)
+    scores = scores - scores.max(axis=1, keepdims=True)
+    w = np.exp(scores)
+    w = w / w.sum(axis=1, keepdims=True)
+    return w @ v, mask
+
+
+def full_causal_attention(q, k, v):
+    t, d = q.shape
+    scores = (q @ k.T) / math.sqrt(d)
+    mask = np.tril(np.ones((t, t), dtype=bool))
+    scores = np.where(mask, scores, -np.inf)
+    scores = scores - scores.max(axis=1, keepdims=True)
+    w = np.exp(scores)
+    return (w / w.sum(axis=1, keepdims=True)) @ v
+
+
+# --------------------------------------------------------------------------
+# Re-rotation of cached keys   ([DYN] "What it does": the cached keys follow a
+# change; [SINK] R_a R_b = R_{a+b})
+# --------------------------------------------------------------------------
+
+
+def rerotate_rows(k_rot: np.ndarray, positions: np.ndarray, cfg_from: RopeCfg, cfg_to: RopeCfg) -> np.ndarray:
+    """Turn keys rotated under cfg_from into keys rotated under cfg_to.
+
+    Each pair i of the row at position p rotates by p (w_to,i - w_from,i) and
+    is scaled by mscale_to / mscale_from; dims r..d-1 are untouched.
+    k_rot has shape [N, d] (or [N, ..., d]), positions [N].
+    """
+    w_a = inv_freq(cfg_from)
+    w_b = inv_freq(cfg_to)
+    p = np.asarray(positions, dtype=np.float64)
+    ang = np.outer(p, w_b - w_a)
+    k_rot = np.asarray(k_rot, dtype=np.float64)
+    extra = k_rot.ndim - 2
+    ang = ang.reshape(ang.shape[0], *([1] * extra), ang.shape[1])
+    gain = mscale(cfg_to) / mscale(cfg_from)
+    return rotate_by_angle(k_rot, ang, cfg_to.rotary_dim, cfg_to.neox, gain)
+
+
+def rerotate_int8_rows(codes: np.ndarray, scale: np.ndarray, positions: np.ndarray,
+                       cfg_from: RopeCfg, cfg_to: RopeCfg):
+    """int8 rows: dequantise, turn as rerotate_rows, requantise the whole row."""
+    x = dequant_int8_rows(codes, scale)
+    y = rerotate_rows(x, positions, cfg_from, cfg_to)
+    return quant_int8_rows(y)
+
+
+# --------------------------------------------------------------------------
+# The dynamic factor policy   ([DYN] "What it does": the factor)
+# --------------------------------------------------------------------------
+
+
+def dynamic_factor(length: int, trained: int, step: float = 0.125, cap: float = 2.0) -> float:
+    """None (1.0) inside the trained range; above it length / trained rounded up to `step`, capped."""
+    if length <= trained:
+        return 1.0
+    f = math.ceil((length / trained) / step) * step
+    return min(f, cap)
