@@ -1,0 +1,213 @@
+/*
+ * ropekv.h - C ABI of libropekv.so: rotary position embedding (RoPE / YaRN)
+ * fused with a sink + sliding-window KV cache, the decode and prefill
+ * attention that read only the visible set, and re-rotation of cached keys
+ * when the YaRN factor changes.  gfx950 (MI355X) only.
+ *
+ * Sources, cited by page title and section:
+ *   [RoPE] "RoPE, scaling, sliding window, attention sinks" (mlinterviewnotes)
+ *   [GOSS] "Inference & 128K Long Context" (GPT-OSS-Lite docs)
+ *   [DYN]  "#2961 rope: --rope-scaling dynamic" (strata pull request)
+ *   [SINK] "Attention Sink 与 Streaming KV Cache" (llm-glossary)
+ *   [VLLM] "vLLM, from the inside out"
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev or documented as "device" point to device memory
+ *     the caller allocated (e.g. with torch); the library never allocates,
+ *     frees or keeps device memory, and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream).  No call synchronises the host.
+ *   - Arguments are validated on the host before any launch; a failing check
+ *     returns a negative ROPEKV_E* code, launches nothing, and leaves a
+ *     message for ropekv_last_error() (thread-local).
+ *   - Conditions that only device data can show (a position outside the
+ *     table, a non-consecutive position, a null block where a key must be
+ *     written or read) are reported by OR-ing ROPEKV_DEV_* bits into the
+ *     cache's err_word; the offending token / tile is skipped, never read or
+ *     written out of bounds.
+ */
+#ifndef ROPEKV_H
+#define ROPEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ropekv_stream_t; /* a hipStream_t */
+
+/* return codes */
+#define ROPEKV_OK 0
+#define ROPEKV_EINVAL (-1)    /* bad size / shape / geometry argument */
+#define ROPEKV_EDTYPE (-2)    /* unsupported dtype combination */
+#define ROPEKV_ERANGE (-3)    /* a size exceeds what the call supports (table, head_dim...) */
+#define ROPEKV_ELAYOUT (-4)   /* cache layout not supported by this call */
+#define ROPEKV_ENOSPACE (-5)  /* workspace or output buffer too small */
+#define ROPEKV_EHIP (-6)      /* a HIP runtime call failed */
+
+/* element types */
+#define ROPEKV_F32 0
+#define ROPEKV_BF16 1
+#define ROPEKV_F16 2
+#define ROPEKV_I8 3
+
+/* cache layouts */
+#define ROPEKV_RING 0   /* [batch, Hkv, C, d]: slots 0..S-1 sinks, S..C-1 a W-slot ring */
+#define ROPEKV_PAGED 1  /* pool [num_blocks, Hkv, block_size, d] + block table [batch, max_blocks] */
+#define ROPEKV_CONTIG 2 /* [T, Hkv, d] per layer (layers back to back), row t = position pos0 + t */
+
+/* device error bits OR-ed into err_word */
+#define ROPEKV_DEV_TABLE_RANGE 1  /* a position < 0 or >= table_len */
+#define ROPEKV_DEV_POSITION 2     /* a token is not at its sequence's next position */
+#define ROPEKV_DEV_NULL_BLOCK 4   /* a needed block-table entry is -1 or >= num_blocks */
+#define ROPEKV_DEV_BLOCK_RANGE 8  /* position / block_size >= max_blocks, or CONTIG row out of range */
+#define ROPEKV_DEV_SEQ_RANGE 16   /* a sequence id outside [0, batch) */
+#define ROPEKV_DEV_PREFIX_LOST 32 /* prefill needs a prefix key the ring no longer holds */
+#define ROPEKV_DEV_FREE_OVERFLOW 64 /* freed-block list capacity exceeded (nothing freed) */
+
+/* Rope parameters, in the notation of [RoPE] ("YaRN, precisely"):
+ * omega_i = 1 / b^(2i/r) for pair i < r/2; with s > 1 the YaRN blend of the
+ * extrapolated and the interpolated (divided by s) frequencies over the
+ * correction band of beta_fast / beta_slow rotations within L0, and the
+ * table scaled by mscale = 0.1 ln s + 1.  s <= 1 is plain RoPE. */
+typedef struct {
+  int32_t head_dim;     /* d_h */
+  int32_t rotary_dim;   /* r: even, 2 <= r <= d_h; dims r..d_h-1 are never touched */
+  int32_t neox;         /* 1: pairs (i, i + r/2); 0: GPT-J pairs (2i, 2i+1) ([RoPE] pairing note) */
+  int32_t orig_max_pos; /* L0, the trained context */
+  double rope_theta;    /* b */
+  double yarn_factor;   /* s */
+  double beta_fast;     /* 32 */
+  double beta_slow;     /* 1 */
+  double extrapolation_factor; /* 1 */
+} ropekv_rope_cfg;
+
+/* One layer's KV cache.  All pointers are device pointers.
+ * Visible set of the query at position p ([SINK] visible-set definition):
+ * key j <= p is visible iff j < sinks or p - j < window; window 0 = full
+ * attention (PAGED only).  For RING, capacity C = sinks + window. */
+typedef struct {
+  int32_t layout;       /* ROPEKV_RING / _PAGED / _CONTIG */
+  int32_t kv_dtype;     /* RING, PAGED: F32 / BF16 / F16 (K and V); CONTIG: F32 / BF16 / F16 / I8 (K) */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* d: 64 or 128 for attention; any even size <= 512 for append / rerotate */
+  int32_t batch;        /* sequences (RING, PAGED) */
+  int32_t capacity;     /* RING: C slots per sequence and head; CONTIG: T rows per layer */
+  int32_t sinks;        /* S */
+  int32_t window;       /* W recent positions including the current one */
+  int32_t block_size;   /* PAGED: tokens per block (16) */
+  int32_t max_blocks;   /* PAGED: row length of block_table */
+  int32_t num_blocks;   /* PAGED: blocks in the pool */
+  int32_t pos0;         /* CONTIG: position of row 0 */
+  void *k;              /* keys (rotated), layout as above */
+  void *v;              /* values (never rotated); NULL allowed for CONTIG */
+  float *k_scale;       /* CONTIG I8: per-row fp32 scale [T, Hkv] per layer */
+  int32_t *ring_head;   /* RING [batch]: next ring index to write */
+  int32_t *ring_count;  /* RING [batch]: valid ring entries (<= W) */
+  int32_t *block_table; /* PAGED [batch, max_blocks]: physical block ids, -1 = null */
+  int32_t *seq_len;     /* RING, PAGED [batch]: tokens appended so far (= next position) */
+  int32_t *err_word;    /* [1]: ROPEKV_DEV_* bits, OR-ed by kernels; caller clears */
+} ropekv_kv_cache;
+
+/* Build the cos/sin table ([RoPE] _compute_cos_sin_cache, YaRN variant):
+ * cos_sin[m][i] = mu cos(m w_i), cos_sin[m][r/2 + i] = mu sin(m w_i) for
+ * m < max_pos, i < r/2, angles and trig in fp64, one rounding to fp32.
+ * cos_sin: device fp32 [max_pos, r], written in place (pointer-stable, so a
+ * rebuild at a new factor keeps graphs that captured it valid, [DYN] "The
+ * table").  mscale_dev: optional device float receiving mu.  Each cell is
+ * computed independently: the result does not depend on the launch shape. */
+int ropekv_build_table(const ropekv_rope_cfg *cfg, int32_t max_pos, float *cos_sin,
+                       float *mscale_dev, ropekv_stream_t stream);
+
+/* Rotate q and k in place and write the rotated k and the raw v into the
+ * cache ([RoPE] "Where the positions come from" and the attention block:
+ * positions and slots from one counter, rotate Q and K never V, the cache
+ * stores keys-at-a-position; [GOSS] 4.8 rotate once at append).
+ *   q   [n_tokens, n_q_heads, d] act_dtype, rotated in place; NULL iff n_q_heads == 0
+ *   k   [n_tokens, Hkv, d] act_dtype, rotated in place
+ *   v   [n_tokens, Hkv, d] act_dtype; copied unrotated (NULL only for a CONTIG cache with v == NULL)
+ *   positions [n_tokens] int32 absolute positions, < table_len
+ *   seq_ids   [n_tokens] int32 sequence of each token (RING, PAGED; ignored for CONTIG)
+ * act_dtype: F32 / BF16 / F16.  RING and PAGED need kv_dtype == act_dtype.
+ * Each sequence appears as one run of consecutive positions starting at its
+ * seq_len; seq_len advances by the run length.
+ * RING ([GOSS] ring buffer, 5.2 append): sinks p < S go to slot p; a chunk of
+ *   k >= W non-sink tokens into an empty ring keeps its last W in order with
+ *   head 0, count W; otherwise head advances per token mod W and count
+ *   saturates at W.  Only the surviving (last) write to a slot is made.
+ * PAGED ([RoPE] block bound and null-block freeing; [VLLM] block tables):
+ *   slot = table[p / bs] * bs + p % bs, the block must be allocated (>= 0).
+ *   Before the writes, blocks wholly below the edge e = max(0, seq_len - W + 1)
+ *   that hold no sink are set to -1 (backward scan stopping at the first null)
+ *   and their ids appended to freed_blocks (device int32 [freed_capacity]),
+ *   counted in *n_freed (device int32, caller zeroes it).  freed_blocks NULL:
+ *   nothing is freed.
+ * CONTIG: row t = p - pos0; F16 stores the rotated row rounded to nearest;
+ *   I8 stores per-row codes rne(x / scale) with scale = max|x| / 127. */
+int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_t table_len,
+                        void *q, int32_t n_q_heads, void *k, const void *v, int32_t act_dtype,
+                        int32_t n_tokens, const int32_t *positions, const int32_t *seq_ids,
+                        const ropekv_kv_cache *cache, int32_t *freed_blocks,
+                        int32_t freed_capacity, int32_t *n_freed, ropekv_stream_t stream);
+
+/* Bytes of fp32 workspace ropekv_decode_attn needs for this batch and cache
+ * (split-K partials [batch, Hkv, splits, n_rep, d + 2]).  0 on bad input. */
+size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const ropekv_kv_cache *cache);
+
+/* Decode attention ([SINK] the incremental path; [GOSS] 4.3 decode, 4.4 GQA):
+ * for each sequence b with n = seq_len[b] > 0 tokens and query head h,
+ * out[b][h] = softmax(q[b][h] . K_j * scale) V_j over the keys j visible to
+ * position n - 1, with K / V of KV head h / (n_q_heads / Hkv).  The keys are
+ * read in place (no gather, no repeat of KV heads).  Split-K partials go to
+ * ws; a second launch combines them.  n == 0 gives a zero row.
+ *   q   [batch, n_q_heads, d] kv_dtype (rotated), out same shape and dtype
+ *   scale: 0 means 1/sqrt(d)
+ * Layouts RING and PAGED; kv_dtype F32 or BF16; d 64 or 128; n_q_heads a
+ * multiple of Hkv with n_rep <= 16. */
+int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
+                       const ropekv_kv_cache *cache, float scale, void *out, void *ws,
+                       size_t ws_bytes, ropekv_stream_t stream);
+
+/* Prefill attention for one sequence's chunk ([GOSS] 5.5 mask alignment):
+ * queries t < T at positions pos0 + t see keys j <= pos0 + t with j < S or
+ * pos0 + t - j < W (W from the cache; 0 = causal).  Keys at positions
+ * >= pos0 come from the chunk's own k, v ([T, Hkv, d], rotated); keys below
+ * pos0 from the cache (RING or PAGED) of sequence seq_id.  For RING the
+ * prefix must still be in the ring (call before appending the chunk, or keep
+ * pos0 + T <= C); a missing key sets ROPEKV_DEV_PREFIX_LOST.
+ *   q [T, n_q_heads, d], out same; dtype = kv_dtype (F32 or BF16), d 64 or 128.
+ * bf16 runs on MFMA with fp32 accumulation; tiles no query can see are skipped. */
+int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, int32_t pos0,
+                        int32_t n_q_heads, const ropekv_kv_cache *cache, int32_t seq_id,
+                        float scale, void *out, ropekv_stream_t stream);
+
+/* Re-rotate cached keys from `from` to `to` in place ([DYN] "What it does":
+ * the cached keys follow a change; [SINK] R_a R_b = R_{a+b}): every pair i of
+ * the row at position p turns by p (w_to,i - w_from,i) and is scaled by
+ * mscale_to / mscale_from; dims r..d-1 are untouched (bitwise for F16/BF16/F32).
+ * I8 rows are dequantised, turned and requantised with a new per-row scale.
+ * cache: CONTIG, kv_dtype F16 / BF16 / F32 / I8, n_layers layers back to back.
+ * Angles and their reduction in fp64, the rotation in fp32.
+ * from / to must agree on head_dim, rotary_dim and neox. */
+int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to,
+                    const ropekv_kv_cache *cache, int32_t n_layers, ropekv_stream_t stream);
+
+/* Test-facing: the visible logical positions of sequence seq's next query
+ * (position seq_len - 1) and the element offset of each key row in the
+ * cache's k buffer, in chronological order, as the attention kernels address
+ * them.  positions_out / offsets_out: device int32 / int64 [max_out];
+ * n_out: device int32 receiving the count (entries beyond max_out dropped). */
+int ropekv_visible_slots(const ropekv_kv_cache *cache, int32_t seq, int32_t *positions_out,
+                         int64_t *offsets_out, int32_t max_out, int32_t *n_out,
+                         ropekv_stream_t stream);
+
+/* The message of the last failing call on this thread ("" if none). */
+const char *ropekv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPEKV_H */

@@ -1,0 +1,268 @@
+// Fused RoPE apply + KV append.
+//
+// "RoPE, scaling, sliding window, attention sinks" (the attention block and
+// "Where the positions come from"): rotate q and k in place by the table row
+// of the token's position, never v, and write the rotated k with the raw v
+// to the cache slot derived from the same position.  Ring rules from
+// "Inference & 128K Long Context" (ring buffer; 5.2 append); paged freeing
+// from the null-block loop and window edge of the first page.
+//
+// Launch 1 (one workgroup per token) rotates and writes; it reads the cache
+// state (seq_len, ring head/count) as it stood before the call.  Launch 2
+// (one thread per token) lets the last token of each sequence's run advance
+// that state and free expired blocks, so no thread reads state another one
+// is changing.
+#include "kernels.hpp"
+
+namespace ropekv {
+
+// 0 if token t (position p of sequence seq, whose cache held nb tokens) is in
+// a run of consecutive positions that starts at nb; else an error bit.
+__device__ inline int token_check(const AppendArgs &a, int t, int p, int seq, int nb) {
+  const int off = p - nb;
+  if (off < 0 || off > t) return ROPEKV_DEV_POSITION;
+  const int t0 = t - off;
+  if (a.seq[t0] != seq || a.pos[t0] != nb) return ROPEKV_DEV_POSITION;
+  if (t0 > 0 && a.seq[t0 - 1] == seq) return ROPEKV_DEV_POSITION;
+  if (t > t0 && (a.seq[t - 1] != seq || a.pos[t - 1] != p - 1)) return ROPEKV_DEV_POSITION;
+  return 0;
+}
+
+// Index of the last token of t's run (binary search; runs are consecutive).
+__device__ inline int run_last(const AppendArgs &a, int t, int p, int seq) {
+  int lo = t, hi = a.n_tokens;
+  while (hi - lo > 1) {
+    const int mid = lo + ((hi - lo) >> 1);
+    if (a.seq[mid] == seq && a.pos[mid] == p + (mid - t))
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int mod_pos(long x, int m) {
+  long r = x % m;
+  return (int)(r < 0 ? r + m : r);
+}
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  __shared__ float rowbuf[4][512];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const ropekv_kv_cache &c = a.c;
+  const int p = a.pos[t];
+  if (p < 0 || p >= a.table_len) {
+    if (threadIdx.x == 0) dev_error(c.err_word, ROPEKV_DEV_TABLE_RANGE);
+    return;
+  }
+  const int d = a.head_dim;
+  const int Hkv = c.num_kv_heads;
+  int err = 0;
+  bool write = true;
+  long base = 0, hstride = 0, scale_base = 0;
+  if (c.layout == ROPEKV_CONTIG) {
+    const long row = (long)p - c.pos0;
+    if (row < 0 || row >= c.capacity) {
+      write = false;
+      err = ROPEKV_DEV_BLOCK_RANGE;
+    } else {
+      base = row * Hkv * d;
+      hstride = d;
+      scale_base = row * Hkv;
+    }
+  } else {
+    const int seq = a.seq[t];
+    if (seq < 0 || seq >= c.batch) {
+      write = false;
+      err = ROPEKV_DEV_SEQ_RANGE;
+    } else {
+      const int nb = c.seq_len[seq];
+      err = token_check(a, t, p, seq, nb);
+      if (err) {
+        write = false;
+      } else if (c.layout == ROPEKV_RING) {
+        const int S = c.sinks, W = c.window, C = c.capacity;
+        int slot = -1;
+        if (p < S) {
+          slot = p;
+        } else {
+          const int n_after = p + (run_last(a, t, p, seq) - t) + 1;
+          const int hb = mod_pos(c.ring_head[seq], W);
+          const int cb = c.ring_count[seq];
+          const int first = nb > S ? nb : S;  // first non-sink position of this run
+          const int kprime = n_after - first;
+          if (p >= n_after - W) {  // survives the chunk
+            if (cb == 0 && kprime >= W)
+              slot = S + (p - (n_after - W));
+            else
+              slot = S + mod_pos((long)hb + (p - first), W);
+          }
+        }
+        if (slot < 0) {
+          write = false;
+        } else {
+          base = ((long)seq * Hkv * C + slot) * d;
+          hstride = (long)C * d;
+        }
+      } else {  // PAGED
+        const int bs = c.block_size;
+        const int blk = p / bs;
+        if (blk >= c.max_blocks) {
+          write = false;
+          err = ROPEKV_DEV_BLOCK_RANGE;
+        } else {
+          const int bid = c.block_table[(long)seq * c.max_blocks + blk];
+          if (bid < 0 || bid >= c.num_blocks) {
+            write = false;
+            err = ROPEKV_DEV_NULL_BLOCK;
+          } else {
+            base = ((long)bid * Hkv * bs + (p % bs)) * d;
+            hstride = (long)bs * d;
+          }
+        }
+      }
+    }
+  }
+  if (err && threadIdx.x == 0) dev_error(c.err_word, err);
+
+  const int r = a.rotary_dim;
+  const int half = r >> 1;
+  const float *trow = a.table + (long)p * r;
+  const int nq = a.n_q_heads;
+  const int act = a.act;
+  const int kvdt = c.kv_dtype;
+  const int n_rows = nq + 2 * Hkv;
+  for (int row = wave; row < n_rows; row += 4) {
+    if (row < nq + Hkv) {
+      const bool is_k = row >= nq;
+      const int h = is_k ? row - nq : row;
+      void *x = is_k ? a.k : a.q;
+      const long xoff = ((long)t * (is_k ? Hkv : nq) + h) * d;
+      const bool to_cache = is_k && write;
+      const long coff = base + (long)h * hstride;
+      for (int j = lane; j < half; j += 64) {
+        const int i1 = a.neox ? j : 2 * j;
+        const int i2 = a.neox ? j + half : 2 * j + 1;
+        const float x1 = load_elem(x, xoff + i1, act);
+        const float x2 = load_elem(x, xoff + i2, act);
+        const float cs = trow[j];
+        const float sn = trow[half + j];
+        const float o1 = x1 * cs - x2 * sn;
+        const float o2 = x2 * cs + x1 * sn;
+        store_elem(x, xoff + i1, act, o1);
+        store_elem(x, xoff + i2, act, o2);
+        if (to_cache) {
+          if (kvdt == ROPEKV_I8) {
+            rowbuf[wave][i1] = o1;
+            rowbuf[wave][i2] = o2;
+          } else {
+            store_elem(c.k, coff + i1, kvdt, o1);
+            store_elem(c.k, coff + i2, kvdt, o2);
+          }
+        }
+      }
+      if (to_cache) {
+        for (int e = r + lane; e < d; e += 64) {
+          const float val = load_elem(x, xoff + e, act);
+          if (kvdt == ROPEKV_I8)
+            rowbuf[wave][e] = val;
+          else
+            store_elem(c.k, coff + e, kvdt, val);
+        }
+        if (kvdt == ROPEKV_I8) {
+          // per-row symmetric int8: scale = max|x| / 127, code = rne(x / scale)
+          wave_lds_sync();
+          float amax = 0.f;
+          for (int e = lane; e < d; e += 64) amax = fmaxf(amax, fabsf(rowbuf[wave][e]));
+          for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);
+          const float scale = amax / 127.0f;
+          int8_t *kc = (int8_t *)c.k;
+          for (int e = lane; e < d; e += 64) {
+            float qv = 0.f;
+            if (scale > 0.f) qv = fminf(fmaxf(rintf(rowbuf[wave][e] / scale), -127.f), 127.f);
+            kc[coff + e] = (int8_t)qv;
+          }
+          if (lane == 0) c.k_scale[scale_base + h] = scale;
+          wave_lds_sync();
+        }
+      }
+    } else {
+      const int h = row - nq - Hkv;
+      if (write && a.v != nullptr && c.v != nullptr) {
+        const long voff = ((long)t * Hkv + h) * d;
+        const long coff = base + (long)h * hstride;
+        for (int e = lane; e < d; e += 64) store_elem(c.v, coff + e, kvdt, load_elem(a.v, voff + e, act));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void append_state_kernel(AppendArgs a) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.n_tokens) return;
+  const ropekv_kv_cache &c = a.c;
+  const int p = a.pos[t];
+  const int seq = a.seq[t];
+  if (p < 0 || p >= a.table_len || seq < 0 || seq >= c.batch) return;
+  const bool last = (t == a.n_tokens - 1) || a.seq[t + 1] != seq || a.pos[t + 1] != p + 1;
+  if (!last) return;
+  const int nb = c.seq_len[seq];
+  if (token_check(a, t, p, seq, nb)) return;
+  const int na = p + 1;
+  if (c.layout == ROPEKV_RING) {
+    const int S = c.sinks, W = c.window;
+    const int first = nb > S ? nb : S;
+    const int kp = na - first;
+    if (kp > 0) {
+      const int hb = mod_pos(c.ring_head[seq], W);
+      const int cb = c.ring_count[seq];
+      if (cb == 0 && kp >= W) {
+        c.ring_head[seq] = 0;
+        c.ring_count[seq] = W;
+      } else {
+        c.ring_head[seq] = mod_pos((long)hb + kp, W);
+        c.ring_count[seq] = (cb + kp < W) ? cb + kp : W;
+      }
+    }
+  } else if (c.layout == ROPEKV_PAGED && c.window > 0 && a.freed != nullptr) {
+    const int bs = c.block_size;
+    const int e = nb - c.window + 1 > 0 ? nb - c.window + 1 : 0;
+    const int last_block = (e / bs < c.max_blocks) ? e / bs : c.max_blocks;
+    const int first_block = (c.sinks + bs - 1) / bs;
+    int32_t *row = c.block_table + (long)seq * c.max_blocks;
+    int cnt = 0;
+    for (int j = last_block - 1; j >= first_block; --j) {
+      if (row[j] == -1) break;
+      ++cnt;
+    }
+    if (cnt > 0) {
+      const int at = atomicAdd(a.n_freed, cnt);
+      if (at + cnt > a.freed_cap) {
+        dev_error(c.err_word, ROPEKV_DEV_FREE_OVERFLOW);
+      } else {
+        int j = last_block - 1;
+        for (int i = 0; i < cnt; ++i, --j) {
+          a.freed[at + i] = row[j];
+          row[j] = -1;
+        }
+      }
+    }
+  }
+  c.seq_len[seq] = na;
+}
+
+hipError_t launch_apply_append(const AppendArgs &a, hipStream_t s) {
+  if (a.n_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3(a.n_tokens), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.c.layout != ROPEKV_CONTIG) {
+    hipLaunchKernelGGL(append_state_kernel, dim3((a.n_tokens + 255) / 256), dim3(256), 0, s, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace ropekv

@@ -1,0 +1,112 @@
+// Device helpers shared by the ropekv HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ropekv.h"
+
+namespace ropekv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short8 __attribute__((ext_vector_type(8)));
+
+// bfloat16 / half stored as raw bits so the arithmetic is always fp32.
+struct bf16_t { uint16_t x; };
+struct f16_t { uint16_t x; };
+
+__device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f(uint16_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, h);
+  return (float)v;
+}
+// fp32 -> half, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t f_to_f16(float f) {
+  _Float16 v = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, v);
+}
+
+// element load/store by runtime dtype code (used off the hot loops)
+__device__ __forceinline__ float load_elem(const void *p, long i, int dt) {
+  switch (dt) {
+    case ROPEKV_F32: return ((const float *)p)[i];
+    case ROPEKV_BF16: return bf16_to_f(((const uint16_t *)p)[i]);
+    case ROPEKV_F16: return f16_to_f(((const uint16_t *)p)[i]);
+    default: return (float)((const int8_t *)p)[i];
+  }
+}
+__device__ __forceinline__ void store_elem(void *p, long i, int dt, float v) {
+  switch (dt) {
+    case ROPEKV_F32: ((float *)p)[i] = v; break;
+    case ROPEKV_BF16: ((uint16_t *)p)[i] = f_to_bf16(v); break;
+    case ROPEKV_F16: ((uint16_t *)p)[i] = f_to_f16(v); break;
+    default: break;
+  }
+}
+
+// Rope parameters as passed to kernels.
+struct RopeParams {
+  double theta, s, beta_fast, beta_slow, ef;
+  int rotary_dim, head_dim, neox, L0;
+};
+
+__host__ inline RopeParams make_rope_params(const ropekv_rope_cfg &c) {
+  RopeParams p;
+  p.theta = c.rope_theta;
+  p.s = c.yarn_factor;
+  p.beta_fast = c.beta_fast;
+  p.beta_slow = c.beta_slow;
+  p.ef = c.extrapolation_factor;
+  p.rotary_dim = c.rotary_dim;
+  p.head_dim = c.head_dim;
+  p.neox = c.neox;
+  p.L0 = c.orig_max_pos;
+  return p;
+}
+
+// Angular frequency of pair i, fp64 (YaRN blend when s > 1).
+__device__ inline double rope_omega(const RopeParams &p, int i) {
+  const double r = (double)p.rotary_dim;
+  const double pos_freq = pow(p.theta, (2.0 * (double)i) / r);
+  const double ext = 1.0 / pos_freq;
+  if (!(p.s > 1.0)) return ext;
+  const double interp = 1.0 / (p.s * pos_freq);
+  const double two_pi = 6.283185307179586476925286766559;
+  const double dlow = r * log((double)p.L0 / (p.beta_fast * two_pi)) / (2.0 * log(p.theta));
+  const double dhigh = r * log((double)p.L0 / (p.beta_slow * two_pi)) / (2.0 * log(p.theta));
+  double low = fmax(floor(dlow), 0.0);
+  double high = fmin(ceil(dhigh), r - 1.0);
+  if (low == high) high += 0.001;
+  double ramp = ((double)i - low) / (high - low);
+  ramp = fmin(fmax(ramp, 0.0), 1.0);
+  const double mask = (1.0 - ramp) * p.ef;
+  return interp * (1.0 - mask) + ext * mask;
+}
+
+__host__ __device__ inline double rope_mscale(double s) { return s > 1.0 ? 0.1 * log(s) + 1.0 : 1.0; }
+
+__device__ __forceinline__ void dev_error(int32_t *err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// Wait for this wave's LDS traffic and keep the compiler from moving memory
+// operations across the point: lanes of one wave may then read what other
+// lanes of the same wave wrote.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
+
+}  // namespace ropekv

@@ -1,0 +1,495 @@
+// Split-K decode attention over the sink + recent visible set.
+//
+// "Attention Sink 与 Streaming KV Cache" (visible set; the incremental cache
+// of the runnable experiment) and "Inference & 128K Long Context" (4.3 decode
+// is memory bound, 4.4 GQA): one query per sequence and query head attends
+// to the keys visible at position n - 1, reading the cache in place.  The
+// n_rep query heads of a KV head share every K/V byte loaded (repeat-free
+// GQA, h -> h / n_rep).
+//
+// Work unit: a "tile" = 16 consecutive cache rows (one 16-token paged block,
+// or 16 ring slots) of one KV head.  A workgroup (4 waves) owns a contiguous
+// run of tiles of one (sequence, KV head); each wave takes every 4th tile and
+// keeps its own online-softmax state; the waves are merged in LDS and one
+// fp32 partial (acc, m, l) per split goes to the workspace.  A second launch
+// merges the splits.
+//
+// Per tile and wave:  S^T[16 keys x 16 cols] = K . Q^T on MFMA (the n_rep
+// query heads fill the first columns, the rest are zero), scores scaled into
+// the log2 domain, masked, online softmax per query head; P and the
+// correction factors go through a small per-wave LDS slot to the layout in
+// which each lane holds 4 keys x (d/16) dims of V, and O += P V in fp32.
+#include <stdlib.h>
+
+#include "kernels.hpp"
+
+namespace ropekv {
+
+namespace {
+
+constexpr int kTile = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+
+// Tiles of one sequence and how a tile maps to cache rows.
+struct SeqTiles {
+  int n;       // tokens in the sequence (query at n - 1)
+  int ntiles;  // tiles to visit
+  int ns, rs;  // PAGED: positions < ns (sinks) and [rs, n) are visible
+  int nsb, fr; // PAGED: sink tiles are blocks 0..nsb-1; then blocks fr, fr+1, ...
+  int oldest, count;  // RING: valid ring indices are oldest .. oldest+count-1 (mod W)
+};
+
+__device__ __forceinline__ int imod(int x, int m) {
+  int r = x % m;
+  return r < 0 ? r + m : r;
+}
+
+__device__ inline SeqTiles seq_tiles(const ropekv_kv_cache &c, int b) {
+  SeqTiles st;
+  st.n = c.seq_len[b];
+  st.ntiles = 0;
+  st.ns = st.rs = st.nsb = st.fr = st.oldest = st.count = 0;
+  const int n = st.n;
+  if (n <= 0) return st;
+  if (c.layout == ROPEKV_PAGED) {
+    if (c.window == 0) {
+      st.ns = n;
+      st.rs = n;
+      st.nsb = (n + kTile - 1) / kTile;
+      st.fr = st.nsb;
+      st.ntiles = st.nsb;
+    } else {
+      const int ns = min(c.sinks, n);
+      const int rs = max(ns, n - c.window);
+      const int nsb = (ns + kTile - 1) / kTile;
+      const int fr = max(rs / kTile, nsb);
+      const int lastb = (n - 1) / kTile;
+      st.ns = ns;
+      st.rs = rs;
+      st.nsb = nsb;
+      st.fr = fr;
+      st.ntiles = nsb + max(0, lastb - fr + 1);
+    }
+  } else {  // RING
+    const int S = c.sinks, W = c.window, C = c.capacity;
+    const int cnt = min(max(c.ring_count[b], 0), W);
+    const int hb = imod(c.ring_head[b], W);
+    const int oldest = imod(hb - cnt, W);
+    const int limit = (cnt < W && oldest + cnt <= W) ? S + oldest + cnt : C;
+    st.ns = min(S, n);
+    st.oldest = oldest;
+    st.count = cnt;
+    st.ntiles = (limit + kTile - 1) / kTile;
+  }
+  return st;
+}
+
+// Row r (< 16) of tile `tile` for (b, g): element offset of the row in k/v
+// (clamped in bounds) and whether the key there is visible.
+struct TileRows {
+  long base;  // element offset of row 0 of the tile (PAGED) or of slot 0 of (b, g) (RING)
+  int slot0;  // RING: first slot of the tile
+  int pos0;   // PAGED: position of row 0
+  bool ok;    // the tile maps to allocated memory
+};
+
+__device__ __forceinline__ TileRows tile_rows(const ropekv_kv_cache &c, const SeqTiles &st, int b, int g,
+                                             int tile, int D) {
+  TileRows tr;
+  tr.ok = true;
+  tr.slot0 = 0;
+  tr.pos0 = 0;
+  if (c.layout == ROPEKV_PAGED) {
+    const int blk = tile < st.nsb ? tile : st.fr + (tile - st.nsb);
+    const int bid = (blk < c.max_blocks) ? c.block_table[(long)b * c.max_blocks + blk] : -1;
+    tr.pos0 = blk * kTile;
+    if (bid < 0 || bid >= c.num_blocks) {
+      tr.ok = false;
+      tr.base = 0;
+    } else {
+      tr.base = ((long)bid * c.num_kv_heads + g) * kTile * D;
+    }
+  } else {
+    tr.slot0 = tile * kTile;
+    tr.base = ((long)b * c.num_kv_heads + g) * (long)c.capacity * D;
+  }
+  return tr;
+}
+
+__device__ __forceinline__ long row_offset(const ropekv_kv_cache &c, const TileRows &tr, int r, int D) {
+  if (c.layout == ROPEKV_PAGED) return tr.base + (long)r * D;
+  const int slot = min(tr.slot0 + r, c.capacity - 1);
+  return tr.base + (long)slot * D;
+}
+
+__device__ __forceinline__ bool row_visible(const ropekv_kv_cache &c, const SeqTiles &st, const TileRows &tr,
+                                            int r) {
+  if (!tr.ok) return false;
+  if (c.layout == ROPEKV_PAGED) {
+    const int pos = tr.pos0 + r;
+    return pos < st.ns || (pos >= st.rs && pos < st.n);
+  }
+  const int slot = tr.slot0 + r;
+  if (slot >= c.capacity) return false;
+  if (slot < c.sinks) return slot < st.ns;
+  const int i = slot - c.sinks;
+  return imod(i - st.oldest, c.window) < st.count;
+}
+
+template <int NB>
+__device__ __forceinline__ void load_bytes(uint32_t *dst, const void *src) {
+  static_assert(NB % 8 == 0, "fragment size");
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const uint4 v = ((const uint4 *)src)[i];
+      dst[4 * i + 0] = v.x;
+      dst[4 * i + 1] = v.y;
+      dst[4 * i + 2] = v.z;
+      dst[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB / 8; ++i) {
+      const uint2 v = ((const uint2 *)src)[i];
+      dst[2 * i + 0] = v.x;
+      dst[2 * i + 1] = v.y;
+    }
+  }
+}
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<float> {
+  static constexpr int kBytes = 4;
+  static __device__ __forceinline__ float get(const uint32_t *w, int i) { return __uint_as_float(w[i]); }
+  static __device__ __forceinline__ void put(void *p, long i, float v) { ((float *)p)[i] = v; }
+};
+template <>
+struct ElemTraits<bf16_t> {
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ float get(const uint32_t *w, int i) {
+    const uint32_t x = w[i >> 1];
+    return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+  static __device__ __forceinline__ void put(void *p, long i, float v) { ((uint16_t *)p)[i] = f_to_bf16(v); }
+};
+
+// S^T (16 keys x 16 columns) += K (16 x D) . Q^T (D x 16), lane-distributed
+// as: kw / qw = the lane's quarter-row of K (row lane%16) / of Q (column
+// lane%16), elements [(D/4)(lane/16), (D/4)(lane/16 + 1)).  The reduction
+// over d is order-free, so lanes feed their quarter-rows to consecutive
+// MFMAs in the same element order on both sides.
+template <typename T, int D>
+__device__ __forceinline__ f32x4 qk_tile(const uint32_t *kw, const uint32_t *qw) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      short8 a, bq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[2 * e] = (short)(kw[4 * t + e] & 0xffff);
+        a[2 * e + 1] = (short)(kw[4 * t + e] >> 16);
+        bq[2 * e] = (short)(qw[4 * t + e] & 0xffff);
+        bq[2 * e + 1] = (short)(qw[4 * t + e] >> 16);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq),
+                                                    acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < D / 4; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[t]), __uint_as_float(qw[t]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+template <typename T, int D, int NREP>
+__global__ __launch_bounds__(256) void decode_split_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
+                                                           float sl2, float *__restrict__ ws, int tps, int splits) {
+  using TR = ElemTraits<T>;
+  constexpr int QB = (D / 4) * TR::kBytes;   // bytes of a lane's K / Q quarter-row
+  constexpr int E = D / 16;                  // V dims per lane per key
+  constexpr int VB = E * TR::kBytes;         // bytes of a lane's V piece per key
+  __shared__ float s_p[4][NREP][kTile];
+  __shared__ float s_corr[4][NREP];
+  __shared__ float s_m[4][NREP], s_l[4][NREP];
+  __shared__ float s_acc[4][NREP][D];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int Hkv = c.num_kv_heads;
+  const SeqTiles st = seq_tiles(c, b);
+  // a length the planned splits cannot cover (table too short for seq_len) is flagged, not read
+  if (split == splits - 1 && threadIdx.x == 0 && st.ntiles > splits * tps) dev_error(c.err_word, ROPEKV_DEV_BLOCK_RANGE);
+  const int t_begin = split * tps;
+  if (t_begin >= st.ntiles) return;
+  const int t_end = min(st.ntiles, t_begin + tps);
+
+  // Q^T fragment: column `col` = query head g * NREP + col (zero beyond NREP)
+  uint32_t qw[QB / 4];
+  if (col < NREP) {
+    const char *qrow = (const char *)qp + ((long)(b * Hkv * NREP + g * NREP + col) * D) * TR::kBytes;
+    load_bytes<QB>(qw, qrow + grp * QB);
+  } else {
+#pragma unroll
+    for (int i = 0; i < QB / 4; ++i) qw[i] = 0u;
+  }
+
+  float m_run = kNegBig, l_run = 0.f;
+  float acc[NREP][E];
+#pragma unroll
+  for (int h = 0; h < NREP; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+
+  const char *kbase = (const char *)c.k;
+  const char *vbase = (const char *)c.v;
+  bool bad_tile = false;
+
+  for (int tile = t_begin + wave; tile < t_end; tile += 4) {
+    const TileRows tr = tile_rows(c, st, b, g, tile, D);
+    if (!tr.ok) {
+      bad_tile = true;
+      continue;
+    }
+    uint32_t kw[QB / 4];
+    load_bytes<QB>(kw, kbase + row_offset(c, tr, col, D) * TR::kBytes + grp * QB);
+    uint32_t vw[4][VB / 4];
+    bool vis[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * grp + j;
+      vis[j] = row_visible(c, st, tr, r);
+      load_bytes<VB>(vw[j], vbase + row_offset(c, tr, r, D) * TR::kBytes + col * VB);
+    }
+    const f32x4 sacc = qk_tile<T, D>(kw, qw);
+    float s[4];
+    float mx = kNegBig;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[j] = vis[j] ? sacc[j] * sl2 : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = exp2f(m_run - m_new);
+    float psum = 0.f;
+    float pj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pj[j] = exp2f(s[j] - m_new);
+      psum += pj[j];
+    }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (col < NREP) {
+      *(float4 *)&s_p[wave][col][4 * grp] = make_float4(pj[0], pj[1], pj[2], pj[3]);
+      if (grp == 0) s_corr[wave][col] = corr;
+    }
+    wave_lds_sync();
+    // V layout: this lane holds keys 4*grp + j, dims [col*E, col*E + E)
+#pragma unroll
+    for (int h = 0; h < NREP; ++h) {
+      const float ch = s_corr[wave][h];
+      const float4 ph = *(const float4 *)&s_p[wave][h][4 * grp];
+      const float pv[4] = {ph.x, ph.y, ph.z, ph.w};
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float a = acc[h][e] * ch;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a += vis[j] ? pv[j] * TR::get(vw[j], e) : 0.f;
+        acc[h][e] = a;
+      }
+    }
+    wave_lds_sync();
+  }
+  if (bad_tile && lane == 0) dev_error(c.err_word, ROPEKV_DEV_NULL_BLOCK);
+
+  // merge the 4 lane groups of this wave (they share m per query head)
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int h = 0; h < NREP; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float a = acc[h][e];
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      acc[h][e] = a;
+    }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < NREP; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_acc[wave][h][col * E + e] = acc[h][e];
+    if (col < NREP) {
+      s_m[wave][col] = m_run;
+      s_l[wave][col] = l_run;
+    }
+  }
+  __syncthreads();
+  // merge the 4 waves and write this split's partial
+  const int nwaves = min(4, t_end - t_begin);
+  float *dst = ws + (((long)(b * Hkv + g) * splits + split) * NREP) * (D + 2);
+  for (int idx = threadIdx.x; idx < NREP * D; idx += 256) {
+    const int h = idx / D, dd = idx % D;
+    float m = kNegBig;
+    for (int w = 0; w < nwaves; ++w) m = fmaxf(m, s_m[w][h]);
+    float a = 0.f, l = 0.f;
+    for (int w = 0; w < nwaves; ++w) {
+      const float f = exp2f(s_m[w][h] - m);
+      a += f * s_acc[w][h][dd];
+      l += f * s_l[w][h];
+    }
+    float *o = dst + (long)h * (D + 2);
+    o[dd] = a;
+    if (dd == 0) {
+      o[D] = m;
+      o[D + 1] = l;
+    }
+  }
+}
+
+template <typename T, int D, int NREP>
+__global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, const float *__restrict__ ws,
+                                                             void *__restrict__ out, int tps, int splits) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int Hkv = c.num_kv_heads;
+  const int g = h / NREP, hh = h % NREP;
+  const SeqTiles st = seq_tiles(c, b);
+  const int used = min((st.ntiles + tps - 1) / tps, splits);
+  const long obase = ((long)b * Hkv * NREP + h) * D;
+  const float *src = ws + (((long)(b * Hkv + g) * splits) * NREP + hh) * (D + 2);
+  const long sstride = (long)NREP * (D + 2);
+  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
+    float m = kNegBig;
+    for (int s = 0; s < used; ++s) m = fmaxf(m, src[s * sstride + D]);
+    float a = 0.f, l = 0.f;
+    for (int s = 0; s < used; ++s) {
+      const float f = exp2f(src[s * sstride + D] - m);
+      a += f * src[s * sstride + dd];
+      l += f * src[s * sstride + D + 1];
+    }
+    ElemTraits<T>::put(out, obase + dd, l > 0.f ? a / l : 0.f);
+  }
+}
+
+template <typename T, int D, int NREP>
+hipError_t launch_decode_t(const void *q, int batch, const ropekv_kv_cache &c, float sl2, void *out, float *ws,
+                           const DecodePlan &pl, hipStream_t s) {
+  dim3 grid(pl.splits, c.num_kv_heads, batch);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, NREP>), grid, dim3(256), 0, s, q, c, sl2, ws, pl.tiles_per_split,
+                     pl.splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, NREP>), dim3(c.num_kv_heads * NREP, batch), dim3(128), 0, s, c,
+                     ws, out, pl.tiles_per_split, pl.splits);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_decode_d(const void *q, int batch, const ropekv_kv_cache &c, float sl2, void *out, float *ws,
+                           const DecodePlan &pl, hipStream_t s) {
+  switch (pl.n_rep) {
+    case 1: return launch_decode_t<T, D, 1>(q, batch, c, sl2, out, ws, pl, s);
+    case 2: return launch_decode_t<T, D, 2>(q, batch, c, sl2, out, ws, pl, s);
+    case 4: return launch_decode_t<T, D, 4>(q, batch, c, sl2, out, ws, pl, s);
+    case 8: return launch_decode_t<T, D, 8>(q, batch, c, sl2, out, ws, pl, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// --- visible-slot enumeration (test-facing; one thread walks the set) ---
+__global__ void visible_slots_kernel(ropekv_kv_cache c, int b, int32_t *pos_out, int64_t *off_out, int max_out,
+                                     int32_t *n_out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const int D = c.head_dim;
+  const int n = c.seq_len[b];
+  int cnt = 0;
+  auto emit = [&](int pos, long off) {
+    if (cnt < max_out) {
+      pos_out[cnt] = pos;
+      off_out[cnt] = off;
+    }
+    ++cnt;
+  };
+  if (n > 0) {
+    if (c.layout == ROPEKV_PAGED) {
+      for (int p = 0; p < n; ++p) {
+        const bool vis = c.window == 0 || p < c.sinks || (n - 1) - p < c.window;
+        if (!vis) continue;
+        const int blk = p / c.block_size;
+        const int bid = blk < c.max_blocks ? c.block_table[(long)b * c.max_blocks + blk] : -1;
+        emit(p, bid < 0 ? -1 : (((long)bid * c.num_kv_heads) * c.block_size + p % c.block_size) * D);
+      }
+    } else {
+      const SeqTiles st = seq_tiles(c, b);
+      const long base = ((long)b * c.num_kv_heads) * (long)c.capacity * D;
+      for (int p = 0; p < st.ns; ++p) emit(p, base + (long)p * D);
+      for (int i = 0; i < st.count; ++i) {
+        const int slot = c.sinks + (st.oldest + i) % c.window;
+        emit(n - st.count + i, base + (long)slot * D);
+      }
+    }
+  }
+  *n_out = cnt;
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c) {
+  DecodePlan pl;
+  pl.n_rep = n_q_heads / c.num_kv_heads;
+  int max_tiles;
+  if (c.layout == ROPEKV_PAGED) {
+    if (c.window == 0) {
+      max_tiles = c.max_blocks;
+    } else {
+      max_tiles = (c.sinks + kTile - 1) / kTile + c.window / kTile + 2;
+      if (max_tiles > c.max_blocks) max_tiles = c.max_blocks;
+    }
+  } else {
+    max_tiles = (c.capacity + kTile - 1) / kTile;
+  }
+  if (max_tiles < 1) max_tiles = 1;
+  int tps = 32;
+  if (const char *e = getenv("ROPEKV_DECODE_TPS")) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= 4096) tps = v;
+  }
+  pl.max_tiles = max_tiles;
+  pl.tiles_per_split = tps;
+  pl.splits = (max_tiles + tps - 1) / tps;
+  const int dd = c.head_dim + 2;
+  pl.ws_bytes = (size_t)batch * c.num_kv_heads * pl.splits * pl.n_rep * dd * sizeof(float);
+  return pl;
+}
+
+hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_kv_cache &c, float scale, void *out,
+                         void *ws, const DecodePlan &pl, hipStream_t s) {
+  (void)n_q_heads;
+  const float sl2 = scale * kLog2e;
+  float *w = (float *)ws;
+  if (c.kv_dtype == ROPEKV_BF16) {
+    if (c.head_dim == 128) return launch_decode_d<bf16_t, 128>(q, batch, c, sl2, out, w, pl, s);
+    if (c.head_dim == 64) return launch_decode_d<bf16_t, 64>(q, batch, c, sl2, out, w, pl, s);
+  } else if (c.kv_dtype == ROPEKV_F32) {
+    if (c.head_dim == 128) return launch_decode_d<float, 128>(q, batch, c, sl2, out, w, pl, s);
+    if (c.head_dim == 64) return launch_decode_d<float, 64>(q, batch, c, sl2, out, w, pl, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_visible_slots(const ropekv_kv_cache &c, int seq, int32_t *pos_out, int64_t *off_out, int max_out,
+                                int32_t *n_out, hipStream_t s) {
+  hipLaunchKernelGGL(visible_slots_kernel, dim3(1), dim3(64), 0, s, c, seq, pos_out, off_out, max_out, n_out);
+  return hipGetLastError();
+}
+
+}  // namespace ropekv

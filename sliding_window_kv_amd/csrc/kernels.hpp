@@ -1,0 +1,55 @@
+// Host-side launchers of the ropekv kernels (called by api.cpp after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace ropekv {
+
+// Launch geometry of the split-K decode, shared by the workspace query and the launch.
+struct DecodePlan {
+  int n_rep;
+  int max_tiles;        // upper bound on 16-row tiles any sequence visits
+  int tiles_per_split;  // tiles handled by one workgroup
+  int splits;           // workgroups per (sequence, KV head)
+  size_t ws_bytes;
+};
+
+DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c);
+
+hipError_t launch_build_table(const RopeParams &rp, int max_pos, float *out, float *mscale_dev,
+                              hipStream_t s);
+
+struct AppendArgs {
+  int rotary_dim, head_dim, neox;
+  const float *table;
+  int table_len;
+  void *q;
+  int n_q_heads;
+  void *k;
+  const void *v;
+  int act;
+  int n_tokens;
+  const int32_t *pos;
+  const int32_t *seq;
+  ropekv_kv_cache c;
+  int32_t *freed;
+  int freed_cap;
+  int32_t *n_freed;
+};
+hipError_t launch_apply_append(const AppendArgs &a, hipStream_t s);
+
+hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_kv_cache &c, float scale,
+                         void *out, void *ws, const DecodePlan &plan, hipStream_t s);
+
+hipError_t launch_prefill(const void *q, const void *k, const void *v, int T, int pos0, int n_q_heads,
+                          const ropekv_kv_cache &c, int seq_id, float scale, void *out, hipStream_t s);
+
+hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const ropekv_kv_cache &c,
+                           int n_layers, hipStream_t s);
+
+hipError_t launch_visible_slots(const ropekv_kv_cache &c, int seq, int32_t *pos_out, int64_t *off_out,
+                                int max_out, int32_t *n_out, hipStream_t s);
+
+}  // namespace ropekv

@@ -1,0 +1,374 @@
+// Prefill attention of one sequence's chunk over the sink + window mask.
+//
+// "Inference & 128K Long Context" (5.5: query t of the chunk sits at
+// absolute position pos0 + t; a key j is allowed iff j <= pos0 + t and
+// pos0 + t - j < window) with the sink rule of "Attention Sink 与 Streaming
+// KV Cache" (keys j < S stay visible).  Key tiles no query of a workgroup can
+// see are never loaded ("FlashAttention can skip invisible tiles").
+//
+// Workgroup: one KV head g and BM = 128 / n_rep consecutive chunk positions
+// for all n_rep query heads of g (128 query rows, so every K/V byte staged in
+// LDS serves all heads of the group).  Four waves, 32 rows each (two 16-row
+// tiles of one head).  Key tiles of 64 keys.
+//   S^T = K . Q^T   (MFMA; lane keeps its query row's 16 scores per tile)
+//   online softmax in the log2 domain, fp32
+//   O^T += V^T . P^T (MFMA; bf16: V staged transposed in LDS, P rounded to bf16)
+#include "kernels.hpp"
+
+namespace ropekv {
+
+namespace {
+
+constexpr int kBN = 64;  // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ int imod2(int x, int m) {
+  int r = x % m;
+  return r < 0 ? r + m : r;
+}
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  int T, pos0, n_q_heads, seq;
+  ropekv_kv_cache c;
+  float sl2;
+  void *out;
+};
+
+// Element offset (into the chunk k/v when *chunk, else into the cache) of the
+// key row at position j for KV head g; -1 when the row is not available.
+__device__ inline long key_row(const PrefillArgs &a, int j, int g, int D, bool *chunk) {
+  const ropekv_kv_cache &c = a.c;
+  *chunk = false;
+  if (j >= a.pos0) {
+    if (j - a.pos0 >= a.T) return -1;
+    *chunk = true;
+    return ((long)(j - a.pos0) * c.num_kv_heads + g) * D;
+  }
+  if (c.layout == ROPEKV_PAGED) {
+    const int blk = j / c.block_size;
+    if (blk >= c.max_blocks) return -1;
+    const int bid = c.block_table[(long)a.seq * c.max_blocks + blk];
+    if (bid < 0 || bid >= c.num_blocks) return -1;
+    return (((long)bid * c.num_kv_heads + g) * c.block_size + j % c.block_size) * D;
+  }
+  if (c.layout == ROPEKV_RING) {
+    const long base = ((long)a.seq * c.num_kv_heads + g) * (long)c.capacity * D;
+    if (j < c.sinks) return base + (long)j * D;
+    const int n = c.seq_len[a.seq];
+    const int cnt = c.ring_count[a.seq];
+    if (j >= n || n - j > cnt) return -1;
+    const int slot = c.sinks + imod2(c.ring_head[a.seq] - (n - j), c.window);
+    return base + (long)slot * D;
+  }
+  return -1;
+}
+
+template <int NB>
+__device__ __forceinline__ void copy16(void *dst, const void *src) {
+#pragma unroll
+  for (int i = 0; i < NB / 16; ++i) ((uint4 *)dst)[i] = ((const uint4 *)src)[i];
+}
+
+template <typename T, int D, int NREP>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  constexpr bool kBF = sizeof(T) == 2;
+  constexpr int EB = sizeof(T);
+  constexpr int BM = 128 / NREP;           // chunk positions per workgroup
+  constexpr int KP = kBF ? D + 8 : D + 4;  // K (and fp32 V) LDS pitch in elements
+  constexpr int VTP = kBN + 8;             // bf16 V^T pitch in elements
+  constexpr int QB = (D / 4) * EB;         // bytes of a quarter row
+  __shared__ __attribute__((aligned(16))) T k_lds[kBN * KP];
+  __shared__ __attribute__((aligned(16))) T v_lds[kBF ? D * VTP : kBN * KP];
+
+  const ropekv_kv_cache &c = a.c;
+  const int g = blockIdx.y;
+  const int t0 = blockIdx.x * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int Hkv = c.num_kv_heads, Hq = a.n_q_heads;
+  const int S = c.sinks, W = c.window;
+  const int qp_lo = a.pos0 + t0;
+  const int qp_hi = a.pos0 + min(t0 + BM, a.T) - 1;
+
+  // this lane's query row in each of its two row tiles
+  int tq[2], head[2];
+  uint32_t qw[2][QB / 4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int R = 32 * wave + 16 * rt + col;
+    tq[rt] = t0 + R % BM;
+    head[rt] = g * NREP + R / BM;
+    if (tq[rt] < a.T) {
+      const char *src = (const char *)a.q + (((long)tq[rt] * Hq + head[rt]) * D) * EB + grp * QB;
+      copy16<QB>(qw[rt], src);
+    } else {
+#pragma unroll
+      for (int i = 0; i < QB / 4; ++i) qw[rt][i] = 0u;
+    }
+  }
+
+  // key tiles: sink tiles [0, nst), then recent tiles [first, last]
+  const int last = qp_hi / kBN;
+  int nst = 0, first = 0;
+  if (W == 0) {
+    first = 0;
+  } else {
+    const int sink_hi = min(S, qp_hi + 1);
+    nst = (sink_hi + kBN - 1) / kBN;
+    const int lo = max(0, qp_lo - W + 1);
+    first = max(lo / kBN, nst);
+  }
+  const int ntiles = nst + max(0, last - first + 1);
+
+  float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
+  f32x4 o[2][D / 16];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bool lost = false;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int kb = kt < nst ? kt : first + (kt - nst);
+    const int j0 = kb * kBN;
+    // ---- stage K (natural) and V (bf16: transposed) in LDS
+    {
+      constexpr int CH = (D / 4) * EB;  // bytes per thread-chunk (a quarter row)
+      const int key = tid >> 2, qd = tid & 3;
+      const int j = j0 + key;
+      bool chunk;
+      long off = key_row(a, j, g, D, &chunk);
+      const bool needed = j <= qp_hi && (W == 0 || j < S || j > qp_lo - W);
+      if (off < 0 && needed && j < a.pos0) lost = true;
+      uint32_t kbuf[CH / 4];
+      if (off >= 0) {
+        const char *src = (const char *)(chunk ? a.k : c.k) + off * EB + qd * CH;
+        copy16<CH>(kbuf, src);
+      } else {
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i) kbuf[i] = 0u;
+      }
+      copy16<CH>(&k_lds[key * KP + qd * (D / 4)], kbuf);
+      if constexpr (!kBF) {
+        uint32_t vbuf[CH / 4];
+        if (off >= 0) {
+          const char *src = (const char *)(chunk ? a.v : c.v) + off * EB + qd * CH;
+          copy16<CH>(vbuf, src);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CH / 4; ++i) vbuf[i] = 0u;
+        }
+        copy16<CH>(&v_lds[key * KP + qd * (D / 4)], vbuf);
+      }
+    }
+    if constexpr (kBF) {
+      // V^T: each item = 2 keys x 16 dims -> 16 dwords (key pair per dim)
+      constexpr int ITEMS = (kBN / 2) * (D / 16);
+      for (int it = tid; it < ITEMS; it += 256) {
+        const int kp = it / (D / 16), dc = it % (D / 16);
+        uint32_t w2[2][8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = j0 + 2 * kp + u;
+          bool chunk;
+          const long off = key_row(a, j, g, D, &chunk);
+          if (off >= 0) {
+            copy16<32>(w2[u], (const char *)(chunk ? a.v : c.v) + (off + dc * 16) * 2);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w2[u][i] = 0u;
+          }
+        }
+        uint32_t *vt = (uint32_t *)v_lds;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t lo16 = (e & 1) ? (w2[0][e >> 1] >> 16) : (w2[0][e >> 1] & 0xffffu);
+          const uint32_t hi16 = (e & 1) ? (w2[1][e >> 1] & 0xffff0000u) : (w2[1][e >> 1] << 16);
+          vt[((dc * 16 + e) * VTP + 2 * kp) >> 1] = lo16 | hi16;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- scores
+    f32x4 sc[2][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t kw[QB / 4];
+      copy16<QB>(kw, &k_lds[(16 * st + col) * KP + grp * (D / 4)]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBF) {
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) {
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 av = {kw[4 * t], kw[4 * t + 1], kw[4 * t + 2], kw[4 * t + 3]};
+            const u32x4 bv = {qw[rt][4 * t], qw[rt][4 * t + 1], qw[rt][4 * t + 2], qw[rt][4 * t + 3]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < D / 4; ++t)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[t]), __uint_as_float(qw[rt][t]), acc, 0,
+                                                       0, 0);
+        }
+        sc[rt][st] = acc;
+      }
+    }
+    // does every query of this workgroup see every key of the tile?
+    const int jmax = j0 + kBN - 1;
+    const bool full = jmax <= qp_lo && (W == 0 || jmax < S || qp_hi - j0 < W);
+    float corr[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int qpos = a.pos0 + tq[rt];
+      float mx = kNegBig;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float s = sc[rt][st][j] * a.sl2;
+          if (!full) {
+            const int jp = j0 + 16 * st + 4 * grp + j;
+            const bool vis = jp <= qpos && (W == 0 || jp < S || qpos - jp < W);
+            s = vis ? s : -INFINITY;
+          }
+          sc[rt][st][j] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m_run[rt], mx);
+      corr[rt] = exp2f(m_run[rt] - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = exp2f(sc[rt][st][j] - m_new);
+          sc[rt][st][j] = p;
+          ps += p;
+        }
+      l_run[rt] = l_run[rt] * corr[rt] + ps;
+      m_run[rt] = m_new;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] *= corr[rt];
+    }
+
+    // ---- O^T += V^T P^T
+    if constexpr (kBF) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        uint32_t pw[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x4 pp = sc[rt][2 * u + h2];
+            pw[rt][2 * h2] = (uint32_t)f_to_bf16(pp[0]) | ((uint32_t)f_to_bf16(pp[1]) << 16);
+            pw[rt][2 * h2 + 1] = (uint32_t)f_to_bf16(pp[2]) | ((uint32_t)f_to_bf16(pp[3]) << 16);
+          }
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+          const uint32_t *vt = (const uint32_t *)v_lds;
+          const int row = 16 * mt + col;
+          const uint2 lo = *(const uint2 *)&vt[(row * VTP + 32 * u + 4 * grp) >> 1];
+          const uint2 hi = *(const uint2 *)&vt[(row * VTP + 32 * u + 16 + 4 * grp) >> 1];
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const u32x4 bv = {pw[rt][0], pw[rt][1], pw[rt][2], pw[rt][3]};
+            o[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                __builtin_bit_cast(bf16x8, bv), o[rt][mt], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float vv = ((const float *)v_lds)[(16 * st + 4 * grp + j) * KP + 16 * mt + col];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+              o[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sc[rt][st][j], o[rt][mt], 0, 0, 0);
+          }
+    }
+    __syncthreads();
+  }
+  if (lost) dev_error(c.err_word, ROPEKV_DEV_PREFIX_LOST);
+
+  // ---- normalise and store: lane holds O^T[16 mt + 4 grp + j][its row]
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float l = l_run[rt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (tq[rt] < a.T) {
+      const long ob = ((long)tq[rt] * Hq + head[rt]) * D;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        const int d0 = 16 * mt + 4 * grp;
+        if constexpr (kBF) {
+          uint2 w;
+          w.x = (uint32_t)f_to_bf16(o[rt][mt][0] * inv) | ((uint32_t)f_to_bf16(o[rt][mt][1] * inv) << 16);
+          w.y = (uint32_t)f_to_bf16(o[rt][mt][2] * inv) | ((uint32_t)f_to_bf16(o[rt][mt][3] * inv) << 16);
+          *(uint2 *)((uint16_t *)a.out + ob + d0) = w;
+        } else {
+          *(float4 *)((float *)a.out + ob + d0) =
+              make_float4(o[rt][mt][0] * inv, o[rt][mt][1] * inv, o[rt][mt][2] * inv, o[rt][mt][3] * inv);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_prefill_d(const PrefillArgs &a, int n_rep, hipStream_t s) {
+  const int bm = 128 / n_rep;
+  dim3 grid((a.T + bm - 1) / bm, a.c.num_kv_heads);
+  switch (n_rep) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<T, D, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<T, D, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<T, D, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<T, D, 8>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const void *q, const void *k, const void *v, int T, int pos0, int n_q_heads,
+                          const ropekv_kv_cache &c, int seq_id, float scale, void *out, hipStream_t s) {
+  PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.T = T;
+  a.pos0 = pos0;
+  a.n_q_heads = n_q_heads;
+  a.seq = seq_id;
+  a.c = c;
+  a.sl2 = scale * kLog2e;
+  a.out = out;
+  const int n_rep = n_q_heads / c.num_kv_heads;
+  if (c.kv_dtype == ROPEKV_BF16) {
+    if (c.head_dim == 128) return launch_prefill_d<bf16_t, 128>(a, n_rep, s);
+    if (c.head_dim == 64) return launch_prefill_d<bf16_t, 64>(a, n_rep, s);
+  } else if (c.kv_dtype == ROPEKV_F32) {
+    if (c.head_dim == 128) return launch_prefill_d<float, 128>(a, n_rep, s);
+    if (c.head_dim == 64) return launch_prefill_d<float, 64>(a, n_rep, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ropekv

@@ -1,0 +1,565 @@
+"""GPU parity: every entry point of libropekv.so against the fp64 oracle.
+
+Integer state (ring head / count, seq_len, block tables, freed ids, visible
+slots) must match bit for bit.  fp32 paths: max |gpu - ref| / max |ref|
+<= 1e-5 per tensor (per row for attention).  bf16 attention: |gpu - ref| <=
+2e-2 + 1e-2 |ref| elementwise.  Oracle inputs are the host copies of the
+seeded inputs (rounded to the activation dtype by torch before upload); no
+oracle input or expected value comes from the HIP path.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import ropekv_oracle as O
+from sliding_window_kv_amd import synth
+from tests.gpu_util import (DevPaged, DevRing, assert_bf16_close, normwise, oracle_cfg, rowwise, to_np64,
+                            torch_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    dev = torch_dev()
+    from sliding_window_kv_amd import ropekv as R
+
+    return R, torch, dev
+
+
+def _table(R, torch, dev, cfg, P):
+    t = torch.empty(P, cfg.rotary_dim, dtype=torch.float32, device=dev)
+    R.build_table(cfg, P, t)
+    return t
+
+
+# ------------------------------------------------------------------ table
+
+TABLE_CASES = [
+    (dict(head_dim=64, rotary_dim=64, rope_theta=1e4), 80),
+    (dict(head_dim=128, rotary_dim=128, rope_theta=5e5), 32768),
+    (dict(head_dim=128, rotary_dim=64, rope_theta=5e5, yarn_factor=2.0, orig_max_pos=262144), 524288),
+    (dict(head_dim=128, rotary_dim=128, rope_theta=1e4, yarn_factor=8.0, orig_max_pos=4096), 32768),
+    (dict(head_dim=96, rotary_dim=32, rope_theta=1e4, yarn_factor=1.125, orig_max_pos=100, neox=False), 1000),
+]
+
+
+@pytest.mark.parametrize("args,P", TABLE_CASES)
+def test_table_matches_oracle(env, args, P):
+    R, torch, dev = env
+    cfg = R.rope_cfg(**args)
+    ms = torch.zeros(1, dtype=torch.float32, device=dev)
+    t = torch.empty(P, cfg.rotary_dim, dtype=torch.float32, device=dev)
+    R.build_table(cfg, P, t, ms)
+    torch.cuda.synchronize()
+    got = t.cpu().numpy().astype(np.float64)
+    ref = O.build_table(oracle_cfg(cfg), P)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= ulp), float(np.max(np.abs(got - ref) / ulp))
+    assert abs(float(ms.item()) - O.yarn_mscale(cfg.yarn_factor)) < 1e-7
+    # the result does not depend on the launch shape: a shorter build is a bitwise prefix
+    P2 = P // 2 + 3
+    t2 = _table(R, torch, dev, cfg, P2)
+    assert torch.equal(t2, t[:P2])
+
+
+def test_table_factor_one_is_plain(env):
+    R, torch, dev = env
+    a = _table(R, torch, dev, R.rope_cfg(128, 64, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144), 4096)
+    b = _table(R, torch, dev, R.rope_cfg(128, 64, rope_theta=5e5), 4096)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ ring: config-1 end to end
+
+def _ring_end_to_end(env, neox, dtype_name, chunks):
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
+    act = {"f32": R.F32, "bf16": R.BF16}[dtype_name]
+    B, Hq, Hkv, d, S, W = 1, 8, 4, 64, 4, 12
+    n_total = sum(chunks)
+    cfg = R.rope_cfg(d, d, rope_theta=1e4, neox=neox)
+    ocfg = oracle_cfg(cfg)
+    table = _table(R, torch, dev, cfg, n_total)
+    otab = O.build_table(ocfg, n_total)
+    # inputs rounded to the activation dtype by torch; the oracle reads the rounded values
+    qd = torch.from_numpy(synth.normal((n_total, Hq, d), 101)).to(dev, dtype)
+    kd = torch.from_numpy(synth.normal((n_total, Hkv, d), 102)).to(dev, dtype)
+    vd = torch.from_numpy(synth.normal((n_total, Hkv, d), 103)).to(dev, dtype)
+    qraw, kraw, vraw = to_np64(qd), to_np64(kd), to_np64(vd)
+    qrot = O.rope_apply(qraw, np.arange(n_total), otab, d, neox)
+    krot = O.rope_apply(kraw, np.arange(n_total), otab, d, neox)
+    cache = DevRing(R, torch, dev, dtype, B, Hkv, d, S, W)
+    oring = O.RingSeq(sinks=S, window=W)
+    out = torch.empty(1, Hq, d, dtype=dtype, device=dev)
+    ws = torch.empty(R.decode_workspace_size(1, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    tol = 1e-5 if dtype_name == "f32" else None
+    p0 = 0
+    for T in chunks:
+        q = qd[p0:p0 + T].clone()
+        k = kd[p0:p0 + T].clone()
+        v = vd[p0:p0 + T].clone()
+        pos = torch.arange(p0, p0 + T, dtype=torch.int32, device=dev)
+        seq = torch.zeros(T, dtype=torch.int32, device=dev)
+        R.apply_append(cfg, table, n_total, q, Hq, k, v, act, T, pos, seq, cache.desc)
+        oring.append(T)
+        torch.cuda.synchronize()
+        assert cache.err.item() == 0
+        # rotated q, k in place
+        if tol:
+            assert normwise(to_np64(q), qrot[p0:p0 + T]) <= tol
+            assert normwise(to_np64(k), krot[p0:p0 + T]) <= tol
+        else:
+            assert_bf16_close(to_np64(q), qrot[p0:p0 + T], atol=1e-2, rtol=1e-2)
+            assert_bf16_close(to_np64(k), krot[p0:p0 + T], atol=1e-2, rtol=1e-2)
+        # integer ring state
+        assert (cache.head.item(), cache.count.item(), cache.seq_len.item()) == (oring.head, oring.count,
+                                                                                  oring.seq_len)
+        # cache contents: every live slot holds the rotated key / raw value of its position
+        kc = to_np64(cache.k[0])
+        vc = to_np64(cache.v[0])
+        for slot, p in oring.slot_pos.items():
+            if tol:
+                assert normwise(kc[:, slot], krot[p]) <= tol
+            else:
+                assert_bf16_close(kc[:, slot], krot[p], atol=1e-2, rtol=1e-2)
+            assert np.array_equal(vc[:, slot], vraw[p])
+        # visible slots, chronological, bit-exact
+        n_out = torch.zeros(1, dtype=torch.int32, device=dev)
+        vp = torch.zeros(64, dtype=torch.int32, device=dev)
+        vo = torch.zeros(64, dtype=torch.int64, device=dev)
+        R.visible_slots(cache.desc, 0, vp, vo, 64, n_out)
+        torch.cuda.synchronize()
+        nv = n_out.item()
+        want_pos = O.visible_positions(oring.seq_len - 1, S, W)
+        assert vp[:nv].cpu().tolist() == want_pos
+        want_slots = oring.chronological_slots()
+        assert (vo[:nv].cpu().numpy() // d).tolist() == want_slots
+        kbp = {j: krot[j] for j in range(n_total)}
+        if T > 1:
+            o = torch.empty(T, Hq, d, dtype=dtype, device=dev)
+            R.prefill_attn(q, k, v, T, p0, Hq, cache.desc, 0, 0.0, o)
+            torch.cuda.synchronize()
+            # prefix keys the chunk's queries need, and whether the ring still holds them
+            needed = {j for t in range(p0, p0 + T) for j in O.visible_positions(t, S, W) if j < p0}
+            present = set(oring.slot_pos.values())
+            if needed <= present:
+                assert cache.err.item() == 0
+                ref = O.prefill_attention(qrot[p0:p0 + T], lambda j: kbp[j], lambda j: vraw[j], p0, S, W, Hkv)
+                if tol:
+                    assert rowwise(to_np64(o), ref) <= tol
+                else:
+                    assert_bf16_close(to_np64(o), ref)
+            else:
+                assert cache.err.item() & R.DEV_PREFIX_LOST
+                cache.err.zero_()
+        R.decode_attn(q[T - 1:T], 1, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
+        torch.cuda.synchronize()
+        ref = O.decode_attention(qrot[p0 + T - 1], lambda j: kbp[j], lambda j: vraw[j], p0 + T, S, W, Hkv)
+        if tol:
+            assert rowwise(to_np64(out[0]), ref) <= tol
+        else:
+            assert_bf16_close(to_np64(out[0]), ref)
+        p0 += T
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_ring_config1_prefill_then_decode(env, neox):
+    # the tiny fp32 case: prefill 0..63, then 16 decode steps
+    _ring_end_to_end(env, neox, "f32", [64] + [1] * 16)
+
+
+@pytest.mark.parametrize("chunks", [[3, 1, 1, 20, 1, 7, 1], [2, 2, 9, 13, 1], [30, 1, 2]])
+def test_ring_chunked_appends(env, chunks):
+    # chunks that fit (pos0 + T <= C), that wrap, and that exceed the window in one call
+    _ring_end_to_end(env, True, "f32", chunks)
+
+
+def test_ring_bf16(env):
+    _ring_end_to_end(env, True, "bf16", [40, 1, 1, 1, 5])
+
+
+# ------------------------------------------------------------------ paged append + freeing + decode
+
+def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
+    act = {"f32": R.F32, "bf16": R.BF16}[dtype_name]
+    rng = synth.rng(seed)
+    max_len = 200
+    bs = 16
+    max_blocks = max_len // bs + 1
+    num_blocks = B * max_blocks + 7
+    table = synth.block_table_permutation(B, max_blocks, num_blocks, seed + 1)
+    cfg = R.rope_cfg(d, d, rope_theta=5e5)
+    ocfg = oracle_cfg(cfg)
+    gtab = _table(R, torch, dev, cfg, max_len)
+    otab = O.build_table(ocfg, max_len)
+    cache = DevPaged(R, torch, dev, dtype, B, Hkv, d, S, W, table, num_blocks)
+    otable = [list(map(int, row)) for row in table]
+    qall = synth.normal((B, max_len, Hq, d), seed + 2)
+    kall = synth.normal((B, max_len, Hkv, d), seed + 3)
+    vall = synth.normal((B, max_len, Hkv, d), seed + 4)
+    # round through the device dtype once so both sides see identical inputs
+    kall = to_np64(torch.from_numpy(kall).to(dtype))
+    vall = to_np64(torch.from_numpy(vall).to(dtype))
+    qall = to_np64(torch.from_numpy(qall).to(dtype))
+    krot = np.stack([O.rope_apply(kall[b], np.arange(max_len), otab, d, True) for b in range(B)])
+    qrot = np.stack([O.rope_apply(qall[b], np.arange(max_len), otab, d, True) for b in range(B)])
+    n = [0] * B
+    freed_dev = torch.full((B * max_blocks,), -7, dtype=torch.int32, device=dev)
+    nfreed = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    for _ in range(rounds):
+        # a mixed step: some sequences prefill a chunk, some decode one token, some idle
+        toks, poss, seqs, oracle_freed = [], [], [], []
+        for b in range(B):
+            step = int(rng.choice([0, 1, 1, int(rng.integers(2, 40))]))
+            step = min(step, max_len - n[b])
+            if step == 0:
+                continue
+            oracle_freed += O.paged_free_expired(otable[b], n[b], S, W, bs)
+            for p in range(n[b], n[b] + step):
+                toks.append((b, p))
+            n[b] += step
+        if not toks:
+            continue
+        N = len(toks)
+        q = torch.from_numpy(np.stack([qall[b, p] for b, p in toks])).to(dev, dtype)
+        k = torch.from_numpy(np.stack([kall[b, p] for b, p in toks])).to(dev, dtype)
+        v = torch.from_numpy(np.stack([vall[b, p] for b, p in toks])).to(dev, dtype)
+        pos = torch.tensor([p for _, p in toks], dtype=torch.int32, device=dev)
+        seq = torch.tensor([b for b, _ in toks], dtype=torch.int32, device=dev)
+        nfreed.zero_()
+        R.apply_append(cfg, gtab, max_len, q, Hq, k, v, act, N, pos, seq, cache.desc, freed_dev, freed_dev.numel(),
+                       nfreed)
+        torch.cuda.synchronize()
+        assert cache.err.item() == 0
+        assert cache.seq_len.cpu().tolist() == n
+        assert cache.table.cpu().numpy().tolist() == otable
+        nf = nfreed.item()
+        assert sorted(freed_dev[:nf].cpu().tolist()) == sorted(oracle_freed)
+        # contents of every live (non-null) block at written positions
+        kc = to_np64(cache.k)
+        vc = to_np64(cache.v)
+        for b in range(B):
+            for p in range(n[b]):
+                bid = otable[b][p // bs]
+                if bid < 0:
+                    continue
+                got_k = kc[bid, :, p % bs]
+                if dtype_name == "f32":
+                    assert normwise(got_k, krot[b, p]) <= 1e-5
+                else:
+                    assert_bf16_close(got_k, krot[b, p], atol=1e-2, rtol=1e-2)
+                assert np.array_equal(vc[bid, :, p % bs], vall[b, p])
+        # decode for every sequence with its latest query
+        qd = torch.from_numpy(np.stack([qrot[b, max(n[b] - 1, 0)] for b in range(B)])).to(dev, dtype)
+        out = torch.empty(B, Hq, d, dtype=dtype, device=dev)
+        R.decode_attn(qd, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
+        torch.cuda.synchronize()
+        assert cache.err.item() == 0
+        got = to_np64(out)
+        qused = to_np64(qd)
+        for b in range(B):
+            if n[b] == 0:
+                assert np.all(got[b] == 0)
+                continue
+            ref = O.decode_attention(qused[b], lambda j: krot[b, j], lambda j: vall[b, j], n[b], S, W, Hkv)
+            if dtype_name == "f32":
+                assert rowwise(got[b], ref) <= 1e-5
+            else:
+                assert_bf16_close(got[b], ref)
+
+
+@pytest.mark.parametrize("S,W", [(4, 12), (0, 20), (4, 0), (3, 33)])
+def test_paged_config1_shape(env, S, W):
+    _paged_end_to_end(env, "f32", S, W, B=3, Hq=8, Hkv=4, d=64, rounds=14, seed=7 + S + W)
+
+
+def test_paged_bf16_gqa4(env):
+    _paged_end_to_end(env, "bf16", 4, 40, B=4, Hq=32, Hkv=8, d=128, rounds=12, seed=300)
+
+
+# ------------------------------------------------------------------ decode at larger shapes (synthetic caches)
+
+def _fill(torch, t, seed):
+    synth.device_normal_(t, seed)
+    return t
+
+
+@pytest.mark.parametrize("n_rep,d", [(4, 128), (8, 128), (2, 64), (1, 128)])
+def test_decode_paged_random_table(env, n_rep, d):
+    # config-2-shaped: paged 16-token blocks, random block table, ragged lengths incl. 1 and block edges
+    R, torch, dev = env
+    Hkv = 8
+    Hq = Hkv * n_rep
+    lens = [1, 15, 16, 17, 300, 1024, 2000, 2049]
+    B = len(lens)
+    max_blocks = 130
+    num_blocks = B * max_blocks + 11
+    table = synth.block_table_permutation(B, max_blocks, num_blocks, 41)
+    cache = DevPaged(R, torch, dev, torch.bfloat16, B, Hkv, d, 0, 0, table, num_blocks)
+    _fill(torch, cache.k, 42)
+    _fill(torch, cache.v, 43)
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev), 44)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    kp = to_np64(cache.k)
+    vp = to_np64(cache.v)
+    qq = to_np64(q)
+    got = to_np64(out)
+    for b, n in enumerate(lens):
+        rows = [table[b, j // 16] for j in range(n)]
+        K = np.stack([kp[rows[j], :, j % 16] for j in range(n)])
+        V = np.stack([vp[rows[j], :, j % 16] for j in range(n)])
+        ref = O.decode_attention(qq[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
+        assert_bf16_close(got[b], ref)
+
+
+def test_decode_paged_window_with_null_blocks(env):
+    # sink + window paged decode where every block below the window edge is null (-1):
+    # the kernel must never touch them and must still see the sinks in block 0.
+    R, torch, dev = env
+    Hkv, n_rep, d, S, W = 8, 4, 128, 4, 100
+    Hq = Hkv * n_rep
+    lens = [5, 99, 100, 101, 104, 117, 500, 1000]
+    B = len(lens)
+    max_blocks = 64
+    num_blocks = B * max_blocks
+    table = synth.block_table_permutation(B, max_blocks, num_blocks, 51)
+    for b, n in enumerate(lens):
+        edge = max(0, (n - 1) - W + 1)
+        for j in range(1, max_blocks):
+            if 16 * j + 16 <= edge:
+                table[b, j] = -1
+    cache = DevPaged(R, torch, dev, torch.bfloat16, B, Hkv, d, S, W, table, num_blocks)
+    _fill(torch, cache.k, 52)
+    _fill(torch, cache.v, 53)
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev), 54)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    kp, vp, qq, got = to_np64(cache.k), to_np64(cache.v), to_np64(q), to_np64(out)
+    for b, n in enumerate(lens):
+        def kb(j, b=b):
+            return kp[table[b, j // 16], :, j % 16]
+
+        def vb(j, b=b):
+            return vp[table[b, j // 16], :, j % 16]
+
+        ref = O.decode_attention(qq[b], kb, vb, n, S, W, Hkv)
+        assert_bf16_close(got[b], ref)
+
+
+def test_decode_ring_random_head(env):
+    # config-3-shaped windowed layer: full ring (count = W), head at a random offset, long positions
+    R, torch, dev = env
+    Hkv, n_rep, d, S, W = 8, 4, 128, 4, 300
+    Hq = Hkv * n_rep
+    B = 5
+    cache = DevRing(R, torch, dev, torch.bfloat16, B, Hkv, d, S, W)
+    _fill(torch, cache.k, 61)
+    _fill(torch, cache.v, 62)
+    heads = synth.uniform_ints(B, 0, W, 63)
+    lens = [131072, 5000, 305, 304 + 7, 9999]
+    cache.head.copy_(torch.from_numpy(heads))
+    cache.count.fill_(W)
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev), 64)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    kc, vc, qq, got = to_np64(cache.k), to_np64(cache.v), to_np64(q), to_np64(out)
+    for b in range(B):
+        ring = O.RingSeq(sinks=S, window=W, head=int(heads[b]), count=W, seq_len=lens[b])
+        slots = ring.chronological_slots()
+        vis = O.visible_positions(lens[b] - 1, S, W)
+        slot_of = dict(zip(vis, slots))
+        ref = O.decode_attention(qq[b], lambda j: kc[b, :, slot_of[j]], lambda j: vc[b, :, slot_of[j]], lens[b], S,
+                                 W, Hkv)
+        assert_bf16_close(got[b], ref)
+
+
+# ------------------------------------------------------------------ prefill (bf16 MFMA)
+
+@pytest.mark.parametrize("T,S,W,n_rep,d", [(300, 4, 100, 8, 128), (200, 0, 0, 4, 128), (129, 4, 64, 2, 64),
+                                           (77, 3, 1000, 1, 128), (333, 4, 65, 8, 64)])
+def test_prefill_chunk_from_zero(env, T, S, W, n_rep, d):
+    R, torch, dev = env
+    Hkv = 8 if n_rep > 1 else 4
+    Hq = Hkv * n_rep
+    cache = DevRing(R, torch, dev, torch.bfloat16, 1, Hkv, d, S, max(W, 1)) if W else \
+        DevPaged(R, torch, dev, torch.bfloat16, 1, Hkv, d, S, 0, np.zeros((1, 1), np.int32), 1)
+    q = _fill(torch, torch.empty(T, Hq, d, dtype=torch.bfloat16, device=dev), 71)
+    k = _fill(torch, torch.empty(T, Hkv, d, dtype=torch.bfloat16, device=dev), 72)
+    v = _fill(torch, torch.empty(T, Hkv, d, dtype=torch.bfloat16, device=dev), 73)
+    out = torch.empty_like(q)
+    R.prefill_attn(q, k, v, T, 0, Hq, cache.desc, 0, 0.0, out)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    qq, kk, vv = to_np64(q), to_np64(k), to_np64(v)
+    ref = O.prefill_attention(qq, lambda j: kk[j], lambda j: vv[j], 0, S, W, Hkv)
+    assert_bf16_close(to_np64(out), ref)
+
+
+def test_prefill_with_paged_prefix_equals_one_shot(env):
+    # chunked prefill into a cached prefix == the same rows of one-shot prefill
+    R, torch, dev = env
+    Hkv, n_rep, d, S, W = 8, 8, 128, 4, 100
+    Hq = Hkv * n_rep
+    T_all, pos0 = 400, 230
+    max_blocks = T_all // 16 + 1
+    table = synth.block_table_permutation(1, max_blocks, max_blocks + 3, 81)
+    cache = DevPaged(R, torch, dev, torch.bfloat16, 1, Hkv, d, S, W, table, max_blocks + 3)
+    q = _fill(torch, torch.empty(T_all, Hq, d, dtype=torch.bfloat16, device=dev), 82)
+    k = _fill(torch, torch.empty(T_all, Hkv, d, dtype=torch.bfloat16, device=dev), 83)
+    v = _fill(torch, torch.empty(T_all, Hkv, d, dtype=torch.bfloat16, device=dev), 84)
+    # place the prefix keys / values in their blocks (plumbing: a torch copy, no kernel of ours)
+    for p in range(pos0):
+        cache.k[table[0, p // 16], :, p % 16] = k[p]
+        cache.v[table[0, p // 16], :, p % 16] = v[p]
+    cache.seq_len.fill_(pos0)
+    T = T_all - pos0
+    out = torch.empty(T, Hq, d, dtype=torch.bfloat16, device=dev)
+    R.prefill_attn(q[pos0:], k[pos0:], v[pos0:], T, pos0, Hq, cache.desc, 0, 0.0, out)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    qq, kk, vv = to_np64(q), to_np64(k), to_np64(v)
+    ref = O.prefill_attention(qq[pos0:], lambda j: kk[j], lambda j: vv[j], pos0, S, W, Hkv)
+    assert_bf16_close(to_np64(out), ref)
+
+
+def test_prefill_ring_prefix_lost_is_flagged(env):
+    # a ring that no longer holds the chunk's prefix keys: flagged, not silently wrong
+    R, torch, dev = env
+    Hkv, d, S, W = 4, 64, 2, 8
+    cache = DevRing(R, torch, dev, torch.bfloat16, 1, Hkv, d, S, W)
+    cache.seq_len.fill_(40)
+    cache.count.fill_(W)
+    q = torch.zeros(6, 8, d, dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros(6, Hkv, d, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    R.prefill_attn(q, kv, kv, 6, 34, 8, cache.desc, 0, 0.0, out)  # needs keys from position 27, ring holds 32..39
+    torch.cuda.synchronize()
+    assert cache.err.item() & R.DEV_PREFIX_LOST
+
+
+# ------------------------------------------------------------------ rerotation (fp16 / int8), config-4-shaped
+
+def _contig_write(R, torch, dev, cfg, table, raw_dev, kv_dtype, L, T, Hkv, d, pos0):
+    """Write raw keys for positions pos0.. into a CONTIG cache via apply_append (one call per layer)."""
+    if kv_dtype == R.F16:
+        kc = torch.zeros(L, T, Hkv, d, dtype=torch.float16, device=dev)
+        sc = None
+    else:
+        kc = torch.zeros(L, T, Hkv, d, dtype=torch.int8, device=dev)
+        sc = torch.zeros(L, T, Hkv, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    pos = torch.arange(pos0, pos0 + T, dtype=torch.int32, device=dev)
+    for layer in range(L):
+        desc = R.kv_cache(R.CONTIG, kv_dtype, Hkv, d, kc[layer], capacity=T, pos0=pos0,
+                          k_scale=None if sc is None else sc[layer], err_word=err)
+        kin = raw_dev[layer].clone()
+        R.apply_append(cfg, table, table.shape[0], None, 0, kin, None, R.F16, T, pos, None, desc)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    desc_all = R.kv_cache(R.CONTIG, kv_dtype, Hkv, d, kc, capacity=T, pos0=pos0, k_scale=sc, err_word=err)
+    return kc, sc, desc_all
+
+
+def _turn_stats(turned, written, truth, unit):
+    """RMS(turned - truth) / RMS(written - truth) and worst |turned - truth| / unit."""
+    rt = np.sqrt(np.mean((turned - truth) ** 2))
+    rw = np.sqrt(np.mean((written - truth) ** 2))
+    worst = float(np.max(np.abs(turned - truth) / unit))
+    return rt / rw, worst
+
+
+@pytest.mark.parametrize("kind", ["f16", "i8"])
+@pytest.mark.parametrize("fa,fb", [(1.0, 2.0), (1.5, 2.0), (2.0, 1.0), (1.0, 1.125)])
+def test_rerotate_bounds(env, kind, fa, fb):
+    # keys written at factor A by apply_append, turned to B, compared with the fp64 key at B;
+    # the error of a key written directly at B is the yardstick (RMS <= 1.6x; worst <= 3 fp16
+    # ulps of the row max, or <= 2 int8 steps of B's row scale).
+    R, torch, dev = env
+    L, T, Hkv, d, r = 2, 512, 8, 128, 64
+    base_kw = dict(rope_theta=5e5, orig_max_pos=262144)
+    ca, cb = R.rope_cfg(d, r, yarn_factor=fa, **base_kw), R.rope_cfg(d, r, yarn_factor=fb, **base_kw)
+    oa, ob = oracle_cfg(ca), oracle_cfg(cb)
+    P = 524288
+    ta = _table(R, torch, dev, ca, P)
+    tb = _table(R, torch, dev, cb, P)
+    kv_dtype = R.F16 if kind == "f16" else R.I8
+    for pos0 in (262144 - T // 2, 519999 - T + 1):
+        raw = torch.from_numpy(synth.normal((L, T, Hkv, d), 90 + pos0 % 97)).to(dev, torch.float16)
+        kc, sc, desc = _contig_write(R, torch, dev, ca, ta, raw, kv_dtype, L, T, Hkv, d, pos0)
+        kw, sw, _ = _contig_write(R, torch, dev, cb, tb, raw, kv_dtype, L, T, Hkv, d, pos0)  # written at B
+        before = kc.clone()
+        R.rerotate(ca, cb, desc, L)
+        torch.cuda.synchronize()
+        rawn = to_np64(raw)
+        pos = np.arange(pos0, pos0 + T)
+        truth = np.stack([O.rotate_by_angle(rawn[l].reshape(T, Hkv, d), np.outer(pos, O.inv_freq(ob))[:, None, :],
+                                            r, True, O.mscale(ob)) for l in range(L)])
+        if kind == "f16":
+            turned, written = to_np64(kc), to_np64(kw)
+            rowmax = np.max(np.abs(written), axis=-1, keepdims=True)
+            unit = np.spacing(rowmax.astype(np.float16)).astype(np.float64)
+            assert np.array_equal(kc[..., r:].cpu().numpy(), before[..., r:].cpu().numpy())  # tail bitwise
+        else:
+            turned = kc.cpu().numpy().astype(np.float64) * sc.cpu().numpy().astype(np.float64)[..., None]
+            written = kw.cpu().numpy().astype(np.float64) * sw.cpu().numpy().astype(np.float64)[..., None]
+            unit = sw.cpu().numpy().astype(np.float64)[..., None]
+        ratio, worst = _turn_stats(turned, written, truth, unit)
+        assert ratio <= 1.6, ratio
+        assert worst <= (3.0 if kind == "f16" else 2.0), worst
+
+
+def test_rerotate_identity_and_oracle_parity(env):
+    R, torch, dev = env
+    L, T, Hkv, d, r = 1, 256, 8, 128, 64
+    ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.25, orig_max_pos=262144)
+    cb = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.875, orig_max_pos=262144)
+    pos0 = 400000
+    k = torch.from_numpy(synth.normal((L, T, Hkv, d), 95)).to(dev, torch.float16)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    desc = R.kv_cache(R.CONTIG, R.F16, Hkv, d, k, capacity=T, pos0=pos0, err_word=err)
+    before = k.clone()
+    R.rerotate(ca, ca, desc, L)  # A -> A: bitwise identity
+    torch.cuda.synchronize()
+    assert torch.equal(k, before)
+    R.rerotate(ca, cb, desc, L)
+    torch.cuda.synchronize()
+    ref = O.rerotate_rows(to_np64(before[0]).reshape(T, Hkv, d), np.arange(pos0, pos0 + T), oracle_cfg(ca),
+                          oracle_cfg(cb))
+    got = to_np64(k[0])
+    unit = np.maximum(np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64), 1e-6)
+    assert np.all(np.abs(got - ref) <= unit)  # within one fp16 ulp of the fp64 turn (fp32 math floor 1e-6)
+    # GPT-J pairing and bf16 / fp32 storage through the same kernel family
+    for dt, tdt in ((R.BF16, torch.bfloat16), (R.F32, torch.float32)):
+        for neox in (True, False):
+            a2 = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144, neox=neox)
+            b2 = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=2.0, orig_max_pos=262144, neox=neox)
+            k2 = torch.from_numpy(synth.normal((2, 64, Hkv, d), 96)).to(dev, tdt)
+            d2 = R.kv_cache(R.CONTIG, dt, Hkv, d, k2, capacity=64, pos0=300000, err_word=err)
+            b4 = to_np64(k2)
+            R.rerotate(a2, b2, d2, 2)
+            torch.cuda.synchronize()
+            ref2 = np.stack([O.rerotate_rows(b4[l], np.arange(300000, 300064), oracle_cfg(a2), oracle_cfg(b2))
+                             for l in range(2)])
+            if dt == R.F32:
+                assert rowwise(to_np64(k2), ref2) <= 1e-5
+            else:
+                assert_bf16_close(to_np64(k2), ref2, atol=2e-2, rtol=1e-2)
