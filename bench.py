@@ -1,0 +1,263 @@
+"""Benchmark of the sink + sliding-window KV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+The headline step is one decode step of a Llama-3-8B-shaped full-attention
+layer over a paged cache (batch 64, 32 query / 8 KV heads, d 128, bf16,
+context 32768 per sequence, 16-token blocks, random block table): rope +
+append of each sequence's new token, then split-K decode attention.
+`value` is the decode's algorithmic KV bytes per step time (GB/s).  The other
+hot-path rows (windowed decode at 128k, mixed prefill + decode, K re-rotation
+at a YaRN switch, table build) are timed in the same run and reported under
+"rows".  All inputs are seeded synthetic data already resident in HBM.
+
+Prints exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+METRIC = "decode-attn KV GB/s + % HBM peak; rerotate GB/s; prefill MFMA util"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def timed(torch, fn, reps, warmup=2):
+    """Average milliseconds of fn() over reps, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sliding_window_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_file: str, profile: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    The summary records the hash of the kernel source it was taken on; a
+    different hash (the kernel changed since) gives None.
+    """
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kernel_file, "common.hpp"):
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(R, torch, wl, budget_s=12.0):
+    """The fp64 oracle on the host, on whole sequences of the same workload until the budget is spent."""
+    import numpy as np
+
+    from oracle import ropekv_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q = wl.q.float().cpu().numpy().astype(np.float64)
+    out = wl.out.float().cpu().numpy().astype(np.float64)
+    n = wl.ctx
+    done, elapsed, worst = 0, 0.0, 0.0
+    order = [0, wl.B - 1] + list(range(1, wl.B - 1))
+    for b in order:
+        k, v = wl.kv_of(b)
+        t0 = time.perf_counter()
+        ref = O.decode_attention(q[b], lambda j: k[j], lambda j: v[j], n, 0, 0, wl.Hkv)
+        elapsed += time.perf_counter() - t0
+        worst = max(worst, float(np.max(np.abs(out[b] - ref) - (2e-2 + 1e-2 * np.abs(ref)))))
+        done += 1
+        if elapsed >= budget_s:
+            break
+    per_seq = wl.decode_bytes() / wl.B
+    return {
+        "value": round(per_seq * done / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {wl.B} sequences, full {n}-token context, all {wl.Hq} query heads (fp64 numpy)",
+        "parity_excess_max": worst,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
+              "see the sharding note in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sliding_window_kv_amd import ropekv as R
+    from sliding_window_kv_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    rows = {}
+
+    # ---------------- headline: paged decode step, batch 64 x 32768
+    log("setup: paged decode B=64 ctx=32768")
+    wl = WL.PagedDecode(R, torch, dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        wl.step()
+    b.record()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / args.steps
+    assert wl.err.item() == 0, f"device error word {wl.err.item()}"
+    dec_bytes = wl.decode_bytes()
+    value = dec_bytes / (ms_step * 1e-3) / 1e9
+    ms_dec = timed(torch, wl.decode, max(args.steps, 20))
+    ms_app = timed(torch, lambda: (wl.seq_len.fill_(wl.ctx - 1), wl.append()), max(args.steps, 20))
+    achieved = dec_bytes / (ms_dec * 1e-3) / 1e9
+    log(f"decode step {ms_step:.3f} ms, decode {ms_dec:.3f} ms = {achieved:.0f} GB/s")
+    traffic = counter_traffic("decode.hip", "decode_split_kernel_b64_ctx32768_pmc.md")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "decode_split_kernel + decode_combine_kernel (one ropekv_decode_attn call)",
+                "algorithmic_bytes_per_launch": dec_bytes}
+    rows["decode_b64_ctx32768"] = {"ms": round(ms_dec, 4), "GBps": round(achieved, 1),
+                                   "frac_hbm": round(achieved / HBM_PEAK_GBS, 4)}
+    rows["rope_append_b64"] = {"ms": round(ms_app, 4)}
+    ms_tab = timed(torch, lambda: R.build_table(wl.cfg, wl.ctx, wl.rope_table), 10)
+    rows["table_build_32768x128"] = {"ms": round(ms_tab, 4)}
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        wl.decode()  # outputs for the current q and cache state (the timing loops above rotated q again)
+        torch.cuda.synchronize()
+        cpu = cpu_baseline(R, torch, wl)
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        # ---------------- windowed decode at 128k: 3 ring layers + 1 full paged layer
+        log("setup: 128k windowed decode (3 ring layers + 1 full layer)")
+        tot_bytes, tot_ms = 0, 0.0
+        for layer in range(3):
+            r = WL.RingDecode(R, torch, dev, seed=3000 + 10 * layer)
+            ms = timed(torch, r.decode, 20)
+            rows[f"decode_ring_w4096_b32_layer{layer}"] = {"ms": round(ms, 4),
+                                                           "GBps": round(r.decode_bytes() / ms / 1e6, 1)}
+            tot_bytes += r.decode_bytes()
+            tot_ms += ms
+            assert r.err.item() == 0
+            del r
+        full = WL.PagedDecode(R, torch, dev, B=32, ctx=131072, seed=3100)
+        full.seq_len.fill_(131072)
+        ms = timed(torch, full.decode, 10)
+        rows["decode_full_b32_ctx131072"] = {"ms": round(ms, 4), "GBps": round(full.decode_bytes() / ms / 1e6, 1)}
+        tot_bytes += full.decode_bytes()
+        tot_ms += ms
+        del full
+        torch.cuda.empty_cache()
+        rows["decode_128k_4layer_total"] = {"ms": round(tot_ms, 4), "GBps": round(tot_bytes / tot_ms / 1e6, 1)}
+
+        # ---------------- mixed: 8192-token prefill chunk + 256-sequence windowed decode
+        log("setup: mixed prefill + decode")
+        pf = WL.Prefill(R, torch, dev)
+        ms = timed(torch, pf.run, 5)
+        tflops = pf.flops() / (ms * 1e-3) / 1e12
+        rows["prefill_t8192_h64_w4096"] = {"ms": round(ms, 4), "TFLOPs": round(tflops, 2),
+                                           "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4),
+                                           "algorithmic_flops": pf.flops()}
+        wd = WL.WindowedPagedDecode(R, torch, dev)
+        ms = timed(torch, wd.decode, 20)
+        rows["decode_windowed_b256_h64"] = {"ms": round(ms, 4), "GBps": round(wd.decode_bytes() / ms / 1e6, 1)}
+        assert wd.err.item() == 0
+        del pf, wd
+        torch.cuda.empty_cache()
+
+        # ---------------- K re-rotation at a YaRN switch, 64 layers x 524288 x 8 heads
+        for kind in ("f16", "i8"):
+            log(f"setup: rerotate {kind}")
+            rr = WL.Rerotate(R, torch, dev, kind=kind)
+            flip = [1.0, 1.125]
+
+            def one(rr=rr, flip=flip):
+                rr.run(flip[0], flip[1])
+                flip.reverse()
+
+            ms = timed(torch, one, 4, warmup=1)
+            rows[f"rerotate_{kind}_L64_T524288"] = {"ms": round(ms, 3), "GBps": round(rr.bytes() / ms / 1e6, 1),
+                                                    "frac_hbm": round(rr.bytes() / ms / 1e6 / HBM_PEAK_GBS, 4)}
+            if kind == "f16":
+                tcfg = rr.cfg(2.0)
+                tab = torch.empty(524288, 64, dtype=torch.float32, device=dev)
+                rows["table_build_524288x64"] = {"ms": round(timed(torch, lambda: R.build_table(tcfg, 524288, tab),
+                                                                   5), 4)}
+                del tab
+            del rr
+            torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "paged decode step (rope+append, split-K decode), Llama-3-8B-shaped layer: "
+                               "batch 64, 32 q / 8 kv heads, d 128, context 32768, 16-token blocks, random table",
+                   "global_batch": 64, "seq_len": 32768, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

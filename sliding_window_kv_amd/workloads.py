@@ -1,0 +1,222 @@
+"""Device-resident synthetic workloads at full size (shared by bench.py and the full-size tests).
+
+Each class allocates its buffers with torch, fills them from seeded
+generators, and exposes the calls the hot path makes.  Nothing here computes
+any part of the method: positions, slots, visibility and attention all run in
+libropekv.so.  Byte and FLOP counts are the algorithmic work of each call
+(what the method must move or compute, not what a dense kernel would).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import synth
+
+BLOCK = 16
+
+
+def visible_count(p: int, sinks: int, window: int) -> int:
+    """Number of keys the query at position p sees (window 0 = causal)."""
+    if window == 0 or p + 1 <= window:
+        return p + 1
+    return window + min(sinks, p + 1 - window)
+
+
+class PagedDecode:
+    """Full-attention paged decode of one layer (Llama-3-8B-shaped by default).
+
+    B sequences of ctx tokens after the step's append, Hq / Hkv heads, d dims,
+    bf16, 16-token blocks, block table = a seeded random permutation of the
+    pool.  A step appends each sequence's new token at position ctx - 1
+    (rotating q and k, writing k and v into the pool) and runs decode.
+    """
+
+    def __init__(self, R, torch, dev, B=64, Hq=32, Hkv=8, d=128, ctx=32768, theta=5e5, seed=2000):
+        self.R, self.torch, self.dev = R, torch, dev
+        self.B, self.Hq, self.Hkv, self.d, self.ctx = B, Hq, Hkv, d, ctx
+        self.max_blocks = (ctx + BLOCK - 1) // BLOCK
+        self.num_blocks = B * self.max_blocks
+        table = synth.block_table_permutation(B, self.max_blocks, self.num_blocks, seed)
+        self.table_host = table
+        bf = torch.bfloat16
+        self.k = synth.device_normal_(torch.empty(self.num_blocks, Hkv, BLOCK, d, dtype=bf, device=dev), seed + 1)
+        self.v = synth.device_normal_(torch.empty(self.num_blocks, Hkv, BLOCK, d, dtype=bf, device=dev), seed + 2)
+        self.table = torch.from_numpy(table).to(dev)
+        self.seq_len = torch.full((B,), ctx - 1, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.desc = R.kv_cache(R.PAGED, R.BF16, Hkv, d, self.k, self.v, batch=B, sinks=0, window=0,
+                               block_size=BLOCK, max_blocks=self.max_blocks, num_blocks=self.num_blocks,
+                               block_table=self.table, seq_len=self.seq_len, err_word=self.err)
+        self.cfg = R.rope_cfg(d, d, rope_theta=theta)
+        self.rope_table = torch.empty(ctx, d, dtype=torch.float32, device=dev)
+        R.build_table(self.cfg, ctx, self.rope_table)
+        self.q = synth.device_normal_(torch.empty(B, Hq, d, dtype=bf, device=dev), seed + 3)
+        self.k_new = synth.device_normal_(torch.empty(B, Hkv, d, dtype=bf, device=dev), seed + 4)
+        self.v_new = synth.device_normal_(torch.empty(B, Hkv, d, dtype=bf, device=dev), seed + 5)
+        self.pos = torch.full((B,), ctx - 1, dtype=torch.int32, device=dev)
+        self.seq_ids = torch.arange(B, dtype=torch.int32, device=dev)
+        self.out = torch.empty(B, Hq, d, dtype=bf, device=dev)
+        self.ws_bytes = R.decode_workspace_size(B, Hq, self.desc)
+        self.ws = torch.empty(self.ws_bytes // 4 + 1, dtype=torch.float32, device=dev)
+
+    def step(self):
+        """One decode step: reset to ctx-1 cached tokens, rope + append the new token, decode."""
+        self.seq_len.fill_(self.ctx - 1)
+        self.append()
+        self.decode()
+
+    def append(self):
+        R = self.R
+        R.apply_append(self.cfg, self.rope_table, self.ctx, self.q, self.Hq, self.k_new, self.v_new, R.BF16, self.B,
+                       self.pos, self.seq_ids, self.desc)
+
+    def decode(self):
+        self.R.decode_attn(self.q, self.B, self.Hq, self.desc, 0.0, self.out, self.ws, self.ws_bytes)
+
+    def decode_bytes(self) -> int:
+        """K + V of the visible keys once per KV head, plus q, out and the block-table entries read."""
+        kv = 2 * self.B * self.Hkv * self.ctx * self.d * 2
+        qo = 2 * self.B * self.Hq * self.d * 2
+        bt = self.B * self.max_blocks * 4
+        return kv + qo + bt
+
+    def kv_of(self, b: int):
+        """Keys / values of sequence b by position, as host float64 [ctx, Hkv, d] (for the oracle)."""
+        rows = self.table[b]
+        k = self.k[rows].permute(0, 2, 1, 3).reshape(-1, self.Hkv, self.d)[: self.ctx]
+        v = self.v[rows].permute(0, 2, 1, 3).reshape(-1, self.Hkv, self.d)[: self.ctx]
+        return (k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64))
+
+
+class RingDecode:
+    """Windowed decode of one ring layer: full ring (count = W), head at a seeded random offset."""
+
+    def __init__(self, R, torch, dev, B=32, Hq=32, Hkv=8, d=128, S=4, W=4096, n=131072, seed=3000):
+        self.R, self.torch = R, torch
+        self.B, self.Hq, self.Hkv, self.d, self.S, self.W, self.n = B, Hq, Hkv, d, S, W, n
+        self.C = S + W
+        bf = torch.bfloat16
+        self.k = synth.device_normal_(torch.empty(B, Hkv, self.C, d, dtype=bf, device=dev), seed + 1)
+        self.v = synth.device_normal_(torch.empty(B, Hkv, self.C, d, dtype=bf, device=dev), seed + 2)
+        self.head = torch.from_numpy(synth.uniform_ints(B, 0, W, seed + 3)).to(dev)
+        self.count = torch.full((B,), W, dtype=torch.int32, device=dev)
+        self.seq_len = torch.full((B,), n, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.desc = R.kv_cache(R.RING, R.BF16, Hkv, d, self.k, self.v, batch=B, capacity=self.C, sinks=S, window=W,
+                               ring_head=self.head, ring_count=self.count, seq_len=self.seq_len, err_word=self.err)
+        self.q = synth.device_normal_(torch.empty(B, Hq, d, dtype=bf, device=dev), seed + 4)
+        self.out = torch.empty_like(self.q)
+        self.ws_bytes = R.decode_workspace_size(B, Hq, self.desc)
+        self.ws = torch.empty(self.ws_bytes // 4 + 1, dtype=torch.float32, device=dev)
+
+    def decode(self):
+        self.R.decode_attn(self.q, self.B, self.Hq, self.desc, 0.0, self.out, self.ws, self.ws_bytes)
+
+    def decode_bytes(self) -> int:
+        vis = min(self.n, self.S + self.W)
+        return 2 * self.B * self.Hkv * vis * self.d * 2 + 2 * self.B * self.Hq * self.d * 2
+
+
+class WindowedPagedDecode:
+    """Sink + window paged decode with ragged lengths; only live blocks are allocated, the rest are null."""
+
+    def __init__(self, R, torch, dev, B=256, Hq=64, Hkv=8, d=128, S=4, W=4096, lo=1024, hi=131072, seed=5000):
+        self.R, self.torch = R, torch
+        self.B, self.Hq, self.Hkv, self.d, self.S, self.W = B, Hq, Hkv, d, S, W
+        self.lens = synth.uniform_lengths(B, lo, hi, seed)
+        self.max_blocks = (int(self.lens.max()) + BLOCK - 1) // BLOCK
+        table = np.full((B, self.max_blocks), -1, dtype=np.int64)
+        nxt = 0
+        for b, n in enumerate(self.lens):
+            live = set(range((min(S, n) + BLOCK - 1) // BLOCK))
+            first = max(0, n - W) // BLOCK
+            live |= set(range(first, (n - 1) // BLOCK + 1))
+            for j in sorted(live):
+                table[b, j] = nxt
+                nxt += 1
+        self.num_blocks = nxt
+        perm = synth.rng(seed + 9).permutation(nxt)  # scatter the live blocks over the pool
+        table = np.where(table >= 0, perm[np.maximum(table, 0)], -1).astype(np.int32)
+        self.table_host = table
+        bf = torch.bfloat16
+        self.k = synth.device_normal_(torch.empty(nxt, Hkv, BLOCK, d, dtype=bf, device=dev), seed + 1)
+        self.v = synth.device_normal_(torch.empty(nxt, Hkv, BLOCK, d, dtype=bf, device=dev), seed + 2)
+        self.table = torch.from_numpy(table).to(dev)
+        self.seq_len = torch.from_numpy(self.lens.astype(np.int32)).to(dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.desc = R.kv_cache(R.PAGED, R.BF16, Hkv, d, self.k, self.v, batch=B, sinks=S, window=W, block_size=BLOCK,
+                               max_blocks=self.max_blocks, num_blocks=nxt, block_table=self.table,
+                               seq_len=self.seq_len, err_word=self.err)
+        self.q = synth.device_normal_(torch.empty(B, Hq, d, dtype=bf, device=dev), seed + 4)
+        self.out = torch.empty_like(self.q)
+        self.ws_bytes = R.decode_workspace_size(B, Hq, self.desc)
+        self.ws = torch.empty(self.ws_bytes // 4 + 1, dtype=torch.float32, device=dev)
+
+    def decode(self):
+        self.R.decode_attn(self.q, self.B, self.Hq, self.desc, 0.0, self.out, self.ws, self.ws_bytes)
+
+    def decode_bytes(self) -> int:
+        vis = sum(visible_count(int(n) - 1, self.S, self.W) for n in self.lens)
+        blocks = int((self.table_host >= 0).sum())
+        return 2 * vis * self.Hkv * self.d * 2 + 2 * self.B * self.Hq * self.d * 2 + blocks * 4
+
+
+class Prefill:
+    """One prompt chunk of T tokens at pos0 = 0 over the sink + window mask, bf16."""
+
+    def __init__(self, R, torch, dev, T=8192, Hq=64, Hkv=8, d=128, S=4, W=4096, seed=6000):
+        self.R, self.torch = R, torch
+        self.T, self.Hq, self.Hkv, self.d, self.S, self.W = T, Hq, Hkv, d, S, W
+        bf = torch.bfloat16
+        self.q = synth.device_normal_(torch.empty(T, Hq, d, dtype=bf, device=dev), seed + 1)
+        self.k = synth.device_normal_(torch.empty(T, Hkv, d, dtype=bf, device=dev), seed + 2)
+        self.v = synth.device_normal_(torch.empty(T, Hkv, d, dtype=bf, device=dev), seed + 3)
+        self.out = torch.empty_like(self.q)
+        # the chunk starts at position 0: the cache only describes the layer (S, W, heads)
+        self.kc = torch.zeros(1, Hkv, S + W, d, dtype=bf, device=dev)
+        self.int_state = torch.zeros(4, dtype=torch.int32, device=dev)
+        st = self.int_state
+        self.desc = R.kv_cache(R.RING, R.BF16, Hkv, d, self.kc, self.kc, batch=1, capacity=S + W, sinks=S, window=W,
+                               ring_head=st[0:1], ring_count=st[1:2], seq_len=st[2:3], err_word=st[3:4])
+
+    def run(self):
+        self.R.prefill_attn(self.q, self.k, self.v, self.T, 0, self.Hq, self.desc, 0, 0.0, self.out)
+
+    def flops(self) -> int:
+        vis = sum(visible_count(p, self.S, self.W) for p in range(self.T))
+        return 4 * self.d * self.Hq * vis
+
+
+class Rerotate:
+    """Cached keys of L layers x T positions x Hkv heads, fp16 or int8 + per-row fp32 scale, turned in place."""
+
+    def __init__(self, R, torch, dev, kind="f16", L=64, T=524288, Hkv=8, d=128, r=64, theta=5e5, L0=262144, pos0=0,
+                 seed=4000):
+        self.R, self.torch = R, torch
+        self.kind, self.L, self.T, self.Hkv, self.d, self.r = kind, L, T, Hkv, d, r
+        self.theta, self.L0 = theta, L0
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        if kind == "f16":
+            self.k = synth.device_normal_(torch.empty(L, T, Hkv, d, dtype=torch.float16, device=dev), seed)
+            self.scale = None
+            dt = R.F16
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed)
+            self.k = torch.randint(-127, 128, (L, T, Hkv, d), dtype=torch.int8, device=dev, generator=g)
+            self.scale = torch.rand(L, T, Hkv, dtype=torch.float32, device=dev, generator=g) * 0.02 + 0.01
+            dt = R.I8
+        self.desc = R.kv_cache(R.CONTIG, dt, Hkv, d, self.k, capacity=T, pos0=pos0, k_scale=self.scale,
+                               err_word=self.err)
+
+    def cfg(self, s: float):
+        return self.R.rope_cfg(self.d, self.r, rope_theta=self.theta, yarn_factor=s, orig_max_pos=self.L0)
+
+    def run(self, s_from: float, s_to: float):
+        self.R.rerotate(self.cfg(s_from), self.cfg(s_to), self.desc, self.L)
+
+    def bytes(self) -> int:
+        rows = self.L * self.T * self.Hkv
+        if self.kind == "f16":
+            return 2 * rows * self.r * 2
+        return 2 * rows * (self.d + 4)
