@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 2 GiB device copy 5 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
@@ -127,6 +129,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        n = 1 << 29  # 2 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read_per_copy": 4 * n, "copy_probe_bytes_written_per_copy": 4 * n}))
+        return
 
     from sliding_window_kv_amd import ropekv as R
     from sliding_window_kv_amd import workloads as WL

@@ -164,8 +164,9 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
  * ws; a second launch combines them.  n == 0 gives a zero row.
  *   q   [batch, n_q_heads, d] kv_dtype (rotated), out same shape and dtype
  *   scale: 0 means 1/sqrt(d)
- * Layouts RING and PAGED; kv_dtype F32 or BF16; d 64 or 128; n_q_heads a
- * multiple of Hkv with n_rep <= 16. */
+ * Layouts RING and PAGED (block_size 16); kv_dtype F32 or BF16; d 64 or 128;
+ * n_rep = n_q_heads / Hkv in {1, 2, 4, 8}.  ws: device, at least
+ * ropekv_decode_workspace_size() bytes, caller-owned, overwritten. */
 int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
                        const ropekv_kv_cache *cache, float scale, void *out, void *ws,
                        size_t ws_bytes, ropekv_stream_t stream);
@@ -177,7 +178,8 @@ int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
  * pos0 from the cache (RING or PAGED) of sequence seq_id.  For RING the
  * prefix must still be in the ring (call before appending the chunk, or keep
  * pos0 + T <= C); a missing key sets ROPEKV_DEV_PREFIX_LOST.
- *   q [T, n_q_heads, d], out same; dtype = kv_dtype (F32 or BF16), d 64 or 128.
+ *   q [T, n_q_heads, d], out same; dtype = kv_dtype (F32 or BF16), d 64 or 128,
+ *   n_rep = n_q_heads / Hkv in {1, 2, 4, 8}; seq_id only read when pos0 > 0.
  * bf16 runs on MFMA with fp32 accumulation; tiles no query can see are skipped. */
 int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, int32_t pos0,
                         int32_t n_q_heads, const ropekv_kv_cache *cache, int32_t seq_id,
