@@ -227,18 +227,21 @@ def round_f16(x: np.ndarray) -> np.ndarray:
 
 
 def quant_int8_rows(x: np.ndarray):
-    """Per-row symmetric int8: scale = max|x| / 127, code = clamp(rne(x / scale), -127, 127).
+    """Per-row symmetric int8: amax = max|x|, scale = amax / 127, code = clamp(rne(x * (127 / amax)), -127, 127).
 
-    Decided in float32 (the row is rounded to float32 first).  An all-zero row
-    gets scale 0 and codes 0.  Returns (codes int8 [..., d], scale float32 [...]).
+    The pages fix only "dequantise, rotate, requantise" with a per-row scale;
+    the integer decision is taken in float32 with the reciprocal 127 / amax
+    (the row is rounded to float32 first), the precision and form the kernels
+    use.  An all-zero row gets scale 0 and codes 0.
+    Returns (codes int8 [..., d], scale float32 [...]).
     """
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
-    amax = np.max(np.abs(x32), axis=-1)
+    amax = np.max(np.abs(x32), axis=-1).astype(np.float32)
     scale = (amax / np.float32(127.0)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    q = np.rint((x32 / safe[..., None]).astype(np.float32))
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    inv = np.where(amax > 0, (np.float32(127.0) / safe).astype(np.float32), np.float32(0.0)).astype(np.float32)
+    q = np.rint((x32 * inv[..., None]).astype(np.float32))
     q = np.clip(q, -127, 127)
-    q = np.where(scale[..., None] > 0, q, 0)
     return q.astype(np.int8), scale
 
 

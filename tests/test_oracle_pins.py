@@ -478,3 +478,14 @@ def test_int8_rows():
     deq = O.dequant_int8_rows(codes, scale)
     err = np.abs(deq - x)
     assert np.all(err <= scale[:, None] * 0.5 + 1e-6)
+    # the code is the nearest integer to x * 127 / max|x| (exact arithmetic), except where
+    # that quotient sits within float32 rounding of a half-integer
+    exact = x * 127.0 / np.max(np.abs(x), axis=1, keepdims=True).clip(1e-300)
+    frac = np.abs(exact - np.floor(exact) - 0.5)
+    safe = frac > 1e-4
+    assert np.array_equal(codes[safe], np.rint(exact)[safe].astype(np.int8))
+    # a row that is already a multiple of its step round-trips exactly
+    k = RNG.integers(-127, 128, (5, 64)).astype(np.float64)
+    k[:, 0] = 127
+    c2, s2 = O.quant_int8_rows(k * 0.25)
+    assert np.array_equal(c2, k.astype(np.int8)) and np.allclose(s2, 0.25)
