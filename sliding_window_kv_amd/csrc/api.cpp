@@ -195,7 +195,7 @@ int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads, const ro
   const DecodePlan pl = plan_decode(batch, n_q_heads, *cache);
   if (ws_bytes < pl.ws_bytes)
     return fail(ROPEKV_ENOSPACE, "workspace %zu bytes < %zu needed", ws_bytes, pl.ws_bytes);
-  if (pl.splits > 65535) return fail(ROPEKV_ERANGE, "too many splits (%d)", pl.splits);
+  if (pl.splits > 1024) return fail(ROPEKV_ERANGE, "cache too long for one decode call (%d splits)", pl.splits);
   return hip_status(launch_decode(q, batch, n_q_heads, *cache, resolve_scale(scale, cache->head_dim), out, ws, pl,
                                   (hipStream_t)stream),
                     "decode launch");

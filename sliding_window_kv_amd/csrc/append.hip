@@ -172,16 +172,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             store_elem(c.k, coff + e, kvdt, val);
         }
         if (kvdt == ROPEKV_I8) {
-          // per-row symmetric int8: scale = max|x| / 127, code = rne(x / scale)
+          // per-row symmetric int8: scale = max|x| / 127, code = rne(x * (127 / max|x|))
           wave_lds_sync();
           float amax = 0.f;
           for (int e = lane; e < d; e += 64) amax = fmaxf(amax, fabsf(rowbuf[wave][e]));
           for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);
           const float scale = amax / 127.0f;
+          const float inv = amax > 0.f ? 127.0f / amax : 0.f;
           int8_t *kc = (int8_t *)c.k;
           for (int e = lane; e < d; e += 64) {
-            float qv = 0.f;
-            if (scale > 0.f) qv = fminf(fmaxf(rintf(rowbuf[wave][e] / scale), -127.f), 127.f);
+            const float qv = fminf(fmaxf(rintf(rowbuf[wave][e] * inv), -127.f), 127.f);
             kc[coff + e] = (int8_t)qv;
           }
           if (lane == 0) c.k_scale[scale_base + h] = scale;

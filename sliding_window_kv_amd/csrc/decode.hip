@@ -159,6 +159,24 @@ __device__ __forceinline__ void load_bytes(uint32_t *dst, const void *src) {
   }
 }
 
+// A lane's share of one K (or Q) row for the 16x16 MFMAs: QB bytes as 16-byte
+// pieces, piece i taken from byte offset (4 i + grp) * 16 of the row.  The four
+// lane groups of a row thus read 64 contiguous bytes per load instruction.
+// Any fixed assignment of row chunks to (piece, group) is valid because the
+// d-reduction is order-free, as long as K and Q use the same one.
+template <int QB>
+__device__ __forceinline__ void load_pieces(uint32_t *dst, const char *row, int grp) {
+  static_assert(QB % 16 == 0, "pieces are 16 bytes");
+#pragma unroll
+  for (int i = 0; i < QB / 16; ++i) {
+    const uint4 v = *(const uint4 *)(row + (4 * i + grp) * 16);
+    dst[4 * i + 0] = v.x;
+    dst[4 * i + 1] = v.y;
+    dst[4 * i + 2] = v.z;
+    dst[4 * i + 3] = v.w;
+  }
+}
+
 template <typename T>
 struct ElemTraits;
 template <>
@@ -178,10 +196,9 @@ struct ElemTraits<bf16_t> {
 };
 
 // S^T (16 keys x 16 columns) += K (16 x D) . Q^T (D x 16), lane-distributed
-// as: kw / qw = the lane's quarter-row of K (row lane%16) / of Q (column
-// lane%16), elements [(D/4)(lane/16), (D/4)(lane/16 + 1)).  The reduction
-// over d is order-free, so lanes feed their quarter-rows to consecutive
-// MFMAs in the same element order on both sides.
+// as: kw / qw = the lane's share (load_pieces) of K row lane%16 / of Q column
+// lane%16.  The reduction over d is order-free, so lanes feed their shares
+// to consecutive MFMAs in the same element order on both sides.
 template <typename T, int D>
 __device__ __forceinline__ f32x4 qk_tile(const uint32_t *kw, const uint32_t *qw) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -207,6 +224,16 @@ __device__ __forceinline__ f32x4 qk_tile(const uint32_t *kw, const uint32_t *qw)
   return acc;
 }
 
+// K and V pieces of one tile held by one lane, plus which of its 4 V keys are visible.
+template <int QB, int VB>
+struct TileFrag {
+  uint32_t kw[QB / 4];
+  uint32_t vw[4][VB / 4];
+  bool vis[4];
+};
+
+constexpr int kMaxTps = 256;  // tiles per split (block-table entries staged in LDS)
+
 template <typename T, int D, int NREP>
 __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
                                                            float sl2, float *__restrict__ ws, int tps, int splits) {
@@ -214,10 +241,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
   constexpr int QB = (D / 4) * TR::kBytes;   // bytes of a lane's K / Q quarter-row
   constexpr int E = D / 16;                  // V dims per lane per key
   constexpr int VB = E * TR::kBytes;         // bytes of a lane's V piece per key
+  using Frag = TileFrag<QB, VB>;
   __shared__ float s_p[4][NREP][kTile];
   __shared__ float s_corr[4][NREP];
   __shared__ float s_m[4][NREP], s_l[4][NREP];
   __shared__ float s_acc[4][NREP][D];
+  __shared__ int s_bid[kMaxTps];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -230,15 +259,69 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
   if (t_begin >= st.ntiles) return;
   const int t_end = min(st.ntiles, t_begin + tps);
 
+  // stage this split's block ids (paged) so no tile waits on a dependent table load
+  if (c.layout == ROPEKV_PAGED) {
+    for (int i = threadIdx.x; i < t_end - t_begin; i += 256) {
+      const int tile = t_begin + i;
+      const int blk = tile < st.nsb ? tile : st.fr + (tile - st.nsb);
+      s_bid[i] = (blk < c.max_blocks) ? c.block_table[(long)b * c.max_blocks + blk] : -1;
+    }
+  }
+
   // Q^T fragment: column `col` = query head g * NREP + col (zero beyond NREP)
   uint32_t qw[QB / 4];
   if (col < NREP) {
     const char *qrow = (const char *)qp + ((long)(b * Hkv * NREP + g * NREP + col) * D) * TR::kBytes;
-    load_bytes<QB>(qw, qrow + grp * QB);
+    load_pieces<QB>(qw, qrow, grp);
   } else {
 #pragma unroll
     for (int i = 0; i < QB / 4; ++i) qw[i] = 0u;
   }
+  __syncthreads();
+
+  const char *kbase = (const char *)c.k;
+  const char *vbase = (const char *)c.v;
+  const long head_base = ((long)b * Hkv + g) * (long)c.capacity * D;  // RING: slot 0 of (b, g)
+
+  // Issue the loads of one tile (all in flight until first use).  Returns false for a null block.
+  auto load_tile = [&](Frag &f, int tile) -> bool {
+    long base;
+    int pos0 = 0, slot0 = 0;
+    bool ok = true;
+    if (c.layout == ROPEKV_PAGED) {
+      const int bid = s_bid[tile - t_begin];
+      const int blk = tile < st.nsb ? tile : st.fr + (tile - st.nsb);
+      pos0 = blk * kTile;
+      ok = bid >= 0 && bid < c.num_blocks;
+      base = ok ? ((long)bid * Hkv + g) * kTile * D : 0;
+    } else {
+      slot0 = tile * kTile;
+      base = head_base;
+    }
+    auto roff = [&](int r) -> long {
+      if (c.layout == ROPEKV_PAGED) return base + (long)r * D;
+      return base + (long)min(slot0 + r, c.capacity - 1) * D;
+    };
+    auto visible = [&](int r) -> bool {
+      if (!ok) return false;
+      if (c.layout == ROPEKV_PAGED) {
+        const int pos = pos0 + r;
+        return pos < st.ns || (pos >= st.rs && pos < st.n);
+      }
+      const int slot = slot0 + r;
+      if (slot >= c.capacity) return false;
+      if (slot < c.sinks) return slot < st.ns;
+      return imod(slot - c.sinks - st.oldest, c.window) < st.count;
+    };
+    if (ok) {
+      load_pieces<QB>(f.kw, kbase + roff(col) * TR::kBytes, grp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_bytes<VB>(f.vw[j], vbase + roff(4 * grp + j) * TR::kBytes + col * VB);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.vis[j] = visible(4 * grp + j);
+    return ok;
+  };
 
   float m_run = kNegBig, l_run = 0.f;
   float acc[NREP][E];
@@ -247,67 +330,77 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
 
-  const char *kbase = (const char *)c.k;
-  const char *vbase = (const char *)c.v;
   bool bad_tile = false;
-
-  for (int tile = t_begin + wave; tile < t_end; tile += 4) {
-    const TileRows tr = tile_rows(c, st, b, g, tile, D);
-    if (!tr.ok) {
+  int tile = t_begin + wave;
+  Frag cur, nxt;
+  bool cur_ok = tile < t_end ? load_tile(cur, tile) : false;
+  for (; tile < t_end; tile += 4) {
+    bool nxt_ok = false;
+    if (tile + 4 < t_end) nxt_ok = load_tile(nxt, tile + 4);
+    if (!cur_ok) {
       bad_tile = true;
-      continue;
-    }
-    uint32_t kw[QB / 4];
-    load_bytes<QB>(kw, kbase + row_offset(c, tr, col, D) * TR::kBytes + grp * QB);
-    uint32_t vw[4][VB / 4];
-    bool vis[4];
+    } else {
+      const f32x4 sacc = qk_tile<T, D>(cur.kw, qw);
+      float s[4];
+      float mx = kNegBig;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * grp + j;
-      vis[j] = row_visible(c, st, tr, r);
-      load_bytes<VB>(vw[j], vbase + row_offset(c, tr, r, D) * TR::kBytes + col * VB);
-    }
-    const f32x4 sacc = qk_tile<T, D>(kw, qw);
-    float s[4];
-    float mx = kNegBig;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s[j] = vis[j] ? sacc[j] * sl2 : -INFINITY;
-      mx = fmaxf(mx, s[j]);
-    }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = exp2f(m_run - m_new);
-    float psum = 0.f;
-    float pj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pj[j] = exp2f(s[j] - m_new);
-      psum += pj[j];
-    }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    if (col < NREP) {
-      *(float4 *)&s_p[wave][col][4 * grp] = make_float4(pj[0], pj[1], pj[2], pj[3]);
-      if (grp == 0) s_corr[wave][col] = corr;
-    }
-    wave_lds_sync();
-    // V layout: this lane holds keys 4*grp + j, dims [col*E, col*E + E)
-#pragma unroll
-    for (int h = 0; h < NREP; ++h) {
-      const float ch = s_corr[wave][h];
-      const float4 ph = *(const float4 *)&s_p[wave][h][4 * grp];
-      const float pv[4] = {ph.x, ph.y, ph.z, ph.w};
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float a = acc[h][e] * ch;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a += vis[j] ? pv[j] * TR::get(vw[j], e) : 0.f;
-        acc[h][e] = a;
+      for (int j = 0; j < 4; ++j) {
+        s[j] = cur.vis[j] ? sacc[j] * sl2 : -INFINITY;
+        mx = fmaxf(mx, s[j]);
       }
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = exp2f(m_run - m_new);
+      float psum = 0.f;
+      float pj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pj[j] = exp2f(s[j] - m_new);
+        psum += pj[j];
+      }
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+      if (col < NREP) {
+        *(float4 *)&s_p[wave][col][4 * grp] = make_float4(pj[0], pj[1], pj[2], pj[3]);
+        if (grp == 0) s_corr[wave][col] = corr;
+      }
+      // invisible keys have p = 0, but their rows may hold anything: zero them once
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!cur.vis[j]) {
+#pragma unroll
+          for (int w = 0; w < VB / 4; ++w) cur.vw[j][w] = 0u;
+        }
+      float vf[4][E];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[j][e] = TR::get(cur.vw[j], e);
+      wave_lds_sync();
+      // V layout: this lane holds keys 4*grp + j, dims [col*E, col*E + E)
+#pragma unroll
+      for (int h = 0; h < NREP; ++h) {
+        const float ch = s_corr[wave][h];  // the same value in every lane: a uniform branch
+        const float4 ph = *(const float4 *)&s_p[wave][h][4 * grp];
+        if (ch != 1.f) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[h][e] *= ch;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float a = acc[h][e];
+          a = fmaf(ph.x, vf[0][e], a);
+          a = fmaf(ph.y, vf[1][e], a);
+          a = fmaf(ph.z, vf[2][e], a);
+          a = fmaf(ph.w, vf[3][e], a);
+          acc[h][e] = a;
+        }
+      }
+      wave_lds_sync();
     }
-    wave_lds_sync();
+    cur = nxt;
+    cur_ok = nxt_ok;
   }
   if (bad_tile && lane == 0) dev_error(c.err_word, ROPEKV_DEV_NULL_BLOCK);
 
@@ -356,27 +449,53 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
   }
 }
 
+// Merge the split partials of one (sequence, query head): weights exp2(m_s - m)
+// computed once per split, then one coalesced pass over the partial rows.
+constexpr int kMaxSplits = 1024;
+
 template <typename T, int D, int NREP>
 __global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, const float *__restrict__ ws,
                                                              void *__restrict__ out, int tps, int splits) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[128];
   const int h = blockIdx.x, b = blockIdx.y;
   const int Hkv = c.num_kv_heads;
   const int g = h / NREP, hh = h % NREP;
   const SeqTiles st = seq_tiles(c, b);
-  const int used = min((st.ntiles + tps - 1) / tps, splits);
+  const int used = min(min((st.ntiles + tps - 1) / tps, splits), kMaxSplits);
   const long obase = ((long)b * Hkv * NREP + h) * D;
   const float *src = ws + (((long)(b * Hkv + g) * splits) * NREP + hh) * (D + 2);
   const long sstride = (long)NREP * (D + 2);
+  // global max over splits
+  float m = kNegBig;
+  for (int s = threadIdx.x; s < used; s += blockDim.x) m = fmaxf(m, src[s * sstride + D]);
+  s_red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) s_red[threadIdx.x] = fmaxf(s_red[threadIdx.x], s_red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  m = s_red[0];
+  __syncthreads();
+  // per-split weights and the total weight l
+  float l = 0.f;
+  for (int s = threadIdx.x; s < used; s += blockDim.x) {
+    const float w = exp2f(src[s * sstride + D] - m);
+    s_w[s] = w;
+    l += w * src[s * sstride + D + 1];
+  }
+  s_red[threadIdx.x] = l;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) s_red[threadIdx.x] += s_red[threadIdx.x + w];
+    __syncthreads();
+  }
+  l = s_red[0];
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float m = kNegBig;
-    for (int s = 0; s < used; ++s) m = fmaxf(m, src[s * sstride + D]);
-    float a = 0.f, l = 0.f;
-    for (int s = 0; s < used; ++s) {
-      const float f = exp2f(src[s * sstride + D] - m);
-      a += f * src[s * sstride + dd];
-      l += f * src[s * sstride + D + 1];
-    }
-    ElemTraits<T>::put(out, obase + dd, l > 0.f ? a / l : 0.f);
+    float a = 0.f;
+    for (int s = 0; s < used; ++s) a = fmaf(s_w[s], src[s * sstride + dd], a);
+    ElemTraits<T>::put(out, obase + dd, a * inv);
   }
 }
 
@@ -458,11 +577,15 @@ DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c) {
     max_tiles = (c.capacity + kTile - 1) / kTile;
   }
   if (max_tiles < 1) max_tiles = 1;
-  int tps = 32;
+  // tiles per split: aim for ~8192 workgroups over the batch, 8..128 tiles each
+  const long work = (long)max_tiles * batch * c.num_kv_heads;
+  int tps = 8;
+  while (tps < 128 && (long)tps * 8192 < work) tps *= 2;
   if (const char *e = getenv("ROPEKV_DECODE_TPS")) {
     const int v = atoi(e);
-    if (v >= 1 && v <= 4096) tps = v;
+    if (v >= 1 && v <= kMaxTps) tps = v;
   }
+  while ((max_tiles + tps - 1) / tps > kMaxSplits && tps < kMaxTps) tps *= 2;
   pl.max_tiles = max_tiles;
   pl.tiles_per_split = tps;
   pl.splits = (max_tiles + tps - 1) / tps;

@@ -9,10 +9,12 @@
 // Workgroup: one KV head g and BM = 128 / n_rep consecutive chunk positions
 // for all n_rep query heads of g (128 query rows, so every K/V byte staged in
 // LDS serves all heads of the group).  Four waves, 32 rows each (two 16-row
-// tiles of one head).  Key tiles of 64 keys.
+// tiles of one head).  Key tiles of 64 keys, double-buffered in LDS: the next
+// tile's global loads are in flight while the current one is computed.
 //   S^T = K . Q^T   (MFMA; lane keeps its query row's 16 scores per tile)
 //   online softmax in the log2 domain, fp32
-//   O^T += V^T . P^T (MFMA; bf16: V staged transposed in LDS, P rounded to bf16)
+//   O^T += V^T . P^T (MFMA; V stays row-major in LDS and the V^T operand is
+//                     read with the gfx950 LDS transpose read; P rounded to bf16)
 #include "kernels.hpp"
 
 namespace ropekv {
@@ -71,23 +73,41 @@ __device__ __forceinline__ void copy16(void *dst, const void *src) {
   for (int i = 0; i < NB / 16; ++i) ((uint4 *)dst)[i] = ((const uint4 *)src)[i];
 }
 
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 (round to nearest even, hardware conversion)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const float2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+// LDS transpose read: within each 16-lane group, lane i receives element i % 4 of
+// the 8 bytes addressed by lanes 4j + i / 4 (j = 0..3) of its group.
+__device__ __forceinline__ uint2 lds_read_tr16(const void *p) {
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v *)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
 template <typename T, int D, int NREP>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr bool kBF = sizeof(T) == 2;
   constexpr int EB = sizeof(T);
   constexpr int BM = 128 / NREP;           // chunk positions per workgroup
-  constexpr int KP = kBF ? D + 8 : D + 4;  // K (and fp32 V) LDS pitch in elements
-  constexpr int VTP = kBN + 8;             // bf16 V^T pitch in elements
+  constexpr int KP = kBF ? D + 8 : D + 4;  // K / V LDS row pitch in elements
   constexpr int QB = (D / 4) * EB;         // bytes of a quarter row
-  __shared__ __attribute__((aligned(16))) T k_lds[kBN * KP];
-  __shared__ __attribute__((aligned(16))) T v_lds[kBF ? D * VTP : kBN * KP];
+  constexpr int CH = QB;                   // bytes staged per thread per tile and tensor
+  constexpr int TILE = kBN * KP;           // elements of one staged tile
+  __shared__ __attribute__((aligned(16))) T k_lds[2][TILE];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][TILE];
 
   const ropekv_kv_cache &c = a.c;
   const int g = blockIdx.y;
   const int t0 = blockIdx.x * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int Hkv = c.num_kv_heads, Hq = a.n_q_heads;
+  const int Hq = a.n_q_heads;
   const int S = c.sinks, W = c.window;
   const int qp_lo = a.pos0 + t0;
   const int qp_hi = a.pos0 + min(t0 + BM, a.T) - 1;
@@ -101,8 +121,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     tq[rt] = t0 + R % BM;
     head[rt] = g * NREP + R / BM;
     if (tq[rt] < a.T) {
-      const char *src = (const char *)a.q + (((long)tq[rt] * Hq + head[rt]) * D) * EB + grp * QB;
-      copy16<QB>(qw[rt], src);
+      copy16<QB>(qw[rt], (const char *)a.q + (((long)tq[rt] * Hq + head[rt]) * D) * EB + grp * QB);
     } else {
 #pragma unroll
       for (int i = 0; i < QB / 4; ++i) qw[rt][i] = 0u;
@@ -112,15 +131,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // key tiles: sink tiles [0, nst), then recent tiles [first, last]
   const int last = qp_hi / kBN;
   int nst = 0, first = 0;
-  if (W == 0) {
-    first = 0;
-  } else {
+  if (W > 0) {
     const int sink_hi = min(S, qp_hi + 1);
     nst = (sink_hi + kBN - 1) / kBN;
     const int lo = max(0, qp_lo - W + 1);
     first = max(lo / kBN, nst);
   }
   const int ntiles = nst + max(0, last - first + 1);
+
+  // staging: thread = (key, quarter of the row); K and V rows go to LDS unchanged
+  const int skey = tid >> 2, sq = tid & 3;
+  bool lost = false;
+  uint32_t kreg[CH / 4], vreg[CH / 4];
+  auto fetch = [&](int kt) {
+    const int kb = kt < nst ? kt : first + (kt - nst);
+    const int j = kb * kBN + skey;
+    bool chunk;
+    const long off = key_row(a, j, g, D, &chunk);
+    const bool needed = j <= qp_hi && (W == 0 || j < S || j > qp_lo - W);
+    if (off < 0 && needed && j < a.pos0) lost = true;
+    if (off >= 0) {
+      copy16<CH>(kreg, (const char *)(chunk ? a.k : c.k) + off * EB + sq * CH);
+      copy16<CH>(vreg, (const char *)(chunk ? a.v : c.v) + off * EB + sq * CH);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CH / 4; ++i) kreg[i] = vreg[i] = 0u;
+    }
+  };
+  auto stash = [&](int buf) {
+    copy16<CH>(&k_lds[buf][skey * KP + sq * (D / 4)], kreg);
+    copy16<CH>(&v_lds[buf][skey * KP + sq * (D / 4)], vreg);
+  };
 
   float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
   f32x4 o[2][D / 16];
@@ -129,75 +170,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bool lost = false;
+  if (ntiles > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) fetch(kt + 1);  // in flight while this tile is computed
+    const T *kl = k_lds[buf];
+    const T *vl = v_lds[buf];
     const int kb = kt < nst ? kt : first + (kt - nst);
     const int j0 = kb * kBN;
-    // ---- stage K (natural) and V (bf16: transposed) in LDS
-    {
-      constexpr int CH = (D / 4) * EB;  // bytes per thread-chunk (a quarter row)
-      const int key = tid >> 2, qd = tid & 3;
-      const int j = j0 + key;
-      bool chunk;
-      long off = key_row(a, j, g, D, &chunk);
-      const bool needed = j <= qp_hi && (W == 0 || j < S || j > qp_lo - W);
-      if (off < 0 && needed && j < a.pos0) lost = true;
-      uint32_t kbuf[CH / 4];
-      if (off >= 0) {
-        const char *src = (const char *)(chunk ? a.k : c.k) + off * EB + qd * CH;
-        copy16<CH>(kbuf, src);
-      } else {
-#pragma unroll
-        for (int i = 0; i < CH / 4; ++i) kbuf[i] = 0u;
-      }
-      copy16<CH>(&k_lds[key * KP + qd * (D / 4)], kbuf);
-      if constexpr (!kBF) {
-        uint32_t vbuf[CH / 4];
-        if (off >= 0) {
-          const char *src = (const char *)(chunk ? a.v : c.v) + off * EB + qd * CH;
-          copy16<CH>(vbuf, src);
-        } else {
-#pragma unroll
-          for (int i = 0; i < CH / 4; ++i) vbuf[i] = 0u;
-        }
-        copy16<CH>(&v_lds[key * KP + qd * (D / 4)], vbuf);
-      }
-    }
-    if constexpr (kBF) {
-      // V^T: each item = 2 keys x 16 dims -> 16 dwords (key pair per dim)
-      constexpr int ITEMS = (kBN / 2) * (D / 16);
-      for (int it = tid; it < ITEMS; it += 256) {
-        const int kp = it / (D / 16), dc = it % (D / 16);
-        uint32_t w2[2][8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = j0 + 2 * kp + u;
-          bool chunk;
-          const long off = key_row(a, j, g, D, &chunk);
-          if (off >= 0) {
-            copy16<32>(w2[u], (const char *)(chunk ? a.v : c.v) + (off + dc * 16) * 2);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w2[u][i] = 0u;
-          }
-        }
-        uint32_t *vt = (uint32_t *)v_lds;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t lo16 = (e & 1) ? (w2[0][e >> 1] >> 16) : (w2[0][e >> 1] & 0xffffu);
-          const uint32_t hi16 = (e & 1) ? (w2[1][e >> 1] & 0xffff0000u) : (w2[1][e >> 1] << 16);
-          vt[((dc * 16 + e) * VTP + 2 * kp) >> 1] = lo16 | hi16;
-        }
-      }
-    }
-    __syncthreads();
 
-    // ---- scores
+    // ---- scores S^T = K Q^T (raw dot products)
     f32x4 sc[2][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint32_t kw[QB / 4];
-      copy16<QB>(kw, &k_lds[(16 * st + col) * KP + grp * (D / 4)]);
+      copy16<QB>(kw, &kl[(16 * st + col) * KP + grp * (D / 4)]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -222,41 +213,49 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // does every query of this workgroup see every key of the tile?
     const int jmax = j0 + kBN - 1;
     const bool full = jmax <= qp_lo && (W == 0 || jmax < S || qp_hi - j0 < W);
+    bool moved = false;
     float corr[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const int qpos = a.pos0 + tq[rt];
-      float mx = kNegBig;
+      if (!full) {
+        const int qpos = a.pos0 + tq[rt];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int jp = j0 + 16 * st + 4 * grp + j;
+            const bool vis = jp <= qpos && (W == 0 || jp < S || qpos - jp < W);
+            sc[rt][st][j] = vis ? sc[rt][st][j] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float s = sc[rt][st][j] * a.sl2;
-          if (!full) {
-            const int jp = j0 + 16 * st + 4 * grp + j;
-            const bool vis = jp <= qpos && (W == 0 || jp < S || qpos - jp < W);
-            s = vis ? s : -INFINITY;
-          }
-          sc[rt][st][j] = s;
-          mx = fmaxf(mx, s);
-        }
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[rt][st][j]);
       mx = wave_max_xor(mx, 16);
       mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m_run[rt], mx);
-      corr[rt] = exp2f(m_run[rt] - m_new);
+      const float m_new = fmaxf(m_run[rt], mx * a.sl2);  // sl2 > 0: the max commutes with the scale
+      corr[rt] = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+      moved |= m_new != m_run[rt];
       float ps = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = exp2f(sc[rt][st][j] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[rt][st][j], a.sl2, -m_new));
           sc[rt][st][j] = p;
           ps += p;
         }
       l_run[rt] = l_run[rt] * corr[rt] + ps;
       m_run[rt] = m_new;
+    }
+    // rows whose max did not move keep their accumulators as they are
+    if (__any(moved)) {
 #pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] *= corr[rt];
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] *= corr[rt];
     }
 
     // ---- O^T += V^T P^T
@@ -269,15 +268,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const f32x4 pp = sc[rt][2 * u + h2];
-            pw[rt][2 * h2] = (uint32_t)f_to_bf16(pp[0]) | ((uint32_t)f_to_bf16(pp[1]) << 16);
-            pw[rt][2 * h2 + 1] = (uint32_t)f_to_bf16(pp[2]) | ((uint32_t)f_to_bf16(pp[3]) << 16);
+            pw[rt][2 * h2] = pack_bf16(pp[0], pp[1]);
+            pw[rt][2 * h2 + 1] = pack_bf16(pp[2], pp[3]);
           }
+        // lane (grp, src = col) points at V[32u + 4grp + src/4 (+16)][16 mt + 4 (src % 4)]
+        const int vrow = 32 * u + 4 * grp + (col >> 2);
+        const int vcol = 4 * (col & 3);
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) {
-          const uint32_t *vt = (const uint32_t *)v_lds;
-          const int row = 16 * mt + col;
-          const uint2 lo = *(const uint2 *)&vt[(row * VTP + 32 * u + 4 * grp) >> 1];
-          const uint2 hi = *(const uint2 *)&vt[(row * VTP + 32 * u + 16 + 4 * grp) >> 1];
+          const uint2 lo = lds_read_tr16(&vl[vrow * KP + 16 * mt + vcol]);
+          const uint2 hi = lds_read_tr16(&vl[(vrow + 16) * KP + 16 * mt + vcol]);
           typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
           const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
@@ -295,12 +295,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int st = 0; st < 4; ++st)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float vv = ((const float *)v_lds)[(16 * st + 4 * grp + j) * KP + 16 * mt + col];
+            const float vv = ((const float *)vl)[(16 * st + 4 * grp + j) * KP + 16 * mt + col];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
               o[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sc[rt][st][j], o[rt][mt], 0, 0, 0);
           }
     }
+    if (kt + 1 < ntiles) stash(buf ^ 1);  // the other buffer was last read before the previous barrier
     __syncthreads();
   }
   if (lost) dev_error(c.err_word, ROPEKV_DEV_PREFIX_LOST);
@@ -319,8 +320,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         const int d0 = 16 * mt + 4 * grp;
         if constexpr (kBF) {
           uint2 w;
-          w.x = (uint32_t)f_to_bf16(o[rt][mt][0] * inv) | ((uint32_t)f_to_bf16(o[rt][mt][1] * inv) << 16);
-          w.y = (uint32_t)f_to_bf16(o[rt][mt][2] * inv) | ((uint32_t)f_to_bf16(o[rt][mt][3] * inv) << 16);
+          w.x = pack_bf16(o[rt][mt][0] * inv, o[rt][mt][1] * inv);
+          w.y = pack_bf16(o[rt][mt][2] * inv, o[rt][mt][3] * inv);
           *(uint2 *)((uint16_t *)a.out + ob + d0) = w;
         } else {
           *(float4 *)((float *)a.out + ob + d0) =

@@ -90,12 +90,15 @@ __device__ __forceinline__ void vst(char *p, const uint32_t *w) {
 }
 
 // Float keys.  A thread turns PP consecutive pairs of one row: NeoX loads PP
-// elements from each half, GPT-J 2 PP interleaved elements.
+// elements from each half, GPT-J 2 PP interleaved elements.  Items (row, pair
+// group) of all layers form one index space; each thread issues the loads of
+// U items before turning any, so U x 32 bytes per lane are in flight.
 template <typename T, int PP>
 __global__ __launch_bounds__(256) void rerotate_float_kernel(RerotArgs a) {
   constexpr int EB = sizeof(T);
   constexpr int NB = PP * EB;
   constexpr int NW = (NB + 3) / 4;
+  constexpr int U = 4;
   __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
   __shared__ double s_dw[256];
   const int t0 = blockIdx.x * kPT;
@@ -103,51 +106,215 @@ __global__ __launch_bounds__(256) void rerotate_float_kernel(RerotArgs a) {
   const int half = a.to.rotary_dim / 2;
   const int tpr = half / PP;
   const int npos = min(kPT, a.rows_T - t0);
-  const int items = npos * a.Hkv * tpr;
+  const int items_pl = npos * a.Hkv * tpr;
+  const int total = items_pl * a.n_layers;
   const int neox = a.to.neox;
   const long layer_stride = (long)a.rows_T * a.Hkv * a.D;
   char *kb = (char *)a.k;
-  for (int layer = 0; layer < a.n_layers; ++layer) {
-    const long lbase = layer * layer_stride + (long)t0 * a.Hkv * a.D;
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-      const int rr = it / tpr, q = it % tpr;
-      const int pt = rr / a.Hkv;
-      const long rbase = lbase + (long)rr * a.D;
+  for (int base = threadIdx.x; base < total; base += 256 * U) {
+    uint32_t w1[U][NW], w2[U][NW];
+    char *p1[U];
+    char *p2[U];
+    int jj[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = base + u * 256;
+      live[u] = it < total;
+      const int itc = live[u] ? it : base;
+      const int layer = itc / items_pl, rem = itc % items_pl;
+      const int rr = rem / tpr, q = rem % tpr;
+      const long rbase = layer * layer_stride + ((long)t0 * a.Hkv + rr) * a.D;
       const int j0 = q * PP;
-      const float *cs = &s_cs[pt * half + j0];
-      const float *sn = &s_sn[pt * half + j0];
+      jj[u] = (rr / a.Hkv) * half + j0;
+      p1[u] = kb + (rbase + (neox ? j0 : 2 * j0)) * EB;
+      p2[u] = neox ? kb + (rbase + half + j0) * EB : p1[u] + NB;
+      if (live[u]) {
+        vld<NB>(w1[u], p1[u]);
+        vld<NB>(w2[u], p2[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!live[u]) continue;
+      const float *cs = &s_cs[jj[u]];
+      const float *sn = &s_sn[jj[u]];
       if (neox) {
-        uint32_t w1[NW], w2[NW];
-        char *p1 = kb + (rbase + j0) * EB;
-        char *p2 = kb + (rbase + half + j0) * EB;
-        vld<NB>(w1, p1);
-        vld<NB>(w2, p2);
 #pragma unroll
-        for (int u = 0; u < PP; ++u) {
-          const float x1 = vget<T>(w1, u), x2 = vget<T>(w2, u);
-          vput<T>(w1, u, (x1 * cs[u] - x2 * sn[u]) * gain);
-          vput<T>(w2, u, (x2 * cs[u] + x1 * sn[u]) * gain);
+        for (int e = 0; e < PP; ++e) {
+          const float x1 = vget<T>(w1[u], e), x2 = vget<T>(w2[u], e);
+          vput<T>(w1[u], e, (x1 * cs[e] - x2 * sn[e]) * gain);
+          vput<T>(w2[u], e, (x2 * cs[e] + x1 * sn[e]) * gain);
         }
-        vst<NB>(p1, w1);
-        vst<NB>(p2, w2);
       } else {
-        uint32_t w[2 * NW];
-        char *p = kb + (rbase + 2 * j0) * EB;
-        vld<NB>(w, p);
-        vld<NB>(w + NW, p + NB);
+        // 2 PP interleaved elements: pair e is (2e, 2e+1) across the two NB-byte halves
 #pragma unroll
-        for (int u = 0; u < PP; ++u) {
-          // element 2u sits at w[...] in the first NB bytes when 2u < PP, else in the second
-          const int e1 = 2 * u, e2 = 2 * u + 1;
-          uint32_t *b1 = e1 < PP ? w : w + NW;
-          uint32_t *b2 = e2 < PP ? w : w + NW;
-          const int i1 = e1 < PP ? e1 : e1 - PP, i2 = e2 < PP ? e2 : e2 - PP;
+        for (int e = 0; e < PP; ++e) {
+          uint32_t *b1 = 2 * e < PP ? w1[u] : w2[u];
+          uint32_t *b2 = 2 * e + 1 < PP ? w1[u] : w2[u];
+          const int i1 = 2 * e < PP ? 2 * e : 2 * e - PP, i2 = 2 * e + 1 < PP ? 2 * e + 1 : 2 * e + 1 - PP;
           const float x1 = vget<T>(b1, i1), x2 = vget<T>(b2, i2);
-          vput<T>(b1, i1, (x1 * cs[u] - x2 * sn[u]) * gain);
-          vput<T>(b2, i2, (x2 * cs[u] + x1 * sn[u]) * gain);
+          vput<T>(b1, i1, (x1 * cs[e] - x2 * sn[e]) * gain);
+          vput<T>(b2, i2, (x2 * cs[e] + x1 * sn[e]) * gain);
         }
-        vst<NB>(p, w);
-        vst<NB>(p + NB, w + NW);
+      }
+      vst<NB>(p1[u], w1[u]);
+      vst<NB>(p2[u], w2[u]);
+    }
+  }
+}
+
+// int8 keys with a per-row fp32 scale, L = D / 16 lanes per row, 16 codes per
+// lane: NeoX lane q holds pairs [qH, qH + H) (H codes from each half) and
+// TL = 16 - 2H tail codes [r + q TL, ...); GPT-J lane q holds the 2H
+// interleaved codes of the same pairs.  No lane exchange is needed to turn a
+// pair; the row's absmax is a reduction over its L lanes.  Codes are
+// requantised as rne(y * (127 / max|y|)).
+template <int N>
+__device__ __forceinline__ void ld_n(uint32_t *w, const int8_t *p) {
+  if constexpr (N == 16) {
+    const uint4 v = *(const uint4 *)p;
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (N == 12) {
+    const uint3 v = *(const uint3 *)p;
+    w[0] = v.x; w[1] = v.y; w[2] = v.z;
+  } else if constexpr (N == 8) {
+    const uint2 v = *(const uint2 *)p;
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (N == 4) {
+    w[0] = *(const uint32_t *)p;
+  } else if constexpr (N == 2) {
+    w[0] = *(const uint16_t *)p;
+  }
+}
+template <int N>
+__device__ __forceinline__ void st_n(int8_t *p, const uint32_t *w) {
+  if constexpr (N == 16) {
+    *(uint4 *)p = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (N == 12) {
+    *(uint3 *)p = make_uint3(w[0], w[1], w[2]);
+  } else if constexpr (N == 8) {
+    *(uint2 *)p = make_uint2(w[0], w[1]);
+  } else if constexpr (N == 4) {
+    *(uint32_t *)p = w[0];
+  } else if constexpr (N == 2) {
+    *(uint16_t *)p = (uint16_t)w[0];
+  }
+}
+// code byte e of a word array -> float (the byte is a signed int8)
+__device__ __forceinline__ float code_at(const uint32_t *w, int e) {
+  return (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
+  constexpr int TL = 16 - 2 * H;
+  constexpr int NR = (2 * H + 3) / 4;   // words of the rotary codes
+  constexpr int NT = (TL + 3) / 4 > 0 ? (TL + 3) / 4 : 1;
+  constexpr int U = 2;
+  __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
+  __shared__ double s_dw[256];
+  const int t0 = blockIdx.x * kPT;
+  const float gain = angle_setup(a, t0, s_cs, s_sn, s_dw);
+  const int half = a.to.rotary_dim / 2;
+  const int r = a.to.rotary_dim;
+  const int L = a.D / 16;
+  const int npos = min(kPT, a.rows_T - t0);
+  const int items_pl = npos * a.Hkv * L;
+  const int total = items_pl * a.n_layers;
+  const int neox = a.to.neox;
+  const long layer_rows = (long)a.rows_T * a.Hkv;
+  int8_t *kc = (int8_t *)a.k;
+  // every thread runs the same number of iterations, so the lane reductions stay converged
+  for (int base = 0; base < total; base += 256 * U) {
+    uint32_t wr[U][NR], wt[U][NT], wr2[U][NR];
+    float sco[U];
+    long row[U];
+    int jj[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = base + u * 256 + (int)threadIdx.x;
+      live[u] = it < total;
+      const int itc = live[u] ? it : 0;
+      const int layer = itc / items_pl, rem = itc % items_pl;
+      const int rr = rem / L, q = rem % L;
+      row[u] = layer * layer_rows + (long)t0 * a.Hkv + rr;
+      jj[u] = (rr / a.Hkv) * half + q * H;
+      const int8_t *rp = kc + row[u] * a.D;
+      sco[u] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) wr[u][i] = wr2[u][i] = 0u;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) wt[u][i] = 0u;
+      if (live[u]) {
+        sco[u] = a.scale[row[u]];
+        if (neox) {
+          ld_n<H>(wr[u], rp + q * H);
+          ld_n<H>(wr2[u], rp + half + q * H);
+        } else {
+          ld_n<2 * H>(wr[u], rp + 2 * q * H);
+        }
+        if constexpr (TL > 0) ld_n<TL>(wt[u], rp + r + q * TL);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float y[16];
+      const float *cs = &s_cs[jj[u]];
+      const float *sn = &s_sn[jj[u]];
+#pragma unroll
+      for (int e = 0; e < H; ++e) {
+        float x1, x2;
+        if (neox) {
+          x1 = code_at(wr[u], e) * sco[u];
+          x2 = code_at(wr2[u], e) * sco[u];
+        } else {
+          x1 = code_at(wr[u], 2 * e) * sco[u];
+          x2 = code_at(wr[u], 2 * e + 1) * sco[u];
+        }
+        y[2 * e] = (x1 * cs[e] - x2 * sn[e]) * gain;
+        y[2 * e + 1] = (x2 * cs[e] + x1 * sn[e]) * gain;
+      }
+#pragma unroll
+      for (int e = 0; e < TL; ++e) y[2 * H + e] = code_at(wt[u], e) * sco[u];
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
+      for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+      const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+      uint32_t o1[NR], o2[NR], ot[NT];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) o1[i] = o2[i] = 0u;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) ot[i] = 0u;
+      auto code = [&](float v) -> uint32_t {
+        return (uint32_t)(uint8_t)(int8_t)fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
+      };
+#pragma unroll
+      for (int e = 0; e < H; ++e) {
+        if (neox) {
+          o1[e >> 2] |= code(y[2 * e]) << (8 * (e & 3));
+          o2[e >> 2] |= code(y[2 * e + 1]) << (8 * (e & 3));
+        } else {
+          o1[(2 * e) >> 2] |= code(y[2 * e]) << (8 * ((2 * e) & 3));
+          o1[(2 * e + 1) >> 2] |= code(y[2 * e + 1]) << (8 * ((2 * e + 1) & 3));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < TL; ++e) ot[e >> 2] |= code(y[2 * H + e]) << (8 * (e & 3));
+      if (live[u]) {
+        const int rem = (base + u * 256 + (int)threadIdx.x) % items_pl;
+        const int q = rem % L;
+        int8_t *rp = kc + row[u] * a.D;
+        if (neox) {
+          st_n<H>(rp + q * H, o1);
+          st_n<H>(rp + half + q * H, o2);
+        } else {
+          st_n<2 * H>(rp + 2 * q * H, o1);
+        }
+        if constexpr (TL > 0) st_n<TL>(rp + r + q * TL, ot);
+        if (q == 0) a.scale[row[u]] = amax / 127.0f;
       }
     }
   }
@@ -224,11 +391,11 @@ __global__ __launch_bounds__(256) void rerotate_int8_kernel(RerotArgs a) {
       for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
       for (int m = lpr >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
       const float sc_new = amax / 127.0f;
+      const float inv = amax > 0.f ? 127.0f / amax : 0.f;
       uint32_t out[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float qv = 0.f;
-        if (sc_new > 0.f) qv = fminf(fmaxf(rintf(y[e] / sc_new), -127.f), 127.f);
+        const float qv = fminf(fmaxf(rintf(y[e] * inv), -127.f), 127.f);
         out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)qv) << (8 * (e & 3));
       }
       if (live) {
@@ -256,7 +423,21 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
   dim3 grid((c.capacity + kPT - 1) / kPT);
   const int half = to.rotary_dim / 2;
   switch (c.kv_dtype) {
-    case ROPEKV_I8: hipLaunchKernelGGL(rerotate_int8_kernel, grid, dim3(256), 0, s, a); break;
+    case ROPEKV_I8: {
+      // lane-local pairs when each lane's 16 codes split into whole pairs and tail: H = half / (D / 16)
+      const int L = c.head_dim / 16;
+      const int H = (half % L == 0) ? half / L : 0;
+      const bool tail_ok = ((c.head_dim - to.rotary_dim) % L) == 0;
+      if (tail_ok && H == 8)
+        hipLaunchKernelGGL(rerotate_int8_lanes_kernel<8>, grid, dim3(256), 0, s, a);
+      else if (tail_ok && H == 4)
+        hipLaunchKernelGGL(rerotate_int8_lanes_kernel<4>, grid, dim3(256), 0, s, a);
+      else if (tail_ok && H == 2)
+        hipLaunchKernelGGL(rerotate_int8_lanes_kernel<2>, grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL(rerotate_int8_kernel, grid, dim3(256), 0, s, a);
+      break;
+    }
     case ROPEKV_F16:
       if (half % 8 == 0)
         hipLaunchKernelGGL((rerotate_float_kernel<f16_t, 8>), grid, dim3(256), 0, s, a);

@@ -568,3 +568,33 @@ def test_rerotate_identity_and_oracle_parity(env):
                 assert rowwise(to_np64(k2), ref2) <= 1e-5
             else:
                 assert_bf16_close(to_np64(k2), ref2, atol=2e-2, rtol=1e-2)
+
+
+@pytest.mark.parametrize("r,neox", [(128, True), (32, True), (96, True), (64, False), (32, False), (64, True)])
+def test_rerotate_int8_shapes_vs_oracle(env, r, neox):
+    # every int8 code path (lane-local pairs with 2, 4 or 8 codes per half, GPT-J, and the
+    # shuffle fallback for r = 96) against the oracle's dequantise-turn-requantise
+    R, torch, dev = env
+    L, T, Hkv, d = 2, 48, 4, 128
+    ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144, neox=neox)
+    cb = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.625, orig_max_pos=262144, neox=neox)
+    pos0 = 300007
+    g = torch.Generator(device=dev)
+    g.manual_seed(97 + r)
+    codes = torch.randint(-127, 128, (L, T, Hkv, d), dtype=torch.int8, device=dev, generator=g)
+    scale = torch.rand(L, T, Hkv, dtype=torch.float32, device=dev, generator=g) * 0.02 + 0.01
+    scale[0, 3, 1] = 0.0  # an all-zero row
+    codes[0, 3, 1] = 0
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    desc = R.kv_cache(R.CONTIG, R.I8, Hkv, d, codes, capacity=T, pos0=pos0, k_scale=scale, err_word=err)
+    c0, s0 = codes.cpu().numpy(), scale.cpu().numpy()
+    R.rerotate(ca, cb, desc, L)
+    torch.cuda.synchronize()
+    c1, s1 = codes.cpu().numpy(), scale.cpu().numpy()
+    pos = np.repeat(np.arange(pos0, pos0 + T), Hkv)
+    for l in range(L):
+        wc, ws_ = O.rerotate_int8_rows(c0[l].reshape(-1, d), s0[l].reshape(-1), pos, oracle_cfg(ca), oracle_cfg(cb))
+        np.testing.assert_allclose(s1[l].reshape(-1), ws_, rtol=1e-5)
+        diff = np.abs(c1[l].reshape(-1, d).astype(np.int32) - wc.astype(np.int32))
+        assert diff.max() <= 1 and diff.mean() < 0.01, (diff.max(), diff.mean())
+    assert s1[0, 3, 1] == 0 and np.all(c1[0, 3, 1] == 0)
