@@ -11,6 +11,7 @@ namespace ropekv {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // bfloat16 / half stored as raw bits so the arithmetic is always fp32.
 struct bf16_t { uint16_t x; };

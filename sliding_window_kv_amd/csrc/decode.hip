@@ -143,7 +143,7 @@ __device__ __forceinline__ void load_bytes(uint32_t *dst, const void *src) {
   if constexpr (NB % 16 == 0) {
 #pragma unroll
     for (int i = 0; i < NB / 16; ++i) {
-      const uint4 v = ((const uint4 *)src)[i];
+      const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)src + i);
       dst[4 * i + 0] = v.x;
       dst[4 * i + 1] = v.y;
       dst[4 * i + 2] = v.z;
@@ -164,17 +164,21 @@ __device__ __forceinline__ void load_bytes(uint32_t *dst, const void *src) {
 // lane groups of a row thus read 64 contiguous bytes per load instruction.
 // Any fixed assignment of row chunks to (piece, group) is valid because the
 // d-reduction is order-free, as long as K and Q use the same one.
+// K and V are streamed once per decode: nontemporal loads keep them from
+// displacing reusable lines in the caches.
+__device__ __forceinline__ void stream16(uint32_t *dst, const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+  dst[0] = v.x;
+  dst[1] = v.y;
+  dst[2] = v.z;
+  dst[3] = v.w;
+}
+
 template <int QB>
 __device__ __forceinline__ void load_pieces(uint32_t *dst, const char *row, int grp) {
   static_assert(QB % 16 == 0, "pieces are 16 bytes");
 #pragma unroll
-  for (int i = 0; i < QB / 16; ++i) {
-    const uint4 v = *(const uint4 *)(row + (4 * i + grp) * 16);
-    dst[4 * i + 0] = v.x;
-    dst[4 * i + 1] = v.y;
-    dst[4 * i + 2] = v.z;
-    dst[4 * i + 3] = v.w;
-  }
+  for (int i = 0; i < QB / 16; ++i) stream16(dst + 4 * i, row + (4 * i + grp) * 16);
 }
 
 template <typename T>

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
   constexpr int TL = 16 - 2 * H;
   constexpr int NR = (2 * H + 3) / 4;   // words of the rotary codes
   constexpr int NT = (TL + 3) / 4 > 0 ? (TL + 3) / 4 : 1;
-  constexpr int U = 2;
+  constexpr int U = 4;
   __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
   __shared__ double s_dw[256];
   const int t0 = blockIdx.x * kPT;
@@ -220,101 +220,93 @@ __global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
   const int r = a.to.rotary_dim;
   const int L = a.D / 16;
   const int npos = min(kPT, a.rows_T - t0);
-  const int items_pl = npos * a.Hkv * L;
-  const int total = items_pl * a.n_layers;
+  const int items = npos * a.Hkv * L;  // a multiple of L: a row's lanes are always active together
   const int neox = a.to.neox;
   const long layer_rows = (long)a.rows_T * a.Hkv;
   int8_t *kc = (int8_t *)a.k;
-  // every thread runs the same number of iterations, so the lane reductions stay converged
-  for (int base = 0; base < total; base += 256 * U) {
-    uint32_t wr[U][NR], wt[U][NT], wr2[U][NR];
-    float sco[U];
-    long row[U];
-    int jj[U];
-    bool live[U];
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int rr = it / L, q = it % L;
+    const float *cs = &s_cs[(rr / a.Hkv) * half + q * H];
+    const float *sn = &s_sn[(rr / a.Hkv) * half + q * H];
+    const long row0 = (long)t0 * a.Hkv + rr;
+    for (int l0 = 0; l0 < a.n_layers; l0 += U) {
+      uint32_t wr[U][NR], wr2[U][NR], wt[U][NT];
+      float sco[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int it = base + u * 256 + (int)threadIdx.x;
-      live[u] = it < total;
-      const int itc = live[u] ? it : 0;
-      const int layer = itc / items_pl, rem = itc % items_pl;
-      const int rr = rem / L, q = rem % L;
-      row[u] = layer * layer_rows + (long)t0 * a.Hkv + rr;
-      jj[u] = (rr / a.Hkv) * half + q * H;
-      const int8_t *rp = kc + row[u] * a.D;
-      sco[u] = 0.f;
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i) wr[u][i] = wr2[u][i] = 0u;
+        for (int i = 0; i < NR; ++i) wr[u][i] = wr2[u][i] = 0u;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) wt[u][i] = 0u;
-      if (live[u]) {
-        sco[u] = a.scale[row[u]];
-        if (neox) {
-          ld_n<H>(wr[u], rp + q * H);
-          ld_n<H>(wr2[u], rp + half + q * H);
-        } else {
-          ld_n<2 * H>(wr[u], rp + 2 * q * H);
-        }
-        if constexpr (TL > 0) ld_n<TL>(wt[u], rp + r + q * TL);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float y[16];
-      const float *cs = &s_cs[jj[u]];
-      const float *sn = &s_sn[jj[u]];
-#pragma unroll
-      for (int e = 0; e < H; ++e) {
-        float x1, x2;
-        if (neox) {
-          x1 = code_at(wr[u], e) * sco[u];
-          x2 = code_at(wr2[u], e) * sco[u];
-        } else {
-          x1 = code_at(wr[u], 2 * e) * sco[u];
-          x2 = code_at(wr[u], 2 * e + 1) * sco[u];
-        }
-        y[2 * e] = (x1 * cs[e] - x2 * sn[e]) * gain;
-        y[2 * e + 1] = (x2 * cs[e] + x1 * sn[e]) * gain;
-      }
-#pragma unroll
-      for (int e = 0; e < TL; ++e) y[2 * H + e] = code_at(wt[u], e) * sco[u];
-      float amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
-      for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-      const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-      uint32_t o1[NR], o2[NR], ot[NT];
-#pragma unroll
-      for (int i = 0; i < NR; ++i) o1[i] = o2[i] = 0u;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) ot[i] = 0u;
-      auto code = [&](float v) -> uint32_t {
-        return (uint32_t)(uint8_t)(int8_t)fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
-      };
-#pragma unroll
-      for (int e = 0; e < H; ++e) {
-        if (neox) {
-          o1[e >> 2] |= code(y[2 * e]) << (8 * (e & 3));
-          o2[e >> 2] |= code(y[2 * e + 1]) << (8 * (e & 3));
-        } else {
-          o1[(2 * e) >> 2] |= code(y[2 * e]) << (8 * ((2 * e) & 3));
-          o1[(2 * e + 1) >> 2] |= code(y[2 * e + 1]) << (8 * ((2 * e + 1) & 3));
+        for (int i = 0; i < NT; ++i) wt[u][i] = 0u;
+        sco[u] = 0.f;
+        if (l0 + u < a.n_layers) {
+          const long row = (l0 + u) * layer_rows + row0;
+          const int8_t *rp = kc + row * a.D;
+          sco[u] = a.scale[row];
+          if (neox) {
+            ld_n<H>(wr[u], rp + q * H);
+            ld_n<H>(wr2[u], rp + half + q * H);
+          } else {
+            ld_n<2 * H>(wr[u], rp + 2 * q * H);
+          }
+          if constexpr (TL > 0) ld_n<TL>(wt[u], rp + r + q * TL);
         }
       }
 #pragma unroll
-      for (int e = 0; e < TL; ++e) ot[e >> 2] |= code(y[2 * H + e]) << (8 * (e & 3));
-      if (live[u]) {
-        const int rem = (base + u * 256 + (int)threadIdx.x) % items_pl;
-        const int q = rem % L;
-        int8_t *rp = kc + row[u] * a.D;
-        if (neox) {
-          st_n<H>(rp + q * H, o1);
-          st_n<H>(rp + half + q * H, o2);
-        } else {
-          st_n<2 * H>(rp + 2 * q * H, o1);
+      for (int u = 0; u < U; ++u) {
+        float y[16];
+#pragma unroll
+        for (int e = 0; e < H; ++e) {
+          float x1, x2;
+          if (neox) {
+            x1 = code_at(wr[u], e) * sco[u];
+            x2 = code_at(wr2[u], e) * sco[u];
+          } else {
+            x1 = code_at(wr[u], 2 * e) * sco[u];
+            x2 = code_at(wr[u], 2 * e + 1) * sco[u];
+          }
+          y[2 * e] = (x1 * cs[e] - x2 * sn[e]) * gain;
+          y[2 * e + 1] = (x2 * cs[e] + x1 * sn[e]) * gain;
         }
-        if constexpr (TL > 0) st_n<TL>(rp + r + q * TL, ot);
-        if (q == 0) a.scale[row[u]] = amax / 127.0f;
+#pragma unroll
+        for (int e = 0; e < TL; ++e) y[2 * H + e] = code_at(wt[u], e) * sco[u];
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
+        for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+        uint32_t o1[NR], o2[NR], ot[NT];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) o1[i] = o2[i] = 0u;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) ot[i] = 0u;
+        auto code = [&](float v) -> uint32_t {
+          return (uint32_t)(uint8_t)(int8_t)fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
+        };
+#pragma unroll
+        for (int e = 0; e < H; ++e) {
+          if (neox) {
+            o1[e >> 2] |= code(y[2 * e]) << (8 * (e & 3));
+            o2[e >> 2] |= code(y[2 * e + 1]) << (8 * (e & 3));
+          } else {
+            o1[(2 * e) >> 2] |= code(y[2 * e]) << (8 * ((2 * e) & 3));
+            o1[(2 * e + 1) >> 2] |= code(y[2 * e + 1]) << (8 * ((2 * e + 1) & 3));
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < TL; ++e) ot[e >> 2] |= code(y[2 * H + e]) << (8 * (e & 3));
+        if (l0 + u < a.n_layers) {
+          const long row = (l0 + u) * layer_rows + row0;
+          int8_t *rp = kc + row * a.D;
+          if (neox) {
+            st_n<H>(rp + q * H, o1);
+            st_n<H>(rp + half + q * H, o2);
+          } else {
+            st_n<2 * H>(rp + 2 * q * H, o1);
+          }
+          if constexpr (TL > 0) st_n<TL>(rp + r + q * TL, ot);
+          if (q == 0) a.scale[row] = amax / 127.0f;
+        }
       }
     }
   }
