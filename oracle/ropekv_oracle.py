@@ -372,24 +372,36 @@ def paged_free_expired(block_table_row: list[int], n_before: int, sinks: int, wi
 # --------------------------------------------------------------------------
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
-    """softmax(q . K^T * scale) V for one query vector over the rows of K, V (float64)."""
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, sink_logit: float | None = None) -> np.ndarray:
+    """softmax(q . K^T * scale) V for one query vector over the rows of K, V (float64).
+
+    With a learned sink ([RoPE] the learned-sink excerpt: a trained per-head
+    logit in the softmax denominator that costs no cache; [GOSS] the sink
+    bias), the normaliser gains exp(sink_logit) and no value is added:
+    out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink}).  The logit is in the
+    units of the scaled scores.
+    """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     s = (K @ q) * scale
-    s = s - np.max(s)
-    w = np.exp(s)
-    w = w / np.sum(w)
-    return w @ V
+    m = np.max(s)
+    if sink_logit is not None:
+        m = max(m, float(sink_logit))
+    w = np.exp(s - m)
+    den = np.sum(w)
+    if sink_logit is not None:
+        den += math.exp(float(sink_logit) - m)
+    return (w @ V) / den
 
 
 def decode_attention(q: np.ndarray, k_by_pos, v_by_pos, n: int, sinks: int, window: int,
-                     n_kv_heads: int, scale: float | None = None) -> np.ndarray:
+                     n_kv_heads: int, scale: float | None = None, sink_logits=None) -> np.ndarray:
     """Decode output for one sequence: q [Hq, d] at position n-1 over the visible keys.
 
     k_by_pos(j) / v_by_pos(j) return the [Hkv, d] key / value rows at logical
     position j.  Query head h reads KV head h // (Hq / Hkv) (repeat-free GQA).
+    sink_logits: optional [Hq] learned sink logits (see attend).
     """
     Hq, d = q.shape
     n_rep = Hq // n_kv_heads
@@ -401,12 +413,13 @@ def decode_attention(q: np.ndarray, k_by_pos, v_by_pos, n: int, sinks: int, wind
     out = np.empty((Hq, d), dtype=np.float64)
     for h in range(Hq):
         g = h // n_rep
-        out[h] = attend(q[h], K[:, g, :], V[:, g, :], scale)
+        sl = None if sink_logits is None else float(sink_logits[h])
+        out[h] = attend(q[h], K[:, g, :], V[:, g, :], scale, sl)
     return out
 
 
 def prefill_attention(q: np.ndarray, k_by_pos, v_by_pos, pos0: int, sinks: int, window: int,
-                      n_kv_heads: int, scale: float | None = None) -> np.ndarray:
+                      n_kv_heads: int, scale: float | None = None, sink_logits=None) -> np.ndarray:
     """Chunk of T queries at positions pos0 .. pos0+T-1; q [T, Hq, d].
 
     Query t sits at absolute position pos0 + t (the idx_q = arange(T_q) + (T_k - T_q)
@@ -415,7 +428,8 @@ def prefill_attention(q: np.ndarray, k_by_pos, v_by_pos, pos0: int, sinks: int, 
     T, Hq, d = q.shape
     out = np.empty((T, Hq, d), dtype=np.float64)
     for t in range(T):
-        out[t] = decode_attention(q[t], k_by_pos, v_by_pos, pos0 + t + 1, sinks, window, n_kv_heads, scale)
+        out[t] = decode_attention(q[t], k_by_pos, v_by_pos, pos0 + t + 1, sinks, window, n_kv_heads, scale,
+                                  sink_logits)
     return out
 
 

@@ -489,3 +489,48 @@ def test_int8_rows():
     k[:, 0] = 127
     c2, s2 = O.quant_int8_rows(k * 0.25)
     assert np.array_equal(c2, k.astype(np.int8)) and np.allclose(s2, 0.25)
+
+
+# ---------------------------------------------------------------- learned sink logits
+
+
+def test_learned_sink_is_a_zero_value_key():
+    # A per-head logit in the denominator equals attending over one extra key whose
+    # score is the logit and whose value is zero (a second formulation of the rule).
+    rng = np.random.default_rng(31)
+    d, n = 16, 23
+    q = rng.standard_normal(d)
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    scale = 1 / math.sqrt(d)
+    for sink in (-10.0, -1.3, 0.0, 2.5, 15.0):
+        got = O.attend(q, K, V, scale, sink)
+        # extra key k* with k* . q * scale = sink: put it along q
+        kstar = q * (sink / (scale * (q @ q)))
+        ref = O.attend(q, np.vstack([K, kstar]), np.vstack([V, np.zeros(d)]), scale)
+        np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_learned_sink_closed_forms():
+    rng = np.random.default_rng(32)
+    d = 8
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((1, d))
+    v = rng.standard_normal((1, d))
+    s = float(k[0] @ q) / math.sqrt(d)
+    for sink in (-4.0, 0.0, 3.0):
+        # one visible key: the value scaled by the logistic of (score - sink)
+        want = v[0] / (1.0 + math.exp(sink - s))
+        np.testing.assert_allclose(O.attend(q, k, v, 1 / math.sqrt(d), sink), want, atol=1e-14)
+    # a very negative sink is plain softmax attention; heads use their own logit
+    K = rng.standard_normal((9, 2, d))
+    V = rng.standard_normal((9, 2, d))
+    Q = rng.standard_normal((4, d))
+    plain = O.decode_attention(Q, lambda j: K[j], lambda j: V[j], 9, 2, 5, 2)
+    far = O.decode_attention(Q, lambda j: K[j], lambda j: V[j], 9, 2, 5, 2, sink_logits=[-800.0] * 4)
+    np.testing.assert_allclose(far, plain, atol=1e-15)
+    mixed = O.decode_attention(Q, lambda j: K[j], lambda j: V[j], 9, 2, 5, 2, sink_logits=[-800.0, 1.0, -800.0, 1.0])
+    np.testing.assert_allclose(mixed[0], plain[0], atol=1e-15)
+    assert np.abs(mixed[1] - plain[1]).max() > 1e-3
+    # the sink only removes mass: every output is a convex combination shrunk by the same factor
+    assert np.linalg.norm(mixed[1]) < np.linalg.norm(plain[1]) + 1e-12
