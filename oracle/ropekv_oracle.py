@@ -490,6 +490,21 @@ def rerotate_rows(k_rot: np.ndarray, positions: np.ndarray, cfg_from: RopeCfg, c
     return rotate_by_angle(k_rot, ang, cfg_to.rotary_dim, cfg_to.neox, gain)
 
 
+def shift_keys(k_rot: np.ndarray, delta: int, cfg: RopeCfg) -> np.ndarray:
+    """Move rotated keys by `delta` positions: every pair turns by delta * w_i, gain 1.
+
+    The local-position implementation of [SINK] ("RoPE: absolute positions and
+    local rerotation"): when attention re-maps the window to positions
+    [0, C-1], each recent key moves from p to p + delta (delta = -1 per slide)
+    without recovering the raw key, because R_a R_b = R_{a+b}; sink keys keep
+    their local positions (the caller shifts only the recent rows).
+    """
+    k_rot = np.asarray(k_rot, dtype=np.float64)
+    ang = float(delta) * inv_freq(cfg)
+    ang = np.broadcast_to(ang, k_rot.shape[:-1] + ang.shape)
+    return rotate_by_angle(k_rot, ang, cfg.rotary_dim, cfg.neox, 1.0)
+
+
 def rerotate_int8_rows(codes: np.ndarray, scale: np.ndarray, positions: np.ndarray,
                        cfg_from: RopeCfg, cfg_to: RopeCfg):
     """int8 rows: dequantise, turn as rerotate_rows, requantise the whole row."""

@@ -534,3 +534,24 @@ def test_learned_sink_closed_forms():
     assert np.abs(mixed[1] - plain[1]).max() > 1e-3
     # the sink only removes mass: every output is a convex combination shrunk by the same factor
     assert np.linalg.norm(mixed[1]) < np.linalg.norm(plain[1]) + 1e-12
+
+
+# ---------------------------------------------------------------- local-position shift
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_shift_keys_group_law(neox):
+    # [SINK] local rerotation: rotated keys at [3,4,5] moved to [2,3,4] equal keys rotated there
+    # directly; moving by -p returns the raw key; two moves compose.
+    cfg = O.RopeCfg(head_dim=40, rotary_dim=32, rope_theta=1e4, neox=neox)
+    T = O.build_table(cfg, 64)
+    rng = np.random.default_rng(41)
+    raw = rng.standard_normal((3, 2, 40))
+    old = np.array([3, 4, 5])
+    rot = O.rope_apply(raw, old, T, 32, neox)
+    np.testing.assert_allclose(O.shift_keys(rot, -1, cfg), O.rope_apply(raw, old - 1, T, 32, neox), atol=1e-12)
+    back = np.stack([O.shift_keys(rot[i:i + 1], -int(old[i]), cfg)[0] for i in range(3)])
+    np.testing.assert_allclose(back, raw, atol=1e-12)
+    np.testing.assert_allclose(O.shift_keys(O.shift_keys(rot, 7, cfg), -3, cfg), O.shift_keys(rot, 4, cfg),
+                               atol=1e-12)
+    np.testing.assert_array_equal(O.shift_keys(rot, 5, cfg)[..., 32:], raw[..., 32:])
