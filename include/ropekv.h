@@ -164,12 +164,16 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
  * ws; a second launch combines them.  n == 0 gives a zero row.
  *   q   [batch, n_q_heads, d] kv_dtype (rotated), out same shape and dtype
  *   scale: 0 means 1/sqrt(d)
+ *   sink_logits: NULL, or device fp32 [n_q_heads] learned sink logits ([RoPE]
+ *     the learned-sink excerpt: a trained per-head logit in the softmax
+ *     denominator, no cache entry): out = sum_j e^{s_j} v_j / (sum_j e^{s_j}
+ *     + e^{sink_h}), the logit in the units of the scaled scores
  * Layouts RING and PAGED (block_size 16); kv_dtype F32 or BF16; d 64 or 128;
  * n_rep = n_q_heads / Hkv in {1, 2, 4, 8}.  ws: device, at least
  * ropekv_decode_workspace_size() bytes, caller-owned, overwritten. */
 int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
-                       const ropekv_kv_cache *cache, float scale, void *out, void *ws,
-                       size_t ws_bytes, ropekv_stream_t stream);
+                       const ropekv_kv_cache *cache, float scale, const float *sink_logits,
+                       void *out, void *ws, size_t ws_bytes, ropekv_stream_t stream);
 
 /* Prefill attention for one sequence's chunk ([GOSS] 5.5 mask alignment):
  * queries t < T at positions pos0 + t see keys j <= pos0 + t with j < S or
@@ -179,11 +183,12 @@ int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
  * prefix must still be in the ring (call before appending the chunk, or keep
  * pos0 + T <= C); a missing key sets ROPEKV_DEV_PREFIX_LOST.
  *   q [T, n_q_heads, d], out same; dtype = kv_dtype (F32 or BF16), d 64 or 128,
- *   n_rep = n_q_heads / Hkv in {1, 2, 4, 8}; seq_id only read when pos0 > 0.
+ *   n_rep = n_q_heads / Hkv in {1, 2, 4, 8}; seq_id only read when pos0 > 0;
+ *   sink_logits as for ropekv_decode_attn. 
  * bf16 runs on MFMA with fp32 accumulation; tiles no query can see are skipped. */
 int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, int32_t pos0,
                         int32_t n_q_heads, const ropekv_kv_cache *cache, int32_t seq_id,
-                        float scale, void *out, ropekv_stream_t stream);
+                        float scale, const float *sink_logits, void *out, ropekv_stream_t stream);
 
 /* Re-rotate cached keys from `from` to `to` in place ([DYN] "What it does":
  * the cached keys follow a change; [SINK] R_a R_b = R_{a+b}): every pair i of
@@ -195,6 +200,19 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
  * from / to must agree on head_dim, rotary_dim and neox. */
 int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to,
                     const ropekv_kv_cache *cache, int32_t n_layers, ropekv_stream_t stream);
+
+/* Move cached (rotated) keys by `delta` positions in place: every rotary pair
+ * turns by delta * w_i with gain 1; dims r..d-1 are untouched ([SINK] "RoPE:
+ * absolute positions and local rerotation": a window implementation that
+ * re-maps attention positions to [0, C-1] moves each recent key from p to
+ * p - 1 per slide, R_a R_b = R_{a+b}, while sink keys keep their positions).
+ *   RING: every valid ring slot (the `count` newest non-sink keys) of every
+ *     sequence and KV head; sink slots, empty slots and values are not
+ *     touched; n_layers must be 1.
+ *   CONTIG: every row of n_layers layers.
+ * kv_dtype F32 / BF16 / F16; angles in fp64, the rotation in fp32. */
+int ropekv_shift_keys(const ropekv_rope_cfg *cfg, const ropekv_kv_cache *cache, int32_t delta,
+                      int32_t n_layers, ropekv_stream_t stream);
 
 /* Test-facing: the visible logical positions of sequence seq's next query
  * (position seq_len - 1) and the element offset of each key row in the

@@ -180,7 +180,7 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
 }
 
 int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads, const ropekv_kv_cache *cache, float scale,
-                       void *out, void *ws, size_t ws_bytes, ropekv_stream_t stream) {
+                       const float *sink_logits, void *out, void *ws, size_t ws_bytes, ropekv_stream_t stream) {
   int e = check_cache(cache);
   if (e) return e;
   if (cache->layout != ROPEKV_RING && cache->layout != ROPEKV_PAGED)
@@ -196,14 +196,14 @@ int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads, const ro
   if (ws_bytes < pl.ws_bytes)
     return fail(ROPEKV_ENOSPACE, "workspace %zu bytes < %zu needed", ws_bytes, pl.ws_bytes);
   if (pl.splits > 1024) return fail(ROPEKV_ERANGE, "cache too long for one decode call (%d splits)", pl.splits);
-  return hip_status(launch_decode(q, batch, n_q_heads, *cache, resolve_scale(scale, cache->head_dim), out, ws, pl,
-                                  (hipStream_t)stream),
+  return hip_status(launch_decode(q, batch, n_q_heads, *cache, resolve_scale(scale, cache->head_dim), sink_logits,
+                                  out, ws, pl, (hipStream_t)stream),
                     "decode launch");
 }
 
 int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, int32_t pos0, int32_t n_q_heads,
-                        const ropekv_kv_cache *cache, int32_t seq_id, float scale, void *out,
-                        ropekv_stream_t stream) {
+                        const ropekv_kv_cache *cache, int32_t seq_id, float scale, const float *sink_logits,
+                        void *out, ropekv_stream_t stream) {
   int e = check_cache(cache);
   if (e) return e;
   e = check_attention_shape(cache, n_q_heads);
@@ -219,7 +219,7 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
   }
   if (T == 0) return ok();
   return hip_status(launch_prefill(q, k, v, T, pos0, n_q_heads, *cache, seq_id,
-                                   resolve_scale(scale, cache->head_dim), out, (hipStream_t)stream),
+                                   resolve_scale(scale, cache->head_dim), sink_logits, out, (hipStream_t)stream),
                     "prefill launch");
 }
 
@@ -247,6 +247,26 @@ int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to, cons
   return hip_status(launch_rerotate(make_rope_params(*from), make_rope_params(*to), *cache, n_layers,
                                     (hipStream_t)stream),
                     "rerotate launch");
+}
+
+int ropekv_shift_keys(const ropekv_rope_cfg *cfg, const ropekv_kv_cache *cache, int32_t delta, int32_t n_layers,
+                      ropekv_stream_t stream) {
+  int e = check_rope(cfg, "cfg");
+  if (e) return e;
+  e = check_cache(cache);
+  if (e) return e;
+  if (cfg->head_dim != cache->head_dim) return fail(ROPEKV_EINVAL, "cfg head_dim != cache head_dim");
+  if (cache->kv_dtype != ROPEKV_F32 && cache->kv_dtype != ROPEKV_BF16 && cache->kv_dtype != ROPEKV_F16)
+    return fail(ROPEKV_EDTYPE, "shift_keys supports F32, BF16 and F16 keys");
+  if (cache->layout == ROPEKV_RING) {
+    if (n_layers != 1) return fail(ROPEKV_EINVAL, "a RING descriptor is one layer (n_layers must be 1)");
+  } else if (cache->layout == ROPEKV_CONTIG) {
+    if (n_layers < 1) return fail(ROPEKV_EINVAL, "n_layers must be >= 1");
+  } else {
+    return fail(ROPEKV_ELAYOUT, "shift_keys needs a RING or CONTIG cache");
+  }
+  return hip_status(launch_shift_keys(make_rope_params(*cfg), *cache, delta, n_layers, (hipStream_t)stream),
+                    "shift_keys launch");
 }
 
 int ropekv_visible_slots(const ropekv_kv_cache *cache, int32_t seq, int32_t *positions_out, int64_t *offsets_out,

@@ -459,7 +459,8 @@ constexpr int kMaxSplits = 1024;
 
 template <typename T, int D, int NREP>
 __global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, const float *__restrict__ ws,
-                                                             void *__restrict__ out, int tps, int splits) {
+                                                             const float *__restrict__ sinks, void *__restrict__ out,
+                                                             int tps, int splits) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[128];
   const int h = blockIdx.x, b = blockIdx.y;
@@ -480,6 +481,9 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, 
     __syncthreads();
   }
   m = s_red[0];
+  // a learned sink logit joins the normaliser (log2 units like the partial maxima)
+  const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+  if (used > 0) m = fmaxf(m, sink2);
   __syncthreads();
   // per-split weights and the total weight l
   float l = 0.f;
@@ -495,6 +499,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, 
     __syncthreads();
   }
   l = s_red[0];
+  if (sinks && used > 0) l += exp2f(sink2 - m);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
     float a = 0.f;
@@ -504,26 +509,26 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, 
 }
 
 template <typename T, int D, int NREP>
-hipError_t launch_decode_t(const void *q, int batch, const ropekv_kv_cache &c, float sl2, void *out, float *ws,
-                           const DecodePlan &pl, hipStream_t s) {
+hipError_t launch_decode_t(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
+                           void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
   dim3 grid(pl.splits, c.num_kv_heads, batch);
   hipLaunchKernelGGL((decode_split_kernel<T, D, NREP>), grid, dim3(256), 0, s, q, c, sl2, ws, pl.tiles_per_split,
                      pl.splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D, NREP>), dim3(c.num_kv_heads * NREP, batch), dim3(128), 0, s, c,
-                     ws, out, pl.tiles_per_split, pl.splits);
+                     ws, sinks, out, pl.tiles_per_split, pl.splits);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_decode_d(const void *q, int batch, const ropekv_kv_cache &c, float sl2, void *out, float *ws,
-                           const DecodePlan &pl, hipStream_t s) {
+hipError_t launch_decode_d(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sk, void *out,
+                           float *ws, const DecodePlan &pl, hipStream_t s) {
   switch (pl.n_rep) {
-    case 1: return launch_decode_t<T, D, 1>(q, batch, c, sl2, out, ws, pl, s);
-    case 2: return launch_decode_t<T, D, 2>(q, batch, c, sl2, out, ws, pl, s);
-    case 4: return launch_decode_t<T, D, 4>(q, batch, c, sl2, out, ws, pl, s);
-    case 8: return launch_decode_t<T, D, 8>(q, batch, c, sl2, out, ws, pl, s);
+    case 1: return launch_decode_t<T, D, 1>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 2: return launch_decode_t<T, D, 2>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 4: return launch_decode_t<T, D, 4>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 8: return launch_decode_t<T, D, 8>(q, batch, c, sl2, sk, out, ws, pl, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -598,17 +603,17 @@ DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c) {
   return pl;
 }
 
-hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_kv_cache &c, float scale, void *out,
-                         void *ws, const DecodePlan &pl, hipStream_t s) {
+hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_kv_cache &c, float scale,
+                         const float *sinks, void *out, void *ws, const DecodePlan &pl, hipStream_t s) {
   (void)n_q_heads;
   const float sl2 = scale * kLog2e;
   float *w = (float *)ws;
   if (c.kv_dtype == ROPEKV_BF16) {
-    if (c.head_dim == 128) return launch_decode_d<bf16_t, 128>(q, batch, c, sl2, out, w, pl, s);
-    if (c.head_dim == 64) return launch_decode_d<bf16_t, 64>(q, batch, c, sl2, out, w, pl, s);
+    if (c.head_dim == 128) return launch_decode_d<bf16_t, 128>(q, batch, c, sl2, sinks, out, w, pl, s);
+    if (c.head_dim == 64) return launch_decode_d<bf16_t, 64>(q, batch, c, sl2, sinks, out, w, pl, s);
   } else if (c.kv_dtype == ROPEKV_F32) {
-    if (c.head_dim == 128) return launch_decode_d<float, 128>(q, batch, c, sl2, out, w, pl, s);
-    if (c.head_dim == 64) return launch_decode_d<float, 64>(q, batch, c, sl2, out, w, pl, s);
+    if (c.head_dim == 128) return launch_decode_d<float, 128>(q, batch, c, sl2, sinks, out, w, pl, s);
+    if (c.head_dim == 64) return launch_decode_d<float, 64>(q, batch, c, sl2, sinks, out, w, pl, s);
   }
   return hipErrorInvalidValue;
 }

@@ -41,13 +41,16 @@ struct AppendArgs {
 hipError_t launch_apply_append(const AppendArgs &a, hipStream_t s);
 
 hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_kv_cache &c, float scale,
-                         void *out, void *ws, const DecodePlan &plan, hipStream_t s);
+                         const float *sink_logits, void *out, void *ws, const DecodePlan &plan, hipStream_t s);
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, int T, int pos0, int n_q_heads,
-                          const ropekv_kv_cache &c, int seq_id, float scale, void *out, hipStream_t s);
+                          const ropekv_kv_cache &c, int seq_id, float scale, const float *sink_logits, void *out,
+                          hipStream_t s);
 
 hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const ropekv_kv_cache &c,
                            int n_layers, hipStream_t s);
+
+hipError_t launch_shift_keys(const RopeParams &p, const ropekv_kv_cache &c, int delta, int n_layers, hipStream_t s);
 
 hipError_t launch_visible_slots(const ropekv_kv_cache &c, int seq, int32_t *pos_out, int64_t *off_out,
                                 int max_out, int32_t *n_out, hipStream_t s);

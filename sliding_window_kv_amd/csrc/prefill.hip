@@ -35,6 +35,7 @@ struct PrefillArgs {
   int T, pos0, n_q_heads, seq;
   ropekv_kv_cache c;
   float sl2;
+  const float *sinks;  // optional learned sink logit per query head
   void *out;
 };
 
@@ -312,7 +313,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     float l = l_run[rt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float inv = l > 0.f ? 1.f / l : 0.f;
+    if (a.sinks) {
+      // learned sink logit in the normaliser: rescale to max(m, sink) and add its weight
+      const float sink2 = a.sinks[head[rt]] * kLog2e;
+      const float m_f = fmaxf(m_run[rt], sink2);
+      const float f = __builtin_amdgcn_exp2f(m_run[rt] - m_f);
+      const float lt = l * f + __builtin_amdgcn_exp2f(sink2 - m_f);
+      inv = lt > 0.f ? f / lt : 0.f;
+    }
     if (tq[rt] < a.T) {
       const long ob = ((long)tq[rt] * Hq + head[rt]) * D;
 #pragma unroll
@@ -349,7 +358,8 @@ hipError_t launch_prefill_d(const PrefillArgs &a, int n_rep, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, int T, int pos0, int n_q_heads,
-                          const ropekv_kv_cache &c, int seq_id, float scale, void *out, hipStream_t s) {
+                          const ropekv_kv_cache &c, int seq_id, float scale, const float *sink_logits, void *out,
+                          hipStream_t s) {
   PrefillArgs a;
   a.q = q;
   a.k = k;
@@ -360,6 +370,7 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, int T, in
   a.seq = seq_id;
   a.c = c;
   a.sl2 = scale * kLog2e;
+  a.sinks = sink_logits;
   a.out = out;
   const int n_rep = n_q_heads / c.num_kv_heads;
   if (c.kv_dtype == ROPEKV_BF16) {

@@ -398,7 +398,117 @@ __global__ __launch_bounds__(256) void rerotate_int8_kernel(RerotArgs a) {
   }
 }
 
+// Uniform shift of cached keys by delta positions (local-position windows).
+struct ShiftArgs {
+  RopeParams p;
+  int delta;
+  void *k;
+  int ring;          // 1: RING rows [B, Hkv, C], only valid ring slots move
+  int Hkv, C, S, W;  // RING geometry
+  const int32_t *head, *count;
+  long rows;
+  int D;
+};
+
+template <typename T, int PP>
+__global__ __launch_bounds__(256) void shift_kernel(ShiftArgs a) {
+  constexpr int EB = sizeof(T);
+  constexpr int NB = PP * EB;
+  constexpr int NW = (NB + 3) / 4;
+  __shared__ float s_cs[256], s_sn[256];
+  const int half = a.p.rotary_dim / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    double sn, cs;
+    sincos((double)a.delta * rope_omega(a.p, i), &sn, &cs);
+    s_cs[i] = (float)cs;
+    s_sn[i] = (float)sn;
+  }
+  __syncthreads();
+  const int tpr = half / PP;
+  const long items = a.rows * tpr;
+  const int neox = a.p.neox;
+  char *kb = (char *)a.k;
+  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (long)gridDim.x * blockDim.x) {
+    const long row = it / tpr;
+    const int q = (int)(it - row * tpr);
+    if (a.ring) {
+      const int slot = (int)(row % a.C);
+      const int b = (int)(row / a.C) / a.Hkv;
+      if (slot < a.S) continue;
+      const int cnt = min(max(a.count[b], 0), a.W);
+      int oldest = (a.head[b] - cnt) % a.W;
+      if (oldest < 0) oldest += a.W;
+      int rel = (slot - a.S - oldest) % a.W;
+      if (rel < 0) rel += a.W;
+      if (rel >= cnt) continue;
+    }
+    const int j0 = q * PP;
+    char *p1 = kb + (row * a.D + (neox ? j0 : 2 * j0)) * EB;
+    char *p2 = neox ? kb + (row * a.D + half + j0) * EB : p1 + NB;
+    uint32_t w1[NW], w2[NW];
+    vld<NB>(w1, p1);
+    vld<NB>(w2, p2);
+    const float *cs = &s_cs[j0];
+    const float *sn = &s_sn[j0];
+#pragma unroll
+    for (int e = 0; e < PP; ++e) {
+      uint32_t *b1, *b2;
+      int i1, i2;
+      if (neox) {
+        b1 = w1; b2 = w2; i1 = e; i2 = e;
+      } else {
+        b1 = 2 * e < PP ? w1 : w2;
+        b2 = 2 * e + 1 < PP ? w1 : w2;
+        i1 = 2 * e < PP ? 2 * e : 2 * e - PP;
+        i2 = 2 * e + 1 < PP ? 2 * e + 1 : 2 * e + 1 - PP;
+      }
+      const float x1 = vget<T>(b1, i1), x2 = vget<T>(b2, i2);
+      vput<T>(b1, i1, x1 * cs[e] - x2 * sn[e]);
+      vput<T>(b2, i2, x2 * cs[e] + x1 * sn[e]);
+    }
+    vst<NB>(p1, w1);
+    vst<NB>(p2, w2);
+  }
+}
+
+template <typename T>
+hipError_t launch_shift_t(const ShiftArgs &a, hipStream_t s) {
+  const int half = a.p.rotary_dim / 2;
+  const bool wide = half % (16 / (int)sizeof(T)) == 0;
+  const long items = a.rows * (wide ? half / (16 / (int)sizeof(T)) : half);
+  long blocks = (items + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  if (wide)
+    hipLaunchKernelGGL((shift_kernel<T, 16 / sizeof(T)>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((shift_kernel<T, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_shift_keys(const RopeParams &p, const ropekv_kv_cache &c, int delta, int n_layers, hipStream_t s) {
+  ShiftArgs a;
+  a.p = p;
+  a.delta = delta;
+  a.k = c.k;
+  a.ring = c.layout == ROPEKV_RING;
+  a.Hkv = c.num_kv_heads;
+  a.C = c.capacity;
+  a.S = c.sinks;
+  a.W = c.window;
+  a.head = c.ring_head;
+  a.count = c.ring_count;
+  a.rows = a.ring ? (long)c.batch * c.num_kv_heads * c.capacity : (long)n_layers * c.capacity * c.num_kv_heads;
+  a.D = c.head_dim;
+  switch (c.kv_dtype) {
+    case ROPEKV_F32: return launch_shift_t<float>(a, s);
+    case ROPEKV_BF16: return launch_shift_t<bf16_t>(a, s);
+    case ROPEKV_F16: return launch_shift_t<f16_t>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const ropekv_kv_cache &c, int n_layers,
                            hipStream_t s) {

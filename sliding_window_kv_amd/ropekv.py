@@ -33,6 +33,7 @@ EXPORTS = [
     "ropekv_decode_attn",
     "ropekv_prefill_attn",
     "ropekv_rerotate",
+    "ropekv_shift_keys",
     "ropekv_visible_slots",
     "ropekv_last_error",
 ]
@@ -93,9 +94,10 @@ def _load():
     lib.ropekv_apply_append.argtypes = [RC, P, I32, P, I32, P, P, I32, I32, P, P, KC, P, I32, P, P]
     lib.ropekv_decode_workspace_size.argtypes = [I32, I32, KC]
     lib.ropekv_decode_workspace_size.restype = SZ
-    lib.ropekv_decode_attn.argtypes = [P, I32, I32, KC, ctypes.c_float, P, P, SZ, P]
-    lib.ropekv_prefill_attn.argtypes = [P, P, P, I32, I32, I32, KC, I32, ctypes.c_float, P, P]
+    lib.ropekv_decode_attn.argtypes = [P, I32, I32, KC, ctypes.c_float, P, P, P, SZ, P]
+    lib.ropekv_prefill_attn.argtypes = [P, P, P, I32, I32, I32, KC, I32, ctypes.c_float, P, P, P]
     lib.ropekv_rerotate.argtypes = [RC, RC, KC, I32, P]
+    lib.ropekv_shift_keys.argtypes = [RC, KC, I32, I32, P]
     lib.ropekv_visible_slots.argtypes = [KC, I32, P, P, I32, P, P]
     lib.ropekv_last_error.argtypes = []
     lib.ropekv_last_error.restype = ctypes.c_char_p
@@ -171,20 +173,24 @@ def decode_workspace_size(batch: int, n_q_heads: int, cache: KVCache) -> int:
 
 
 def decode_attn(q, batch: int, n_q_heads: int, cache: KVCache, scale: float, out, ws, ws_bytes: int,
-                stream=None) -> int:
-    return _check(LIB.ropekv_decode_attn(_ptr(q), batch, n_q_heads, ctypes.byref(cache), scale, _ptr(out), _ptr(ws),
-                                         ws_bytes, _stream(stream)))
+                stream=None, sink_logits=None) -> int:
+    return _check(LIB.ropekv_decode_attn(_ptr(q), batch, n_q_heads, ctypes.byref(cache), scale, _ptr(sink_logits),
+                                         _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def prefill_attn(q, k, v, T: int, pos0: int, n_q_heads: int, cache: KVCache, seq_id: int, scale: float, out,
-                 stream=None) -> int:
+                 stream=None, sink_logits=None) -> int:
     return _check(LIB.ropekv_prefill_attn(_ptr(q), _ptr(k), _ptr(v), T, pos0, n_q_heads, ctypes.byref(cache),
-                                          seq_id, scale, _ptr(out), _stream(stream)))
+                                          seq_id, scale, _ptr(sink_logits), _ptr(out), _stream(stream)))
 
 
 def rerotate(cfg_from: RopeCfg, cfg_to: RopeCfg, cache: KVCache, n_layers: int, stream=None) -> int:
     return _check(LIB.ropekv_rerotate(ctypes.byref(cfg_from), ctypes.byref(cfg_to), ctypes.byref(cache), n_layers,
                                       _stream(stream)))
+
+
+def shift_keys(cfg: RopeCfg, cache: KVCache, delta: int, n_layers: int = 1, stream=None) -> int:
+    return _check(LIB.ropekv_shift_keys(ctypes.byref(cfg), ctypes.byref(cache), delta, n_layers, _stream(stream)))
 
 
 def visible_slots(cache: KVCache, seq: int, positions_out, offsets_out, max_out: int, n_out, stream=None) -> int:

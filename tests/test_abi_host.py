@@ -122,21 +122,21 @@ def test_attention_argument_errors():
     dec = R.raw("ropekv_decode_attn")
     pre = R.raw("ropekv_prefill_attn")
     c = _ring()
-    assert dec(FAKE, 1, 6, ctypes.byref(c), 0.0, FAKE, FAKE, 1 << 30, None) == R.EINVAL   # 6 % 4
-    assert dec(FAKE, 1, 64, ctypes.byref(c), 0.0, FAKE, FAKE, 1 << 30, None) == R.ERANGE  # n_rep 16
-    assert dec(FAKE, 2, 8, ctypes.byref(c), 0.0, FAKE, FAKE, 1 << 30, None) == R.EINVAL   # batch > cache batch
-    assert dec(FAKE, 1, 8, ctypes.byref(c), 0.0, FAKE, FAKE, 1, None) == R.ENOSPACE       # workspace
-    assert dec(FAKE, 1, 8, ctypes.byref(c), float("nan"), FAKE, FAKE, 1 << 30, None) == R.EINVAL
+    assert dec(FAKE, 1, 6, ctypes.byref(c), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.EINVAL   # 6 % 4
+    assert dec(FAKE, 1, 64, ctypes.byref(c), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.ERANGE  # n_rep 16
+    assert dec(FAKE, 2, 8, ctypes.byref(c), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.EINVAL   # batch > cache batch
+    assert dec(FAKE, 1, 8, ctypes.byref(c), 0.0, None, FAKE, FAKE, 1, None) == R.ENOSPACE       # workspace
+    assert dec(FAKE, 1, 8, ctypes.byref(c), float("nan"), None, FAKE, FAKE, 1 << 30, None) == R.EINVAL
     c2 = _ring(head_dim=96)
-    assert dec(FAKE, 1, 8, ctypes.byref(c2), 0.0, FAKE, FAKE, 1 << 30, None) == R.ERANGE
+    assert dec(FAKE, 1, 8, ctypes.byref(c2), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.ERANGE
     c3 = _ring(kv_dtype=R.F16)
-    assert dec(FAKE, 1, 8, ctypes.byref(c3), 0.0, FAKE, FAKE, 1 << 30, None) == R.EDTYPE
+    assert dec(FAKE, 1, 8, ctypes.byref(c3), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.EDTYPE
     contig = R.kv_cache(R.CONTIG, R.F32, 4, 64, FAKE, capacity=10, err_word=FAKE)
-    assert dec(FAKE, 1, 8, ctypes.byref(contig), 0.0, FAKE, FAKE, 1 << 30, None) == R.ELAYOUT
-    assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(contig), 0, 0.0, FAKE, None) == R.ELAYOUT  # prefix needs cache
-    assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(c), 3, 0.0, FAKE, None) == R.EINVAL        # seq outside batch
-    assert pre(FAKE, FAKE, FAKE, -1, 0, 8, ctypes.byref(c), 0, 0.0, FAKE, None) == R.EINVAL
-    assert pre(FAKE, FAKE, FAKE, 0, 0, 8, ctypes.byref(c), 0, 0.0, FAKE, None) == R.OK
+    assert dec(FAKE, 1, 8, ctypes.byref(contig), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.ELAYOUT
+    assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(contig), 0, 0.0, None, FAKE, None) == R.ELAYOUT  # prefix needs cache
+    assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(c), 3, 0.0, None, FAKE, None) == R.EINVAL        # seq outside batch
+    assert pre(FAKE, FAKE, FAKE, -1, 0, 8, ctypes.byref(c), 0, 0.0, None, FAKE, None) == R.EINVAL
+    assert pre(FAKE, FAKE, FAKE, 0, 0, 8, ctypes.byref(c), 0, 0.0, None, FAKE, None) == R.OK
 
 
 def test_workspace_size_formula():

@@ -598,3 +598,121 @@ def test_rerotate_int8_shapes_vs_oracle(env, r, neox):
         diff = np.abs(c1[l].reshape(-1, d).astype(np.int32) - wc.astype(np.int32))
         assert diff.max() <= 1 and diff.mean() < 0.01, (diff.max(), diff.mean())
     assert s1[0, 3, 1] == 0 and np.all(c1[0, 3, 1] == 0)
+
+
+# ------------------------------------------------------------------ learned per-head sink logits
+
+@pytest.mark.parametrize("dtype_name,n_rep,d", [("bf16", 4, 128), ("f32", 2, 64), ("bf16", 8, 128)])
+def test_decode_learned_sink_logits(env, dtype_name, n_rep, d):
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
+    Hkv = 4
+    Hq = Hkv * n_rep
+    lens = [0, 1, 17, 300, 1000]
+    B = len(lens)
+    max_blocks = 64
+    table = synth.block_table_permutation(B, max_blocks, B * max_blocks, 111)
+    cache = DevPaged(R, torch, dev, dtype, B, Hkv, d, 4, 200, table, B * max_blocks)
+    _fill(torch, cache.k, 112)
+    _fill(torch, cache.v, 113)
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=dtype, device=dev), 114)
+    sinks = torch.from_numpy(synth.normal((Hq,), 115) * 3.0).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4, sink_logits=sinks)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    kp, vp, qq, got = to_np64(cache.k), to_np64(cache.v), to_np64(q), to_np64(out)
+    sk = sinks.cpu().numpy().astype(np.float64)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0)
+            continue
+        ref = O.decode_attention(qq[b], lambda j: kp[table[b, j // 16], :, j % 16],
+                                 lambda j: vp[table[b, j // 16], :, j % 16], n, 4, 200, Hkv, sink_logits=sk)
+        if dtype_name == "f32":
+            assert rowwise(got[b], ref) <= 1e-5
+        else:
+            assert_bf16_close(got[b], ref)
+
+
+@pytest.mark.parametrize("dtype_name", ["bf16", "f32"])
+def test_prefill_learned_sink_logits(env, dtype_name):
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
+    T, Hkv, n_rep, d, S, W = 150, 4, 4, 64, 4, 40
+    Hq = Hkv * n_rep
+    cache = DevRing(R, torch, dev, dtype, 1, Hkv, d, S, W)
+    q = _fill(torch, torch.empty(T, Hq, d, dtype=dtype, device=dev), 121)
+    k = _fill(torch, torch.empty(T, Hkv, d, dtype=dtype, device=dev), 122)
+    v = _fill(torch, torch.empty(T, Hkv, d, dtype=dtype, device=dev), 123)
+    sinks = torch.from_numpy(synth.normal((Hq,), 124) * 3.0).to(dev)
+    out = torch.empty_like(q)
+    R.prefill_attn(q, k, v, T, 0, Hq, cache.desc, 0, 0.0, out, sink_logits=sinks)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    qq, kk, vv = to_np64(q), to_np64(k), to_np64(v)
+    ref = O.prefill_attention(qq, lambda j: kk[j], lambda j: vv[j], 0, S, W, Hkv,
+                              sink_logits=sinks.cpu().numpy().astype(np.float64))
+    if dtype_name == "f32":
+        assert rowwise(to_np64(out), ref) <= 1e-5
+    else:
+        assert_bf16_close(to_np64(out), ref)
+
+
+# ------------------------------------------------------------------ local-position key shift
+
+@pytest.mark.parametrize("dtype_name,r,neox,delta", [("bf16", 64, True, -1), ("f32", 32, True, 5),
+                                                      ("f32", 64, False, -3), ("bf16", 48, True, -1)])
+def test_shift_keys_ring(env, dtype_name, r, neox, delta):
+    # only valid ring slots move (by delta positions); sinks, empty slots and values stay bitwise
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
+    B, Hkv, d, S, W = 3, 4, 64, 4, 12
+    cfg = R.rope_cfg(d, r, rope_theta=1e4, neox=neox)
+    cache = DevRing(R, torch, dev, dtype, B, Hkv, d, S, W)
+    _fill(torch, cache.k, 131)
+    _fill(torch, cache.v, 132)
+    heads, counts, lens = [5, 0, 7], [5, 12, 12], [9, 100, 16]
+    cache.head.copy_(torch.tensor(heads, dtype=torch.int32))
+    cache.count.copy_(torch.tensor(counts, dtype=torch.int32))
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    k0, v0 = cache.k.clone(), cache.v.clone()
+    R.shift_keys(cfg, cache.desc, delta)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.v, v0)
+    k0n, k1n = to_np64(k0), to_np64(cache.k)
+    ocfg = oracle_cfg(cfg)
+    for b in range(B):
+        ring = O.RingSeq(sinks=S, window=W, head=heads[b], count=counts[b], seq_len=lens[b])
+        live = set(ring.chronological_slots()[min(S, lens[b]):])
+        for slot in range(S + W):
+            if slot in live:
+                ref = O.shift_keys(k0n[b, :, slot], delta, ocfg)
+                if dtype_name == "f32":
+                    assert normwise(k1n[b, :, slot], ref) <= 1e-5
+                else:
+                    assert_bf16_close(k1n[b, :, slot], ref, atol=1e-2, rtol=1e-2)
+                assert np.array_equal(k1n[b, :, slot, r:], k0n[b, :, slot, r:])
+            else:
+                assert np.array_equal(k1n[b, :, slot], k0n[b, :, slot])
+
+
+def test_shift_keys_contig_f16_roundtrip(env):
+    # shifting by +7 then -7 returns the keys within fp16 rounding; every row of every layer moves
+    R, torch, dev = env
+    L, T, Hkv, d, r = 2, 40, 4, 128, 64
+    cfg = R.rope_cfg(d, r, rope_theta=5e5)
+    k = _fill(torch, torch.empty(L, T, Hkv, d, dtype=torch.float16, device=dev), 141)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    desc = R.kv_cache(R.CONTIG, R.F16, Hkv, d, k, capacity=T, err_word=err)
+    k0 = to_np64(k)
+    R.shift_keys(cfg, desc, 7, L)
+    torch.cuda.synchronize()
+    ref = O.shift_keys(k0.reshape(-1, d), 7, oracle_cfg(cfg)).reshape(k0.shape)
+    unit = np.maximum(np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64), 1e-6)
+    assert np.all(np.abs(to_np64(k) - ref) <= unit)
+    R.shift_keys(cfg, desc, -7, L)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(to_np64(k) - k0)) < 1e-2
