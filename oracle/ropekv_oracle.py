@@ -48,12 +48,17 @@ class RopeCfg:
     head_dim: int
     rotary_dim: int
     rope_theta: float = 10000.0
-    yarn_factor: float = 1.0
-    orig_max_pos: int = 4096
+    yarn_factor: float = 1.0          # the scaling factor s of every scheme below
+    orig_max_pos: int = 4096          # L0, the trained context
     beta_fast: float = 32.0
     beta_slow: float = 1.0
     extrapolation_factor: float = 1.0
     neox: bool = True
+    rope_type: str = "yarn"           # "yarn" (plain when s <= 1), "linear", "ntk", "dynamic_ntk", "llama3"
+    pruned_pairs: int = 0             # leading pairs kept unrotated (identity)
+    served_len: int = 0               # dynamic NTK: the served length P
+    low_freq_factor: float = 1.0      # Llama-3 blend
+    high_freq_factor: float = 4.0
 
 
 # --------------------------------------------------------------------------
@@ -98,7 +103,7 @@ def yarn_mscale(scale: float) -> float:
     return 0.1 * math.log(scale) + 1.0
 
 
-def inv_freq(cfg: RopeCfg) -> np.ndarray:
+def yarn_inv_freq(cfg: RopeCfg) -> np.ndarray:
     """Per-pair angular frequency of the (possibly YaRN-scaled) rotation.
 
     Plain RoPE when s <= 1.  Otherwise the extrapolated set 1/b^(2i/r) and
@@ -119,8 +124,65 @@ def inv_freq(cfg: RopeCfg) -> np.ndarray:
     return interp * (1.0 - mask) + extrap * mask
 
 
+def ntk_base(base: float, factor: float, rotary_dim: int) -> float:
+    """NTK-aware base: b * s^(r / (r - 2)) (the scheme edits the base, [RoPE] the four families)."""
+    return base * factor ** (rotary_dim / (rotary_dim - 2))
+
+
+def dynamic_ntk_base(base: float, factor: float, served: int, trained: int, rotary_dim: int) -> float:
+    """Dynamic NTK: b * (s * P / L0 - (s - 1))^(r / (r - 2)) ([RoPE] the printed dynamic-NTK excerpt)."""
+    return base * ((factor * served / trained) - (factor - 1)) ** (rotary_dim / (rotary_dim - 2))
+
+
+def llama3_inv_freq(cfg: RopeCfg) -> np.ndarray:
+    """Llama-3 blend ([RoPE] the four families): pairs whose wavelength is below L0 / high_freq_factor
+    keep their frequency, pairs above L0 / low_freq_factor are divided by s, and between the two the
+    frequency moves linearly in L0 / wavelength from one to the other."""
+    w = plain_inv_freq(cfg.rotary_dim, cfg.rope_theta)
+    s, L0 = float(cfg.yarn_factor), float(cfg.orig_max_pos)
+    lo, hi = float(cfg.low_freq_factor), float(cfg.high_freq_factor)
+    out = np.empty_like(w)
+    for i, wi in enumerate(w):
+        wavelen = 2 * math.pi / wi
+        if wavelen < L0 / hi:
+            out[i] = wi
+        elif wavelen > L0 / lo:
+            out[i] = wi / s
+        else:
+            smooth = (L0 / wavelen - lo) / (hi - lo)
+            out[i] = (1 - smooth) * wi / s + smooth * wi
+    return out
+
+
+def inv_freq(cfg: RopeCfg) -> np.ndarray:
+    """Per-pair angular frequency under cfg.rope_type, with the first pruned_pairs pairs at 0.
+
+    "linear" is position interpolation: angles of position m / s ([RoPE] the PI
+    note), i.e. every frequency divided by s.  "ntk" / "dynamic_ntk" recompute the
+    base.  Pruned pairs rotate by nothing ([GOSS] pruned RoPE: cos 1, sin 0).
+    """
+    t = cfg.rope_type
+    r, b, s = cfg.rotary_dim, float(cfg.rope_theta), float(cfg.yarn_factor)
+    if t == "yarn":
+        w = yarn_inv_freq(cfg)
+    elif t == "linear":
+        w = plain_inv_freq(r, b) / s
+    elif t == "ntk":
+        w = plain_inv_freq(r, ntk_base(b, s, r))
+    elif t == "dynamic_ntk":
+        w = plain_inv_freq(r, dynamic_ntk_base(b, s, cfg.served_len, cfg.orig_max_pos, r))
+    elif t == "llama3":
+        w = llama3_inv_freq(cfg)
+    else:
+        raise ValueError(f"unknown rope_type {t}")
+    w = np.array(w, dtype=np.float64)
+    w[: cfg.pruned_pairs] = 0.0
+    return w
+
+
 def mscale(cfg: RopeCfg) -> float:
-    return yarn_mscale(cfg.yarn_factor)
+    """The YaRN attention-temperature factor; the other schemes leave magnitudes alone."""
+    return yarn_mscale(cfg.yarn_factor) if cfg.rope_type == "yarn" else 1.0
 
 
 def build_table(cfg: RopeCfg, max_pos: int) -> np.ndarray:

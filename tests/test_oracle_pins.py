@@ -555,3 +555,64 @@ def test_shift_keys_group_law(neox):
     np.testing.assert_allclose(O.shift_keys(O.shift_keys(rot, 7, cfg), -3, cfg), O.shift_keys(rot, 4, cfg),
                                atol=1e-12)
     np.testing.assert_array_equal(O.shift_keys(rot, 5, cfg)[..., 32:], raw[..., 32:])
+
+
+# ---------------------------------------------------------------- table variants
+
+
+def test_linear_scaling_is_position_interpolation():
+    # PI scales the position axis: the table at position s*m equals the plain table at m.
+    base = O.RopeCfg(head_dim=64, rotary_dim=64, rope_theta=1e4)
+    pi = O.RopeCfg(head_dim=64, rotary_dim=64, rope_theta=1e4, yarn_factor=4.0, rope_type="linear")
+    Tp, Tb = O.build_table(pi, 4000), O.build_table(base, 1000)
+    np.testing.assert_allclose(Tp[::4], Tb, atol=1e-12)
+    assert O.mscale(pi) == 1.0
+
+
+def test_ntk_fixed_and_dynamic():
+    r, b = 128, 1e4
+    cfg = O.RopeCfg(head_dim=r, rotary_dim=r, rope_theta=b, yarn_factor=8.0, rope_type="ntk")
+    w, w0 = O.inv_freq(cfg), O.plain_inv_freq(r, b)
+    # NTK-aware: the fastest pair is untouched, the slowest is interpolated exactly by s, geometric between
+    assert w[0] == 1.0 and abs(w[-1] / w0[-1] - 1 / 8.0) < 1e-12
+    ratio = w[1:] / w[:-1]
+    np.testing.assert_allclose(ratio, ratio[0], rtol=1e-12)
+    # dynamic NTK at the trained length is plain RoPE; at P it equals fixed NTK with s' = s P / L0 - (s - 1)
+    dyn = O.RopeCfg(head_dim=r, rotary_dim=r, rope_theta=b, yarn_factor=2.0, rope_type="dynamic_ntk",
+                    orig_max_pos=4096, served_len=4096)
+    np.testing.assert_allclose(O.inv_freq(dyn), w0, rtol=1e-14)
+    dyn2 = O.RopeCfg(head_dim=r, rotary_dim=r, rope_theta=b, yarn_factor=2.0, rope_type="dynamic_ntk",
+                     orig_max_pos=4096, served_len=16384)
+    fixed = O.RopeCfg(head_dim=r, rotary_dim=r, rope_theta=b, yarn_factor=2.0 * 4 - 1, rope_type="ntk")
+    np.testing.assert_allclose(O.inv_freq(dyn2), O.inv_freq(fixed), rtol=1e-13)
+
+
+def test_llama3_blend():
+    r, b, L0, s = 128, 5e5, 8192, 8.0
+    cfg = O.RopeCfg(head_dim=r, rotary_dim=r, rope_theta=b, yarn_factor=s, orig_max_pos=L0, rope_type="llama3",
+                    low_freq_factor=1.0, high_freq_factor=4.0)
+    w, w0 = O.inv_freq(cfg), O.plain_inv_freq(r, b)
+    wl = 2 * math.pi / w0
+    fast, slow = wl < L0 / 4.0, wl > L0 / 1.0
+    assert fast.any() and slow.any() and (~fast & ~slow).any()
+    np.testing.assert_array_equal(w[fast], w0[fast])
+    np.testing.assert_allclose(w[slow], w0[slow] / s, rtol=1e-15)
+    mid = w[~fast & ~slow] / w0[~fast & ~slow]
+    assert np.all(mid < 1) and np.all(mid > 1 / s) and np.all(np.diff(mid) < 0)
+    # continuous at both thresholds: the smoothing weight is 1 at L0/wl = 4 and 0 at L0/wl = 1
+    for k, want in ((4.0, 1.0), (1.0, 1.0 / s)):
+        smooth = (k - 1.0) / 3.0
+        assert abs(((1 - smooth) / s + smooth) - want) < 1e-15
+
+
+def test_pruned_pairs_are_identity():
+    cfg = O.RopeCfg(head_dim=96, rotary_dim=96, rope_theta=1e4, pruned_pairs=12)
+    T = O.build_table(cfg, 300)
+    np.testing.assert_array_equal(T[:, :12], 1.0)
+    np.testing.assert_array_equal(T[:, 48:60], 0.0)
+    full = O.build_table(O.RopeCfg(head_dim=96, rotary_dim=96, rope_theta=1e4), 300)
+    np.testing.assert_array_equal(T[:, 12:48], full[:, 12:48])
+    x = RNG.standard_normal((300, 96))
+    y = O.rope_apply(x, np.arange(300), T, 96, True)
+    np.testing.assert_array_equal(y[:, :12], x[:, :12])
+    np.testing.assert_array_equal(y[:, 48:60], x[:, 48:60])
