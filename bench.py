@@ -176,6 +176,10 @@ def main():
     rows["decode_b64_ctx32768"] = {"ms": round(ms_dec, 4), "GBps": round(achieved, 1),
                                    "frac_hbm": round(achieved / HBM_PEAK_GBS, 4)}
     rows["rope_append_b64"] = {"ms": round(ms_app, 4)}
+    sinks = torch.linspace(-2.0, 6.0, wl.Hq, device=dev)
+    ms_dsk = timed(torch, lambda: R.decode_attn(wl.q, wl.B, wl.Hq, wl.desc, 0.0, wl.out, wl.ws, wl.ws_bytes,
+                                                sink_logits=sinks), max(args.steps, 20))
+    rows["decode_b64_ctx32768_learned_sinks"] = {"ms": round(ms_dsk, 4), "GBps": round(dec_bytes / ms_dsk / 1e6, 1)}
     ms_tab = timed(torch, lambda: R.build_table(wl.cfg, wl.ctx, wl.rope_table), 10)
     rows["table_build_32768x128"] = {"ms": round(ms_tab, 4)}
 
@@ -200,6 +204,18 @@ def main():
             tot_bytes += r.decode_bytes()
             tot_ms += ms
             assert r.err.item() == 0
+            if layer == 0:
+                # local-position window: every valid ring key moves by one position (sinks stay)
+                scfg = R.rope_cfg(r.d, r.d, rope_theta=5e5)
+                flip = [-1]
+
+                def shift(r=r, scfg=scfg, flip=flip):
+                    R.shift_keys(scfg, r.desc, flip[0])
+                    flip[0] = -flip[0]
+
+                ms_sh = timed(torch, shift, 20)
+                sh_bytes = 2 * r.B * r.Hkv * r.W * r.d * 2  # rotary slice (r = d) of every ring row, read + write
+                rows["shift_keys_ring_w4096_b32"] = {"ms": round(ms_sh, 4), "GBps": round(sh_bytes / ms_sh / 1e6, 1)}
             del r
         full = WL.PagedDecode(R, torch, dev, B=32, ctx=131072, seed=3100)
         full.seq_len.fill_(131072)

@@ -67,21 +67,38 @@ typedef void *ropekv_stream_t; /* a hipStream_t */
 #define ROPEKV_DEV_PREFIX_LOST 32 /* prefill needs a prefix key the ring no longer holds */
 #define ROPEKV_DEV_FREE_OVERFLOW 64 /* freed-block list capacity exceeded (nothing freed) */
 
-/* Rope parameters, in the notation of [RoPE] ("YaRN, precisely"):
- * omega_i = 1 / b^(2i/r) for pair i < r/2; with s > 1 the YaRN blend of the
+/* rope_type values */
+#define ROPEKV_ROPE_YARN 0        /* plain RoPE when s <= 1, else YaRN (default) */
+#define ROPEKV_ROPE_LINEAR 1      /* position interpolation: angles of position m / s */
+#define ROPEKV_ROPE_NTK 2         /* base b * s^(r / (r - 2)) */
+#define ROPEKV_ROPE_DYNAMIC_NTK 3 /* base b * (s P / L0 - (s - 1))^(r / (r - 2)), P = served_len */
+#define ROPEKV_ROPE_LLAMA3 4      /* wavelength-thresholded blend (low / high_freq_factor) */
+
+/* Rope parameters, in the notation of [RoPE] ("YaRN, precisely" and the four
+ * families of fixes): omega_i = 1 / b^(2i/r) for pair i < r/2, edited by the
+ * scheme in rope_type with scaling factor s.  YaRN (s > 1) blends the
  * extrapolated and the interpolated (divided by s) frequencies over the
- * correction band of beta_fast / beta_slow rotations within L0, and the
- * table scaled by mscale = 0.1 ln s + 1.  s <= 1 is plain RoPE. */
+ * correction band of beta_fast / beta_slow rotations within L0 and scales the
+ * table by mscale = 0.1 ln s + 1; the other schemes keep mscale 1.  Llama-3
+ * keeps pairs with wavelength < L0 / high_freq_factor, divides those with
+ * wavelength > L0 / low_freq_factor by s, and moves linearly in L0 / wavelength
+ * between.  The first pruned_pairs pairs are identity (omega 0). */
 typedef struct {
   int32_t head_dim;     /* d_h */
   int32_t rotary_dim;   /* r: even, 2 <= r <= d_h; dims r..d_h-1 are never touched */
   int32_t neox;         /* 1: pairs (i, i + r/2); 0: GPT-J pairs (2i, 2i+1) ([RoPE] pairing note) */
   int32_t orig_max_pos; /* L0, the trained context */
   double rope_theta;    /* b */
-  double yarn_factor;   /* s */
+  double yarn_factor;   /* s, the scaling factor of every scheme */
   double beta_fast;     /* 32 */
   double beta_slow;     /* 1 */
   double extrapolation_factor; /* 1 */
+  int32_t rope_type;    /* ROPEKV_ROPE_* */
+  int32_t pruned_pairs; /* leading identity pairs, 0 <= pruned_pairs <= r/2 */
+  int32_t served_len;   /* dynamic NTK: the served length P (> 0) */
+  int32_t reserved;     /* 0 */
+  double low_freq_factor;  /* Llama-3: 1 */
+  double high_freq_factor; /* Llama-3: 4 (> low_freq_factor) */
 } ropekv_rope_cfg;
 
 /* One layer's KV cache.  All pointers are device pointers.

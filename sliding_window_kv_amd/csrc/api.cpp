@@ -44,11 +44,36 @@ int check_rope(const ropekv_rope_cfg *c, const char *name) {
   if (!(c->rope_theta > 1.0) || !isfinite(c->rope_theta))
     return fail(ROPEKV_EINVAL, "%s: rope_theta must be finite and > 1", name);
   if (!isfinite(c->yarn_factor)) return fail(ROPEKV_EINVAL, "%s: yarn_factor must be finite", name);
-  if (c->yarn_factor > 1.0) {
-    if (c->orig_max_pos < 1) return fail(ROPEKV_EINVAL, "%s: orig_max_pos must be >= 1 with yarn", name);
-    if (!(c->beta_fast > 0.0) || !(c->beta_slow > 0.0))
-      return fail(ROPEKV_EINVAL, "%s: beta_fast and beta_slow must be > 0", name);
-    if (!isfinite(c->extrapolation_factor)) return fail(ROPEKV_EINVAL, "%s: extrapolation_factor", name);
+  if (c->rope_type < ROPEKV_ROPE_YARN || c->rope_type > ROPEKV_ROPE_LLAMA3)
+    return fail(ROPEKV_EINVAL, "%s: unknown rope_type %d", name, c->rope_type);
+  if (c->pruned_pairs < 0 || c->pruned_pairs > c->rotary_dim / 2)
+    return fail(ROPEKV_EINVAL, "%s: pruned_pairs must be in [0, r/2]", name);
+  const double s = c->yarn_factor;
+  switch (c->rope_type) {
+    case ROPEKV_ROPE_YARN:
+      if (s > 1.0) {
+        if (c->orig_max_pos < 1) return fail(ROPEKV_EINVAL, "%s: orig_max_pos must be >= 1 with yarn", name);
+        if (!(c->beta_fast > 0.0) || !(c->beta_slow > 0.0))
+          return fail(ROPEKV_EINVAL, "%s: beta_fast and beta_slow must be > 0", name);
+        if (!isfinite(c->extrapolation_factor)) return fail(ROPEKV_EINVAL, "%s: extrapolation_factor", name);
+      }
+      break;
+    case ROPEKV_ROPE_LINEAR:
+    case ROPEKV_ROPE_NTK:
+      if (!(s > 0.0)) return fail(ROPEKV_EINVAL, "%s: the scaling factor must be > 0", name);
+      if (c->rope_type == ROPEKV_ROPE_NTK && c->rotary_dim < 4) return fail(ROPEKV_EINVAL, "%s: NTK needs r >= 4", name);
+      break;
+    case ROPEKV_ROPE_DYNAMIC_NTK:
+      if (!(s > 0.0) || c->served_len < 1 || c->orig_max_pos < 1 || c->rotary_dim < 4)
+        return fail(ROPEKV_EINVAL, "%s: dynamic NTK needs s > 0, served_len >= 1, orig_max_pos >= 1, r >= 4", name);
+      if (!(s * (double)c->served_len / (double)c->orig_max_pos - (s - 1.0) > 0.0))
+        return fail(ROPEKV_EINVAL, "%s: dynamic NTK base factor s P / L0 - (s - 1) must be > 0", name);
+      break;
+    case ROPEKV_ROPE_LLAMA3:
+      if (!(s > 0.0) || c->orig_max_pos < 1 || !(c->low_freq_factor > 0.0) ||
+          !(c->high_freq_factor > c->low_freq_factor))
+        return fail(ROPEKV_EINVAL, "%s: Llama-3 needs s > 0, orig_max_pos >= 1, 0 < low < high freq factor", name);
+      break;
   }
   return ROPEKV_OK;
 }

@@ -57,8 +57,8 @@ __device__ __forceinline__ void store_elem(void *p, long i, int dt, float v) {
 
 // Rope parameters as passed to kernels.
 struct RopeParams {
-  double theta, s, beta_fast, beta_slow, ef;
-  int rotary_dim, head_dim, neox, L0;
+  double theta, s, beta_fast, beta_slow, ef, lff, hff;
+  int rotary_dim, head_dim, neox, L0, type, pruned, served;
 };
 
 __host__ inline RopeParams make_rope_params(const ropekv_rope_cfg &c) {
@@ -68,15 +68,50 @@ __host__ inline RopeParams make_rope_params(const ropekv_rope_cfg &c) {
   p.beta_fast = c.beta_fast;
   p.beta_slow = c.beta_slow;
   p.ef = c.extrapolation_factor;
+  p.lff = c.low_freq_factor;
+  p.hff = c.high_freq_factor;
   p.rotary_dim = c.rotary_dim;
   p.head_dim = c.head_dim;
   p.neox = c.neox;
   p.L0 = c.orig_max_pos;
+  p.type = c.rope_type;
+  p.pruned = c.pruned_pairs;
+  p.served = c.served_len;
   return p;
 }
 
-// Angular frequency of pair i, fp64 (YaRN blend when s > 1).
+__device__ inline double yarn_omega(const RopeParams &p, int i);
+
+// Angular frequency of pair i under the configured scheme, fp64.
 __device__ inline double rope_omega(const RopeParams &p, int i) {
+  if (i < p.pruned) return 0.0;
+  const double r = (double)p.rotary_dim;
+  const double e = (2.0 * (double)i) / r;
+  switch (p.type) {
+    case ROPEKV_ROPE_LINEAR: return 1.0 / pow(p.theta, e) / p.s;
+    case ROPEKV_ROPE_NTK: return 1.0 / pow(p.theta * pow(p.s, r / (r - 2.0)), e);
+    case ROPEKV_ROPE_DYNAMIC_NTK: {
+      const double base = p.theta * pow(p.s * (double)p.served / (double)p.L0 - (p.s - 1.0), r / (r - 2.0));
+      return 1.0 / pow(base, e);
+    }
+    case ROPEKV_ROPE_LLAMA3: {
+      const double w = 1.0 / pow(p.theta, e);
+      const double wavelen = 6.283185307179586476925286766559 / w;
+      const double L0 = (double)p.L0;
+      if (wavelen < L0 / p.hff) return w;
+      if (wavelen > L0 / p.lff) return w / p.s;
+      const double smooth = (L0 / wavelen - p.lff) / (p.hff - p.lff);
+      return (1.0 - smooth) * w / p.s + smooth * w;
+    }
+    default: return yarn_omega(p, i);
+  }
+}
+
+__host__ __device__ inline double rope_mscale(double s);
+__device__ inline double params_mscale(const RopeParams &p) { return p.type == ROPEKV_ROPE_YARN ? rope_mscale(p.s) : 1.0; }
+
+// YaRN frequency of pair i (plain RoPE when s <= 1).
+__device__ inline double yarn_omega(const RopeParams &p, int i) {
   const double r = (double)p.rotary_dim;
   const double pos_freq = pow(p.theta, (2.0 * (double)i) / r);
   const double ext = 1.0 / pos_freq;

@@ -41,7 +41,7 @@ __device__ inline float angle_setup(const RerotArgs &a, int t0, float *s_cs, flo
     s_sn[idx] = (float)sn;
   }
   __syncthreads();
-  return (float)(rope_mscale(a.to.s) / rope_mscale(a.from.s));
+  return (float)(params_mscale(a.to) / params_mscale(a.from));
 }
 
 // Raw 16-bit / 32-bit element access inside a register vector.

@@ -13,7 +13,7 @@ __global__ __launch_bounds__(256) void table_kernel(RopeParams rp, int max_pos, 
   const int half = rp.rotary_dim / 2;
   for (int i = threadIdx.x; i < half; i += blockDim.x) w[i] = rope_omega(rp, i);
   __syncthreads();
-  const double mu = rope_mscale(rp.s);
+  const double mu = params_mscale(rp);
   const long total = (long)max_pos * half;
   for (long c = (long)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (long)gridDim.x * blockDim.x) {
     const long m = c / half;

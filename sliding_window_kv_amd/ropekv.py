@@ -50,6 +50,12 @@ class RopeCfg(ctypes.Structure):
         ("beta_fast", ctypes.c_double),
         ("beta_slow", ctypes.c_double),
         ("extrapolation_factor", ctypes.c_double),
+        ("rope_type", ctypes.c_int32),
+        ("pruned_pairs", ctypes.c_int32),
+        ("served_len", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("low_freq_factor", ctypes.c_double),
+        ("high_freq_factor", ctypes.c_double),
     ]
 
 
@@ -138,11 +144,17 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+ROPE_YARN, ROPE_LINEAR, ROPE_NTK, ROPE_DYNAMIC_NTK, ROPE_LLAMA3 = 0, 1, 2, 3, 4
+
+
 def rope_cfg(head_dim, rotary_dim, rope_theta=10000.0, yarn_factor=1.0, orig_max_pos=4096, neox=True,
-             beta_fast=32.0, beta_slow=1.0, extrapolation_factor=1.0) -> RopeCfg:
+             beta_fast=32.0, beta_slow=1.0, extrapolation_factor=1.0, rope_type=ROPE_YARN, pruned_pairs=0,
+             served_len=0, low_freq_factor=1.0, high_freq_factor=4.0) -> RopeCfg:
     return RopeCfg(head_dim=head_dim, rotary_dim=rotary_dim, neox=1 if neox else 0, orig_max_pos=orig_max_pos,
                    rope_theta=rope_theta, yarn_factor=yarn_factor, beta_fast=beta_fast, beta_slow=beta_slow,
-                   extrapolation_factor=extrapolation_factor)
+                   extrapolation_factor=extrapolation_factor, rope_type=rope_type, pruned_pairs=pruned_pairs,
+                   served_len=served_len, reserved=0, low_freq_factor=low_freq_factor,
+                   high_freq_factor=high_freq_factor)
 
 
 def kv_cache(layout, kv_dtype, num_kv_heads, head_dim, k, v=None, *, batch=0, capacity=0, sinks=0, window=0,

@@ -41,9 +41,12 @@ def assert_bf16_close(gpu: np.ndarray, ref: np.ndarray, atol=2e-2, rtol=1e-2):
 
 def oracle_cfg(cfg) -> O.RopeCfg:
     """The oracle's view of a ctypes RopeCfg (same numbers)."""
+    types = {0: "yarn", 1: "linear", 2: "ntk", 3: "dynamic_ntk", 4: "llama3"}
     return O.RopeCfg(head_dim=cfg.head_dim, rotary_dim=cfg.rotary_dim, rope_theta=cfg.rope_theta,
                      yarn_factor=cfg.yarn_factor, orig_max_pos=cfg.orig_max_pos, beta_fast=cfg.beta_fast,
-                     beta_slow=cfg.beta_slow, extrapolation_factor=cfg.extrapolation_factor, neox=bool(cfg.neox))
+                     beta_slow=cfg.beta_slow, extrapolation_factor=cfg.extrapolation_factor, neox=bool(cfg.neox),
+                     rope_type=types[cfg.rope_type], pruned_pairs=cfg.pruned_pairs, served_len=cfg.served_len,
+                     low_freq_factor=cfg.low_freq_factor, high_freq_factor=cfg.high_freq_factor)
 
 
 class DevRing:

@@ -81,6 +81,12 @@ def test_build_table_argument_errors():
     for cfg in bad:
         assert f(ctypes.byref(cfg), 16, FAKE, None, None) == R.EINVAL
         assert R.last_error() != ""
+    bad2 = [R.rope_cfg(64, 64, rope_type=9), R.rope_cfg(64, 64, pruned_pairs=33),
+            R.rope_cfg(64, 64, rope_type=R.ROPE_DYNAMIC_NTK, yarn_factor=8.0, served_len=10, orig_max_pos=4096),
+            R.rope_cfg(64, 64, rope_type=R.ROPE_LLAMA3, yarn_factor=8.0, low_freq_factor=4.0, high_freq_factor=1.0),
+            R.rope_cfg(64, 64, rope_type=R.ROPE_LINEAR, yarn_factor=0.0)]
+    for cfg in bad2:
+        assert f(ctypes.byref(cfg), 16, FAKE, None, None) == R.EINVAL, R.last_error()
     good = R.rope_cfg(64, 64)
     assert f(ctypes.byref(good), 0, FAKE, None, None) == R.EINVAL
     assert f(ctypes.byref(good), 16, None, None, None) == R.EINVAL

@@ -44,6 +44,14 @@ TABLE_CASES = [
     (dict(head_dim=128, rotary_dim=64, rope_theta=5e5, yarn_factor=2.0, orig_max_pos=262144), 524288),
     (dict(head_dim=128, rotary_dim=128, rope_theta=1e4, yarn_factor=8.0, orig_max_pos=4096), 32768),
     (dict(head_dim=96, rotary_dim=32, rope_theta=1e4, yarn_factor=1.125, orig_max_pos=100, neox=False), 1000),
+    (dict(head_dim=64, rotary_dim=64, rope_theta=1e4, yarn_factor=4.0, rope_type=1), 4000),
+    (dict(head_dim=128, rotary_dim=128, rope_theta=1e4, yarn_factor=8.0, rope_type=2), 32768),
+    (dict(head_dim=128, rotary_dim=128, rope_theta=1e4, yarn_factor=2.0, rope_type=3, orig_max_pos=4096,
+          served_len=16384), 16384),
+    (dict(head_dim=128, rotary_dim=128, rope_theta=5e5, yarn_factor=8.0, rope_type=4, orig_max_pos=8192,
+          low_freq_factor=1.0, high_freq_factor=4.0), 65536),
+    (dict(head_dim=96, rotary_dim=96, rope_theta=1e4, pruned_pairs=12), 3000),
+    (dict(head_dim=128, rotary_dim=128, rope_theta=1e4, yarn_factor=4.0, orig_max_pos=4096, pruned_pairs=16), 8000),
 ]
 
 
@@ -64,7 +72,7 @@ def test_table_matches_oracle(env, args, P):
     ang = np.concatenate([ang, ang], axis=1)
     tol = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) + 4 * 2.0 ** -52 * ang * O.mscale(oc)
     assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) / tol))
-    assert abs(float(ms.item()) - O.yarn_mscale(cfg.yarn_factor)) < 1e-7
+    assert abs(float(ms.item()) - O.mscale(oc)) < 1e-7
     # the result does not depend on the launch shape: a shorter build is a bitwise prefix
     P2 = P // 2 + 3
     t2 = _table(R, torch, dev, cfg, P2)
@@ -716,3 +724,22 @@ def test_shift_keys_contig_f16_roundtrip(env):
     R.shift_keys(cfg, desc, -7, L)
     torch.cuda.synchronize()
     assert np.max(np.abs(to_np64(k) - k0)) < 1e-2
+
+
+def test_rerotate_across_schemes(env):
+    # a key written under one scheme is turned to another: PI -> Llama-3 -> NTK, fp32 cache
+    R, torch, dev = env
+    T, Hkv, d, r = 64, 4, 128, 128
+    cfgs = [R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=4.0, rope_type=1),
+            R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=8.0, rope_type=4, orig_max_pos=8192),
+            R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=2.0, rope_type=2)]
+    k = _fill(torch, torch.empty(1, T, Hkv, d, dtype=torch.float32, device=dev), 151)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    desc = R.kv_cache(R.CONTIG, R.F32, Hkv, d, k, capacity=T, pos0=100000, err_word=err)
+    cur = to_np64(k[0])
+    pos = np.arange(100000, 100000 + T)
+    for a_, b_ in zip(cfgs[:-1], cfgs[1:]):
+        R.rerotate(a_, b_, desc, 1)
+        torch.cuda.synchronize()
+        cur = O.rerotate_rows(cur, pos, oracle_cfg(a_), oracle_cfg(b_))
+        assert rowwise(to_np64(k[0]), cur) <= 1e-5
