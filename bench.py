@@ -183,6 +183,19 @@ def main():
     ms_tab = timed(torch, lambda: R.build_table(wl.cfg, wl.ctx, wl.rope_table), 10)
     rows["table_build_32768x128"] = {"ms": round(ms_tab, 4)}
 
+    # the same decode over an int8 cache (codes + per-row scales): half the K/V bytes per key
+    wq = WL.PagedDecode(R, torch, dev, kv_int8=True)
+    wq.step()
+    ms_q = timed(torch, wq.decode, max(args.steps, 20))
+    ms_qapp = timed(torch, lambda: (wq.seq_len.fill_(wq.ctx - 1), wq.append()), max(args.steps, 20))
+    assert wq.err.item() == 0, f"device error word {wq.err.item()}"
+    rows["decode_b64_ctx32768_int8kv"] = {"ms": round(ms_q, 4), "GBps": round(wq.decode_bytes() / ms_q / 1e6, 1),
+                                          "frac_hbm": round(wq.decode_bytes() / ms_q / 1e6 / HBM_PEAK_GBS, 4),
+                                          "speedup_vs_bf16": round(ms_dec / ms_q, 3)}
+    rows["rope_append_b64_int8kv"] = {"ms": round(ms_qapp, 4)}
+    del wq
+    torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")

@@ -107,7 +107,7 @@ typedef struct {
  * attention (PAGED only).  For RING, capacity C = sinks + window. */
 typedef struct {
   int32_t layout;       /* ROPEKV_RING / _PAGED / _CONTIG */
-  int32_t kv_dtype;     /* RING, PAGED: F32 / BF16 / F16 (K and V); CONTIG: F32 / BF16 / F16 / I8 (K) */
+  int32_t kv_dtype;     /* F32 / BF16 / F16 / I8 (K and V; CONTIG holds K, V optional) */
   int32_t num_kv_heads; /* Hkv */
   int32_t head_dim;     /* d: 64 or 128 for attention; any even size <= 512 for append / rerotate */
   int32_t batch;        /* sequences (RING, PAGED) */
@@ -120,12 +120,14 @@ typedef struct {
   int32_t pos0;         /* CONTIG: position of row 0 */
   void *k;              /* keys (rotated), layout as above */
   void *v;              /* values (never rotated); NULL allowed for CONTIG */
-  float *k_scale;       /* CONTIG I8: per-row fp32 scale [T, Hkv] per layer */
+  float *k_scale;       /* I8: per-row fp32 key scale, one per K row (PAGED [num_blocks, Hkv, block_size],
+                           RING [batch, Hkv, C], CONTIG [T, Hkv] per layer) */
   int32_t *ring_head;   /* RING [batch]: next ring index to write */
   int32_t *ring_count;  /* RING [batch]: valid ring entries (<= W) */
   int32_t *block_table; /* PAGED [batch, max_blocks]: physical block ids, -1 = null */
   int32_t *seq_len;     /* RING, PAGED [batch]: tokens appended so far (= next position) */
   int32_t *err_word;    /* [1]: ROPEKV_DEV_* bits, OR-ed by kernels; caller clears */
+  float *v_scale;       /* I8 RING / PAGED: per-row fp32 value scale, laid out like k_scale */
 } ropekv_kv_cache;
 
 /* Build the cos/sin table ([RoPE] _compute_cos_sin_cache, YaRN variant):
@@ -147,7 +149,7 @@ int ropekv_build_table(const ropekv_rope_cfg *cfg, int32_t max_pos, float *cos_s
  *   v   [n_tokens, Hkv, d] act_dtype; copied unrotated (NULL only for a CONTIG cache with v == NULL)
  *   positions [n_tokens] int32 absolute positions, < table_len
  *   seq_ids   [n_tokens] int32 sequence of each token (RING, PAGED; ignored for CONTIG)
- * act_dtype: F32 / BF16 / F16.  RING and PAGED need kv_dtype == act_dtype.
+ * act_dtype: F32 / BF16 / F16.  RING and PAGED need kv_dtype == act_dtype or I8.
  * Each sequence appears as one run of consecutive positions starting at its
  * seq_len; seq_len advances by the run length.
  * RING ([GOSS] ring buffer, 5.2 append): sinks p < S go to slot p; a chunk of
@@ -161,8 +163,10 @@ int ropekv_build_table(const ropekv_rope_cfg *cfg, int32_t max_pos, float *cos_s
  *   and their ids appended to freed_blocks (device int32 [freed_capacity]),
  *   counted in *n_freed (device int32, caller zeroes it).  freed_blocks NULL:
  *   nothing is freed.
- * CONTIG: row t = p - pos0; F16 stores the rotated row rounded to nearest;
- *   I8 stores per-row codes rne(x / scale) with scale = max|x| / 127. */
+ * CONTIG: row t = p - pos0.
+ * Stored dtype: F32 / BF16 / F16 round the fp32 result to nearest; I8 stores
+ *   per-row codes rne(x * (127 / max|x|)) with scale = max|x| / 127 (keys
+ *   after rotation, values as given; an all-zero row has scale 0). */
 int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_t table_len,
                         void *q, int32_t n_q_heads, void *k, const void *v, int32_t act_dtype,
                         int32_t n_tokens, const int32_t *positions, const int32_t *seq_ids,
@@ -185,7 +189,8 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
  *     the learned-sink excerpt: a trained per-head logit in the softmax
  *     denominator, no cache entry): out = sum_j e^{s_j} v_j / (sum_j e^{s_j}
  *     + e^{sink_h}), the logit in the units of the scaled scores
- * Layouts RING and PAGED (block_size 16); kv_dtype F32 or BF16; d 64 or 128;
+ * Layouts RING and PAGED (block_size 16); kv_dtype F32, BF16 or I8 (q and out are
+ * then BF16; keys and values are dequantised with their row scales); d 64 or 128;
  * n_rep = n_q_heads / Hkv in {1, 2, 4, 8}.  ws: device, at least
  * ropekv_decode_workspace_size() bytes, caller-owned, overwritten. */
 int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,

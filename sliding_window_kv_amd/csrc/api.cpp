@@ -91,7 +91,8 @@ int check_cache(const ropekv_kv_cache *c) {
   if (c->sinks < 0 || c->window < 0) return fail(ROPEKV_EINVAL, "sinks and window must be >= 0");
   switch (c->layout) {
     case ROPEKV_RING:
-      if (c->kv_dtype == ROPEKV_I8) return fail(ROPEKV_EDTYPE, "RING cache cannot be int8");
+      if (c->kv_dtype == ROPEKV_I8 && (!c->k_scale || !c->v_scale))
+        return fail(ROPEKV_EINVAL, "int8 RING needs k_scale and v_scale");
       if (c->batch < 1) return fail(ROPEKV_EINVAL, "batch must be >= 1");
       if (c->window < 1) return fail(ROPEKV_EINVAL, "RING needs window >= 1");
       if (c->capacity != c->sinks + c->window)
@@ -100,7 +101,8 @@ int check_cache(const ropekv_kv_cache *c) {
         return fail(ROPEKV_EINVAL, "RING needs v, ring_head, ring_count and seq_len");
       break;
     case ROPEKV_PAGED:
-      if (c->kv_dtype == ROPEKV_I8) return fail(ROPEKV_EDTYPE, "PAGED cache cannot be int8");
+      if (c->kv_dtype == ROPEKV_I8 && (!c->k_scale || !c->v_scale))
+        return fail(ROPEKV_EINVAL, "int8 PAGED needs k_scale and v_scale");
       if (c->batch < 1) return fail(ROPEKV_EINVAL, "batch must be >= 1");
       if (c->block_size < 1 || c->max_blocks < 1 || c->num_blocks < 1)
         return fail(ROPEKV_EINVAL, "PAGED needs block_size, max_blocks, num_blocks >= 1");
@@ -113,7 +115,7 @@ int check_cache(const ropekv_kv_cache *c) {
       if ((long)c->pos0 + c->capacity - 1 > 0x7fffffffL) return fail(ROPEKV_ERANGE, "CONTIG positions overflow int32");
       if (c->kv_dtype == ROPEKV_I8) {
         if (!c->k_scale) return fail(ROPEKV_EINVAL, "CONTIG int8 needs k_scale");
-        if (c->v) return fail(ROPEKV_EDTYPE, "CONTIG int8 holds keys only (v must be NULL)");
+        if (c->v && !c->v_scale) return fail(ROPEKV_EINVAL, "CONTIG int8 values need v_scale");
       }
       break;
     default: return fail(ROPEKV_ELAYOUT, "unknown layout %d", c->layout);
@@ -121,9 +123,10 @@ int check_cache(const ropekv_kv_cache *c) {
   return ROPEKV_OK;
 }
 
-int check_attention_shape(const ropekv_kv_cache *c, int n_q_heads) {
-  if (c->kv_dtype != ROPEKV_F32 && c->kv_dtype != ROPEKV_BF16)
-    return fail(ROPEKV_EDTYPE, "attention supports F32 and BF16 caches");
+int check_attention_shape(const ropekv_kv_cache *c, int n_q_heads, bool int8_ok) {
+  if (c->kv_dtype != ROPEKV_F32 && c->kv_dtype != ROPEKV_BF16 && !(int8_ok && c->kv_dtype == ROPEKV_I8))
+    return fail(ROPEKV_EDTYPE, int8_ok ? "decode supports F32, BF16 and I8 caches"
+                                       : "prefill supports F32 and BF16 caches");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(ROPEKV_ERANGE, "attention supports head_dim 64 and 128");
   if (n_q_heads < 1 || n_q_heads % c->num_kv_heads)
     return fail(ROPEKV_EINVAL, "n_q_heads %d must be a positive multiple of num_kv_heads %d", n_q_heads,
@@ -170,7 +173,8 @@ int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_
     return fail(ROPEKV_EINVAL, "q must be given exactly when n_q_heads > 0");
   if (!k || !positions) return fail(ROPEKV_EINVAL, "k and positions are required");
   if (cache->layout != ROPEKV_CONTIG) {
-    if (cache->kv_dtype != act_dtype) return fail(ROPEKV_EDTYPE, "RING / PAGED need kv_dtype == act_dtype");
+    if (cache->kv_dtype != act_dtype && cache->kv_dtype != ROPEKV_I8)
+      return fail(ROPEKV_EDTYPE, "RING / PAGED need kv_dtype == act_dtype or I8");
     if (!seq_ids) return fail(ROPEKV_EINVAL, "seq_ids are required for RING / PAGED");
   }
   if (cache->v && !v) return fail(ROPEKV_EINVAL, "v is required when the cache holds values");
@@ -210,7 +214,7 @@ int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads, const ro
   if (e) return e;
   if (cache->layout != ROPEKV_RING && cache->layout != ROPEKV_PAGED)
     return fail(ROPEKV_ELAYOUT, "decode needs a RING or PAGED cache");
-  e = check_attention_shape(cache, n_q_heads);
+  e = check_attention_shape(cache, n_q_heads, true);
   if (e) return e;
   if (cache->layout == ROPEKV_PAGED && cache->block_size != 16)
     return fail(ROPEKV_EINVAL, "decode needs block_size 16");
@@ -231,7 +235,7 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
                         void *out, ropekv_stream_t stream) {
   int e = check_cache(cache);
   if (e) return e;
-  e = check_attention_shape(cache, n_q_heads);
+  e = check_attention_shape(cache, n_q_heads, false);
   if (e) return e;
   if (T < 0 || pos0 < 0) return fail(ROPEKV_EINVAL, "T and pos0 must be >= 0");
   if ((long)pos0 + T > 0x7fffffffL) return fail(ROPEKV_ERANGE, "positions overflow int32");

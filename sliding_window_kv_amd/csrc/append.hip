@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int Hkv = c.num_kv_heads;
   int err = 0;
   bool write = true;
-  long base = 0, hstride = 0, scale_base = 0;
+  long base = 0, hstride = 0;
   if (c.layout == ROPEKV_CONTIG) {
     const long row = (long)p - c.pos0;
     if (row < 0 || row >= c.capacity) {
@@ -70,7 +70,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     } else {
       base = row * Hkv * d;
       hstride = d;
-      scale_base = row * Hkv;
     }
   } else {
     const int seq = a.seq[t];
@@ -184,7 +183,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             const float qv = fminf(fmaxf(rintf(rowbuf[wave][e] * inv), -127.f), 127.f);
             kc[coff + e] = (int8_t)qv;
           }
-          if (lane == 0) c.k_scale[scale_base + h] = scale;
+          if (lane == 0) c.k_scale[coff / d] = scale;
           wave_lds_sync();
         }
       }
@@ -193,7 +192,25 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       if (write && a.v != nullptr && c.v != nullptr) {
         const long voff = ((long)t * Hkv + h) * d;
         const long coff = base + (long)h * hstride;
-        for (int e = lane; e < d; e += 64) store_elem(c.v, coff + e, kvdt, load_elem(a.v, voff + e, act));
+        if (kvdt == ROPEKV_I8) {
+          // values: the same per-row int8 quantiser as the keys, scale in v_scale
+          float amax = 0.f;
+          for (int e = lane; e < d; e += 64) {
+            const float val = load_elem(a.v, voff + e, act);
+            rowbuf[wave][e] = val;
+            amax = fmaxf(amax, fabsf(val));
+          }
+          for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);
+          wave_lds_sync();
+          const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+          int8_t *vc = (int8_t *)c.v;
+          for (int e = lane; e < d; e += 64)
+            vc[coff + e] = (int8_t)fminf(fmaxf(rintf(rowbuf[wave][e] * inv), -127.f), 127.f);
+          if (lane == 0) c.v_scale[coff / d] = amax / 127.0f;
+          wave_lds_sync();
+        } else {
+          for (int e = lane; e < d; e += 64) store_elem(c.v, coff + e, kvdt, load_elem(a.v, voff + e, act));
+        }
       }
     }
   }

@@ -453,6 +453,250 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
   }
 }
 
+// ---- int8 KV (codes + one fp32 scale per cached row) ----
+//
+// K and V rows are int8 codes c with a per-row scale sc (x ~ c * sc, the row
+// quantizer of the append).  |c| <= 127 is exact in bf16, so both products run
+// on bf16 MFMAs with the codes converted in registers:
+//   S^T = Kc . Q^T (16x16x32), then s = S^T * k_scale(key) in the log2 domain;
+//   O  += (P * v_scale(key)) . Vc (16x16x16, one MFMA per V column block).
+// The S^T fragment a lane holds (head `col`, keys 4 grp + j) is exactly the A
+// operand of the second MFMA, so P never leaves registers.  The V operand of
+// MFMA e is column dim col * (D / 16) + e, keys 4 grp + j: a lane loads D / 16
+// contiguous bytes of each of its 4 key rows.  Output row 4 grp + j of MFMA e
+// is query head 4 grp + j, dim col * (D / 16) + e.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// two floats that are exact in bf16 -> one packed word
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const float2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+__device__ __forceinline__ float code_f(uint32_t w, int byte) { return (float)(int8_t)(w >> (8 * byte)); }
+
+template <int NB>
+__device__ __forceinline__ void stream_small(uint32_t *dst, const char *src) {
+  if constexpr (NB == 4) {
+    dst[0] = __builtin_nontemporal_load((const uint32_t *)src);
+  } else {
+    load_bytes<NB>(dst, src);
+  }
+}
+
+template <int D>
+struct I8Frag {
+  uint32_t kw[D / 16];      // D / 4 key codes (pieces as for the 16-bit caches)
+  uint32_t vw[4][D / 64];   // D / 16 value codes of each of the lane's 4 keys
+  float ks[4], vs[4];       // row scales of those keys (vs = 0 for an invisible key)
+  bool vis[4];
+};
+
+template <int D, int NREP>
+__global__ __launch_bounds__(256) void decode_split_i8_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
+                                                              float sl2, float *__restrict__ ws, int tps,
+                                                              int splits) {
+  constexpr int QB = D / 4;   // key-code bytes per lane per tile
+  constexpr int E = D / 16;   // value-code bytes per lane per key = PV MFMAs per tile
+  using Frag = I8Frag<D>;
+  __shared__ float s_m[4][NREP], s_l[4][NREP];
+  __shared__ float s_acc[4][NREP][D];
+  __shared__ int s_bid[kMaxTps];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int Hkv = c.num_kv_heads;
+  const SeqTiles st = seq_tiles(c, b);
+  if (split == splits - 1 && threadIdx.x == 0 && st.ntiles > splits * tps) dev_error(c.err_word, ROPEKV_DEV_BLOCK_RANGE);
+  const int t_begin = split * tps;
+  if (t_begin >= st.ntiles) return;
+  const int t_end = min(st.ntiles, t_begin + tps);
+
+  if (c.layout == ROPEKV_PAGED) {
+    for (int i = threadIdx.x; i < t_end - t_begin; i += 256) {
+      const int tile = t_begin + i;
+      const int blk = tile < st.nsb ? tile : st.fr + (tile - st.nsb);
+      s_bid[i] = (blk < c.max_blocks) ? c.block_table[(long)b * c.max_blocks + blk] : -1;
+    }
+  }
+
+  // Q^T fragment (bf16): local element u of this lane is d = (4 (u / 16) + grp) * 16 + u % 16,
+  // the same d the key piece bytes of the lane hold.
+  uint32_t qw[D / 8];
+  if (col < NREP) {
+    const char *qrow = (const char *)qp + (long)(b * Hkv * NREP + g * NREP + col) * D * 2;
+#pragma unroll
+    for (int i = 0; i < QB / 16; ++i) load_bytes<32>(qw + 8 * i, qrow + (4 * i + grp) * 32);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) qw[i] = 0u;
+  }
+  __syncthreads();
+
+  const char *kbase = (const char *)c.k;
+  const char *vbase = (const char *)c.v;
+  const long head_base = ((long)b * Hkv + g) * (long)c.capacity * D;
+
+  auto load_tile = [&](Frag &f, int tile) -> bool {
+    long base;
+    int pos0 = 0, slot0 = 0;
+    bool ok = true;
+    if (c.layout == ROPEKV_PAGED) {
+      const int bid = s_bid[tile - t_begin];
+      const int blk = tile < st.nsb ? tile : st.fr + (tile - st.nsb);
+      pos0 = blk * kTile;
+      ok = bid >= 0 && bid < c.num_blocks;
+      base = ok ? ((long)bid * Hkv + g) * kTile * D : 0;
+    } else {
+      slot0 = tile * kTile;
+      base = head_base;
+    }
+    auto roff = [&](int r) -> long {
+      if (c.layout == ROPEKV_PAGED) return base + (long)r * D;
+      return base + (long)min(slot0 + r, c.capacity - 1) * D;
+    };
+    auto visible = [&](int r) -> bool {
+      if (!ok) return false;
+      if (c.layout == ROPEKV_PAGED) {
+        const int pos = pos0 + r;
+        return pos < st.ns || (pos >= st.rs && pos < st.n);
+      }
+      const int slot = slot0 + r;
+      if (slot >= c.capacity) return false;
+      if (slot < c.sinks) return slot < st.ns;
+      return imod(slot - c.sinks - st.oldest, c.window) < st.count;
+    };
+    if (ok) {
+      load_pieces<QB>(f.kw, kbase + roff(col), grp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) stream_small<E>(f.vw[j], vbase + roff(4 * grp + j) + col * E);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.vis[j] = visible(4 * grp + j);
+      const long srow = ok ? roff(4 * grp + j) / D : 0;  // scales are one float per cached row
+      f.ks[j] = ok ? c.k_scale[srow] : 0.f;
+      f.vs[j] = ok ? c.v_scale[srow] : 0.f;
+      if (!f.vis[j]) f.vs[j] = 0.f;
+    }
+    return ok;
+  };
+
+  float m_run = kNegBig, l_run = 0.f;
+  f32x4 acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bool bad_tile = false;
+  int tile = t_begin + wave;
+  Frag cur, nxt;
+  bool cur_ok = tile < t_end ? load_tile(cur, tile) : false;
+  for (; tile < t_end; tile += 4) {
+    bool nxt_ok = false;
+    if (tile + 4 < t_end) nxt_ok = load_tile(nxt, tile + 4);
+    if (!cur_ok) {
+      bad_tile = true;
+    } else {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        uint32_t a[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w = cur.kw[2 * t + h];
+          a[2 * h] = pack2_bf16(code_f(w, 0), code_f(w, 1));
+          a[2 * h + 1] = pack2_bf16(code_f(w, 2), code_f(w, 3));
+        }
+        const u32x4_t av = {a[0], a[1], a[2], a[3]};
+        const u32x4_t bv = {qw[4 * t], qw[4 * t + 1], qw[4 * t + 2], qw[4 * t + 3]};
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
+                                                       sacc, 0, 0, 0);
+      }
+      float s[4];
+      float mx = kNegBig;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[j] = cur.vis[j] ? sacc[j] * (cur.ks[j] * sl2) : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = exp2f(m_run - m_new);
+      float pj[4], psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pj[j] = exp2f(s[j] - m_new);
+        psum += pj[j];
+      }
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+      // rescale the output rows (heads 4 grp + j) whose running maximum moved
+      if (__any(corr != 1.f)) {
+        float cj[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cj[j] = __shfl(corr, 4 * grp + j);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[e][j] *= cj[j];
+      }
+      const uint32_t p01 = pack2_bf16(pj[0] * cur.vs[0], pj[1] * cur.vs[1]);
+      const uint32_t p23 = pack2_bf16(pj[2] * cur.vs[2], pj[3] * cur.vs[3]);
+      const short4_t pa = __builtin_bit_cast(short4_t, (uint2){p01, p23});
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int wsel = e >> 2, byte = e & 3;
+        const uint32_t v01 = pack2_bf16(code_f(cur.vw[0][wsel], byte), code_f(cur.vw[1][wsel], byte));
+        const uint32_t v23 = pack2_bf16(code_f(cur.vw[2][wsel], byte), code_f(cur.vw[3][wsel], byte));
+        const short4_t vb = __builtin_bit_cast(short4_t, (uint2){v01, v23});
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[e], 0, 0, 0);
+      }
+    }
+    cur = nxt;
+    cur_ok = nxt_ok;
+  }
+  if (bad_tile && lane == 0) dev_error(c.err_word, ROPEKV_DEV_NULL_BLOCK);
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * grp + j;
+    if (h < NREP) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_acc[wave][h][col * E + e] = acc[e][j];
+    }
+  }
+  if (grp == 0 && col < NREP) {
+    s_m[wave][col] = m_run;
+    s_l[wave][col] = l_run;
+  }
+  __syncthreads();
+  const int nwaves = min(4, t_end - t_begin);
+  float *dst = ws + (((long)(b * Hkv + g) * splits + split) * NREP) * (D + 2);
+  for (int idx = threadIdx.x; idx < NREP * D; idx += 256) {
+    const int h = idx / D, dd = idx % D;
+    float m = kNegBig;
+    for (int w = 0; w < nwaves; ++w) m = fmaxf(m, s_m[w][h]);
+    float a = 0.f, l = 0.f;
+    for (int w = 0; w < nwaves; ++w) {
+      const float f = exp2f(s_m[w][h] - m);
+      a += f * s_acc[w][h][dd];
+      l += f * s_l[w][h];
+    }
+    float *o = dst + (long)h * (D + 2);
+    o[dd] = a;
+    if (dd == 0) {
+      o[D] = m;
+      o[D + 1] = l;
+    }
+  }
+}
+
 // Merge the split partials of one (sequence, query head): weights exp2(m_s - m)
 // computed once per split, then one coalesced pass over the partial rows.
 constexpr int kMaxSplits = 1024;
@@ -529,6 +773,31 @@ hipError_t launch_decode_d(const void *q, int batch, const ropekv_kv_cache &c, f
     case 2: return launch_decode_t<T, D, 2>(q, batch, c, sl2, sk, out, ws, pl, s);
     case 4: return launch_decode_t<T, D, 4>(q, batch, c, sl2, sk, out, ws, pl, s);
     case 8: return launch_decode_t<T, D, 8>(q, batch, c, sl2, sk, out, ws, pl, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int NREP>
+hipError_t launch_decode_i8_t(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
+                              void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
+  dim3 grid(pl.splits, c.num_kv_heads, batch);
+  hipLaunchKernelGGL((decode_split_i8_kernel<D, NREP>), grid, dim3(256), 0, s, q, c, sl2, ws, pl.tiles_per_split,
+                     pl.splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<bf16_t, D, NREP>), dim3(c.num_kv_heads * NREP, batch), dim3(128), 0, s,
+                     c, ws, sinks, out, pl.tiles_per_split, pl.splits);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_i8_d(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sk,
+                              void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
+  switch (pl.n_rep) {
+    case 1: return launch_decode_i8_t<D, 1>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 2: return launch_decode_i8_t<D, 2>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 4: return launch_decode_i8_t<D, 4>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 8: return launch_decode_i8_t<D, 8>(q, batch, c, sl2, sk, out, ws, pl, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -614,6 +883,9 @@ hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_k
   } else if (c.kv_dtype == ROPEKV_F32) {
     if (c.head_dim == 128) return launch_decode_d<float, 128>(q, batch, c, sl2, sinks, out, w, pl, s);
     if (c.head_dim == 64) return launch_decode_d<float, 64>(q, batch, c, sl2, sinks, out, w, pl, s);
+  } else if (c.kv_dtype == ROPEKV_I8) {  // int8 codes, bf16 q and out
+    if (c.head_dim == 128) return launch_decode_i8_d<128>(q, batch, c, sl2, sinks, out, w, pl, s);
+    if (c.head_dim == 64) return launch_decode_i8_d<64>(q, batch, c, sl2, sinks, out, w, pl, s);
   }
   return hipErrorInvalidValue;
 }

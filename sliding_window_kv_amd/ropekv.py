@@ -81,6 +81,7 @@ class KVCache(ctypes.Structure):
         ("block_table", ctypes.c_void_p),
         ("seq_len", ctypes.c_void_p),
         ("err_word", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -159,12 +160,12 @@ def rope_cfg(head_dim, rotary_dim, rope_theta=10000.0, yarn_factor=1.0, orig_max
 
 def kv_cache(layout, kv_dtype, num_kv_heads, head_dim, k, v=None, *, batch=0, capacity=0, sinks=0, window=0,
              block_size=16, max_blocks=0, num_blocks=0, pos0=0, k_scale=None, ring_head=None, ring_count=None,
-             block_table=None, seq_len=None, err_word=None) -> KVCache:
+             block_table=None, seq_len=None, err_word=None, v_scale=None) -> KVCache:
     return KVCache(layout=layout, kv_dtype=kv_dtype, num_kv_heads=num_kv_heads, head_dim=head_dim, batch=batch,
                    capacity=capacity, sinks=sinks, window=window, block_size=block_size, max_blocks=max_blocks,
                    num_blocks=num_blocks, pos0=pos0, k=_ptr(k), v=_ptr(v), k_scale=_ptr(k_scale),
                    ring_head=_ptr(ring_head), ring_count=_ptr(ring_count), block_table=_ptr(block_table),
-                   seq_len=_ptr(seq_len), err_word=_ptr(err_word))
+                   seq_len=_ptr(seq_len), err_word=_ptr(err_word), v_scale=_ptr(v_scale))
 
 
 def build_table(cfg: RopeCfg, max_pos: int, cos_sin, mscale=None, stream=None) -> int:

@@ -48,3 +48,25 @@ def device_normal_(tensor, seed: int):
     else:
         raise TypeError(f"unsupported dtype {tensor.dtype}")
     return tensor
+
+
+def device_int8_codes_(tensor, seed: int):
+    """Fill an int8 device tensor in place with codes uniform in [-127, 127] (seeded device generator)."""
+    import torch
+
+    if tensor.dtype != torch.int8:
+        raise TypeError(f"expected int8, got {tensor.dtype}")
+    g = torch.Generator(device=tensor.device)
+    g.manual_seed(seed)
+    tensor.copy_(torch.randint(-127, 128, tensor.shape, generator=g, device=tensor.device, dtype=torch.int16))
+    return tensor
+
+
+def device_uniform_(tensor, lo: float, hi: float, seed: int):
+    """Fill a float device tensor in place with U(lo, hi) from a seeded device generator."""
+    import torch
+
+    g = torch.Generator(device=tensor.device)
+    g.manual_seed(seed)
+    tensor.uniform_(lo, hi, generator=g)
+    return tensor

@@ -60,9 +60,13 @@ class DevRing:
         self.count = torch.zeros(B, dtype=torch.int32, device=dev)
         self.seq_len = torch.zeros(B, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        kvdt = {torch.float32: R.F32, torch.bfloat16: R.BF16, torch.float16: R.F16}[dtype]
+        kvdt = {torch.float32: R.F32, torch.bfloat16: R.BF16, torch.float16: R.F16, torch.int8: R.I8}[dtype]
+        # int8 caches: one fp32 scale per cached row, K and V
+        self.k_scale = torch.zeros(B, Hkv, self.C, dtype=torch.float32, device=dev) if dtype == torch.int8 else None
+        self.v_scale = torch.zeros_like(self.k_scale) if dtype == torch.int8 else None
         self.desc = R.kv_cache(R.RING, kvdt, Hkv, d, self.k, self.v, batch=B, capacity=self.C, sinks=S, window=W,
-                               ring_head=self.head, ring_count=self.count, seq_len=self.seq_len, err_word=self.err)
+                               ring_head=self.head, ring_count=self.count, seq_len=self.seq_len, err_word=self.err,
+                               k_scale=self.k_scale, v_scale=self.v_scale)
 
 
 class DevPaged:
@@ -74,7 +78,10 @@ class DevPaged:
         self.table = torch.from_numpy(np.ascontiguousarray(table.astype(np.int32))).to(dev)
         self.seq_len = torch.zeros(B, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        kvdt = {torch.float32: R.F32, torch.bfloat16: R.BF16, torch.float16: R.F16}[dtype]
+        kvdt = {torch.float32: R.F32, torch.bfloat16: R.BF16, torch.float16: R.F16, torch.int8: R.I8}[dtype]
+        i8 = dtype == torch.int8
+        self.k_scale = torch.zeros(num_blocks, Hkv, bs, dtype=torch.float32, device=dev) if i8 else None
+        self.v_scale = torch.zeros_like(self.k_scale) if i8 else None
         self.desc = R.kv_cache(R.PAGED, kvdt, Hkv, d, self.k, self.v, batch=B, sinks=S, window=W, block_size=bs,
                                max_blocks=table.shape[1], num_blocks=num_blocks, block_table=self.table,
-                               seq_len=self.seq_len, err_word=self.err)
+                               seq_len=self.seq_len, err_word=self.err, k_scale=self.k_scale, v_scale=self.v_scale)

@@ -120,6 +120,9 @@ def test_apply_append_argument_errors():
     assert call(None) == R.EINVAL
     assert call(_ring(), freed=FAKE, nfreed=None) == R.EINVAL
     assert call(_ring(), n=0) == R.OK                         # nothing to do, nothing launched
+    assert call(_ring(kv_dtype=R.I8)) == R.EINVAL             # int8 cache without scales
+    assert call(_ring(kv_dtype=R.I8, k_scale=FAKE)) == R.EINVAL  # int8 cache without value scales
+    assert call(_ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE), n=0) == R.OK
 
 
 def test_attention_argument_errors():
@@ -137,6 +140,9 @@ def test_attention_argument_errors():
     assert dec(FAKE, 1, 8, ctypes.byref(c2), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.ERANGE
     c3 = _ring(kv_dtype=R.F16)
     assert dec(FAKE, 1, 8, ctypes.byref(c3), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.EDTYPE
+    c4 = _ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE)
+    assert dec(FAKE, 1, 8, ctypes.byref(c4), 0.0, None, FAKE, FAKE, 1, None) == R.ENOSPACE      # int8 accepted
+    assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(c4), 0, 0.0, None, FAKE, None) == R.EDTYPE  # prefill: no int8
     contig = R.kv_cache(R.CONTIG, R.F32, 4, 64, FAKE, capacity=10, err_word=FAKE)
     assert dec(FAKE, 1, 8, ctypes.byref(contig), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.ELAYOUT
     assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(contig), 0, 0.0, None, FAKE, None) == R.ELAYOUT  # prefix needs cache

@@ -52,6 +52,32 @@ def test_paged_decode_b64_ctx32768(env):
         assert_bf16_close(out[b], ref)
 
 
+def test_paged_decode_b64_ctx32768_int8(env):
+    # the same step over an int8 cache: the appended token quantised, decode over codes x scales
+    R, torch, dev, WL = env
+    wl = WL.PagedDecode(R, torch, dev, kv_int8=True)
+    q_raw, k_raw, v_raw = to_np64(wl.q), to_np64(wl.k_new), to_np64(wl.v_new)
+    wl.step()
+    torch.cuda.synchronize()
+    assert wl.err.item() == 0
+    otab_row = O.build_table(oracle_cfg(wl.cfg), wl.ctx)
+    q_rot = to_np64(wl.q)
+    out = to_np64(wl.out)
+    p = wl.ctx - 1
+    for b in (0, 41, 63):
+        kc, ks, vc, vs = wl.codes_of(b)
+        want_k = O.rope_apply(k_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
+        wk_codes, wk_scale = O.quant_int8_rows(want_k)
+        assert int(np.max(np.abs(kc[p].astype(np.int32) - wk_codes.astype(np.int32)))) <= 1
+        np.testing.assert_allclose(ks[p], wk_scale, rtol=1e-6, atol=0)
+        wv_codes, wv_scale = O.quant_int8_rows(v_raw[b])
+        assert np.array_equal(vc[p], wv_codes) and np.array_equal(vs[p], wv_scale)
+        k = O.dequant_int8_rows(kc, ks)
+        v = O.dequant_int8_rows(vc, vs)
+        ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
+        assert_bf16_close(out[b], ref)
+
+
 def test_ring_decode_128k(env):
     R, torch, dev, WL = env
     r = WL.RingDecode(R, torch, dev)
