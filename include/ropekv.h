@@ -101,7 +101,8 @@ typedef struct {
   double high_freq_factor; /* Llama-3: 4 (> low_freq_factor) */
 } ropekv_rope_cfg;
 
-/* One layer's KV cache.  All pointers are device pointers.
+/* One layer's KV cache.  All pointers are device pointers; k, v, k_scale and
+ * v_scale must be 16-byte aligned (ROPEKV_EINVAL otherwise).
  * Visible set of the query at position p ([SINK] visible-set definition):
  * key j <= p is visible iff j < sinks or p - j < window; window 0 = full
  * attention (PAGED only).  For RING, capacity C = sinks + window. */
@@ -192,7 +193,8 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
  * Layouts RING and PAGED (block_size 16); kv_dtype F32, BF16 or I8 (q and out are
  * then BF16; keys and values are dequantised with their row scales); d 64 or 128;
  * n_rep = n_q_heads / Hkv in {1, 2, 4, 8}.  ws: device, at least
- * ropekv_decode_workspace_size() bytes, caller-owned, overwritten. */
+ * ropekv_decode_workspace_size() bytes, caller-owned, overwritten.
+ * q, out and ws must be 16-byte aligned. */
 int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
                        const ropekv_kv_cache *cache, float scale, const float *sink_logits,
                        void *out, void *ws, size_t ws_bytes, ropekv_stream_t stream);
@@ -206,7 +208,7 @@ int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
  * pos0 + T <= C); a missing key sets ROPEKV_DEV_PREFIX_LOST.
  *   q [T, n_q_heads, d], out same; dtype = kv_dtype (F32 or BF16), d 64 or 128,
  *   n_rep = n_q_heads / Hkv in {1, 2, 4, 8}; seq_id only read when pos0 > 0;
- *   sink_logits as for ropekv_decode_attn. 
+ *   sink_logits as for ropekv_decode_attn; q, k, v and out 16-byte aligned.
  * bf16 runs on MFMA with fp32 accumulation; tiles no query can see are skipped. */
 int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, int32_t pos0,
                         int32_t n_q_heads, const ropekv_kv_cache *cache, int32_t seq_id,

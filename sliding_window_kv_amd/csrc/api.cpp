@@ -1,6 +1,7 @@
 // C ABI of libropekv.so: host-side validation, then launches on the caller's
 // stream.  Nothing here allocates device memory or synchronises the host.
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -78,6 +79,9 @@ int check_rope(const ropekv_rope_cfg *c, const char *name) {
   return ROPEKV_OK;
 }
 
+// The kernels move cache rows, scales, queries and outputs with 16-byte vector accesses.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 bool valid_dtype(int dt) { return dt == ROPEKV_F32 || dt == ROPEKV_BF16 || dt == ROPEKV_F16 || dt == ROPEKV_I8; }
 
 int check_cache(const ropekv_kv_cache *c) {
@@ -89,6 +93,8 @@ int check_cache(const ropekv_kv_cache *c) {
   if (!c->k) return fail(ROPEKV_EINVAL, "cache k is NULL");
   if (!c->err_word) return fail(ROPEKV_EINVAL, "cache err_word is NULL");
   if (c->sinks < 0 || c->window < 0) return fail(ROPEKV_EINVAL, "sinks and window must be >= 0");
+  if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->k_scale) || !aligned16(c->v_scale))
+    return fail(ROPEKV_EINVAL, "cache k, v, k_scale and v_scale must be 16-byte aligned");
   switch (c->layout) {
     case ROPEKV_RING:
       if (c->kv_dtype == ROPEKV_I8 && (!c->k_scale || !c->v_scale))
@@ -220,6 +226,8 @@ int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads, const ro
     return fail(ROPEKV_EINVAL, "decode needs block_size 16");
   if (batch < 1 || batch > cache->batch) return fail(ROPEKV_EINVAL, "batch %d outside [1, %d]", batch, cache->batch);
   if (!q || !out || !ws) return fail(ROPEKV_EINVAL, "q, out and ws are required");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws))
+    return fail(ROPEKV_EINVAL, "q, out and ws must be 16-byte aligned");
   if (!(scale >= 0.f) || !isfinite(scale)) return fail(ROPEKV_EINVAL, "scale must be finite and >= 0");
   const DecodePlan pl = plan_decode(batch, n_q_heads, *cache);
   if (ws_bytes < pl.ws_bytes)
@@ -240,6 +248,8 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
   if (T < 0 || pos0 < 0) return fail(ROPEKV_EINVAL, "T and pos0 must be >= 0");
   if ((long)pos0 + T > 0x7fffffffL) return fail(ROPEKV_ERANGE, "positions overflow int32");
   if (!q || !k || !v || !out) return fail(ROPEKV_EINVAL, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(ROPEKV_EINVAL, "q, k, v and out must be 16-byte aligned");
   if (!(scale >= 0.f) || !isfinite(scale)) return fail(ROPEKV_EINVAL, "scale must be finite and >= 0");
   if (pos0 > 0) {
     if (cache->layout != ROPEKV_RING && cache->layout != ROPEKV_PAGED)

@@ -123,6 +123,8 @@ def test_apply_append_argument_errors():
     assert call(_ring(kv_dtype=R.I8)) == R.EINVAL             # int8 cache without scales
     assert call(_ring(kv_dtype=R.I8, k_scale=FAKE)) == R.EINVAL  # int8 cache without value scales
     assert call(_ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE), n=0) == R.OK
+    assert call(_ring(k=FAKE + 8)) == R.EINVAL                # cache pools must be 16-byte aligned
+    assert call(_ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE + 4)) == R.EINVAL
 
 
 def test_attention_argument_errors():
@@ -140,6 +142,8 @@ def test_attention_argument_errors():
     assert dec(FAKE, 1, 8, ctypes.byref(c2), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.ERANGE
     c3 = _ring(kv_dtype=R.F16)
     assert dec(FAKE, 1, 8, ctypes.byref(c3), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.EDTYPE
+    assert dec(FAKE + 2, 1, 8, ctypes.byref(c), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.EINVAL  # q alignment
+    assert pre(FAKE, FAKE, FAKE, 8, 0, 8, ctypes.byref(c), 0, 0.0, None, FAKE + 4, None) == R.EINVAL  # out alignment
     c4 = _ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE)
     assert dec(FAKE, 1, 8, ctypes.byref(c4), 0.0, None, FAKE, FAKE, 1, None) == R.ENOSPACE      # int8 accepted
     assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(c4), 0, 0.0, None, FAKE, None) == R.EDTYPE  # prefill: no int8
