@@ -575,6 +575,83 @@ def rerotate_int8_rows(codes: np.ndarray, scale: np.ndarray, positions: np.ndarr
     return quant_int8_rows(y)
 
 
+def rerotate_int8_keep_scale_rows(codes: np.ndarray, scale: np.ndarray, positions: np.ndarray,
+                                  cfg_from: RopeCfg, cfg_to: RopeCfg):
+    """int8 rows, keeping each row's scale unless a turned code overflows.
+
+    [DYN] "Measured on this branch" notes that, without the Hadamard, a turn
+    leaves the dims past the rotary slice (codes and scales) bitwise as they
+    were written.  With one scale per row that holds only if the scale stays:
+    dequantise, turn the rotary pairs, and re-code the rotary dims with the old
+    scale (code = rne(x * (1 / scale)), decided in float32 like the row
+    quantiser); the tail codes and the scale are kept.  If any re-coded value
+    leaves [-127, 127] (the turn can grow a pair's larger component up to
+    sqrt(2) times, and the gain mscale_to / mscale_from may exceed 1), the row
+    is re-quantised whole as in rerotate_int8_rows.  A zero scale (all-zero
+    row) stays zero.
+    """
+    codes = np.asarray(codes)
+    scale = np.asarray(scale, dtype=np.float32)
+    x = dequant_int8_rows(codes, scale)
+    y = rerotate_rows(x, positions, cfg_from, cfg_to)
+    r = cfg_to.rotary_dim
+    inv = np.where(scale > 0, (np.float32(1.0) / np.where(scale > 0, scale, np.float32(1.0))).astype(np.float32),
+                   np.float32(0.0)).astype(np.float32)
+    y32 = y[..., :r].astype(np.float32)
+    cand = np.rint((y32 * inv[..., None]).astype(np.float32))
+    overflow = np.any(np.abs(cand) > 127, axis=-1)
+    out_codes = codes.astype(np.int8).copy()
+    out_scale = scale.copy()
+    keep = ~overflow
+    out_codes[keep, :r] = cand[keep].astype(np.int8)
+    full_codes, full_scale = quant_int8_rows(y)
+    out_codes[overflow] = full_codes[overflow]
+    out_scale[overflow] = full_scale[overflow]
+    return out_codes, out_scale, overflow
+
+
+# --------------------------------------------------------------------------
+# Hadamard-rotated int8 keys   ([DYN] "What it does": K with the Hadamard)
+# --------------------------------------------------------------------------
+
+
+def hadamard(x: np.ndarray) -> np.ndarray:
+    """Orthonormal Walsh-Hadamard transform over the last axis (length n = 2^k).
+
+    H_n = H_2 (x) ... (x) H_2 / sqrt(n) with H_2 = [[1, 1], [1, -1]]
+    (Sylvester order: H[i, j] = (-1)^popcount(i & j) / sqrt(n)).  H is
+    symmetric and orthogonal, so it is its own inverse.  Written as the k
+    butterfly passes over pairs (j, j + h), h = 1, 2, 4, ...
+    """
+    y = np.array(x, dtype=np.float64, copy=True)
+    n = y.shape[-1]
+    if n < 1 or n & (n - 1):
+        raise ValueError("length must be a power of two")
+    h = 1
+    while h < n:
+        for start in range(0, n, 2 * h):
+            a = y[..., start:start + h].copy()
+            b = y[..., start + h:start + 2 * h].copy()
+            y[..., start:start + h] = a + b
+            y[..., start + h:start + 2 * h] = a - b
+        h *= 2
+    return y / math.sqrt(n)
+
+
+def quant_int8_hadamard_rows(k_rot: np.ndarray):
+    """Store a rotated key as int8 codes of H k (per-row scale over the transformed row)."""
+    return quant_int8_rows(hadamard(k_rot))
+
+
+def rerotate_int8_hadamard_rows(codes: np.ndarray, scale: np.ndarray, positions: np.ndarray,
+                                cfg_from: RopeCfg, cfg_to: RopeCfg):
+    """Hadamard-rotated int8 rows: dequantise, H (back to the rotated key), turn the
+    rotary pairs as rerotate_rows, H, requantise the row ([DYN] "What it does")."""
+    k = hadamard(dequant_int8_rows(codes, scale))
+    y = rerotate_rows(k, positions, cfg_from, cfg_to)
+    return quant_int8_rows(hadamard(y))
+
+
 # --------------------------------------------------------------------------
 # The dynamic factor policy   ([DYN] "What it does": the factor)
 # --------------------------------------------------------------------------
