@@ -256,7 +256,7 @@ def main():
         torch.cuda.empty_cache()
 
         # ---------------- K re-rotation at a YaRN switch, 64 layers x 524288 x 8 heads
-        for kind in ("f16", "i8"):
+        for kind in ("f16", "i8", "i8_keep", "i8_hadamard"):
             log(f"setup: rerotate {kind}")
             rr = WL.Rerotate(R, torch, dev, kind=kind)
             flip = [1.0, 1.125]
@@ -265,9 +265,18 @@ def main():
                 rr.run(flip[0], flip[1])
                 flip.reverse()
 
+            kept = None
+            if kind == "i8_keep":
+                before = rr.scale.clone()
+                one()
+                torch.cuda.synchronize()
+                kept = round(float((rr.scale == before).float().mean().item()), 4)  # rows that kept their scale
+                del before
             ms = timed(torch, one, 4, warmup=1)
             rows[f"rerotate_{kind}_L64_T524288"] = {"ms": round(ms, 3), "GBps": round(rr.bytes() / ms / 1e6, 1),
                                                     "frac_hbm": round(rr.bytes() / ms / 1e6 / HBM_PEAK_GBS, 4)}
+            if kept is not None:
+                rows[f"rerotate_{kind}_L64_T524288"]["rows_kept_scale"] = kept
             if kind == "f16":
                 tcfg = rr.cfg(2.0)
                 tab = torch.empty(524288, 64, dtype=torch.float32, device=dev)

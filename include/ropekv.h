@@ -53,6 +53,17 @@ typedef void *ropekv_stream_t; /* a hipStream_t */
 #define ROPEKV_F16 2
 #define ROPEKV_I8 3
 
+/* k_int8_mode bits (int8 keys only) */
+#define ROPEKV_I8_KEEP_SCALE 1 /* rerotate keeps each row's scale (tail codes bitwise) unless a turned
+                                  rotary code leaves [-127, 127]; then the row is requantised whole
+                                  ([DYN] "Measured on this branch": without the Hadamard the dims past
+                                  the rotary slice stay as written).  Not with ROPEKV_I8_HADAMARD. */
+#define ROPEKV_I8_HADAMARD 2   /* K rows hold int8 codes of H k, H the orthonormal Walsh-Hadamard
+                                  transform over all d dims (d a power of two): apply_append
+                                  transforms before quantising, decode transforms the query (scores
+                                  are unchanged: H is orthogonal), rerotate turns H (dequantised row)
+                                  and transforms back ([DYN] "What it does": K with the Hadamard) */
+
 /* cache layouts */
 #define ROPEKV_RING 0   /* [batch, Hkv, C, d]: slots 0..S-1 sinks, S..C-1 a W-slot ring */
 #define ROPEKV_PAGED 1  /* pool [num_blocks, Hkv, block_size, d] + block table [batch, max_blocks] */
@@ -129,6 +140,8 @@ typedef struct {
   int32_t *seq_len;     /* RING, PAGED [batch]: tokens appended so far (= next position) */
   int32_t *err_word;    /* [1]: ROPEKV_DEV_* bits, OR-ed by kernels; caller clears */
   float *v_scale;       /* I8 RING / PAGED: per-row fp32 value scale, laid out like k_scale */
+  int32_t k_int8_mode;  /* I8 keys: 0 or ROPEKV_I8_* bits; must be 0 for other dtypes */
+  int32_t reserved;     /* 0 */
 } ropekv_kv_cache;
 
 /* Build the cos/sin table ([RoPE] _compute_cos_sin_cache, YaRN variant):

@@ -95,6 +95,15 @@ int check_cache(const ropekv_kv_cache *c) {
   if (c->sinks < 0 || c->window < 0) return fail(ROPEKV_EINVAL, "sinks and window must be >= 0");
   if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->k_scale) || !aligned16(c->v_scale))
     return fail(ROPEKV_EINVAL, "cache k, v, k_scale and v_scale must be 16-byte aligned");
+  if (c->k_int8_mode != 0) {
+    if (c->kv_dtype != ROPEKV_I8) return fail(ROPEKV_EINVAL, "k_int8_mode needs an I8 cache");
+    if (c->k_int8_mode & ~(ROPEKV_I8_KEEP_SCALE | ROPEKV_I8_HADAMARD))
+      return fail(ROPEKV_EINVAL, "unknown k_int8_mode bits %d", c->k_int8_mode);
+    if (c->k_int8_mode == (ROPEKV_I8_KEEP_SCALE | ROPEKV_I8_HADAMARD))
+      return fail(ROPEKV_EINVAL, "ROPEKV_I8_KEEP_SCALE does not apply to Hadamard-rotated keys");
+    if ((c->k_int8_mode & ROPEKV_I8_HADAMARD) && (c->head_dim < 64 || (c->head_dim & (c->head_dim - 1))))
+      return fail(ROPEKV_ERANGE, "Hadamard-rotated keys need head_dim = 2^k in [64, 512]");
+  }
   switch (c->layout) {
     case ROPEKV_RING:
       if (c->kv_dtype == ROPEKV_I8 && (!c->k_scale || !c->v_scale))
@@ -282,6 +291,8 @@ int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to, cons
       return fail(ROPEKV_ERANGE, "int8 rerotate needs head_dim = 16 * 2^k <= 1024");
     if (to->neox ? (r % 32) : (r % 16))
       return fail(ROPEKV_ERANGE, "int8 rerotate needs rotary_dim %% %d == 0", to->neox ? 32 : 16);
+    if ((cache->k_int8_mode & ROPEKV_I8_HADAMARD) && to->neox && (r < 64 || (r & (r - 1))))
+      return fail(ROPEKV_ERANGE, "Hadamard-rotated NeoX keys need rotary_dim = 2^k >= 64");
   }
   return hip_status(launch_rerotate(make_rope_params(*from), make_rope_params(*to), *cache, n_layers,
                                     (hipStream_t)stream),

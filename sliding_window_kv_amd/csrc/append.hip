@@ -171,8 +171,25 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             store_elem(c.k, coff + e, kvdt, val);
         }
         if (kvdt == ROPEKV_I8) {
-          // per-row symmetric int8: scale = max|x| / 127, code = rne(x * (127 / max|x|))
           wave_lds_sync();
+          if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {
+            // Hadamard-rotated storage: the row becomes H k (orthonormal Walsh-Hadamard,
+            // butterflies over pairs (j, j + h) for h = 1, 2, 4, ... < d), then is quantised
+            float *x = rowbuf[wave];
+            for (int h = 1; h < d; h <<= 1) {
+              for (int bf = lane; bf < d / 2; bf += 64) {
+                const int j = (bf / h) * 2 * h + (bf % h);
+                const float u = x[j], w = x[j + h];
+                x[j] = u + w;
+                x[j + h] = u - w;
+              }
+              wave_lds_sync();
+            }
+            const float norm = 1.0f / sqrtf((float)d);
+            for (int e = lane; e < d; e += 64) x[e] *= norm;
+            wave_lds_sync();
+          }
+          // per-row symmetric int8: scale = max|x| / 127, code = rne(x * (127 / max|x|))
           float amax = 0.f;
           for (int e = lane; e < d; e += 64) amax = fmaxf(amax, fabsf(rowbuf[wave][e]));
           for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);

@@ -566,6 +566,36 @@ __global__ __launch_bounds__(256) void decode_split_i8_kernel(const void *__rest
     for (int i = 0; i < D / 8; ++i) qw[i] = 0u;
   }
   wait_vmcnt<0>();
+  if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {
+    // Keys hold codes of H k: score with H q (H orthonormal, so (H q).(H k) = q.k).  The lane's
+    // local index u covers the bits of d other than the two lane-group bits (d = (4 (u / 16) + grp) * 16
+    // + u % 16), so the butterflies over u stay in the lane and the other two are lane-group exchanges.
+    constexpr int NU = D / 4;
+    float f[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) f[u] = __uint_as_float((u & 1) ? (qw[u >> 1] & 0xffff0000u) : (qw[u >> 1] << 16));
+#pragma unroll
+    for (int h = 1; h < NU; h <<= 1)
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if ((u & h) == 0) {
+          const float x0 = f[u], x1 = f[u + h];
+          f[u] = x0 + x1;
+          f[u + h] = x0 - x1;
+        }
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const float p = __shfl_xor(f[u], m);
+        f[u] = upper ? p - f[u] : f[u] + p;
+      }
+    }
+    const float norm = 1.0f / sqrtf((float)D);
+#pragma unroll
+    for (int w = 0; w < NU / 2; ++w) qw[w] = pack2_bf16(f[2 * w] * norm, f[2 * w + 1] * norm);
+  }
   __syncthreads();
 
   const char *kbase = (const char *)c.k;

@@ -24,7 +24,17 @@ struct RerotArgs {
   float *scale;
   int rows_T;  // rows (positions) per layer
   int Hkv, D, pos0, n_layers;
+  int keep_scale;  // int8: keep each row's scale unless a turned rotary code overflows
 };
+
+// Keep-scale decision for one int8 row: every turned rotary value of the row must
+// re-code within [-127, 127] at the row's old scale (decided like the quantiser, in
+// fp32 with the reciprocal of the scale).  `mx` is this lane's largest such code,
+// `lanes` the row's lane count (a power of two, lanes of a row adjacent).
+__device__ __forceinline__ bool row_keeps_scale(float mx, int lanes) {
+  for (int m = lanes >> 1; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  return mx <= 127.f;
+}
 
 // Fills s_cs / s_sn [kPT][half] with cos / sin of (pos) * (w_to - w_from) in
 // fp64, rounded to fp32, and returns the gain mu_to / mu_from.
@@ -270,11 +280,22 @@ __global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < TL; ++e) y[2 * H + e] = code_at(wt[u], e) * sco[u];
-        float amax = 0.f;
+        bool keep = false;
+        float inv = 0.f, amax = 0.f;
+        if (a.keep_scale) {
+          const float inv_old = sco[u] > 0.f ? 1.0f / sco[u] : 0.f;
+          float mx = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
-        for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+          for (int e = 0; e < 2 * H; ++e) mx = fmaxf(mx, fabsf(rintf(y[e] * inv_old)));
+          keep = row_keeps_scale(mx, L);
+          inv = inv_old;
+        }
+        if (!keep) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
+          for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+          inv = amax > 0.f ? 127.0f / amax : 0.f;
+        }
         uint32_t o1[NR], o2[NR], ot[NT];
 #pragma unroll
         for (int i = 0; i < NR; ++i) o1[i] = o2[i] = 0u;
@@ -304,8 +325,10 @@ __global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
           } else {
             st_n<2 * H>(rp + 2 * q * H, o1);
           }
-          if constexpr (TL > 0) st_n<TL>(rp + r + q * TL, ot);
-          if (q == 0) a.scale[row] = amax / 127.0f;
+          if constexpr (TL > 0) {
+            if (!keep) st_n<TL>(rp + r + q * TL, ot);
+          }
+          if (q == 0 && !keep) a.scale[row] = amax / 127.0f;
         }
       }
     }
@@ -378,12 +401,25 @@ __global__ __launch_bounds__(256) void rerotate_int8_kernel(RerotArgs a) {
           }
         }
       }
-      float amax = 0.f;
+      const bool rot_chunk = 16 * q < r;  // rotary_dim is a multiple of 16: chunks are rotary or tail
+      bool keep = false;
+      float inv = 0.f, amax = 0.f;
+      if (a.keep_scale) {
+        const float inv_old = sc_old > 0.f ? 1.0f / sc_old : 0.f;
+        float mx = 0.f;
+        if (rot_chunk) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
-      for (int m = lpr >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-      const float sc_new = amax / 127.0f;
-      const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(rintf(y[e] * inv_old)));
+        }
+        keep = row_keeps_scale(mx, lpr);
+        inv = inv_old;
+      }
+      if (!keep) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
+        for (int m = lpr >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+        inv = amax > 0.f ? 127.0f / amax : 0.f;
+      }
       uint32_t out[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -391,8 +427,126 @@ __global__ __launch_bounds__(256) void rerotate_int8_kernel(RerotArgs a) {
         out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)qv) << (8 * (e & 3));
       }
       if (live) {
-        *(uint4 *)(kc + row * a.D + q * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-        if (q == 0) a.scale[row] = sc_new;
+        if (!keep || rot_chunk) *(uint4 *)(kc + row * a.D + q * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+        if (q == 0 && !keep) a.scale[row] = amax / 127.0f;
+      }
+    }
+  }
+}
+
+// Hadamard-rotated int8 keys: a row holds the codes of H k, H the orthonormal
+// Walsh-Hadamard transform over its D dims.  Per row: transform the codes
+// (unnormalised butterflies, exact in fp32), turn the rotary pairs, transform
+// again and multiply by scale / D (the two transforms' normalisation), then
+// requantise the row.  L = D / 32 lanes per row; lane q holds dims
+// [32 q, 32 q + 32), so butterflies over bits 0..4 stay in the lane and the
+// rest are lane exchanges.  NeoX partners (i, i + r/2) sit r / 64 lanes apart,
+// GPT-J partners in the same lane.
+__device__ __forceinline__ void fwht_lane32(float (&x)[32], int q, int L) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if ((j & h) == 0) {
+        const float u = x[j], v = x[j + h];
+        x[j] = u + v;
+        x[j + h] = u - v;
+      }
+  for (int m = 1; m < L; m <<= 1) {
+    const bool upper = (q & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = __shfl_xor(x[j], m);
+      x[j] = upper ? p - x[j] : x[j] + p;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void rerotate_int8_hadamard_kernel(RerotArgs a) {
+  __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
+  __shared__ double s_dw[256];
+  const int t0 = blockIdx.x * kPT;
+  const float gain = angle_setup(a, t0, s_cs, s_sn, s_dw);
+  const int half = a.to.rotary_dim / 2;
+  const int r = a.to.rotary_dim;
+  const int L = a.D / 32;                // lanes per row (power of two, 2..16)
+  const int rows_per_pass = 256 / L;
+  const int npos = min(kPT, a.rows_T - t0);
+  const int nrows = npos * a.Hkv;
+  const int q = threadIdx.x % L;
+  const int part = half / 32;            // NeoX partner distance in lanes (power of two)
+  const int neox = a.to.neox;
+  const float post = 1.0f / (float)a.D;  // H H unnormalised = D x identity
+  const long layer_rows = (long)a.rows_T * a.Hkv;
+  int8_t *kc = (int8_t *)a.k;
+  for (int layer = 0; layer < a.n_layers; ++layer) {
+    const long row0 = layer * layer_rows + (long)t0 * a.Hkv;
+    // every lane runs the same number of passes so the lane exchanges stay converged
+    for (int base = 0; base < nrows; base += rows_per_pass) {
+      const int rr = base + threadIdx.x / L;
+      const bool live = rr < nrows;
+      const long row = row0 + (live ? rr : 0);
+      const int pt = (live ? rr : 0) / a.Hkv;
+      const float sc_old = live ? a.scale[row] : 0.f;
+      const int8_t *src = kc + row * a.D + 32 * q;
+      const uint4 w0 = live ? *(const uint4 *)src : make_uint4(0, 0, 0, 0);
+      const uint4 w1 = live ? *(const uint4 *)(src + 16) : make_uint4(0, 0, 0, 0);
+      const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float x[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = (float)(int8_t)((ww[e >> 2] >> (8 * (e & 3))) & 0xff);
+      fwht_lane32(x, q, L);
+      float y[32];
+      if (neox) {
+        const bool rot = q < 2 * part, first = q < part;
+        const int i0 = 32 * (first ? q : q - part);
+        float px[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) px[e] = __shfl_xor(x[e], part);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          if (rot) {
+            const float cs = s_cs[pt * half + i0 + e], sn = s_sn[pt * half + i0 + e];
+            y[e] = first ? (x[e] * cs - px[e] * sn) * gain : (x[e] * cs + px[e] * sn) * gain;
+          } else {
+            y[e] = x[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 32; e += 2) {
+          if (32 * q + e < r) {
+            const int i = (32 * q + e) / 2;
+            const float cs = s_cs[pt * half + i], sn = s_sn[pt * half + i];
+            y[e] = (x[e] * cs - x[e + 1] * sn) * gain;
+            y[e + 1] = (x[e + 1] * cs + x[e] * sn) * gain;
+          } else {
+            y[e] = x[e];
+            y[e + 1] = x[e + 1];
+          }
+        }
+      }
+      fwht_lane32(y, q, L);
+      const float f = sc_old * post;
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        y[e] *= f;
+        amax = fmaxf(amax, fabsf(y[e]));
+      }
+      for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+      const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+      uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float qv = fminf(fmaxf(rintf(y[e] * inv), -127.f), 127.f);
+        out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)qv) << (8 * (e & 3));
+      }
+      if (live) {
+        int8_t *dst = kc + row * a.D + 32 * q;
+        *(uint4 *)dst = make_uint4(out[0], out[1], out[2], out[3]);
+        *(uint4 *)(dst + 16) = make_uint4(out[4], out[5], out[6], out[7]);
+        if (q == 0) a.scale[row] = amax / 127.0f;
       }
     }
   }
@@ -522,10 +676,15 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
   a.D = c.head_dim;
   a.pos0 = c.pos0;
   a.n_layers = n_layers;
+  a.keep_scale = (c.k_int8_mode & ROPEKV_I8_KEEP_SCALE) != 0;
   dim3 grid((c.capacity + kPT - 1) / kPT);
   const int half = to.rotary_dim / 2;
   switch (c.kv_dtype) {
     case ROPEKV_I8: {
+      if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {
+        hipLaunchKernelGGL(rerotate_int8_hadamard_kernel, grid, dim3(256), 0, s, a);
+        break;
+      }
       // lane-local pairs when each lane's 16 codes split into whole pairs and tail: H = half / (D / 16)
       const int L = c.head_dim / 16;
       const int H = (half % L == 0) ? half / L : 0;

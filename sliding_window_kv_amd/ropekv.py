@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG, "libropekv.so")
 
 F32, BF16, F16, I8 = 0, 1, 2, 3
 RING, PAGED, CONTIG = 0, 1, 2
+I8_KEEP_SCALE, I8_HADAMARD = 1, 2
 
 DEV_TABLE_RANGE = 1
 DEV_POSITION = 2
@@ -82,6 +83,8 @@ class KVCache(ctypes.Structure):
         ("seq_len", ctypes.c_void_p),
         ("err_word", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+        ("k_int8_mode", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -160,12 +163,13 @@ def rope_cfg(head_dim, rotary_dim, rope_theta=10000.0, yarn_factor=1.0, orig_max
 
 def kv_cache(layout, kv_dtype, num_kv_heads, head_dim, k, v=None, *, batch=0, capacity=0, sinks=0, window=0,
              block_size=16, max_blocks=0, num_blocks=0, pos0=0, k_scale=None, ring_head=None, ring_count=None,
-             block_table=None, seq_len=None, err_word=None, v_scale=None) -> KVCache:
+             block_table=None, seq_len=None, err_word=None, v_scale=None, k_int8_mode=0) -> KVCache:
     return KVCache(layout=layout, kv_dtype=kv_dtype, num_kv_heads=num_kv_heads, head_dim=head_dim, batch=batch,
                    capacity=capacity, sinks=sinks, window=window, block_size=block_size, max_blocks=max_blocks,
                    num_blocks=num_blocks, pos0=pos0, k=_ptr(k), v=_ptr(v), k_scale=_ptr(k_scale),
                    ring_head=_ptr(ring_head), ring_count=_ptr(ring_count), block_table=_ptr(block_table),
-                   seq_len=_ptr(seq_len), err_word=_ptr(err_word), v_scale=_ptr(v_scale))
+                   seq_len=_ptr(seq_len), err_word=_ptr(err_word), v_scale=_ptr(v_scale),
+                   k_int8_mode=k_int8_mode, reserved=0)
 
 
 def build_table(cfg: RopeCfg, max_pos: int, cos_sin, mscale=None, stream=None) -> int:

@@ -216,7 +216,12 @@ class Prefill:
 
 
 class Rerotate:
-    """Cached keys of L layers x T positions x Hkv heads, fp16 or int8 + per-row fp32 scale, turned in place."""
+    """Cached keys of L layers x T positions x Hkv heads, fp16 or int8 + per-row fp32 scale, turned in place.
+
+    kind "f16" and "i8": seeded N(0, 1) fp16 keys / uniform int8 codes with U(0.01, 0.03) scales.
+    "i8_keep" (keep the row scale unless a code overflows) and "i8_hadamard" (rows hold codes of H k):
+    seeded N(0, 1) raw keys written at factor 1 by apply_append, so rows look like quantised keys.
+    """
 
     def __init__(self, R, torch, dev, kind="f16", L=64, T=524288, Hkv=8, d=128, r=64, theta=5e5, L0=262144, pos0=0,
                  seed=4000):
@@ -224,18 +229,34 @@ class Rerotate:
         self.kind, self.L, self.T, self.Hkv, self.d, self.r = kind, L, T, Hkv, d, r
         self.theta, self.L0 = theta, L0
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        mode = {"i8_keep": R.I8_KEEP_SCALE, "i8_hadamard": R.I8_HADAMARD}.get(kind, 0)
         if kind == "f16":
             self.k = synth.device_normal_(torch.empty(L, T, Hkv, d, dtype=torch.float16, device=dev), seed)
             self.scale = None
             dt = R.F16
-        else:
+        elif kind == "i8":
             g = torch.Generator(device=dev)
             g.manual_seed(seed)
             self.k = torch.randint(-127, 128, (L, T, Hkv, d), dtype=torch.int8, device=dev, generator=g)
             self.scale = torch.rand(L, T, Hkv, dtype=torch.float32, device=dev, generator=g) * 0.02 + 0.01
             dt = R.I8
+        else:
+            self.k = torch.empty(L, T, Hkv, d, dtype=torch.int8, device=dev)
+            self.scale = torch.empty(L, T, Hkv, dtype=torch.float32, device=dev)
+            dt = R.I8
+            cfg = self.cfg(1.0)
+            table = torch.empty(pos0 + T, r, dtype=torch.float32, device=dev)
+            R.build_table(cfg, pos0 + T, table)
+            pos = torch.arange(pos0, pos0 + T, dtype=torch.int32, device=dev)
+            raw = torch.empty(T, Hkv, d, dtype=torch.float16, device=dev)
+            for layer in range(L):
+                synth.device_normal_(raw, seed + layer)
+                dl = R.kv_cache(R.CONTIG, dt, Hkv, d, self.k[layer], capacity=T, pos0=pos0,
+                                k_scale=self.scale[layer], err_word=self.err, k_int8_mode=mode)
+                R.apply_append(cfg, table, pos0 + T, None, 0, raw, None, R.F16, T, pos, None, dl)
+            del raw, table
         self.desc = R.kv_cache(R.CONTIG, dt, Hkv, d, self.k, capacity=T, pos0=pos0, k_scale=self.scale,
-                               err_word=self.err)
+                               err_word=self.err, k_int8_mode=mode)
 
     def cfg(self, s: float):
         return self.R.rope_cfg(self.d, self.r, rope_theta=self.theta, yarn_factor=s, orig_max_pos=self.L0)
@@ -244,7 +265,11 @@ class Rerotate:
         self.R.rerotate(self.cfg(s_from), self.cfg(s_to), self.desc, self.L)
 
     def bytes(self) -> int:
+        """fp16: the rotary slice read and written.  int8: the row and its scale read and written
+        (keep-scale: the row read, the rotary codes written; rows that overflow write more, uncounted)."""
         rows = self.L * self.T * self.Hkv
         if self.kind == "f16":
             return 2 * rows * self.r * 2
+        if self.kind == "i8_keep":
+            return rows * (self.d + 4 + self.r)
         return 2 * rows * (self.d + 4)

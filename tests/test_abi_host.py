@@ -123,6 +123,11 @@ def test_apply_append_argument_errors():
     assert call(_ring(kv_dtype=R.I8)) == R.EINVAL             # int8 cache without scales
     assert call(_ring(kv_dtype=R.I8, k_scale=FAKE)) == R.EINVAL  # int8 cache without value scales
     assert call(_ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE), n=0) == R.OK
+    assert call(_ring(k_int8_mode=R.I8_HADAMARD)) == R.EINVAL  # int8 key modes need an I8 cache
+    i8 = dict(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE)
+    assert call(_ring(k_int8_mode=4, **i8)) == R.EINVAL       # unknown mode bit
+    assert call(_ring(k_int8_mode=R.I8_HADAMARD | R.I8_KEEP_SCALE, **i8)) == R.EINVAL
+    assert call(_ring(k_int8_mode=R.I8_HADAMARD, head_dim=96, **i8)) == R.ERANGE  # H needs d = 2^k
     assert call(_ring(k=FAKE + 8)) == R.EINVAL                # cache pools must be 16-byte aligned
     assert call(_ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE + 4)) == R.EINVAL
 
@@ -185,3 +190,8 @@ def test_rerotate_argument_errors():
     d = R.rope_cfg(128, 48, rope_theta=5e5)
     e = R.rope_cfg(128, 48, rope_theta=5e5, yarn_factor=2.0, orig_max_pos=262144)
     assert f(ctypes.byref(d), ctypes.byref(e), ctypes.byref(i8b), 1, None) == R.ERANGE
+    i8h = R.kv_cache(R.CONTIG, R.I8, 8, 128, FAKE, capacity=100, err_word=FAKE, k_scale=FAKE,
+                     k_int8_mode=R.I8_HADAMARD)
+    g = R.rope_cfg(128, 96, rope_theta=5e5)
+    h = R.rope_cfg(128, 96, rope_theta=5e5, yarn_factor=2.0, orig_max_pos=262144)
+    assert f(ctypes.byref(g), ctypes.byref(h), ctypes.byref(i8h), 1, None) == R.ERANGE  # H + NeoX: r = 2^k
