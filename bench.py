@@ -58,7 +58,10 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel_file: str, profile: str):
+DECODE_SOURCES = ("decode.hip", "decode_common.hpp", "common.hpp")
+
+
+def counter_traffic(sources, profile: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
 
     The summary records the hash of the kernel source it was taken on; a
@@ -70,7 +73,7 @@ def counter_traffic(kernel_file: str, profile: str):
     text = open(path).read()
     m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kernel_file, "common.hpp"):
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(*sources):
         return None
     return float(m_bytes.group(1))
 
@@ -168,7 +171,7 @@ def main():
     ms_app = timed(torch, lambda: (wl.seq_len.fill_(wl.ctx - 1), wl.append()), max(args.steps, 20))
     achieved = dec_bytes / (ms_dec * 1e-3) / 1e9
     log(f"decode step {ms_step:.3f} ms, decode {ms_dec:.3f} ms = {achieved:.0f} GB/s")
-    traffic = counter_traffic("decode.hip", "decode_split_kernel_b64_ctx32768_pmc.md")
+    traffic = counter_traffic(DECODE_SOURCES, "decode_split_kernel_b64_ctx32768_pmc.md")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "decode_split_kernel + decode_combine_kernel (one ropekv_decode_attn call)",
@@ -191,7 +194,9 @@ def main():
     assert wq.err.item() == 0, f"device error word {wq.err.item()}"
     rows["decode_b64_ctx32768_int8kv"] = {"ms": round(ms_q, 4), "GBps": round(wq.decode_bytes() / ms_q / 1e6, 1),
                                           "frac_hbm": round(wq.decode_bytes() / ms_q / 1e6 / HBM_PEAK_GBS, 4),
-                                          "speedup_vs_bf16": round(ms_dec / ms_q, 3)}
+                                          "speedup_vs_bf16": round(ms_dec / ms_q, 3),
+                                          "traffic": counter_traffic(("decode_i8.hip", "decode_common.hpp", "common.hpp"),
+                                                                     "decode_split_i8_kernel_b64_ctx32768_pmc.md")}
     rows["rope_append_b64_int8kv"] = {"ms": round(ms_qapp, 4)}
     del wq
     torch.cuda.empty_cache()

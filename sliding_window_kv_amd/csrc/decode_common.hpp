@@ -1,0 +1,191 @@
+// Shared pieces of the split-K decode kernels (16-bit / fp32 and int8 caches):
+// the tile walk over a sequence's visible cache rows, fragment loads, and the
+// launch that merges the split partials.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace ropekv {
+namespace decode_detail {
+namespace {  // each decode source gets its own copies of these kernels and helpers
+
+constexpr int kTile = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+
+// Tiles of one sequence and how a tile maps to cache rows.
+struct SeqTiles {
+  int n;       // tokens in the sequence (query at n - 1)
+  int ntiles;  // tiles to visit
+  int ns, rs;  // PAGED: positions < ns (sinks) and [rs, n) are visible
+  int nsb, fr; // PAGED: sink tiles are blocks 0..nsb-1; then blocks fr, fr+1, ...
+  int oldest, count;  // RING: valid ring indices are oldest .. oldest+count-1 (mod W)
+};
+
+__device__ __forceinline__ int imod(int x, int m) {
+  int r = x % m;
+  return r < 0 ? r + m : r;
+}
+
+__device__ inline SeqTiles seq_tiles(const ropekv_kv_cache &c, int b) {
+  SeqTiles st;
+  st.n = c.seq_len[b];
+  st.ntiles = 0;
+  st.ns = st.rs = st.nsb = st.fr = st.oldest = st.count = 0;
+  const int n = st.n;
+  if (n <= 0) return st;
+  if (c.layout == ROPEKV_PAGED) {
+    if (c.window == 0) {
+      st.ns = n;
+      st.rs = n;
+      st.nsb = (n + kTile - 1) / kTile;
+      st.fr = st.nsb;
+      st.ntiles = st.nsb;
+    } else {
+      const int ns = min(c.sinks, n);
+      const int rs = max(ns, n - c.window);
+      const int nsb = (ns + kTile - 1) / kTile;
+      const int fr = max(rs / kTile, nsb);
+      const int lastb = (n - 1) / kTile;
+      st.ns = ns;
+      st.rs = rs;
+      st.nsb = nsb;
+      st.fr = fr;
+      st.ntiles = nsb + max(0, lastb - fr + 1);
+    }
+  } else {  // RING
+    const int S = c.sinks, W = c.window, C = c.capacity;
+    const int cnt = min(max(c.ring_count[b], 0), W);
+    const int hb = imod(c.ring_head[b], W);
+    const int oldest = imod(hb - cnt, W);
+    const int limit = (cnt < W && oldest + cnt <= W) ? S + oldest + cnt : C;
+    st.ns = min(S, n);
+    st.oldest = oldest;
+    st.count = cnt;
+    st.ntiles = (limit + kTile - 1) / kTile;
+  }
+  return st;
+}
+
+template <int NB>
+__device__ __forceinline__ void load_bytes(uint32_t *dst, const void *src) {
+  static_assert(NB % 8 == 0, "fragment size");
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)src + i);
+      dst[4 * i + 0] = v.x;
+      dst[4 * i + 1] = v.y;
+      dst[4 * i + 2] = v.z;
+      dst[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB / 8; ++i) {
+      const uint2 v = ((const uint2 *)src)[i];
+      dst[2 * i + 0] = v.x;
+      dst[2 * i + 1] = v.y;
+    }
+  }
+}
+
+// A lane's share of one K (or Q) row for the 16x16 MFMAs: QB bytes as 16-byte
+// pieces, piece i taken from byte offset (4 i + grp) * 16 of the row.  The four
+// lane groups of a row thus read 64 contiguous bytes per load instruction.
+// Any fixed assignment of row chunks to (piece, group) is valid because the
+// d-reduction is order-free, as long as K and Q use the same one.
+// K and V are streamed once per decode: nontemporal loads keep them from
+// displacing reusable lines in the caches.
+__device__ __forceinline__ void stream16(uint32_t *dst, const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+  dst[0] = v.x;
+  dst[1] = v.y;
+  dst[2] = v.z;
+  dst[3] = v.w;
+}
+
+template <int QB>
+__device__ __forceinline__ void load_pieces(uint32_t *dst, const char *row, int grp) {
+  static_assert(QB % 16 == 0, "pieces are 16 bytes");
+#pragma unroll
+  for (int i = 0; i < QB / 16; ++i) stream16(dst + 4 * i, row + (4 * i + grp) * 16);
+}
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<float> {
+  static constexpr int kBytes = 4;
+  static __device__ __forceinline__ float get(const uint32_t *w, int i) { return __uint_as_float(w[i]); }
+  static __device__ __forceinline__ void put(void *p, long i, float v) { ((float *)p)[i] = v; }
+};
+template <>
+struct ElemTraits<bf16_t> {
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ float get(const uint32_t *w, int i) {
+    const uint32_t x = w[i >> 1];
+    return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+  static __device__ __forceinline__ void put(void *p, long i, float v) { ((uint16_t *)p)[i] = f_to_bf16(v); }
+};
+
+constexpr int kMaxTps = 256;  // tiles per split (block-table entries staged in LDS)
+
+// Merge the split partials of one (sequence, query head): weights exp2(m_s - m)
+// computed once per split, then one coalesced pass over the partial rows.
+constexpr int kMaxSplits = 1024;
+
+template <typename T, int D, int NREP>
+__global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, const float *__restrict__ ws,
+                                                             const float *__restrict__ sinks, void *__restrict__ out,
+                                                             int tps, int splits) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[128];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int Hkv = c.num_kv_heads;
+  const int g = h / NREP, hh = h % NREP;
+  const SeqTiles st = seq_tiles(c, b);
+  const int used = min(min((st.ntiles + tps - 1) / tps, splits), kMaxSplits);
+  const long obase = ((long)b * Hkv * NREP + h) * D;
+  const float *src = ws + (((long)(b * Hkv + g) * splits) * NREP + hh) * (D + 2);
+  const long sstride = (long)NREP * (D + 2);
+  // global max over splits
+  float m = kNegBig;
+  for (int s = threadIdx.x; s < used; s += blockDim.x) m = fmaxf(m, src[s * sstride + D]);
+  s_red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) s_red[threadIdx.x] = fmaxf(s_red[threadIdx.x], s_red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  m = s_red[0];
+  // a learned sink logit joins the normaliser (log2 units like the partial maxima)
+  const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+  if (used > 0) m = fmaxf(m, sink2);
+  __syncthreads();
+  // per-split weights and the total weight l
+  float l = 0.f;
+  for (int s = threadIdx.x; s < used; s += blockDim.x) {
+    const float w = exp2f(src[s * sstride + D] - m);
+    s_w[s] = w;
+    l += w * src[s * sstride + D + 1];
+  }
+  s_red[threadIdx.x] = l;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) s_red[threadIdx.x] += s_red[threadIdx.x + w];
+    __syncthreads();
+  }
+  l = s_red[0];
+  if (sinks && used > 0) l += exp2f(sink2 - m);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
+    float a = 0.f;
+    for (int s = 0; s < used; ++s) a = fmaf(s_w[s], src[s * sstride + dd], a);
+    ElemTraits<T>::put(out, obase + dd, a * inv);
+  }
+}
+
+}  // namespace
+}  // namespace decode_detail
+}  // namespace ropekv
