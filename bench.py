@@ -253,10 +253,28 @@ def main():
         rows["prefill_t8192_h64_w4096"] = {"ms": round(ms, 4), "TFLOPs": round(tflops, 2),
                                            "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4),
                                            "algorithmic_flops": pf.flops()}
+        ms_app = timed(torch, pf.append, 10)
+        assert pf.int_state[3].item() == 0
+        rows["rope_append_prefill_t8192"] = {"ms": round(ms_app, 4), "GBps": round(pf.append_bytes() / ms_app / 1e6, 1)}
         wd = WL.WindowedPagedDecode(R, torch, dev)
-        ms = timed(torch, wd.decode, 20)
-        rows["decode_windowed_b256_h64"] = {"ms": round(ms, 4), "GBps": round(wd.decode_bytes() / ms / 1e6, 1)}
+        ms_wd = timed(torch, wd.decode, 20)
+        rows["decode_windowed_b256_h64"] = {"ms": round(ms_wd, 4), "GBps": round(wd.decode_bytes() / ms_wd / 1e6, 1)}
         assert wd.err.item() == 0
+        # one mixed step: the prefill chunk and the decode batch on two streams (default priority)
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+        def mixed():
+            cur = torch.cuda.current_stream()
+            s1.wait_stream(cur)
+            s2.wait_stream(cur)
+            pf.run(stream=s1)
+            wd.decode(stream=s2)
+            cur.wait_stream(s1)
+            cur.wait_stream(s2)
+
+        ms_mix = timed(torch, mixed, 10)
+        rows["mixed_prefill_decode_two_streams"] = {"ms": round(ms_mix, 4), "alone_sum_ms": round(ms + ms_wd, 4),
+                                                    "overlap_gain": round((ms + ms_wd) / ms_mix, 3)}
         del pf, wd
         torch.cuda.empty_cache()
 

@@ -180,8 +180,8 @@ class WindowedPagedDecode:
         self.ws_bytes = R.decode_workspace_size(B, Hq, self.desc)
         self.ws = torch.empty(self.ws_bytes // 4 + 1, dtype=torch.float32, device=dev)
 
-    def decode(self):
-        self.R.decode_attn(self.q, self.B, self.Hq, self.desc, 0.0, self.out, self.ws, self.ws_bytes)
+    def decode(self, stream=None):
+        self.R.decode_attn(self.q, self.B, self.Hq, self.desc, 0.0, self.out, self.ws, self.ws_bytes, stream=stream)
 
     def decode_bytes(self) -> int:
         vis = sum(visible_count(int(n) - 1, self.S, self.W) for n in self.lens)
@@ -200,15 +200,34 @@ class Prefill:
         self.k = synth.device_normal_(torch.empty(T, Hkv, d, dtype=bf, device=dev), seed + 2)
         self.v = synth.device_normal_(torch.empty(T, Hkv, d, dtype=bf, device=dev), seed + 3)
         self.out = torch.empty_like(self.q)
-        # the chunk starts at position 0: the cache only describes the layer (S, W, heads)
+        # the chunk starts at position 0; its rope + append writes the survivors into a ring layer
         self.kc = torch.zeros(1, Hkv, S + W, d, dtype=bf, device=dev)
+        self.vc = torch.zeros(1, Hkv, S + W, d, dtype=bf, device=dev)
         self.int_state = torch.zeros(4, dtype=torch.int32, device=dev)
         st = self.int_state
-        self.desc = R.kv_cache(R.RING, R.BF16, Hkv, d, self.kc, self.kc, batch=1, capacity=S + W, sinks=S, window=W,
+        self.desc = R.kv_cache(R.RING, R.BF16, Hkv, d, self.kc, self.vc, batch=1, capacity=S + W, sinks=S, window=W,
                                ring_head=st[0:1], ring_count=st[1:2], seq_len=st[2:3], err_word=st[3:4])
+        self.cfg = R.rope_cfg(d, d, rope_theta=5e5)
+        self.rope_table = torch.empty(T, d, dtype=torch.float32, device=dev)
+        R.build_table(self.cfg, T, self.rope_table)
+        self.pos = torch.arange(T, dtype=torch.int32, device=dev)
+        self.seq_ids = torch.zeros(T, dtype=torch.int32, device=dev)
 
-    def run(self):
-        self.R.prefill_attn(self.q, self.k, self.v, self.T, 0, self.Hq, self.desc, 0, 0.0, self.out)
+    def run(self, stream=None):
+        self.R.prefill_attn(self.q, self.k, self.v, self.T, 0, self.Hq, self.desc, 0, 0.0, self.out, stream=stream)
+
+    def append(self):
+        """Rope + append of the whole chunk into an empty ring (state reset first)."""
+        self.int_state[0:3].zero_()
+        self.R.apply_append(self.cfg, self.rope_table, self.T, self.q, self.Hq, self.k, self.v, self.R.BF16, self.T,
+                            self.pos, self.seq_ids, self.desc)
+
+    def append_bytes(self) -> int:
+        """q and k read and written in place, v read, and the C surviving rows of k and v written."""
+        qb = self.T * self.Hq * self.d * 2
+        kb = self.T * self.Hkv * self.d * 2
+        written = min(self.T, self.S + self.W) * self.Hkv * self.d * 2
+        return 2 * qb + 2 * kb + kb + 2 * written
 
     def flops(self) -> int:
         vis = sum(visible_count(p, self.S, self.W) for p in range(self.T))
