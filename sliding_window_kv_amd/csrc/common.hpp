@@ -145,4 +145,31 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
 
+// Direct global -> LDS loads: the 64 lanes' N-byte reads land at LDS [m0 + N * lane]
+// (m0 = the wave-uniform LDS base).  Issued as inline assembly so the compiler adds
+// no waits of its own on them: callers wait with wait_vmcnt before reading the LDS
+// they fill, and never fill a buffer that is still being read.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// lds_base must be the same for every lane of the wave (it is taken from the first lane).
+__device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0)
+                   : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *gsrc, const void *lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(m0)
+                   : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+  __asm__ volatile("" ::: "memory");
+}
+
 }  // namespace ropekv

@@ -30,20 +30,6 @@ using namespace decode_detail;
 // ring of NST tile stages and runs NST - 1 tiles ahead, waiting on the vector
 // memory counter for the oldest.  Key rows are stored with their 16-byte
 // chunks XOR-swizzled by row so the MFMA operand reads hit distinct banks.
-// Direct global -> LDS loads: 64 lanes x N bytes land at LDS [m0 + N * lane].  Issued as
-// inline assembly so the only waits on them are the explicit vmcnt waits of the
-// pipeline (the stage being read is never the one being filled).
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-__device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_offset(lds_base))
-                   : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void *gsrc, const void *lds_base) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(lds_offset(lds_base))
-                   : "memory", "m0");
-}
 
 __device__ __forceinline__ float code_f(uint32_t w, int byte) { return (float)(int8_t)(w >> (8 * byte)); }
 
@@ -57,13 +43,6 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
-  __asm__ volatile("" ::: "memory");
-}
 
 template <int D>
 struct I8Stage {

@@ -341,16 +341,312 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// ---- bf16: tiles staged by direct global -> LDS loads into swizzled rows ----
+//
+// Same workgroup and tile walk as above.  K and V tiles are copied into LDS
+// with direct loads (no staging registers, the next tile in flight while the
+// current one is computed) in rows of D / 8 16-byte chunks, chunk c of row r
+// stored at c ^ kswz(r) (K) or c ^ vswz(r) (V).  The swizzles make the MFMA
+// operand reads conflict-free: the 16 lanes reading a K chunk of 16 different
+// rows hit 16 different 16-byte bank groups, and the 32 lanes of a transposing
+// V read (8 rows x 4 column groups) hit 32 different 8-byte bank slots.
+//
+// The running maximum is raised only when a tile's maximum exceeds it by more
+// than kLazy (log2 units): in between, p = exp2(s - m) stays below 2^kLazy,
+// which fp32 sums and bf16 P hold exactly as well, and the output accumulators
+// are rescaled only on those (rare) raises.
+constexpr float kLazy = 8.0f;
+
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  constexpr int CPR = D / 8;
+  return (row * CPR / 16) % CPR;
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  constexpr int CPR = D / 8;
+  return ((row * CPR / 16) & (CPR / 2 - 1)) << 1;
+}
+
+template <int D, int NREP>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int BM = 128 / NREP;      // chunk positions per workgroup
+  constexpr int CPR = D / 8;          // 16-byte chunks per K / V row
+  constexpr int QC = D / 32;          // chunks of a lane's quarter row = MFMA k-steps
+  constexpr int TB = kBN * D * 2;     // bytes of one staged tile
+  constexpr int NI = TB / 4096;       // direct loads per thread per tile and tensor
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][TB];
+
+  const ropekv_kv_cache &c = a.c;
+  const int g = blockIdx.y;
+  const int t0 = blockIdx.x * BM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int Hq = a.n_q_heads;
+  const int S = c.sinks, W = c.window;
+  const int qp_lo = a.pos0 + t0;
+  const int qp_hi = a.pos0 + min(t0 + BM, a.T) - 1;
+
+  // this lane's query row in each of its two row tiles; chunk grp * QC + t of the row
+  int tq[2], head[2];
+  u32x4 qv[2][QC];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int R = 32 * wave + 16 * rt + col;
+    tq[rt] = t0 + R % BM;
+    head[rt] = g * NREP + R / BM;
+    const char *qrow = (const char *)a.q + ((long)tq[rt] * Hq + head[rt]) * D * 2;
+#pragma unroll
+    for (int t = 0; t < QC; ++t)
+      qv[rt][t] = tq[rt] < a.T ? *(const u32x4 *)(qrow + (grp * QC + t) * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // key tiles: sink tiles [0, nst), then recent tiles [first, last]
+  const int last = qp_hi / kBN;
+  int nst = 0, first = 0;
+  if (W > 0) {
+    const int sink_hi = min(S, qp_hi + 1);
+    nst = (sink_hi + kBN - 1) / kBN;
+    const int lo = max(0, qp_lo - W + 1);
+    first = max(lo / kBN, nst);
+  }
+  const int ntiles = nst + max(0, last - first + 1);
+
+  // Direct loads of one tile: instruction n of wave w fills chunk slots 64 (4 n + w) + lane,
+  // i.e. row r = slot / CPR, stored chunk slot % CPR (= logical chunk ^ swizzle of r).
+  int row_n[NI], kch_n[NI], vch_n[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int p = 64 * (4 * n + wave) + lane;
+    row_n[n] = p / CPR;
+    kch_n[n] = ((p % CPR) ^ kswz<D>(row_n[n])) * 16;
+    vch_n[n] = ((p % CPR) ^ vswz<D>(row_n[n])) * 16;
+  }
+  const long chunk_row_bytes = (long)c.num_kv_heads * D * 2;  // one position of the chunk's k / v
+  bool lost = false;
+  auto issue = [&](int kt, int buf) {
+    const int kb = kt < nst ? kt : first + (kt - nst);
+    const int j0 = kb * kBN;
+    if (j0 >= a.pos0 && j0 + kBN <= a.pos0 + a.T) {
+      // every key of the tile is in the chunk: rows are (j - pos0, g) of k and v
+      const long tb = (long)(j0 - a.pos0) * chunk_row_bytes + (long)g * D * 2;
+#pragma unroll
+      for (int n = 0; n < NI; ++n)
+        dma16((const char *)a.k + tb + row_n[n] * chunk_row_bytes + kch_n[n], &k_lds[buf][(4 * n + wave) * 1024]);
+#pragma unroll
+      for (int n = 0; n < NI; ++n)
+        dma16((const char *)a.v + tb + row_n[n] * chunk_row_bytes + vch_n[n], &v_lds[buf][(4 * n + wave) * 1024]);
+      return;
+    }
+    const char *ksrc[NI];
+    const char *vsrc[NI];
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int j = j0 + row_n[n];
+      bool chunk;
+      long off = key_row(a, j, g, D, &chunk);
+      const bool needed = j <= qp_hi && (W == 0 || j < S || j > qp_lo - W);
+      if (off < 0 && needed && j < a.pos0) lost = true;
+      if (off < 0) {  // beyond the chunk or not in the cache: an in-bounds row, never visible
+        off = (long)g * D;
+        chunk = true;
+      }
+      ksrc[n] = (const char *)(chunk ? a.k : c.k) + off * 2 + kch_n[n];
+      vsrc[n] = (const char *)(chunk ? a.v : c.v) + off * 2 + vch_n[n];
+    }
+#pragma unroll
+    for (int n = 0; n < NI; ++n) dma16(ksrc[n], &k_lds[buf][(4 * n + wave) * 1024]);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) dma16(vsrc[n], &v_lds[buf][(4 * n + wave) * 1024]);
+  };
+
+  float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
+  f32x4 o[2][D / 16];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) issue(0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  // unrolled by two so that the buffer (kt & 1) is a constant in each copy and the
+  // buffer offsets become instruction immediates
+#pragma unroll 2
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) issue(kt + 1, buf ^ 1);  // in flight while this tile is computed
+    const uint8_t *kl = k_lds[buf];
+    const uint8_t *vl = v_lds[buf];
+    const int kb = kt < nst ? kt : first + (kt - nst);
+    const int j0 = kb * kBN;
+
+    // ---- scores S^T = K Q^T (raw dot products); two key sub-tiles at a time, four
+    // independent accumulation chains
+    f32x4 sc[2][4];
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      u32x4 kf[2][QC];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int row = 16 * (2 * sp + s2) + col;
+#pragma unroll
+        for (int t = 0; t < QC; ++t)
+          kf[s2][t] = *(const u32x4 *)(kl + (row * CPR + ((grp * QC + t) ^ kswz<D>(row))) * 16);
+      }
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[s2][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < QC; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            acc[s2][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[s2][t]),
+                                                                  __builtin_bit_cast(bf16x8, qv[rt][t]), acc[s2][rt],
+                                                                  0, 0, 0);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) sc[rt][2 * sp + s2] = acc[s2][rt];
+    }
+    // does every query of this workgroup see every key of the tile?
+    const int jmax = j0 + kBN - 1;
+    const bool full = jmax <= qp_lo && (W == 0 || jmax < S || qp_hi - j0 < W);
+    bool raised = false;
+    float corr[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      if (!full) {
+        const int qpos = a.pos0 + tq[rt];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int jp = j0 + 16 * st + 4 * grp + j;
+            const bool vis = jp <= qpos && (W == 0 || jp < S || qpos - jp < W);
+            sc[rt][st][j] = vis ? sc[rt][st][j] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[rt][st][j]);
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_tile = mx * a.sl2;  // sl2 > 0: the max commutes with the scale; -inf if all masked
+      corr[rt] = 1.f;
+      if (m_tile > m_run[rt] + kLazy) {
+        corr[rt] = __builtin_amdgcn_exp2f(m_run[rt] - m_tile);
+        m_run[rt] = m_tile;
+        raised = true;
+      }
+      float ps = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[rt][st][j], a.sl2, -m_run[rt]));
+          sc[rt][st][j] = p;
+          ps += p;
+        }
+      l_run[rt] = l_run[rt] * corr[rt] + ps;
+    }
+    if (__any(raised)) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] *= corr[rt];
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4 pb[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const f32x4 p0 = sc[rt][2 * u], p1 = sc[rt][2 * u + 1];
+        pb[rt] = u32x4{pack_bf16(p0[0], p0[1]), pack_bf16(p0[2], p0[3]), pack_bf16(p1[0], p1[1]),
+                       pack_bf16(p1[2], p1[3])};
+      }
+      // lane (grp, col) addresses V[32u + 4grp + col/4 (+16)][16 mt + 4 (col % 4)]
+      const int vrow = 32 * u + 4 * grp + (col >> 2);
+      const int vx = vswz<D>(vrow);  // the same for vrow + 16
+      const int half = (col & 1) * 8;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        const int ch = (2 * mt + ((col & 3) >> 1)) ^ vx;
+        typedef __attribute__((address_space(3))) short4v lds_s4;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vl + (vrow * CPR + ch) * 16 + half));
+        const short4v hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vl + ((vrow + 16) * CPR + ch) * 16 + half));
+        const short8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          o[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                              __builtin_bit_cast(bf16x8, pb[rt]), o[rt][mt], 0, 0, 0);
+      }
+    }
+    wait_vmcnt<0>();  // this wave's loads of the next tile have landed
+    __syncthreads();  // ... and everyone's; this tile's buffers may be refilled
+  }
+  if (lost) dev_error(c.err_word, ROPEKV_DEV_PREFIX_LOST);
+
+  // ---- normalise and store: lane holds O^T[16 mt + 4 grp + j][its row]
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float l = l_run[rt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    float inv = l > 0.f ? 1.f / l : 0.f;
+    if (a.sinks) {
+      const float sink2 = a.sinks[head[rt]] * kLog2e;
+      const float m_f = fmaxf(m_run[rt], sink2);
+      const float f = __builtin_amdgcn_exp2f(m_run[rt] - m_f);
+      const float lt = l * f + __builtin_amdgcn_exp2f(sink2 - m_f);
+      inv = lt > 0.f ? f / lt : 0.f;
+    }
+    if (tq[rt] < a.T) {
+      const long ob = ((long)tq[rt] * Hq + head[rt]) * D;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        const int d0 = 16 * mt + 4 * grp;
+        uint2 w;
+        w.x = pack_bf16(o[rt][mt][0] * inv, o[rt][mt][1] * inv);
+        w.y = pack_bf16(o[rt][mt][2] * inv, o[rt][mt][3] * inv);
+        *(uint2 *)((uint16_t *)a.out + ob + d0) = w;
+      }
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_prefill_d(const PrefillArgs &a, int n_rep, hipStream_t s) {
   const int bm = 128 / n_rep;
   dim3 grid((a.T + bm - 1) / bm, a.c.num_kv_heads);
-  switch (n_rep) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<T, D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<T, D, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<T, D, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<T, D, 8>), grid, dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {
+    switch (n_rep) {
+      case 1: hipLaunchKernelGGL((prefill_bf16_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((prefill_bf16_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+      case 8: hipLaunchKernelGGL((prefill_bf16_kernel<D, 8>), grid, dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (n_rep) {
+      case 1: hipLaunchKernelGGL((prefill_kernel<T, D, 1>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((prefill_kernel<T, D, 2>), grid, dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((prefill_kernel<T, D, 4>), grid, dim3(256), 0, s, a); break;
+      case 8: hipLaunchKernelGGL((prefill_kernel<T, D, 8>), grid, dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
