@@ -484,6 +484,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     const int kb = kt < nst ? kt : first + (kt - nst);
     const int j0 = kb * kBN;
 
+    __builtin_amdgcn_s_setprio(1);
     // ---- scores S^T = K Q^T (raw dot products); two key sub-tiles at a time, four
     // independent accumulation chains
     f32x4 sc[2][4];
@@ -516,6 +517,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) sc[rt][2 * sp + s2] = acc[s2][rt];
     }
+    __builtin_amdgcn_s_setprio(0);
     // does every query of this workgroup see every key of the tile?
     const int jmax = j0 + kBN - 1;
     const bool full = jmax <= qp_lo && (W == 0 || jmax < S || qp_hi - j0 < W);
@@ -566,6 +568,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] *= corr[rt];
     }
 
+    __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority: the SIMD keeps issuing them
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -594,6 +597,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
                                                               __builtin_bit_cast(bf16x8, pb[rt]), o[rt][mt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();  // this wave's loads of the next tile have landed
     __syncthreads();  // ... and everyone's; this tile's buffers may be refilled
   }
