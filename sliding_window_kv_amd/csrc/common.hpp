@@ -19,13 +19,8 @@ struct f16_t { uint16_t x; };
 
 __device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even; NaN stays NaN (hardware conversion).
+__device__ __forceinline__ uint16_t f_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float f16_to_f(uint16_t h) {
   _Float16 v = __builtin_bit_cast(_Float16, h);
@@ -35,6 +30,18 @@ __device__ __forceinline__ float f16_to_f(uint16_t h) {
 __device__ __forceinline__ uint16_t f_to_f16(float f) {
   _Float16 v = (_Float16)f;
   return __builtin_bit_cast(uint16_t, v);
+}
+
+// Two fp32 -> one word of two 16-bit values (lo in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16_rne(float lo, float hi) {
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2v_t));
+}
+__device__ __forceinline__ uint32_t pack2_f16_rne(float lo, float hi) {
+  typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2v_t));
 }
 
 // element load/store by runtime dtype code (used off the hot loops)

@@ -73,6 +73,19 @@ __device__ __forceinline__ void vput(uint32_t *w, int e, float v) {
     w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0xffffu) | (h << 16)) : ((w[e >> 1] & 0xffff0000u) | h);
   }
 }
+// elements e and e + 1 (e even) in one go: one packed conversion for 16-bit types
+template <typename T>
+__device__ __forceinline__ void vput2(uint32_t *w, int e, float v0, float v1) {
+  if constexpr (sizeof(T) == 4) {
+    w[e] = __float_as_uint(v0);
+    w[e + 1] = __float_as_uint(v1);
+  } else if constexpr (__is_same(T, bf16_t)) {
+    w[e >> 1] = pack2_bf16_rne(v0, v1);
+  } else {
+    w[e >> 1] = pack2_f16_rne(v0, v1);
+  }
+}
+
 template <int NB>
 __device__ __forceinline__ void vld(uint32_t *w, const char *p) {
   if constexpr (NB % 16 == 0) {
@@ -149,7 +162,26 @@ __global__ __launch_bounds__(256) void rerotate_float_kernel(RerotArgs a) {
       if (!live[u]) continue;
       const float *cs = &s_cs[jj[u]];
       const float *sn = &s_sn[jj[u]];
-      if (neox) {
+      if constexpr (PP % 2 == 0) {
+        if (neox) {
+#pragma unroll
+          for (int e = 0; e < PP; e += 2) {
+            const float x1a = vget<T>(w1[u], e), x2a = vget<T>(w2[u], e);
+            const float x1b = vget<T>(w1[u], e + 1), x2b = vget<T>(w2[u], e + 1);
+            vput2<T>(w1[u], e, (x1a * cs[e] - x2a * sn[e]) * gain, (x1b * cs[e + 1] - x2b * sn[e + 1]) * gain);
+            vput2<T>(w2[u], e, (x2a * cs[e] + x1a * sn[e]) * gain, (x2b * cs[e + 1] + x1b * sn[e + 1]) * gain);
+          }
+        } else {
+          // 2 PP interleaved elements: pair e is (2e, 2e+1), both in one NB-byte half
+#pragma unroll
+          for (int e = 0; e < PP; ++e) {
+            uint32_t *b = 2 * e < PP ? w1[u] : w2[u];
+            const int i1 = 2 * e < PP ? 2 * e : 2 * e - PP;
+            const float x1 = vget<T>(b, i1), x2 = vget<T>(b, i1 + 1);
+            vput2<T>(b, i1, (x1 * cs[e] - x2 * sn[e]) * gain, (x2 * cs[e] + x1 * sn[e]) * gain);
+          }
+        }
+      } else if (neox) {
 #pragma unroll
         for (int e = 0; e < PP; ++e) {
           const float x1 = vget<T>(w1[u], e), x2 = vget<T>(w2[u], e);
@@ -157,16 +189,10 @@ __global__ __launch_bounds__(256) void rerotate_float_kernel(RerotArgs a) {
           vput<T>(w2[u], e, (x2 * cs[e] + x1 * sn[e]) * gain);
         }
       } else {
-        // 2 PP interleaved elements: pair e is (2e, 2e+1) across the two NB-byte halves
-#pragma unroll
-        for (int e = 0; e < PP; ++e) {
-          uint32_t *b1 = 2 * e < PP ? w1[u] : w2[u];
-          uint32_t *b2 = 2 * e + 1 < PP ? w1[u] : w2[u];
-          const int i1 = 2 * e < PP ? 2 * e : 2 * e - PP, i2 = 2 * e + 1 < PP ? 2 * e + 1 : 2 * e + 1 - PP;
-          const float x1 = vget<T>(b1, i1), x2 = vget<T>(b2, i2);
-          vput<T>(b1, i1, (x1 * cs[e] - x2 * sn[e]) * gain);
-          vput<T>(b2, i2, (x2 * cs[e] + x1 * sn[e]) * gain);
-        }
+        // PP = 1: the pair is element 0 of each half
+        const float x1 = vget<T>(w1[u], 0), x2 = vget<T>(w2[u], 0);
+        vput<T>(w1[u], 0, (x1 * cs[0] - x2 * sn[0]) * gain);
+        vput<T>(w2[u], 0, (x2 * cs[0] + x1 * sn[0]) * gain);
       }
       vst<NB>(p1[u], w1[u]);
       vst<NB>(p2[u], w2[u]);
@@ -604,21 +630,29 @@ __global__ __launch_bounds__(256) void shift_kernel(ShiftArgs a) {
     vld<NB>(w2, p2);
     const float *cs = &s_cs[j0];
     const float *sn = &s_sn[j0];
-#pragma unroll
-    for (int e = 0; e < PP; ++e) {
-      uint32_t *b1, *b2;
-      int i1, i2;
+    if constexpr (PP % 2 == 0) {
       if (neox) {
-        b1 = w1; b2 = w2; i1 = e; i2 = e;
+#pragma unroll
+        for (int e = 0; e < PP; e += 2) {
+          const float x1a = vget<T>(w1, e), x2a = vget<T>(w2, e);
+          const float x1b = vget<T>(w1, e + 1), x2b = vget<T>(w2, e + 1);
+          vput2<T>(w1, e, x1a * cs[e] - x2a * sn[e], x1b * cs[e + 1] - x2b * sn[e + 1]);
+          vput2<T>(w2, e, x2a * cs[e] + x1a * sn[e], x2b * cs[e + 1] + x1b * sn[e + 1]);
+        }
       } else {
-        b1 = 2 * e < PP ? w1 : w2;
-        b2 = 2 * e + 1 < PP ? w1 : w2;
-        i1 = 2 * e < PP ? 2 * e : 2 * e - PP;
-        i2 = 2 * e + 1 < PP ? 2 * e + 1 : 2 * e + 1 - PP;
+#pragma unroll
+        for (int e = 0; e < PP; ++e) {
+          uint32_t *b = 2 * e < PP ? w1 : w2;
+          const int i1 = 2 * e < PP ? 2 * e : 2 * e - PP;
+          const float x1 = vget<T>(b, i1), x2 = vget<T>(b, i1 + 1);
+          vput2<T>(b, i1, x1 * cs[e] - x2 * sn[e], x2 * cs[e] + x1 * sn[e]);
+        }
       }
-      const float x1 = vget<T>(b1, i1), x2 = vget<T>(b2, i2);
-      vput<T>(b1, i1, x1 * cs[e] - x2 * sn[e]);
-      vput<T>(b2, i2, x2 * cs[e] + x1 * sn[e]);
+    } else {
+      // PP = 1: the pair is element 0 of each half (NeoX) or of the two halves (GPT-J)
+      const float x1 = vget<T>(w1, 0), x2 = vget<T>(w2, 0);
+      vput<T>(w1, 0, x1 * cs[0] - x2 * sn[0]);
+      vput<T>(w2, 0, x2 * cs[0] + x1 * sn[0]);
     }
     vst<NB>(p1, w1);
     vst<NB>(p2, w2);
