@@ -214,6 +214,15 @@ int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_
   a.freed = cache->layout == ROPEKV_PAGED ? freed_blocks : nullptr;
   a.freed_cap = freed_capacity;
   a.n_freed = n_freed;
+  {
+    // the vector path moves 16-byte units: same dtype in and out, units that tile the halves
+    // of the rotary slice and the tail, 16-byte aligned activations
+    const int esz = act_dtype == ROPEKV_F32 ? 4 : 2;
+    const int pp = 16 / esz;
+    const int r = cfg->rotary_dim, d = cfg->head_dim;
+    a.vec = cache->kv_dtype == act_dtype && act_dtype != ROPEKV_I8 && (r / 2) % pp == 0 && (d - r) % pp == 0 &&
+            aligned16(q) && aligned16(k) && aligned16(v) && d % pp == 0;
+  }
   return hip_status(launch_apply_append(a, (hipStream_t)stream), "apply_append launch");
 }
 

@@ -28,8 +28,11 @@ __device__ inline int token_check(const AppendArgs &a, int t, int p, int seq, in
   return 0;
 }
 
-// Index of the last token of t's run (binary search; runs are consecutive).
+// Index of the last token of t's run (runs are consecutive): the call's last token when
+// the run reaches it (one chunk of one sequence), else a binary search.
 __device__ inline int run_last(const AppendArgs &a, int t, int p, int seq) {
+  const int tl = a.n_tokens - 1;
+  if (a.seq[tl] == seq && a.pos[tl] == p + (tl - t)) return tl;
   int lo = t, hi = a.n_tokens;
   while (hi - lo > 1) {
     const int mid = lo + ((hi - lo) >> 1);
@@ -44,6 +47,106 @@ __device__ inline int run_last(const AppendArgs &a, int t, int p, int seq) {
 __device__ __forceinline__ int mod_pos(long x, int m) {
   long r = x % m;
   return (int)(r < 0 ? r + m : r);
+}
+
+// 16-byte unit of T values <-> fp32
+template <typename T>
+__device__ __forceinline__ float unit_get(const uint4 &u, int e) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if constexpr (sizeof(T) == 4) {
+    return __uint_as_float(w[e]);
+  } else {
+    const uint16_t h = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    return __is_same(T, bf16_t) ? bf16_to_f(h) : f16_to_f(h);
+  }
+}
+template <typename T>
+__device__ __forceinline__ uint4 unit_pack(const float *y) {
+  uint32_t w[4];
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(y[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = __is_same(T, bf16_t) ? pack2_bf16_rne(y[2 * i], y[2 * i + 1]) : pack2_f16_rne(y[2 * i], y[2 * i + 1]);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The vector path of one token: every thread of the workgroup takes 16-byte units
+// (NeoX: a unit of each half; GPT-J: a unit of interleaved pairs; k tail and v units
+// are copies), rotating q and k in place and writing k and v to the cache row.
+template <typename T>
+__device__ __forceinline__ void append_units(const AppendArgs &a, int t, const float *trow, bool write, long base,
+                                             long hstride) {
+  constexpr int PP = 16 / (int)sizeof(T);
+  const ropekv_kv_cache &c = a.c;
+  const int d = a.head_dim, r = a.rotary_dim, half = r / 2;
+  const int Hkv = c.num_kv_heads, nq = a.n_q_heads;
+  const int iq = a.neox ? half / PP : r / PP;  // rotation items per row
+  const int tu = (d - r) / PP, du = d / PP;
+  const int nqi = nq * iq, nki = Hkv * (iq + tu);
+  const int nvi = (write && a.v != nullptr && c.v != nullptr) ? Hkv * du : 0;
+  const int total = nqi + nki + nvi;
+  for (int it = threadIdx.x; it < total; it += blockDim.x) {
+    if (it < nqi + nki) {
+      const bool is_k = it >= nqi;
+      const int kk = is_k ? it - nqi : it;
+      const int per = is_k ? iq + tu : iq;
+      const int h = kk / per, j = kk - h * per;
+      char *x = (char *)(is_k ? a.k : a.q) + ((long)t * (is_k ? Hkv : nq) + h) * d * (long)sizeof(T);
+      char *cd = (write && is_k) ? (char *)c.k + (base + (long)h * hstride) * (long)sizeof(T) : nullptr;
+      if (j < iq) {
+        if (a.neox) {
+          const int e0 = j * PP;
+          uint4 *p1 = (uint4 *)(x + e0 * sizeof(T));
+          uint4 *p2 = (uint4 *)(x + (half + e0) * sizeof(T));
+          const uint4 u1 = *p1, u2 = *p2;
+          float y1[PP], y2[PP];
+#pragma unroll
+          for (int e = 0; e < PP; ++e) {
+            const float x1 = unit_get<T>(u1, e), x2 = unit_get<T>(u2, e);
+            const float cs = trow[e0 + e], sn = trow[half + e0 + e];
+            y1[e] = x1 * cs - x2 * sn;
+            y2[e] = x2 * cs + x1 * sn;
+          }
+          const uint4 o1 = unit_pack<T>(y1), o2 = unit_pack<T>(y2);
+          *p1 = o1;
+          *p2 = o2;
+          if (cd) {
+            *(uint4 *)(cd + e0 * sizeof(T)) = o1;
+            *(uint4 *)(cd + (half + e0) * sizeof(T)) = o2;
+          }
+        } else {
+          const int e0 = j * PP;  // elements e0 .. e0 + PP - 1 = pairs e0 / 2 ..
+          uint4 *p = (uint4 *)(x + e0 * sizeof(T));
+          const uint4 u = *p;
+          float y[PP];
+#pragma unroll
+          for (int e = 0; e < PP / 2; ++e) {
+            const float x1 = unit_get<T>(u, 2 * e), x2 = unit_get<T>(u, 2 * e + 1);
+            const int pi = e0 / 2 + e;
+            const float cs = trow[pi], sn = trow[half + pi];
+            y[2 * e] = x1 * cs - x2 * sn;
+            y[2 * e + 1] = x2 * cs + x1 * sn;
+          }
+          const uint4 o = unit_pack<T>(y);
+          *p = o;
+          if (cd) *(uint4 *)(cd + e0 * sizeof(T)) = o;
+        }
+      } else if (cd) {  // tail unit of a k row: unchanged, copied to the cache
+        const int e0 = r + (j - iq) * PP;
+        *(uint4 *)(cd + e0 * sizeof(T)) = *(const uint4 *)(x + e0 * sizeof(T));
+      }
+    } else {
+      const int kk = it - nqi - nki;
+      const int h = kk / du, j = kk - h * du;
+      const char *vr = (const char *)a.v + ((long)t * Hkv + h) * d * (long)sizeof(T);
+      char *cd = (char *)c.v + (base + (long)h * hstride) * (long)sizeof(T);
+      *(uint4 *)(cd + j * 16) = *(const uint4 *)(vr + j * 16);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
@@ -132,6 +235,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int nq = a.n_q_heads;
   const int act = a.act;
   const int kvdt = c.kv_dtype;
+  if (a.vec) {
+    if (act == ROPEKV_BF16) append_units<bf16_t>(a, t, trow, write, base, hstride);
+    else if (act == ROPEKV_F16) append_units<f16_t>(a, t, trow, write, base, hstride);
+    else append_units<float>(a, t, trow, write, base, hstride);
+    return;
+  }
   const int n_rows = nq + 2 * Hkv;
   for (int row = wave; row < n_rows; row += 4) {
     if (row < nq + Hkv) {

@@ -37,6 +37,7 @@ struct AppendArgs {
   int32_t *freed;
   int freed_cap;
   int32_t *n_freed;
+  int vec;  // 1: the 16-byte vector path applies (same 16-bit or fp32 dtype in and out, aligned rows)
 };
 hipError_t launch_apply_append(const AppendArgs &a, hipStream_t s);
 
