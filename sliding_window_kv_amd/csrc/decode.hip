@@ -359,10 +359,12 @@ DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c) {
     max_tiles = (c.capacity + kTile - 1) / kTile;
   }
   if (max_tiles < 1) max_tiles = 1;
-  // tiles per split: aim for ~8192 workgroups over the batch, 8..128 tiles each
+  // tiles per split: aim for ~4096 workgroups over the batch, 8..128 tiles each, then
+  // spread the tiles evenly over the splits that takes (no nearly empty last split)
   const long work = (long)max_tiles * batch * c.num_kv_heads;
   int tps = 8;
-  while (tps < 128 && (long)tps * 8192 < work) tps *= 2;
+  while (tps < 128 && (long)tps * 4096 < work) tps *= 2;
+  tps = (max_tiles + (max_tiles + tps - 1) / tps - 1) / ((max_tiles + tps - 1) / tps);
   if (const char *e = getenv("ROPEKV_DECODE_TPS")) {
     const int v = atoi(e);
     if (v >= 1 && v <= kMaxTps) tps = v;
