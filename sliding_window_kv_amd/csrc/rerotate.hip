@@ -238,6 +238,27 @@ __device__ __forceinline__ void st_n(int8_t *p, const uint32_t *w) {
   }
 }
 // code byte e of a word array -> float (the byte is a signed int8)
+// rne(v * inv) as an int8 code in the low byte: the fp32 product, then adding 1.5 * 2^23
+// rounds it to an integer (nearest even) held in the low mantissa bits.  Callers keep
+// |v * inv| <= 127.5 (inv = 127 / row max, or a kept scale that passed the overflow
+// test), so the code needs no clamp.
+__device__ __forceinline__ uint32_t code_bits(float v, float inv) {
+  return __float_as_uint(__fmul_rn(v, inv) + 12582912.0f);
+}
+// the low bytes of a, b, c, d -> one word (a in the low byte)
+__device__ __forceinline__ uint32_t pack4_codes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+// n codes (n a multiple of 2, up to 16) -> n / 4 words (the last one half filled when n % 4 == 2)
+template <int N>
+__device__ __forceinline__ void pack_codes(uint32_t *w, const uint32_t *cb) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) w[i] = pack4_codes(cb[4 * i], cb[4 * i + 1], cb[4 * i + 2], cb[4 * i + 3]);
+  if constexpr (N % 4 == 2) w[N / 4] = __builtin_amdgcn_perm(cb[N - 1], cb[N - 2], 0x0c0c0400u);
+}
+
 __device__ __forceinline__ float code_at(const uint32_t *w, int e) {
   return (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
 }
@@ -323,25 +344,27 @@ __global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
           inv = amax > 0.f ? 127.0f / amax : 0.f;
         }
         uint32_t o1[NR], o2[NR], ot[NT];
+        if (neox) {
+          uint32_t c1[H], c2[H];
 #pragma unroll
-        for (int i = 0; i < NR; ++i) o1[i] = o2[i] = 0u;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) ot[i] = 0u;
-        auto code = [&](float v) -> uint32_t {
-          return (uint32_t)(uint8_t)(int8_t)fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
-        };
-#pragma unroll
-        for (int e = 0; e < H; ++e) {
-          if (neox) {
-            o1[e >> 2] |= code(y[2 * e]) << (8 * (e & 3));
-            o2[e >> 2] |= code(y[2 * e + 1]) << (8 * (e & 3));
-          } else {
-            o1[(2 * e) >> 2] |= code(y[2 * e]) << (8 * ((2 * e) & 3));
-            o1[(2 * e + 1) >> 2] |= code(y[2 * e + 1]) << (8 * ((2 * e + 1) & 3));
+          for (int e = 0; e < H; ++e) {
+            c1[e] = code_bits(y[2 * e], inv);
+            c2[e] = code_bits(y[2 * e + 1], inv);
           }
-        }
+          pack_codes<H>(o1, c1);
+          pack_codes<H>(o2, c2);
+        } else {
+          uint32_t c1[2 * H];
 #pragma unroll
-        for (int e = 0; e < TL; ++e) ot[e >> 2] |= code(y[2 * H + e]) << (8 * (e & 3));
+          for (int e = 0; e < 2 * H; ++e) c1[e] = code_bits(y[e], inv);
+          pack_codes<2 * H>(o1, c1);
+        }
+        if constexpr (TL > 0) {
+          uint32_t ct[TL];
+#pragma unroll
+          for (int e = 0; e < TL; ++e) ct[e] = code_bits(y[2 * H + e], inv);
+          pack_codes<TL>(ot, ct);
+        }
         if (l0 + u < a.n_layers) {
           const long row = (l0 + u) * layer_rows + row0;
           int8_t *rp = kc + row * a.D;
@@ -446,12 +469,10 @@ __global__ __launch_bounds__(256) void rerotate_int8_kernel(RerotArgs a) {
         for (int m = lpr >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
         inv = amax > 0.f ? 127.0f / amax : 0.f;
       }
-      uint32_t out[4] = {0u, 0u, 0u, 0u};
+      uint32_t out[4], cb[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float qv = fminf(fmaxf(rintf(y[e] * inv), -127.f), 127.f);
-        out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)qv) << (8 * (e & 3));
-      }
+      for (int e = 0; e < 16; ++e) cb[e] = code_bits(y[e], inv);
+      pack_codes<16>(out, cb);
       if (live) {
         if (!keep || rot_chunk) *(uint4 *)(kc + row * a.D + q * 16) = make_uint4(out[0], out[1], out[2], out[3]);
         if (q == 0 && !keep) a.scale[row] = amax / 127.0f;
@@ -562,12 +583,11 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard_kernel(RerotArgs a
       }
       for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
       const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-      uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      uint32_t out[8], cb[32];
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const float qv = fminf(fmaxf(rintf(y[e] * inv), -127.f), 127.f);
-        out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)qv) << (8 * (e & 3));
-      }
+      for (int e = 0; e < 32; ++e) cb[e] = code_bits(y[e], inv);
+      pack_codes<16>(out, cb);
+      pack_codes<16>(out + 4, cb + 16);
       if (live) {
         int8_t *dst = kc + row * a.D + 32 * q;
         *(uint4 *)dst = make_uint4(out[0], out[1], out[2], out[3]);
