@@ -59,6 +59,7 @@ def source_hash(*names):
 
 
 DECODE_SOURCES = ("decode.hip", "decode_common.hpp", "common.hpp")
+DECODE_8BIT_SOURCES = ("decode_8bit.hip", "decode_common.hpp", "common.hpp")
 
 
 def counter_traffic(sources, profile: str):
@@ -186,20 +187,21 @@ def main():
     ms_tab = timed(torch, lambda: R.build_table(wl.cfg, wl.ctx, wl.rope_table), 10)
     rows["table_build_32768x128"] = {"ms": round(ms_tab, 4)}
 
-    # the same decode over an int8 cache (codes + per-row scales): half the K/V bytes per key
-    wq = WL.PagedDecode(R, torch, dev, kv_int8=True)
-    wq.step()
-    ms_q = timed(torch, wq.decode, max(args.steps, 20))
-    ms_qapp = timed(torch, lambda: (wq.seq_len.fill_(wq.ctx - 1), wq.append()), max(args.steps, 20))
-    assert wq.err.item() == 0, f"device error word {wq.err.item()}"
-    rows["decode_b64_ctx32768_int8kv"] = {"ms": round(ms_q, 4), "GBps": round(wq.decode_bytes() / ms_q / 1e6, 1),
-                                          "frac_hbm": round(wq.decode_bytes() / ms_q / 1e6 / HBM_PEAK_GBS, 4),
-                                          "speedup_vs_bf16": round(ms_dec / ms_q, 3),
-                                          "traffic": counter_traffic(("decode_i8.hip", "decode_common.hpp", "common.hpp"),
-                                                                     "decode_split_i8_kernel_b64_ctx32768_pmc.md")}
-    rows["rope_append_b64_int8kv"] = {"ms": round(ms_qapp, 4)}
-    del wq
-    torch.cuda.empty_cache()
+    # the same decode over 8-bit caches (int8 or E4M3 codes + per-row scales): about half the K/V bytes per key
+    for kind, name in (("i8", "int8kv"), ("fp8", "fp8kv")):
+        wq = WL.PagedDecode(R, torch, dev, kv8=kind)
+        wq.step()
+        ms_q = timed(torch, wq.decode, max(args.steps, 20))
+        ms_qapp = timed(torch, lambda: (wq.seq_len.fill_(wq.ctx - 1), wq.append()), max(args.steps, 20))
+        assert wq.err.item() == 0, f"device error word {wq.err.item()}"
+        rows[f"decode_b64_ctx32768_{name}"] = {
+            "ms": round(ms_q, 4), "GBps": round(wq.decode_bytes() / ms_q / 1e6, 1),
+            "frac_hbm": round(wq.decode_bytes() / ms_q / 1e6 / HBM_PEAK_GBS, 4),
+            "speedup_vs_bf16": round(ms_dec / ms_q, 3),
+            "traffic": counter_traffic(DECODE_8BIT_SOURCES, f"decode_split_8bit_kernel_{kind}_b64_ctx32768_pmc.md")}
+        rows[f"rope_append_b64_{name}"] = {"ms": round(ms_qapp, 4)}
+        del wq
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

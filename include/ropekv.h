@@ -52,6 +52,9 @@ typedef void *ropekv_stream_t; /* a hipStream_t */
 #define ROPEKV_BF16 1
 #define ROPEKV_F16 2
 #define ROPEKV_I8 3
+#define ROPEKV_FP8 4 /* 8-bit float E4M3 (OCP "fn": bias 7, 3 mantissa bits, max 448, no
+                        infinities, S.1111.111 NaN) codes with one fp32 scale per row, like I8
+                        ([VLLM] the KV cache stored as FP8) */
 
 /* k_int8_mode bits (int8 keys only) */
 #define ROPEKV_I8_KEEP_SCALE 1 /* rerotate keeps each row's scale (tail codes bitwise) unless a turned
@@ -119,7 +122,7 @@ typedef struct {
  * attention (PAGED only).  For RING, capacity C = sinks + window. */
 typedef struct {
   int32_t layout;       /* ROPEKV_RING / _PAGED / _CONTIG */
-  int32_t kv_dtype;     /* F32 / BF16 / F16 / I8 (K and V; CONTIG holds K, V optional) */
+  int32_t kv_dtype;     /* F32 / BF16 / F16 / I8 / FP8 (K and V; CONTIG holds K, V optional) */
   int32_t num_kv_heads; /* Hkv */
   int32_t head_dim;     /* d: 64 or 128 for attention; any even size <= 512 for append / rerotate */
   int32_t batch;        /* sequences (RING, PAGED) */
@@ -132,14 +135,14 @@ typedef struct {
   int32_t pos0;         /* CONTIG: position of row 0 */
   void *k;              /* keys (rotated), layout as above */
   void *v;              /* values (never rotated); NULL allowed for CONTIG */
-  float *k_scale;       /* I8: per-row fp32 key scale, one per K row (PAGED [num_blocks, Hkv, block_size],
+  float *k_scale;       /* I8, FP8: per-row fp32 key scale, one per K row (PAGED [num_blocks, Hkv, block_size],
                            RING [batch, Hkv, C], CONTIG [T, Hkv] per layer) */
   int32_t *ring_head;   /* RING [batch]: next ring index to write */
   int32_t *ring_count;  /* RING [batch]: valid ring entries (<= W) */
   int32_t *block_table; /* PAGED [batch, max_blocks]: physical block ids, -1 = null */
   int32_t *seq_len;     /* RING, PAGED [batch]: tokens appended so far (= next position) */
   int32_t *err_word;    /* [1]: ROPEKV_DEV_* bits, OR-ed by kernels; caller clears */
-  float *v_scale;       /* I8 RING / PAGED: per-row fp32 value scale, laid out like k_scale */
+  float *v_scale;       /* I8, FP8 RING / PAGED: per-row fp32 value scale, laid out like k_scale */
   int32_t k_int8_mode;  /* I8 keys: 0 or ROPEKV_I8_* bits; must be 0 for other dtypes */
   int32_t reserved;     /* 0 */
 } ropekv_kv_cache;
@@ -163,7 +166,7 @@ int ropekv_build_table(const ropekv_rope_cfg *cfg, int32_t max_pos, float *cos_s
  *   v   [n_tokens, Hkv, d] act_dtype; copied unrotated (NULL only for a CONTIG cache with v == NULL)
  *   positions [n_tokens] int32 absolute positions, < table_len
  *   seq_ids   [n_tokens] int32 sequence of each token (RING, PAGED; ignored for CONTIG)
- * act_dtype: F32 / BF16 / F16.  RING and PAGED need kv_dtype == act_dtype or I8.
+ * act_dtype: F32 / BF16 / F16.  RING and PAGED need kv_dtype == act_dtype, I8 or FP8.
  * Each sequence appears as one run of consecutive positions starting at its
  * seq_len; seq_len advances by the run length.
  * RING ([GOSS] ring buffer, 5.2 append): sinks p < S go to slot p; a chunk of
@@ -180,7 +183,9 @@ int ropekv_build_table(const ropekv_rope_cfg *cfg, int32_t max_pos, float *cos_s
  * CONTIG: row t = p - pos0.
  * Stored dtype: F32 / BF16 / F16 round the fp32 result to nearest; I8 stores
  *   per-row codes rne(x * (127 / max|x|)) with scale = max|x| / 127 (keys
- *   after rotation, values as given; an all-zero row has scale 0). */
+ *   after rotation, values as given; an all-zero row has scale 0).  FP8 stores
+ *   the E4M3 code nearest (ties to even) to x * (448 / max|x|), computed in
+ *   fp32 and clamped to [-448, 448], with scale = max|x| / 448. */
 int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_t table_len,
                         void *q, int32_t n_q_heads, void *k, const void *v, int32_t act_dtype,
                         int32_t n_tokens, const int32_t *positions, const int32_t *seq_ids,
@@ -203,8 +208,9 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
  *     the learned-sink excerpt: a trained per-head logit in the softmax
  *     denominator, no cache entry): out = sum_j e^{s_j} v_j / (sum_j e^{s_j}
  *     + e^{sink_h}), the logit in the units of the scaled scores
- * Layouts RING and PAGED (block_size 16); kv_dtype F32, BF16 or I8 (q and out are
- * then BF16; keys and values are dequantised with their row scales); d 64 or 128;
+ * Layouts RING and PAGED (block_size 16); kv_dtype F32, BF16, I8 or FP8 (for the
+ * 8-bit caches q and out are BF16; keys and values are dequantised with their row
+ * scales); d 64 or 128;
  * n_rep = n_q_heads / Hkv in {1, 2, 4, 8}.  ws: device, at least
  * ropekv_decode_workspace_size() bytes, caller-owned, overwritten.
  * q, out and ws must be 16-byte aligned. */
@@ -232,7 +238,8 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
  * the row at position p turns by p (w_to,i - w_from,i) and is scaled by
  * mscale_to / mscale_from; dims r..d-1 are untouched (bitwise for F16/BF16/F32).
  * I8 rows are dequantised, turned and requantised with a new per-row scale.
- * cache: CONTIG, kv_dtype F16 / BF16 / F32 / I8, n_layers layers back to back.
+ * cache: CONTIG, kv_dtype F16 / BF16 / F32 / I8, n_layers layers back to back
+ * (FP8: ROPEKV_EDTYPE).
  * Angles and their reduction in fp64, the rotation in fp32.
  * from / to must agree on head_dim, rotary_dim and neox. */
 int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to,

@@ -311,6 +311,65 @@ def dequant_int8_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return codes.astype(np.float64) * scale.astype(np.float64)[..., None]
 
 
+# 8-bit float E4M3 ([VLLM] memory levers: the KV cache itself stored as FP8).
+# The pages name no FP8 layout; the reading taken is the OCP E4M3 "fn" format
+# (the one this chip converts natively) with the same per-row absmax scale as
+# the int8 rows, 448 (the largest E4M3 value) taking the place of 127.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of each E4M3 byte: bit 7 the sign, bits 6..3 the exponent e (bias 7), bits 2..0
+    the mantissa m.  e = 0 is subnormal, m / 8 * 2^-6; otherwise (1 + m / 8) * 2^(e - 7).
+    S.1111.111 is NaN; there are no infinities, so the largest value is 1.75 * 2^8 = 448."""
+    c = np.asarray(code).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def round_e4m3(y) -> np.ndarray:
+    """The E4M3 byte nearest to each value of y, ties to the byte with an even mantissa (the
+    IEEE rule), magnitudes beyond 448 saturating to 448; the sign of a zero is kept.
+    Non-negative finite bytes 0 .. 126 have increasing values, so the nearest one is found by
+    bisection among them."""
+    y = np.asarray(y, dtype=np.float64)
+    mags = e4m3_value(np.arange(127))  # 0x00 .. 0x7e
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    mag_code = np.where(pick_hi, hi, lo)
+    return (mag_code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quant_fp8_rows(x: np.ndarray):
+    """Per-row E4M3: amax = max|x|, scale = amax / 448, code = round_e4m3(x * (448 / amax)).
+
+    As for the int8 rows, the row is rounded to float32 first and the product is taken
+    in float32 with the float32 reciprocal (the precision and form the kernels use),
+    clamped to [-448, 448].  An all-zero row gets scale 0 (its codes are zeros).
+    Returns (codes uint8 [..., d], scale float32 [...]).
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=-1).astype(np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    inv = np.where(amax > 0, (np.float32(E4M3_MAX) / safe).astype(np.float32), np.float32(0.0)).astype(np.float32)
+    y = (x32 * inv[..., None]).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return round_e4m3(y.astype(np.float64)), scale
+
+
+def dequant_fp8_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    return e4m3_value(codes) * scale.astype(np.float64)[..., None]
+
+
 # --------------------------------------------------------------------------
 # Ring-buffer state   ([GOSS] "Windowed layers — ring buffer", "5.2 append", "5.3 get")
 # --------------------------------------------------------------------------

@@ -82,7 +82,12 @@ int check_rope(const ropekv_rope_cfg *c, const char *name) {
 // The kernels move cache rows, scales, queries and outputs with 16-byte vector accesses.
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool valid_dtype(int dt) { return dt == ROPEKV_F32 || dt == ROPEKV_BF16 || dt == ROPEKV_F16 || dt == ROPEKV_I8; }
+bool valid_dtype(int dt) {
+  return dt == ROPEKV_F32 || dt == ROPEKV_BF16 || dt == ROPEKV_F16 || dt == ROPEKV_I8 || dt == ROPEKV_FP8;
+}
+
+// 8-bit caches: codes plus one fp32 scale per row
+bool coded8(int dt) { return dt == ROPEKV_I8 || dt == ROPEKV_FP8; }
 
 int check_cache(const ropekv_kv_cache *c) {
   if (!c) return fail(ROPEKV_EINVAL, "cache is NULL");
@@ -106,8 +111,8 @@ int check_cache(const ropekv_kv_cache *c) {
   }
   switch (c->layout) {
     case ROPEKV_RING:
-      if (c->kv_dtype == ROPEKV_I8 && (!c->k_scale || !c->v_scale))
-        return fail(ROPEKV_EINVAL, "int8 RING needs k_scale and v_scale");
+      if (coded8(c->kv_dtype) && (!c->k_scale || !c->v_scale))
+        return fail(ROPEKV_EINVAL, "8-bit RING needs k_scale and v_scale");
       if (c->batch < 1) return fail(ROPEKV_EINVAL, "batch must be >= 1");
       if (c->window < 1) return fail(ROPEKV_EINVAL, "RING needs window >= 1");
       if (c->capacity != c->sinks + c->window)
@@ -116,8 +121,8 @@ int check_cache(const ropekv_kv_cache *c) {
         return fail(ROPEKV_EINVAL, "RING needs v, ring_head, ring_count and seq_len");
       break;
     case ROPEKV_PAGED:
-      if (c->kv_dtype == ROPEKV_I8 && (!c->k_scale || !c->v_scale))
-        return fail(ROPEKV_EINVAL, "int8 PAGED needs k_scale and v_scale");
+      if (coded8(c->kv_dtype) && (!c->k_scale || !c->v_scale))
+        return fail(ROPEKV_EINVAL, "8-bit PAGED needs k_scale and v_scale");
       if (c->batch < 1) return fail(ROPEKV_EINVAL, "batch must be >= 1");
       if (c->block_size < 1 || c->max_blocks < 1 || c->num_blocks < 1)
         return fail(ROPEKV_EINVAL, "PAGED needs block_size, max_blocks, num_blocks >= 1");
@@ -128,9 +133,9 @@ int check_cache(const ropekv_kv_cache *c) {
       if (c->capacity < 1) return fail(ROPEKV_EINVAL, "CONTIG capacity must be >= 1");
       if (c->pos0 < 0) return fail(ROPEKV_EINVAL, "CONTIG pos0 must be >= 0");
       if ((long)c->pos0 + c->capacity - 1 > 0x7fffffffL) return fail(ROPEKV_ERANGE, "CONTIG positions overflow int32");
-      if (c->kv_dtype == ROPEKV_I8) {
-        if (!c->k_scale) return fail(ROPEKV_EINVAL, "CONTIG int8 needs k_scale");
-        if (c->v && !c->v_scale) return fail(ROPEKV_EINVAL, "CONTIG int8 values need v_scale");
+      if (coded8(c->kv_dtype)) {
+        if (!c->k_scale) return fail(ROPEKV_EINVAL, "CONTIG 8-bit keys need k_scale");
+        if (c->v && !c->v_scale) return fail(ROPEKV_EINVAL, "CONTIG 8-bit values need v_scale");
       }
       break;
     default: return fail(ROPEKV_ELAYOUT, "unknown layout %d", c->layout);
@@ -139,8 +144,8 @@ int check_cache(const ropekv_kv_cache *c) {
 }
 
 int check_attention_shape(const ropekv_kv_cache *c, int n_q_heads, bool int8_ok) {
-  if (c->kv_dtype != ROPEKV_F32 && c->kv_dtype != ROPEKV_BF16 && !(int8_ok && c->kv_dtype == ROPEKV_I8))
-    return fail(ROPEKV_EDTYPE, int8_ok ? "decode supports F32, BF16 and I8 caches"
+  if (c->kv_dtype != ROPEKV_F32 && c->kv_dtype != ROPEKV_BF16 && !(int8_ok && coded8(c->kv_dtype)))
+    return fail(ROPEKV_EDTYPE, int8_ok ? "decode supports F32, BF16, I8 and FP8 caches"
                                        : "prefill supports F32 and BF16 caches");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(ROPEKV_ERANGE, "attention supports head_dim 64 and 128");
   if (n_q_heads < 1 || n_q_heads % c->num_kv_heads)
@@ -188,8 +193,8 @@ int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_
     return fail(ROPEKV_EINVAL, "q must be given exactly when n_q_heads > 0");
   if (!k || !positions) return fail(ROPEKV_EINVAL, "k and positions are required");
   if (cache->layout != ROPEKV_CONTIG) {
-    if (cache->kv_dtype != act_dtype && cache->kv_dtype != ROPEKV_I8)
-      return fail(ROPEKV_EDTYPE, "RING / PAGED need kv_dtype == act_dtype or I8");
+    if (cache->kv_dtype != act_dtype && !coded8(cache->kv_dtype))
+      return fail(ROPEKV_EDTYPE, "RING / PAGED need kv_dtype == act_dtype, I8 or FP8");
     if (!seq_ids) return fail(ROPEKV_EINVAL, "seq_ids are required for RING / PAGED");
   }
   if (cache->v && !v) return fail(ROPEKV_EINVAL, "v is required when the cache holds values");
@@ -293,6 +298,7 @@ int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to, cons
     return fail(ROPEKV_EINVAL, "from / to differ in head_dim, rotary_dim or pairing");
   if (to->head_dim != cache->head_dim) return fail(ROPEKV_EINVAL, "cfg head_dim != cache head_dim");
   if (n_layers < 1) return fail(ROPEKV_EINVAL, "n_layers must be >= 1");
+  if (cache->kv_dtype == ROPEKV_FP8) return fail(ROPEKV_EDTYPE, "rerotate supports F32, BF16, F16 and I8 keys");
   if (cache->kv_dtype == ROPEKV_I8) {
     const int d = cache->head_dim, r = to->rotary_dim;
     const int lpr = d / 16;

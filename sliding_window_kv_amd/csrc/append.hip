@@ -44,6 +44,16 @@ __device__ inline int run_last(const AppendArgs &a, int t, int p, int seq) {
   return lo;
 }
 
+// One 8-bit code of y = x * (qmax / max|x|) (qmax 127 for int8, 448 for E4M3):
+// int8 rounds to nearest even and clamps to [-127, 127]; E4M3 clamps to
+// [-448, 448] and takes the nearest code, ties to even, by the hardware's
+// fp32 -> fp8 conversion (the OCP format on this chip).
+__device__ __forceinline__ uint8_t code8(float y, int kvdt) {
+  if (kvdt == ROPEKV_FP8)
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(y, -448.f), 448.f), 0.f, 0, false) & 0xff);
+  return (uint8_t)(int8_t)fminf(fmaxf(rintf(y), -127.f), 127.f);
+}
+
 __device__ __forceinline__ int mod_pos(long x, int m) {
   long r = x % m;
   return (int)(r < 0 ? r + m : r);
@@ -235,6 +245,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int nq = a.n_q_heads;
   const int act = a.act;
   const int kvdt = c.kv_dtype;
+  const bool q8 = kvdt == ROPEKV_I8 || kvdt == ROPEKV_FP8;  // codes + per-row scale
+  const float qmax = kvdt == ROPEKV_FP8 ? 448.f : 127.f;
   if (a.vec) {
     if (act == ROPEKV_BF16) append_units<bf16_t>(a, t, trow, write, base, hstride);
     else if (act == ROPEKV_F16) append_units<f16_t>(a, t, trow, write, base, hstride);
@@ -262,7 +274,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         store_elem(x, xoff + i1, act, o1);
         store_elem(x, xoff + i2, act, o2);
         if (to_cache) {
-          if (kvdt == ROPEKV_I8) {
+          if (q8) {
             rowbuf[wave][i1] = o1;
             rowbuf[wave][i2] = o2;
           } else {
@@ -274,12 +286,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       if (to_cache) {
         for (int e = r + lane; e < d; e += 64) {
           const float val = load_elem(x, xoff + e, act);
-          if (kvdt == ROPEKV_I8)
+          if (q8)
             rowbuf[wave][e] = val;
           else
             store_elem(c.k, coff + e, kvdt, val);
         }
-        if (kvdt == ROPEKV_I8) {
+        if (q8) {
           wave_lds_sync();
           if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {
             // Hadamard-rotated storage: the row becomes H k (orthonormal Walsh-Hadamard,
@@ -298,17 +310,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             for (int e = lane; e < d; e += 64) x[e] *= norm;
             wave_lds_sync();
           }
-          // per-row symmetric int8: scale = max|x| / 127, code = rne(x * (127 / max|x|))
+          // per-row symmetric codes: scale = max|x| / qmax, code = code8(x * (qmax / max|x|))
           float amax = 0.f;
           for (int e = lane; e < d; e += 64) amax = fmaxf(amax, fabsf(rowbuf[wave][e]));
           for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);
-          const float scale = amax / 127.0f;
-          const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-          int8_t *kc = (int8_t *)c.k;
-          for (int e = lane; e < d; e += 64) {
-            const float qv = fminf(fmaxf(rintf(rowbuf[wave][e] * inv), -127.f), 127.f);
-            kc[coff + e] = (int8_t)qv;
-          }
+          const float scale = amax / qmax;
+          const float inv = amax > 0.f ? qmax / amax : 0.f;
+          uint8_t *kc = (uint8_t *)c.k;
+          for (int e = lane; e < d; e += 64) kc[coff + e] = code8(rowbuf[wave][e] * inv, kvdt);
           if (lane == 0) c.k_scale[coff / d] = scale;
           wave_lds_sync();
         }
@@ -318,8 +327,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       if (write && a.v != nullptr && c.v != nullptr) {
         const long voff = ((long)t * Hkv + h) * d;
         const long coff = base + (long)h * hstride;
-        if (kvdt == ROPEKV_I8) {
-          // values: the same per-row int8 quantiser as the keys, scale in v_scale
+        if (q8) {
+          // values: the same per-row quantiser as the keys, scale in v_scale
           float amax = 0.f;
           for (int e = lane; e < d; e += 64) {
             const float val = load_elem(a.v, voff + e, act);
@@ -328,11 +337,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
           }
           for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);
           wave_lds_sync();
-          const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-          int8_t *vc = (int8_t *)c.v;
-          for (int e = lane; e < d; e += 64)
-            vc[coff + e] = (int8_t)fminf(fmaxf(rintf(rowbuf[wave][e] * inv), -127.f), 127.f);
-          if (lane == 0) c.v_scale[coff / d] = amax / 127.0f;
+          const float inv = amax > 0.f ? qmax / amax : 0.f;
+          uint8_t *vc = (uint8_t *)c.v;
+          for (int e = lane; e < d; e += 64) vc[coff + e] = code8(rowbuf[wave][e] * inv, kvdt);
+          if (lane == 0) c.v_scale[coff / d] = amax / qmax;
           wave_lds_sync();
         } else {
           for (int e = lane; e < d; e += 64) store_elem(c.v, coff + e, kvdt, load_elem(a.v, voff + e, act));

@@ -389,8 +389,8 @@ hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_k
   } else if (c.kv_dtype == ROPEKV_F32) {
     if (c.head_dim == 128) return launch_decode_d<float, 128>(q, batch, c, sl2, sinks, out, w, pl, s);
     if (c.head_dim == 64) return launch_decode_d<float, 64>(q, batch, c, sl2, sinks, out, w, pl, s);
-  } else if (c.kv_dtype == ROPEKV_I8) {  // int8 codes, bf16 q and out
-    return launch_decode_i8(q, batch, c, sl2, sinks, out, w, pl, s);
+  } else if (c.kv_dtype == ROPEKV_I8 || c.kv_dtype == ROPEKV_FP8) {  // 8-bit codes, bf16 q and out
+    return launch_decode_8bit(q, batch, c, sl2, sinks, out, w, pl, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,9 +1,11 @@
-// Split-K decode attention over an int8 KV cache (codes + one fp32 scale per
-// cached row), the same visible-set walk and split merge as the 16-bit path.
+// Split-K decode attention over an 8-bit KV cache (int8 or E4M3 codes + one fp32
+// scale per cached row), the same visible-set walk and split merge as the 16-bit
+// path.
 //
 // "#2961 rope: --rope-scaling dynamic" ("What it does": int8 K with or without
-// the Hadamard) stores keys as int8 rows; "Inference & 128K Long Context"
-// (4.3: decode is memory bound) is why halving the bytes per key matters.
+// the Hadamard) stores keys as int8 rows; "vLLM, from the inside out" (memory
+// levers) stores the KV cache as FP8; "Inference & 128K Long Context" (4.3:
+// decode is memory bound) is why halving the bytes per key matters.
 #include "decode_common.hpp"
 
 namespace ropekv {
@@ -12,11 +14,12 @@ namespace {
 
 using namespace decode_detail;
 
-// ---- int8 KV (codes + one fp32 scale per cached row) ----
+// ---- 8-bit KV (codes + one fp32 scale per cached row) ----
 //
-// K and V rows are int8 codes c with a per-row scale sc (x ~ c * sc, the row
-// quantizer of the append).  |c| <= 127 is exact in bf16, so both products run
-// on bf16 MFMAs with the codes converted in registers:
+// K and V rows are 8-bit codes c with a per-row scale sc (x ~ c * sc, the row
+// quantizer of the append).  Every int8 code (|c| <= 127) and every finite E4M3
+// value (3 mantissa bits, exponents -9 .. 8) is exact in bf16, so both products
+// run on bf16 MFMAs with the codes converted in registers:
 //   S^T = Kc . Q^T (16x16x32), then s = S^T * k_scale(key) in the log2 domain;
 //   O  += (P * v_scale(key)) . Vc (16x16x16, one MFMA per V column block).
 // The S^T fragment a lane holds (head `col`, keys 4 grp + j) is exactly the A
@@ -31,11 +34,26 @@ using namespace decode_detail;
 // memory counter for the oldest.  Key rows are stored with their 16-byte
 // chunks XOR-swizzled by row so the MFMA operand reads hit distinct banks.
 
-__device__ __forceinline__ float code_f(uint32_t w, int byte) { return (float)(int8_t)(w >> (8 * byte)); }
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// The four codes of a word (byte b = code b) as exact floats: int8 by sign
+// extension, E4M3 by the hardware's fp8 -> fp32 conversion (two per instruction).
+template <int KVDT>
+__device__ __forceinline__ void codes4(uint32_t w, float *f) {
+  if constexpr (KVDT == ROPEKV_FP8) {
+    const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    f[0] = lo.x;
+    f[1] = lo.y;
+    f[2] = hi.x;
+    f[3] = hi.y;
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[b] = (float)(int8_t)(w >> (8 * b));
+  }
+}
 
 // two floats -> one packed bf16 word (round to nearest even; exact for codes)
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
@@ -57,8 +75,8 @@ __device__ __forceinline__ int kswz(int row) {
   return (row * CPR / 8) % CPR;
 }
 
-template <int D, int NREP, int LAYOUT, int NST>
-__global__ __launch_bounds__(256) void decode_split_i8_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
+template <int D, int NREP, int LAYOUT, int NST, int KVDT>
+__global__ __launch_bounds__(256) void decode_split_8bit_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
                                                               float sl2, float *__restrict__ ws, int tps,
                                                               int splits) {
   constexpr int QB = D / 4;         // key-code bytes per lane per tile
@@ -234,9 +252,11 @@ __global__ __launch_bounds__(256) void decode_split_i8_kernel(const void *__rest
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int tt = 2 * i + h;  // MFMA step: local elements 8 tt .. 8 tt + 7
-        const uint32_t w0 = kp[2 * h], w1 = kp[2 * h + 1];
-        const u32x4_t av = {pack2_bf16(code_f(w0, 0), code_f(w0, 1)), pack2_bf16(code_f(w0, 2), code_f(w0, 3)),
-                            pack2_bf16(code_f(w1, 0), code_f(w1, 1)), pack2_bf16(code_f(w1, 2), code_f(w1, 3))};
+        float kf[8];
+        codes4<KVDT>(kp[2 * h], kf);
+        codes4<KVDT>(kp[2 * h + 1], kf + 4);
+        const u32x4_t av = {pack2_bf16(kf[0], kf[1]), pack2_bf16(kf[2], kf[3]), pack2_bf16(kf[4], kf[5]),
+                            pack2_bf16(kf[6], kf[7])};
         const u32x4_t bv = {qw[4 * tt], qw[4 * tt + 1], qw[4 * tt + 2], qw[4 * tt + 3]};
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
                                                        sacc, 0, 0, 0);
@@ -289,12 +309,15 @@ __global__ __launch_bounds__(256) void decode_split_i8_kernel(const void *__rest
         vw[j][0] = *(const uint32_t *)src;
       }
     }
+    float vf[4][E];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < E / 4; ++w) codes4<KVDT>(vw[j][w], vf[j] + 4 * w);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int wsel = e >> 2, byte = e & 3;
       const short4_t vb = __builtin_bit_cast(
-          short4_t, (uint2){pack2_bf16(code_f(vw[0][wsel], byte), code_f(vw[1][wsel], byte)),
-                            pack2_bf16(code_f(vw[2][wsel], byte), code_f(vw[3][wsel], byte))});
+          short4_t, (uint2){pack2_bf16(vf[0][e], vf[1][e]), pack2_bf16(vf[2][e], vf[3][e])});
       acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[e], 0, 0, 0);
     }
   };
@@ -343,19 +366,26 @@ __global__ __launch_bounds__(256) void decode_split_i8_kernel(const void *__rest
   }
 }
 
-constexpr int kI8Stages = 3;  // tile stages per wave (int8 decode)
+constexpr int k8bitStages = 3;  // tile stages per wave (8-bit decode)
 
-template <int D, int NREP>
-hipError_t launch_decode_i8_t(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
-                              void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
+template <int D, int NREP, int KVDT>
+hipError_t launch_split_8bit(const void *q, int batch, const ropekv_kv_cache &c, float sl2, float *ws,
+                             const DecodePlan &pl, hipStream_t s) {
   dim3 grid(pl.splits, c.num_kv_heads, batch);
   if (c.layout == ROPEKV_PAGED)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NREP, ROPEKV_PAGED, kI8Stages>), grid, dim3(256), 0, s, q, c, sl2, ws,
-                       pl.tiles_per_split, pl.splits);
+    hipLaunchKernelGGL((decode_split_8bit_kernel<D, NREP, ROPEKV_PAGED, k8bitStages, KVDT>), grid, dim3(256), 0, s, q,
+                       c, sl2, ws, pl.tiles_per_split, pl.splits);
   else
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NREP, ROPEKV_RING, kI8Stages>), grid, dim3(256), 0, s, q, c, sl2, ws,
-                       pl.tiles_per_split, pl.splits);
-  hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((decode_split_8bit_kernel<D, NREP, ROPEKV_RING, k8bitStages, KVDT>), grid, dim3(256), 0, s, q,
+                       c, sl2, ws, pl.tiles_per_split, pl.splits);
+  return hipGetLastError();
+}
+
+template <int D, int NREP>
+hipError_t launch_decode_8bit_t(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
+                                void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
+  hipError_t e = c.kv_dtype == ROPEKV_FP8 ? launch_split_8bit<D, NREP, ROPEKV_FP8>(q, batch, c, sl2, ws, pl, s)
+                                          : launch_split_8bit<D, NREP, ROPEKV_I8>(q, batch, c, sl2, ws, pl, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<bf16_t, D, NREP>), dim3(c.num_kv_heads * NREP, batch), dim3(128), 0, s,
                      c, ws, sinks, out, pl.tiles_per_split, pl.splits);
@@ -363,23 +393,23 @@ hipError_t launch_decode_i8_t(const void *q, int batch, const ropekv_kv_cache &c
 }
 
 template <int D>
-hipError_t launch_decode_i8_d(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sk,
-                              void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
+hipError_t launch_decode_8bit_d(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sk,
+                                void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
   switch (pl.n_rep) {
-    case 1: return launch_decode_i8_t<D, 1>(q, batch, c, sl2, sk, out, ws, pl, s);
-    case 2: return launch_decode_i8_t<D, 2>(q, batch, c, sl2, sk, out, ws, pl, s);
-    case 4: return launch_decode_i8_t<D, 4>(q, batch, c, sl2, sk, out, ws, pl, s);
-    case 8: return launch_decode_i8_t<D, 8>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 1: return launch_decode_8bit_t<D, 1>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 2: return launch_decode_8bit_t<D, 2>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 4: return launch_decode_8bit_t<D, 4>(q, batch, c, sl2, sk, out, ws, pl, s);
+    case 8: return launch_decode_8bit_t<D, 8>(q, batch, c, sl2, sk, out, ws, pl, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_i8(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
-                            void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
-  if (c.head_dim == 128) return launch_decode_i8_d<128>(q, batch, c, sl2, sinks, out, ws, pl, s);
-  if (c.head_dim == 64) return launch_decode_i8_d<64>(q, batch, c, sl2, sinks, out, ws, pl, s);
+hipError_t launch_decode_8bit(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
+                              void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
+  if (c.head_dim == 128) return launch_decode_8bit_d<128>(q, batch, c, sl2, sinks, out, ws, pl, s);
+  if (c.head_dim == 64) return launch_decode_8bit_d<64>(q, batch, c, sl2, sinks, out, ws, pl, s);
   return hipErrorInvalidValue;
 }
 

@@ -44,9 +44,9 @@ hipError_t launch_apply_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_kv_cache &c, float scale,
                          const float *sink_logits, void *out, void *ws, const DecodePlan &plan, hipStream_t s);
 
-// int8 caches (bf16 q and out); sl2 = softmax scale x log2(e)
-hipError_t launch_decode_i8(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
-                            void *out, float *ws, const DecodePlan &plan, hipStream_t s);
+// 8-bit caches, int8 or E4M3 codes (bf16 q and out); sl2 = softmax scale x log2(e)
+hipError_t launch_decode_8bit(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
+                              void *out, float *ws, const DecodePlan &plan, hipStream_t s);
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, int T, int pos0, int n_q_heads,
                           const ropekv_kv_cache &c, int seq_id, float scale, const float *sink_logits, void *out,

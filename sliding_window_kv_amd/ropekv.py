@@ -13,7 +13,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libropekv.so")
 
-F32, BF16, F16, I8 = 0, 1, 2, 3
+F32, BF16, F16, I8, FP8 = 0, 1, 2, 3, 4
 RING, PAGED, CONTIG = 0, 1, 2
 I8_KEEP_SCALE, I8_HADAMARD = 1, 2
 

@@ -62,6 +62,20 @@ def device_int8_codes_(tensor, seed: int):
     return tensor
 
 
+def device_fp8_codes_(tensor, seed: int):
+    """Fill a uint8 device tensor in place with bytes uniform over [0, 255] minus 127 and 255
+    (the two bytes an E4M3 cache never holds: they are NaN), seeded device generator."""
+    import torch
+
+    if tensor.dtype != torch.uint8:
+        raise TypeError(f"expected uint8, got {tensor.dtype}")
+    g = torch.Generator(device=tensor.device)
+    g.manual_seed(seed)
+    x = torch.randint(0, 254, tensor.shape, generator=g, device=tensor.device, dtype=torch.int16)
+    tensor.copy_(x + (x >= 127).to(torch.int16))
+    return tensor
+
+
 def device_uniform_(tensor, lo: float, hi: float, seed: int):
     """Fill a float device tensor in place with U(lo, hi) from a seeded device generator."""
     import torch

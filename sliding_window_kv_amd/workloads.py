@@ -27,28 +27,35 @@ class PagedDecode:
 
     B sequences of ctx tokens after the step's append, Hq / Hkv heads, d dims,
     bf16, 16-token blocks, block table = a seeded random permutation of the
-    pool.  A step appends each sequence's new token at position ctx - 1
+    pool.  kv8 "i8" or "fp8" holds the cache as 8-bit codes (int8 or E4M3)
+    with one fp32 scale per row instead of bf16.  A step appends each sequence's new token at position ctx - 1
     (rotating q and k, writing k and v into the pool) and runs decode.
     """
 
-    def __init__(self, R, torch, dev, B=64, Hq=32, Hkv=8, d=128, ctx=32768, theta=5e5, seed=2000, kv_int8=False):
+    def __init__(self, R, torch, dev, B=64, Hq=32, Hkv=8, d=128, ctx=32768, theta=5e5, seed=2000, kv8=None):
         self.R, self.torch, self.dev = R, torch, dev
         self.B, self.Hq, self.Hkv, self.d, self.ctx = B, Hq, Hkv, d, ctx
-        self.kv_int8 = kv_int8
+        if kv8 not in (None, "i8", "fp8"):
+            raise ValueError(f"kv8 must be None, 'i8' or 'fp8', not {kv8!r}")
+        self.kv8 = kv8
         self.max_blocks = (ctx + BLOCK - 1) // BLOCK
         self.num_blocks = B * self.max_blocks
         table = synth.block_table_permutation(B, self.max_blocks, self.num_blocks, seed)
         self.table_host = table
         bf = torch.bfloat16
         pool = (self.num_blocks, Hkv, BLOCK, d)
-        if kv_int8:
-            # int8 codes uniform in [-127, 127] with per-row scales: rows of magnitude ~ N(0, 1) data
-            self.k = synth.device_int8_codes_(torch.empty(pool, dtype=torch.int8, device=dev), seed + 1)
-            self.v = synth.device_int8_codes_(torch.empty(pool, dtype=torch.int8, device=dev), seed + 2)
+        if kv8:
+            # 8-bit codes (int8 uniform in [-127, 127]; E4M3 uniform over its finite bytes) with
+            # per-row scales that put the largest code near 2 .. 3.5: rows of magnitude ~ N(0, 1) data
+            fill = synth.device_int8_codes_ if kv8 == "i8" else synth.device_fp8_codes_
+            store = torch.int8 if kv8 == "i8" else torch.uint8
+            qmax = 127.0 if kv8 == "i8" else 448.0
+            self.k = fill(torch.empty(pool, dtype=store, device=dev), seed + 1)
+            self.v = fill(torch.empty(pool, dtype=store, device=dev), seed + 2)
             self.k_scale = synth.device_uniform_(torch.empty(pool[:3], dtype=torch.float32, device=dev),
-                                                 2.0 / 127, 3.5 / 127, seed + 6)
+                                                 2.0 / qmax, 3.5 / qmax, seed + 6)
             self.v_scale = synth.device_uniform_(torch.empty(pool[:3], dtype=torch.float32, device=dev),
-                                                 2.0 / 127, 3.5 / 127, seed + 7)
+                                                 2.0 / qmax, 3.5 / qmax, seed + 7)
         else:
             self.k = synth.device_normal_(torch.empty(pool, dtype=bf, device=dev), seed + 1)
             self.v = synth.device_normal_(torch.empty(pool, dtype=bf, device=dev), seed + 2)
@@ -56,7 +63,7 @@ class PagedDecode:
         self.table = torch.from_numpy(table).to(dev)
         self.seq_len = torch.full((B,), ctx - 1, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.desc = R.kv_cache(R.PAGED, R.I8 if kv_int8 else R.BF16, Hkv, d, self.k, self.v, batch=B, sinks=0,
+        self.desc = R.kv_cache(R.PAGED, {None: R.BF16, "i8": R.I8, "fp8": R.FP8}[kv8], Hkv, d, self.k, self.v, batch=B, sinks=0,
                                window=0, block_size=BLOCK, max_blocks=self.max_blocks, num_blocks=self.num_blocks,
                                block_table=self.table, seq_len=self.seq_len, err_word=self.err,
                                k_scale=self.k_scale, v_scale=self.v_scale)
@@ -87,9 +94,9 @@ class PagedDecode:
         self.R.decode_attn(self.q, self.B, self.Hq, self.desc, 0.0, self.out, self.ws, self.ws_bytes)
 
     def decode_bytes(self) -> int:
-        """K + V of the visible keys once per KV head (int8: codes + one fp32 scale per row),
+        """K + V of the visible keys once per KV head (8-bit: codes + one fp32 scale per row),
         plus q, out and the block-table entries read."""
-        row = self.d + 4 if self.kv_int8 else 2 * self.d
+        row = self.d + 4 if self.kv8 else 2 * self.d
         kv = 2 * self.B * self.Hkv * self.ctx * row
         qo = 2 * self.B * self.Hq * self.d * 2
         bt = self.B * self.max_blocks * 4
@@ -97,16 +104,16 @@ class PagedDecode:
 
     def kv_of(self, b: int):
         """Keys / values of sequence b by position, as host float64 [ctx, Hkv, d] (for the oracle)."""
-        if self.kv_int8:
-            raise ValueError("int8 cache: use codes_of")
+        if self.kv8:
+            raise ValueError("8-bit cache: use codes_of")
         rows = self.table[b]
         k = self.k[rows].permute(0, 2, 1, 3).reshape(-1, self.Hkv, self.d)[: self.ctx]
         v = self.v[rows].permute(0, 2, 1, 3).reshape(-1, self.Hkv, self.d)[: self.ctx]
         return (k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64))
 
     def codes_of(self, b: int):
-        """int8 cache: (k codes, k scales, v codes, v scales) of sequence b by position, host arrays
-        [ctx, Hkv, d] int8 and [ctx, Hkv] float32."""
+        """8-bit cache: (k codes, k scales, v codes, v scales) of sequence b by position, host arrays
+        [ctx, Hkv, d] int8 / uint8 and [ctx, Hkv] float32."""
         rows = self.table[b]
 
         def by_pos(t, tail):

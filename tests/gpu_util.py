@@ -49,21 +49,30 @@ def oracle_cfg(cfg) -> O.RopeCfg:
                      low_freq_factor=cfg.low_freq_factor, high_freq_factor=cfg.high_freq_factor)
 
 
+def _kv_kind(R, torch, dtype):
+    """(kv_dtype, torch storage dtype, has row scales) of a cache dtype: a torch dtype, or
+    "fp8" for E4M3 codes held as raw bytes (uint8)."""
+    if dtype == "fp8":
+        return R.FP8, torch.uint8, True
+    kvdt = {torch.float32: R.F32, torch.bfloat16: R.BF16, torch.float16: R.F16, torch.int8: R.I8}[dtype]
+    return kvdt, dtype, dtype == torch.int8
+
+
 class DevRing:
     """A RING cache in device memory (torch) plus its descriptor."""
 
     def __init__(self, R, torch, dev, dtype, B, Hkv, d, S, W):
         self.C = S + W
-        self.k = torch.zeros(B, Hkv, self.C, d, dtype=dtype, device=dev)
+        kvdt, store, coded = _kv_kind(R, torch, dtype)
+        self.k = torch.zeros(B, Hkv, self.C, d, dtype=store, device=dev)
         self.v = torch.zeros_like(self.k)
         self.head = torch.zeros(B, dtype=torch.int32, device=dev)
         self.count = torch.zeros(B, dtype=torch.int32, device=dev)
         self.seq_len = torch.zeros(B, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        kvdt = {torch.float32: R.F32, torch.bfloat16: R.BF16, torch.float16: R.F16, torch.int8: R.I8}[dtype]
-        # int8 caches: one fp32 scale per cached row, K and V
-        self.k_scale = torch.zeros(B, Hkv, self.C, dtype=torch.float32, device=dev) if dtype == torch.int8 else None
-        self.v_scale = torch.zeros_like(self.k_scale) if dtype == torch.int8 else None
+        # 8-bit caches: one fp32 scale per cached row, K and V
+        self.k_scale = torch.zeros(B, Hkv, self.C, dtype=torch.float32, device=dev) if coded else None
+        self.v_scale = torch.zeros_like(self.k_scale) if coded else None
         self.desc = R.kv_cache(R.RING, kvdt, Hkv, d, self.k, self.v, batch=B, capacity=self.C, sinks=S, window=W,
                                ring_head=self.head, ring_count=self.count, seq_len=self.seq_len, err_word=self.err,
                                k_scale=self.k_scale, v_scale=self.v_scale)
@@ -73,15 +82,14 @@ class DevPaged:
     """A PAGED cache (pool + block table) in device memory plus its descriptor."""
 
     def __init__(self, R, torch, dev, dtype, B, Hkv, d, S, W, table: np.ndarray, num_blocks: int, bs: int = 16):
-        self.k = torch.zeros(num_blocks, Hkv, bs, d, dtype=dtype, device=dev)
+        kvdt, store, coded = _kv_kind(R, torch, dtype)
+        self.k = torch.zeros(num_blocks, Hkv, bs, d, dtype=store, device=dev)
         self.v = torch.zeros_like(self.k)
         self.table = torch.from_numpy(np.ascontiguousarray(table.astype(np.int32))).to(dev)
         self.seq_len = torch.zeros(B, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        kvdt = {torch.float32: R.F32, torch.bfloat16: R.BF16, torch.float16: R.F16, torch.int8: R.I8}[dtype]
-        i8 = dtype == torch.int8
-        self.k_scale = torch.zeros(num_blocks, Hkv, bs, dtype=torch.float32, device=dev) if i8 else None
-        self.v_scale = torch.zeros_like(self.k_scale) if i8 else None
+        self.k_scale = torch.zeros(num_blocks, Hkv, bs, dtype=torch.float32, device=dev) if coded else None
+        self.v_scale = torch.zeros_like(self.k_scale) if coded else None
         self.desc = R.kv_cache(R.PAGED, kvdt, Hkv, d, self.k, self.v, batch=B, sinks=S, window=W, block_size=bs,
                                max_blocks=table.shape[1], num_blocks=num_blocks, block_table=self.table,
                                seq_len=self.seq_len, err_word=self.err, k_scale=self.k_scale, v_scale=self.v_scale)

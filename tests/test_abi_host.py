@@ -130,6 +130,13 @@ def test_apply_append_argument_errors():
     assert call(_ring(k_int8_mode=R.I8_HADAMARD, head_dim=96, **i8)) == R.ERANGE  # H needs d = 2^k
     assert call(_ring(k=FAKE + 8)) == R.EINVAL                # cache pools must be 16-byte aligned
     assert call(_ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE + 4)) == R.EINVAL
+    # E4M3 caches: the same scale rules as int8, no int8 key modes
+    assert call(_ring(kv_dtype=R.FP8)) == R.EINVAL
+    assert call(_ring(kv_dtype=R.FP8, k_scale=FAKE)) == R.EINVAL
+    assert call(_ring(kv_dtype=R.FP8, k_scale=FAKE, v_scale=FAKE), n=0) == R.OK
+    assert call(_ring(kv_dtype=R.FP8, k_scale=FAKE, v_scale=FAKE, k_int8_mode=R.I8_KEEP_SCALE)) == R.EINVAL
+    assert call(_ring(), act=R.FP8) == R.EDTYPE               # activations are never 8-bit
+    assert call(_ring(kv_dtype=5, k_scale=FAKE, v_scale=FAKE)) == R.EDTYPE
 
 
 def test_attention_argument_errors():
@@ -152,6 +159,9 @@ def test_attention_argument_errors():
     c4 = _ring(kv_dtype=R.I8, k_scale=FAKE, v_scale=FAKE)
     assert dec(FAKE, 1, 8, ctypes.byref(c4), 0.0, None, FAKE, FAKE, 1, None) == R.ENOSPACE      # int8 accepted
     assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(c4), 0, 0.0, None, FAKE, None) == R.EDTYPE  # prefill: no int8
+    c5 = _ring(kv_dtype=R.FP8, k_scale=FAKE, v_scale=FAKE)
+    assert dec(FAKE, 1, 8, ctypes.byref(c5), 0.0, None, FAKE, FAKE, 1, None) == R.ENOSPACE      # E4M3 accepted
+    assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(c5), 0, 0.0, None, FAKE, None) == R.EDTYPE
     contig = R.kv_cache(R.CONTIG, R.F32, 4, 64, FAKE, capacity=10, err_word=FAKE)
     assert dec(FAKE, 1, 8, ctypes.byref(contig), 0.0, None, FAKE, FAKE, 1 << 30, None) == R.ELAYOUT
     assert pre(FAKE, FAKE, FAKE, 8, 5, 8, ctypes.byref(contig), 0, 0.0, None, FAKE, None) == R.ELAYOUT  # prefix needs cache
@@ -195,3 +205,5 @@ def test_rerotate_argument_errors():
     g = R.rope_cfg(128, 96, rope_theta=5e5)
     h = R.rope_cfg(128, 96, rope_theta=5e5, yarn_factor=2.0, orig_max_pos=262144)
     assert f(ctypes.byref(g), ctypes.byref(h), ctypes.byref(i8h), 1, None) == R.ERANGE  # H + NeoX: r = 2^k
+    f8 = R.kv_cache(R.CONTIG, R.FP8, 8, 128, FAKE, capacity=100, err_word=FAKE, k_scale=FAKE)
+    assert f(ctypes.byref(a), ctypes.byref(b), ctypes.byref(f8), 1, None) == R.EDTYPE    # no E4M3 re-rotation

@@ -52,10 +52,14 @@ def test_paged_decode_b64_ctx32768(env):
         assert_bf16_close(out[b], ref)
 
 
-def test_paged_decode_b64_ctx32768_int8(env):
-    # the same step over an int8 cache: the appended token quantised, decode over codes x scales
+@pytest.mark.parametrize("kind", ["i8", "fp8"])
+def test_paged_decode_b64_ctx32768_8bit(env, kind):
+    # the same step over an 8-bit cache (int8 or E4M3 codes + per-row scales): the appended
+    # token quantised, decode over codes x scales
     R, torch, dev, WL = env
-    wl = WL.PagedDecode(R, torch, dev, kv_int8=True)
+    wl = WL.PagedDecode(R, torch, dev, kv8=kind)
+    quant = O.quant_int8_rows if kind == "i8" else O.quant_fp8_rows
+    dequant = O.dequant_int8_rows if kind == "i8" else O.dequant_fp8_rows
     q_raw, k_raw, v_raw = to_np64(wl.q), to_np64(wl.k_new), to_np64(wl.v_new)
     wl.step()
     torch.cuda.synchronize()
@@ -67,13 +71,19 @@ def test_paged_decode_b64_ctx32768_int8(env):
     for b in (0, 41, 63):
         kc, ks, vc, vs = wl.codes_of(b)
         want_k = O.rope_apply(k_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
-        wk_codes, wk_scale = O.quant_int8_rows(want_k)
-        assert int(np.max(np.abs(kc[p].astype(np.int32) - wk_codes.astype(np.int32)))) <= 1
+        wk_codes, wk_scale = quant(want_k)
+        # a rotated key may round to the neighbouring code (float32 vs fp64 rotation)
+        if kind == "i8":
+            assert int(np.max(np.abs(kc[p].astype(np.int32) - wk_codes.astype(np.int32)))) <= 1
+        else:
+            got_v, want_v = O.e4m3_value(kc[p]), O.e4m3_value(wk_codes)
+            step = np.maximum(np.abs(want_v), 2.0 ** -6) * 2.0 ** -3
+            assert np.all(np.abs(got_v - want_v) <= step + 1e-12)
         np.testing.assert_allclose(ks[p], wk_scale, rtol=1e-6, atol=0)
-        wv_codes, wv_scale = O.quant_int8_rows(v_raw[b])
-        assert np.array_equal(vc[p], wv_codes) and np.array_equal(vs[p], wv_scale)
-        k = O.dequant_int8_rows(kc, ks)
-        v = O.dequant_int8_rows(vc, vs)
+        wv_codes, wv_scale = quant(v_raw[b])
+        assert np.array_equal(vc[p].view(np.uint8), wv_codes.view(np.uint8)) and np.array_equal(vs[p], wv_scale)
+        k = dequant(kc, ks)
+        v = dequant(vc, vs)
         ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
         assert_bf16_close(out[b], ref)
 

@@ -1,12 +1,14 @@
-"""GPU parity of the int8 KV cache: per-row quantised K and V in apply_append, decode over codes x scales.
+"""GPU parity of the 8-bit KV caches (int8 and E4M3 codes, one fp32 scale per row):
+per-row quantised K and V in apply_append, decode over codes x scales.
 
-Reference values: the oracle's row quantiser (scale = max|x| / 127, codes
-decided in float32 with the reciprocal 127 / max|x|, the precision the kernels
-use) applied to the oracle's fp64 rotation, and the oracle's decode over the
-dequantised rows.  Values are not rotated, so their codes and scales must match
-bit for bit; a rotated key may land on the other side of a rounding boundary
-(float32 vs fp64 rotation), so its codes may differ by one step.  Decode outputs
-(bf16) meet |gpu - ref| <= 2e-2 + 1e-2 |ref|.
+Reference values: the oracle's row quantisers (scale = max|x| / qmax with qmax
+127 for int8 and 448 for E4M3, codes decided in float32 with the reciprocal
+qmax / max|x|, the precision the kernels use) applied to the oracle's fp64
+rotation, and the oracle's decode over the dequantised rows.  Values are not
+rotated, so their codes and scales must match bit for bit; a rotated key may
+land on the other side of a rounding boundary (float32 vs fp64 rotation), so
+its code may be the neighbouring one.  Decode outputs (bf16) meet
+|gpu - ref| <= 2e-2 + 1e-2 |ref|.
 """
 import numpy as np
 import pytest
@@ -28,24 +30,37 @@ def env():
     return R, torch, dev
 
 
-def _dequant(codes_t, scale_t):
-    return O.dequant_int8_rows(codes_t.cpu().numpy(), scale_t.cpu().numpy())
+KINDS = ["i8", "fp8"]
+QMAX = {"i8": 127.0, "fp8": 448.0}
+
+
+def _store(torch, kind):
+    return torch.int8 if kind == "i8" else "fp8"
+
+
+def _dequant(kind, codes_t, scale_t):
+    if kind == "i8":
+        return O.dequant_int8_rows(codes_t.cpu().numpy(), scale_t.cpu().numpy())
+    return O.dequant_fp8_rows(codes_t.cpu().numpy(), scale_t.cpu().numpy())
 
 
 def _ws(R, torch, dev, B, Hq, desc):
     return torch.empty(R.decode_workspace_size(B, Hq, desc) // 4 + 1, dtype=torch.float32, device=dev)
 
 
-def _random_int8(torch, cache, seed):
-    synth.device_int8_codes_(cache.k, seed)
-    synth.device_int8_codes_(cache.v, seed + 1)
-    synth.device_uniform_(cache.k_scale, 0.5 / 127, 3.0 / 127, seed + 2)
-    synth.device_uniform_(cache.v_scale, 0.5 / 127, 3.0 / 127, seed + 3)
+def _random_codes(torch, cache, seed, kind):
+    fill = synth.device_int8_codes_ if kind == "i8" else synth.device_fp8_codes_
+    fill(cache.k, seed)
+    fill(cache.v, seed + 1)
+    qmax = QMAX[kind]
+    synth.device_uniform_(cache.k_scale, 0.5 / qmax, 3.0 / qmax, seed + 2)
+    synth.device_uniform_(cache.v_scale, 0.5 / qmax, 3.0 / qmax, seed + 3)
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("n_rep,d,S,W,sinks", [(4, 128, 0, 0, False), (8, 128, 4, 100, False), (1, 64, 0, 0, False),
                                                (2, 64, 4, 40, True), (4, 128, 4, 300, True)])
-def test_int8_decode_paged(env, n_rep, d, S, W, sinks):
+def test_kv8_decode_paged(env, kind, n_rep, d, S, W, sinks):
     # paged 16-token blocks, random block table (null below the window edge), ragged lengths
     R, torch, dev = env
     Hkv = 8
@@ -61,8 +76,8 @@ def test_int8_decode_paged(env, n_rep, d, S, W, sinks):
             for j in range(1, max_blocks):
                 if 16 * j + 16 <= edge:
                     table[b, j] = -1
-    cache = DevPaged(R, torch, dev, torch.int8, B, Hkv, d, S, W, table, num_blocks)
-    _random_int8(torch, cache, 82)
+    cache = DevPaged(R, torch, dev, _store(torch, kind), B, Hkv, d, S, W, table, num_blocks)
+    _random_codes(torch, cache, 82, kind)
     cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
     q = synth.device_normal_(torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev), 86)
     sl = synth.device_normal_(torch.empty(Hq, dtype=torch.float32, device=dev), 87) if sinks else None
@@ -71,8 +86,8 @@ def test_int8_decode_paged(env, n_rep, d, S, W, sinks):
     R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4, sink_logits=sl)
     torch.cuda.synchronize()
     assert cache.err.item() == 0
-    kd = _dequant(cache.k, cache.k_scale)
-    vd = _dequant(cache.v, cache.v_scale)
+    kd = _dequant(kind, cache.k, cache.k_scale)
+    vd = _dequant(kind, cache.v, cache.v_scale)
     qq, got = to_np64(q), to_np64(out)
     slh = None if sl is None else sl.cpu().numpy().astype(np.float64)
     for b, n in enumerate(lens):
@@ -86,15 +101,16 @@ def test_int8_decode_paged(env, n_rep, d, S, W, sinks):
         assert_bf16_close(got[b], ref)
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("n_rep,d", [(4, 128), (8, 64)])
-def test_int8_decode_ring(env, n_rep, d):
+def test_kv8_decode_ring(env, kind, n_rep, d):
     # windowed layer: full ring (count = W), head at a random offset, long positions, C not a multiple of 16
     R, torch, dev = env
     Hkv, S, W = 8, 4, 300
     Hq = Hkv * n_rep
     B = 5
-    cache = DevRing(R, torch, dev, torch.int8, B, Hkv, d, S, W)
-    _random_int8(torch, cache, 91)
+    cache = DevRing(R, torch, dev, _store(torch, kind), B, Hkv, d, S, W)
+    _random_codes(torch, cache, 91, kind)
     heads = synth.uniform_ints(B, 0, W, 95)
     lens = [131072, 5000, 305, 304 + 7, 9999]
     cache.head.copy_(torch.from_numpy(heads))
@@ -106,8 +122,8 @@ def test_int8_decode_ring(env, n_rep, d):
     R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
     torch.cuda.synchronize()
     assert cache.err.item() == 0
-    kd = _dequant(cache.k, cache.k_scale)
-    vd = _dequant(cache.v, cache.v_scale)
+    kd = _dequant(kind, cache.k, cache.k_scale)
+    vd = _dequant(kind, cache.v, cache.v_scale)
     qq, got = to_np64(q), to_np64(out)
     for b in range(B):
         ring = O.RingSeq(sinks=S, window=W, head=int(heads[b]), count=W, seq_len=lens[b])
@@ -117,10 +133,19 @@ def test_int8_decode_ring(env, n_rep, d):
         assert_bf16_close(got[b], ref)
 
 
-def _check_rows(got_codes, got_scale, want_codes, want_scale, rotated):
+def _ordinal(kind, codes):
+    """Codes as integers in value order (neighbouring values differ by 1; E4M3 +0 and -0 are both 0)."""
+    c = np.asarray(codes)
+    if kind == "i8":
+        return c.astype(np.int32)
+    u = c.view(np.uint8).astype(np.int32)
+    return np.where(u & 0x80, -(u & 0x7F), u)
+
+
+def _check_rows(kind, got_codes, got_scale, want_codes, want_scale, rotated):
     """Codes / scales of cached rows against the oracle quantiser."""
     if rotated:
-        diff = np.abs(got_codes.astype(np.int32) - want_codes.astype(np.int32))
+        diff = np.abs(_ordinal(kind, got_codes) - _ordinal(kind, want_codes))
         assert int(diff.max()) <= 1
         assert float(np.mean(diff)) <= 1e-2
         np.testing.assert_allclose(got_scale, want_scale, rtol=1e-6, atol=0)
@@ -129,13 +154,17 @@ def _check_rows(got_codes, got_scale, want_codes, want_scale, rotated):
         assert np.array_equal(got_scale, want_scale)
 
 
-def _oracle_quant(rows):
-    codes, scale = O.quant_int8_rows(rows)
-    return codes, scale, O.dequant_int8_rows(codes, scale)
+def _oracle_quant(kind, rows):
+    if kind == "i8":
+        codes, scale = O.quant_int8_rows(rows)
+        return codes, scale, O.dequant_int8_rows(codes, scale)
+    codes, scale = O.quant_fp8_rows(rows)
+    return codes, scale, O.dequant_fp8_rows(codes, scale)
 
 
-def test_int8_paged_append_and_decode(env):
-    # bf16 activations into an int8 paged cache with sinks + window: mixed steps, freeing, decode each round
+@pytest.mark.parametrize("kind", KINDS)
+def test_kv8_paged_append_and_decode(env, kind):
+    # bf16 activations into an 8-bit paged cache with sinks + window: mixed steps, freeing, decode each round
     R, torch, dev = env
     B, Hq, Hkv, d, S, W = 4, 32, 8, 128, 4, 40
     max_len, bs = 200, 16
@@ -147,7 +176,7 @@ def test_int8_paged_append_and_decode(env):
     gtab = torch.empty(max_len, d, dtype=torch.float32, device=dev)
     R.build_table(cfg, max_len, gtab)
     otab = O.build_table(oracle_cfg(cfg), max_len)
-    cache = DevPaged(R, torch, dev, torch.int8, B, Hkv, d, S, W, table, num_blocks)
+    cache = DevPaged(R, torch, dev, _store(torch, kind), B, Hkv, d, S, W, table, num_blocks)
     otable = [list(map(int, row)) for row in table]
     bf = torch.bfloat16
     qall = to_np64(torch.from_numpy(synth.normal((B, max_len, Hq, d), 502)).to(bf))
@@ -155,8 +184,8 @@ def test_int8_paged_append_and_decode(env):
     vall = to_np64(torch.from_numpy(synth.normal((B, max_len, Hkv, d), 504)).to(bf))
     krot = np.stack([O.rope_apply(kall[b], np.arange(max_len), otab, d, True) for b in range(B)])
     qrot = np.stack([O.rope_apply(qall[b], np.arange(max_len), otab, d, True) for b in range(B)])
-    kq_codes, kq_scale, kdeq = _oracle_quant(krot)
-    vq_codes, vq_scale, vdeq = _oracle_quant(vall)
+    kq_codes, kq_scale, kdeq = _oracle_quant(kind, krot)
+    vq_codes, vq_scale, vdeq = _oracle_quant(kind, vall)
     n = [0] * B
     freed_dev = torch.full((B * max_blocks,), -7, dtype=torch.int32, device=dev)
     nfreed = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -199,8 +228,8 @@ def test_int8_paged_append_and_decode(env):
             gv.append(vc[bid, :, p % bs]), gvs.append(vs[bid, :, p % bs])
             wv.append(vq_codes[b, p]), wvs.append(vq_scale[b, p])
         if gk:
-            _check_rows(np.stack(gk), np.stack(gks), np.stack(wk), np.stack(wks), rotated=True)
-            _check_rows(np.stack(gv), np.stack(gvs), np.stack(wv), np.stack(wvs), rotated=False)
+            _check_rows(kind, np.stack(gk), np.stack(gks), np.stack(wk), np.stack(wks), rotated=True)
+            _check_rows(kind, np.stack(gv), np.stack(gvs), np.stack(wv), np.stack(wvs), rotated=False)
         qd = torch.from_numpy(np.stack([qrot[b, max(n[b] - 1, 0)] for b in range(B)])).to(dev, bf)
         out = torch.empty(B, Hq, d, dtype=bf, device=dev)
         R.decode_attn(qd, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
@@ -215,9 +244,10 @@ def test_int8_paged_append_and_decode(env):
             assert_bf16_close(got[b], ref)
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("chunks", [[40, 1, 1, 1, 5], [3, 1, 20, 1, 7, 1]])
-def test_int8_ring_append_and_decode(env, chunks):
-    # bf16 activations into an int8 ring (S = 4, W = 12): survivors quantised, ring state bit-exact
+def test_kv8_ring_append_and_decode(env, kind, chunks):
+    # bf16 activations into an 8-bit ring (S = 4, W = 12): survivors quantised, ring state bit-exact
     R, torch, dev = env
     B, Hq, Hkv, d, S, W = 1, 8, 4, 64, 4, 12
     n_total = sum(chunks)
@@ -231,9 +261,9 @@ def test_int8_ring_append_and_decode(env, chunks):
     vd = torch.from_numpy(synth.normal((n_total, Hkv, d), 513)).to(dev, bf)
     qrot = O.rope_apply(to_np64(qd), np.arange(n_total), otab, d, True)
     krot = O.rope_apply(to_np64(kd), np.arange(n_total), otab, d, True)
-    kq_codes, kq_scale, kdeq = _oracle_quant(krot)
-    vq_codes, vq_scale, vdeq = _oracle_quant(to_np64(vd))
-    cache = DevRing(R, torch, dev, torch.int8, B, Hkv, d, S, W)
+    kq_codes, kq_scale, kdeq = _oracle_quant(kind, krot)
+    vq_codes, vq_scale, vdeq = _oracle_quant(kind, to_np64(vd))
+    cache = DevRing(R, torch, dev, _store(torch, kind), B, Hkv, d, S, W)
     oring = O.RingSeq(sinks=S, window=W)
     out = torch.empty(1, Hq, d, dtype=bf, device=dev)
     ws = _ws(R, torch, dev, 1, Hq, cache.desc)
@@ -253,8 +283,8 @@ def test_int8_ring_append_and_decode(env, chunks):
         vc, vs = cache.v[0].cpu().numpy(), cache.v_scale[0].cpu().numpy()
         slots = sorted(oring.slot_pos)
         ps = [oring.slot_pos[s] for s in slots]
-        _check_rows(kc[:, slots].transpose(1, 0, 2), ks[:, slots].T, kq_codes[ps], kq_scale[ps], rotated=True)
-        _check_rows(vc[:, slots].transpose(1, 0, 2), vs[:, slots].T, vq_codes[ps], vq_scale[ps], rotated=False)
+        _check_rows(kind, kc[:, slots].transpose(1, 0, 2), ks[:, slots].T, kq_codes[ps], kq_scale[ps], rotated=True)
+        _check_rows(kind, vc[:, slots].transpose(1, 0, 2), vs[:, slots].T, vq_codes[ps], vq_scale[ps], rotated=False)
         R.decode_attn(q[T - 1:T], 1, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
         torch.cuda.synchronize()
         ref = O.decode_attention(qrot[p0 + T - 1], lambda j: kdeq[j], lambda j: vdeq[j], p0 + T, S, W, Hkv)
