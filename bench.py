@@ -311,6 +311,19 @@ def main():
             del rr
             torch.cuda.empty_cache()
 
+    if not args.no_extras:
+        # practical HBM ceilings of plain streams on this device (torch's own elementwise kernels):
+        # a 32 GiB in-place read-modify-write, the access shape of the re-rotation, and a 16 GiB copy
+        log("hbm ceilings: in-place read-modify-write and copy")
+        x = torch.zeros(8 << 30, dtype=torch.int32, device=dev)
+        ms = timed(torch, lambda: x.add_(1), 4, warmup=1)
+        rows["ceiling_inplace_rmw_32GiB"] = {"ms": round(ms, 3), "GBps": round(2 * x.numel() * 4 / ms / 1e6, 1)}
+        h = x.numel() // 2
+        ms = timed(torch, lambda: x[h:].copy_(x[:h]), 4, warmup=1)
+        rows["ceiling_copy_16GiB"] = {"ms": round(ms, 3), "GBps": round(2 * h * 4 / ms / 1e6, 1)}
+        del x
+        torch.cuda.empty_cache()
+
     line = {
         "metric": METRIC,
         "value": round(value, 1),

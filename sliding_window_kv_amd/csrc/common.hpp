@@ -87,10 +87,10 @@ __host__ inline RopeParams make_rope_params(const ropekv_rope_cfg &c) {
   return p;
 }
 
-__device__ inline double yarn_omega(const RopeParams &p, int i);
+__host__ __device__ inline double yarn_omega(const RopeParams &p, int i);
 
 // Angular frequency of pair i under the configured scheme, fp64.
-__device__ inline double rope_omega(const RopeParams &p, int i) {
+__host__ __device__ inline double rope_omega(const RopeParams &p, int i) {
   if (i < p.pruned) return 0.0;
   const double r = (double)p.rotary_dim;
   const double e = (2.0 * (double)i) / r;
@@ -115,10 +115,10 @@ __device__ inline double rope_omega(const RopeParams &p, int i) {
 }
 
 __host__ __device__ inline double rope_mscale(double s);
-__device__ inline double params_mscale(const RopeParams &p) { return p.type == ROPEKV_ROPE_YARN ? rope_mscale(p.s) : 1.0; }
+__host__ __device__ inline double params_mscale(const RopeParams &p) { return p.type == ROPEKV_ROPE_YARN ? rope_mscale(p.s) : 1.0; }
 
 // YaRN frequency of pair i (plain RoPE when s <= 1).
-__device__ inline double yarn_omega(const RopeParams &p, int i) {
+__host__ __device__ inline double yarn_omega(const RopeParams &p, int i) {
   const double r = (double)p.rotary_dim;
   const double pos_freq = pow(p.theta, (2.0 * (double)i) / r);
   const double ext = 1.0 / pos_freq;

@@ -7,9 +7,10 @@
 //
 // A workgroup owns PT consecutive positions and walks every layer and KV
 // head at those positions, so the fp64 angle work (PT x r/2 sincos) is shared
-// by n_layers x Hkv rows.  Float caches read and write only the rotary slice
-// (the tail is never touched); int8 rows are read whole, dequantised, turned,
-// and requantised with a fresh per-row scale.
+// by n_layers x Hkv rows; the per-pair frequency change w_B,i - w_A,i and the
+// gain are evaluated once per call on the host, in fp64.  Float caches read and
+// write only the rotary slice (the tail is never touched); int8 rows are read
+// whole, turned in code units and requantised with a fresh per-row scale.
 #include "kernels.hpp"
 
 namespace ropekv {
@@ -17,6 +18,9 @@ namespace ropekv {
 namespace {
 
 constexpr int kPT = 16;  // positions per workgroup
+constexpr int kI8Threads = 256;  // int8 lane kernel: threads per workgroup
+constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup (1: 16.4 ms, 2: 14.4, 4: 15.3 on
+                                 // the 64-layer int8 switch; the float kernel is fastest at 1)
 
 struct RerotArgs {
   RopeParams from, to;
@@ -25,7 +29,62 @@ struct RerotArgs {
   int rows_T;  // rows (positions) per layer
   int Hkv, D, pos0, n_layers;
   int keep_scale;  // int8: keep each row's scale unless a turned rotary code overflows
+  int rpb;         // chunked kernels: rows per workgroup
+  int chunks;      // chunked kernels: row chunks per layer
+  int lg;          // chunked kernels: layers per workgroup
+  double gain;     // mu_to / mu_from
+  double dw[256];  // w_to,i - w_from,i per rotary pair, fp64, set on the host
 };
+
+// Chunked workgroups: each owns rpb consecutive rows (position-major, head-minor)
+// of lg consecutive layers, and the grid runs chunk-major within a layer group,
+// so the whole chip sweeps the cache front to back.  A thread reads its piece of
+// a row, turns it and writes it back right away: on this part an in-place stream
+// runs fastest that way (a probe with one read-modify-write per thread in 4 KiB
+// workgroups moved 5.9 TB/s, against 4.7-5.1 TB/s when each workgroup walks many
+// pieces or many layers).
+struct ChunkRows {
+  long row0;  // first row of the workgroup in its first layer (all layers counted)
+  int nl;     // layers the workgroup walks
+  int r0;     // first row within its layer
+  int nrows;  // live rows
+  int pa;     // position index (from pos0) of the first row
+  int np;     // positions the rows span
+};
+__device__ inline ChunkRows chunk_rows(const RerotArgs &a) {
+  const int group = blockIdx.x / a.chunks, chunk = blockIdx.x - group * a.chunks;
+  const int layer = group * a.lg;
+  const long layer_rows = (long)a.rows_T * a.Hkv;
+  const int r0 = chunk * a.rpb;
+  ChunkRows c;
+  c.nrows = (int)min((long)a.rpb, layer_rows - r0);
+  c.row0 = layer * layer_rows + r0;
+  c.nl = min(a.lg, a.n_layers - layer);
+  c.r0 = r0;
+  c.pa = r0 / a.Hkv;
+  c.np = (r0 + c.nrows - 1) / a.Hkv - c.pa + 1;
+  return c;
+}
+
+// cos / sin of the turn of every rotary pair at positions pos0 + pa .. + np - 1,
+// times the gain, into s_cs / s_sn [np][half].  The angle p (w_to,i - w_from,i)
+// and its reduction modulo 2 pi are fp64; cos and sin of the reduced angle
+// (|r| <= pi) are fp32, within a few 1e-7 of the exact values.
+__device__ inline void turn_table(const RerotArgs &a, int pa, int np, float *s_cs, float *s_sn) {
+  const int half = a.to.rotary_dim / 2;
+  const float gain = (float)a.gain;
+  for (int idx = threadIdx.x; idx < np * half; idx += blockDim.x) {
+    const int pt = idx / half, i = idx - pt * half;
+    const double th = (double)(a.pos0 + pa + pt) * a.dw[i];
+    const double k = rint(th * 0.15915494309189535);                  // turns of 2 pi
+    const double rd = fma(-k, 2.4492935982947064e-16, fma(-k, 6.283185307179586, th));
+    float sf, cf;
+    sincosf((float)rd, &sf, &cf);
+    s_cs[idx] = cf * gain;
+    s_sn[idx] = sf * gain;
+  }
+  __syncthreads();
+}
 
 // Keep-scale decision for one int8 row: every turned rotary value of the row must
 // re-code within [-127, 127] at the row's old scale (decided like the quantiser, in
@@ -38,20 +97,18 @@ __device__ __forceinline__ bool row_keeps_scale(float mx, int lanes) {
 
 // Fills s_cs / s_sn [kPT][half] with cos / sin of (pos) * (w_to - w_from) in
 // fp64, rounded to fp32, and returns the gain mu_to / mu_from.
-__device__ inline float angle_setup(const RerotArgs &a, int t0, float *s_cs, float *s_sn, double *s_dw) {
+__device__ inline float angle_setup(const RerotArgs &a, int t0, float *s_cs, float *s_sn) {
   const int half = a.to.rotary_dim / 2;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) s_dw[i] = rope_omega(a.to, i) - rope_omega(a.from, i);
-  __syncthreads();
   for (int idx = threadIdx.x; idx < kPT * half; idx += blockDim.x) {
     const int pt = idx / half, i = idx % half;
-    const double ang = (double)(a.pos0 + t0 + pt) * s_dw[i];
+    const double ang = (double)(a.pos0 + t0 + pt) * a.dw[i];
     double sn, cs;
     sincos(ang, &sn, &cs);
     s_cs[idx] = (float)cs;
     s_sn[idx] = (float)sn;
   }
   __syncthreads();
-  return (float)(params_mscale(a.to) / params_mscale(a.from));
+  return (float)a.gain;
 }
 
 // Raw 16-bit / 32-bit element access inside a register vector.
@@ -112,91 +169,61 @@ __device__ __forceinline__ void vst(char *p, const uint32_t *w) {
   }
 }
 
-// Float keys.  A thread turns PP consecutive pairs of one row: NeoX loads PP
-// elements from each half, GPT-J 2 PP interleaved elements.  Items (row, pair
-// group) of all layers form one index space; each thread issues the loads of
-// U items before turning any, so U x 32 bytes per lane are in flight.
+// Float keys.  A thread turns PP consecutive pairs of one row: NeoX reads PP
+// elements from each half, GPT-J 2 PP interleaved elements; tpr = half / PP
+// threads per row, rpb = 256 / tpr rows per one-shot workgroup.
 template <typename T, int PP>
 __global__ __launch_bounds__(256) void rerotate_float_kernel(RerotArgs a) {
   constexpr int EB = sizeof(T);
   constexpr int NB = PP * EB;
   constexpr int NW = (NB + 3) / 4;
-  constexpr int U = 4;
-  __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
-  __shared__ double s_dw[256];
-  const int t0 = blockIdx.x * kPT;
-  const float gain = angle_setup(a, t0, s_cs, s_sn, s_dw);
+  extern __shared__ float s_tab[];
   const int half = a.to.rotary_dim / 2;
+  const ChunkRows c = chunk_rows(a);
+  float *s_cs = s_tab, *s_sn = s_tab + c.np * half;
+  turn_table(a, c.pa, c.np, s_cs, s_sn);
   const int tpr = half / PP;
-  const int npos = min(kPT, a.rows_T - t0);
-  const int items_pl = npos * a.Hkv * tpr;
-  const int total = items_pl * a.n_layers;
-  const int neox = a.to.neox;
-  const long layer_stride = (long)a.rows_T * a.Hkv * a.D;
-  char *kb = (char *)a.k;
-  for (int base = threadIdx.x; base < total; base += 256 * U) {
-    uint32_t w1[U][NW], w2[U][NW];
-    char *p1[U];
-    char *p2[U];
-    int jj[U];
-    bool live[U];
+  const int rr = threadIdx.x / tpr, q = threadIdx.x - rr * tpr;
+  if (rr >= c.nrows) return;
+  const int j0 = q * PP;
+  const int tab = ((c.r0 + rr) / a.Hkv - c.pa) * half + j0;
+  const long layer_bytes = (long)a.rows_T * a.Hkv * a.D * EB;
+  char *kb = (char *)a.k + (c.row0 + rr) * a.D * EB;
+  char *p1 = kb + (a.to.neox ? j0 : 2 * j0) * EB;
+  char *p2 = a.to.neox ? kb + (half + j0) * EB : p1 + NB;
+  for (int l = 0; l < c.nl; ++l, p1 += layer_bytes, p2 += layer_bytes) {
+  uint32_t w1[NW], w2[NW];
+  vld<NB>(w1, p1);
+  vld<NB>(w2, p2);
+  const float *cs = &s_cs[tab];
+  const float *sn = &s_sn[tab];
+  if constexpr (PP % 2 == 0) {
+    if (a.to.neox) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int it = base + u * 256;
-      live[u] = it < total;
-      const int itc = live[u] ? it : base;
-      const int layer = itc / items_pl, rem = itc % items_pl;
-      const int rr = rem / tpr, q = rem % tpr;
-      const long rbase = layer * layer_stride + ((long)t0 * a.Hkv + rr) * a.D;
-      const int j0 = q * PP;
-      jj[u] = (rr / a.Hkv) * half + j0;
-      p1[u] = kb + (rbase + (neox ? j0 : 2 * j0)) * EB;
-      p2[u] = neox ? kb + (rbase + half + j0) * EB : p1[u] + NB;
-      if (live[u]) {
-        vld<NB>(w1[u], p1[u]);
-        vld<NB>(w2[u], p2[u]);
+      for (int e = 0; e < PP; e += 2) {
+        const float x1a = vget<T>(w1, e), x2a = vget<T>(w2, e);
+        const float x1b = vget<T>(w1, e + 1), x2b = vget<T>(w2, e + 1);
+        vput2<T>(w1, e, x1a * cs[e] - x2a * sn[e], x1b * cs[e + 1] - x2b * sn[e + 1]);
+        vput2<T>(w2, e, x2a * cs[e] + x1a * sn[e], x2b * cs[e + 1] + x1b * sn[e + 1]);
+      }
+    } else {
+      // 2 PP interleaved elements: pair e is (2e, 2e+1), both in one NB-byte half
+#pragma unroll
+      for (int e = 0; e < PP; ++e) {
+        uint32_t *b = 2 * e < PP ? w1 : w2;
+        const int i1 = 2 * e < PP ? 2 * e : 2 * e - PP;
+        const float x1 = vget<T>(b, i1), x2 = vget<T>(b, i1 + 1);
+        vput2<T>(b, i1, x1 * cs[e] - x2 * sn[e], x2 * cs[e] + x1 * sn[e]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!live[u]) continue;
-      const float *cs = &s_cs[jj[u]];
-      const float *sn = &s_sn[jj[u]];
-      if constexpr (PP % 2 == 0) {
-        if (neox) {
-#pragma unroll
-          for (int e = 0; e < PP; e += 2) {
-            const float x1a = vget<T>(w1[u], e), x2a = vget<T>(w2[u], e);
-            const float x1b = vget<T>(w1[u], e + 1), x2b = vget<T>(w2[u], e + 1);
-            vput2<T>(w1[u], e, (x1a * cs[e] - x2a * sn[e]) * gain, (x1b * cs[e + 1] - x2b * sn[e + 1]) * gain);
-            vput2<T>(w2[u], e, (x2a * cs[e] + x1a * sn[e]) * gain, (x2b * cs[e + 1] + x1b * sn[e + 1]) * gain);
-          }
-        } else {
-          // 2 PP interleaved elements: pair e is (2e, 2e+1), both in one NB-byte half
-#pragma unroll
-          for (int e = 0; e < PP; ++e) {
-            uint32_t *b = 2 * e < PP ? w1[u] : w2[u];
-            const int i1 = 2 * e < PP ? 2 * e : 2 * e - PP;
-            const float x1 = vget<T>(b, i1), x2 = vget<T>(b, i1 + 1);
-            vput2<T>(b, i1, (x1 * cs[e] - x2 * sn[e]) * gain, (x2 * cs[e] + x1 * sn[e]) * gain);
-          }
-        }
-      } else if (neox) {
-#pragma unroll
-        for (int e = 0; e < PP; ++e) {
-          const float x1 = vget<T>(w1[u], e), x2 = vget<T>(w2[u], e);
-          vput<T>(w1[u], e, (x1 * cs[e] - x2 * sn[e]) * gain);
-          vput<T>(w2[u], e, (x2 * cs[e] + x1 * sn[e]) * gain);
-        }
-      } else {
-        // PP = 1: the pair is element 0 of each half
-        const float x1 = vget<T>(w1[u], 0), x2 = vget<T>(w2[u], 0);
-        vput<T>(w1[u], 0, (x1 * cs[0] - x2 * sn[0]) * gain);
-        vput<T>(w2[u], 0, (x2 * cs[0] + x1 * sn[0]) * gain);
-      }
-      vst<NB>(p1[u], w1[u]);
-      vst<NB>(p2[u], w2[u]);
-    }
+  } else {
+    // PP = 1: the pair is element 0 of each half (NeoX) or of the two halves (GPT-J)
+    const float x1 = vget<T>(w1, 0), x2 = vget<T>(w2, 0);
+    vput<T>(w1, 0, x1 * cs[0] - x2 * sn[0]);
+    vput<T>(w2, 0, x2 * cs[0] + x1 * sn[0]);
+  }
+  vst<NB>(p1, w1);
+  vst<NB>(p2, w2);
   }
 }
 
@@ -263,124 +290,132 @@ __device__ __forceinline__ float code_at(const uint32_t *w, int e) {
   return (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
 }
 
-template <int H>
-__global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
-  constexpr int TL = 16 - 2 * H;
-  constexpr int NR = (2 * H + 3) / 4;   // words of the rotary codes
-  constexpr int NT = (TL + 3) / 4 > 0 ? (TL + 3) / 4 : 1;
-  constexpr int U = 4;
-  __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
-  __shared__ double s_dw[256];
-  const int t0 = blockIdx.x * kPT;
-  const float gain = angle_setup(a, t0, s_cs, s_sn, s_dw);
+// Turn table of one block in code units: cos and sin of pos (w_to - w_from), times
+// the gain mu_to / mu_from, in fp64 and rounded once to fp32.  [kPT][half] each,
+// in dynamic LDS (kPT x half x 8 bytes).
+__device__ inline void gain_table(const RerotArgs &a, int t0, float *s_cs, float *s_sn) {
   const int half = a.to.rotary_dim / 2;
+  for (int idx = threadIdx.x; idx < kPT * half; idx += blockDim.x) {
+    const int pt = idx / half, i = idx - pt * half;
+    double sn, cs;
+    sincos((double)(a.pos0 + t0 + pt) * a.dw[i], &sn, &cs);
+    s_cs[idx] = (float)(cs * a.gain);
+    s_sn[idx] = (float)(sn * a.gain);
+  }
+  __syncthreads();
+}
+
+// int8 keys turned in code units.  A row x = c * sc (codes c, row scale sc) turns
+// into y * sc with y = R c (the pair turn with the gain folded into cos / sin),
+// so the requantised row needs only the codes: amax = max|y| over the row (tail
+// codes included), new codes rne(y * 127 / amax), new scale sc * amax / 127.
+// Keep-scale: the row keeps sc (tail codes untouched) when every turned rotary
+// value re-codes within [-127, 127], i.e. max|y| < 127.5, and stores rne(y).
+// A row with sc = 0 becomes all zero with scale 0, as its dequantised values are.
+// Codes are rne(y * inv) by one fma with 1.5 * 2^23 (the integer lands in the
+// low mantissa bits); |y * inv| <= 127.5 holds by the choice of inv.
+__device__ __forceinline__ uint32_t code_fma(float y, float inv) {
+  return __float_as_uint(__builtin_fmaf(y, inv, 12582912.0f));
+}
+
+// Lane-local pairs: L = D / 16 lanes per row, 16 codes per lane; NeoX lane q
+// holds pairs [qH, qH + H) (H codes from each half) and TL = 16 - 2H tail codes
+// [r + q TL, ...); GPT-J lane q holds the 2H interleaved codes of the same
+// pairs.  No lane exchange is needed to turn a pair; the row maxima are
+// reductions over the row's L adjacent lanes.  One-shot workgroups of
+// rpb = kI8Threads / L whole rows, walking lg layers.
+template <int H, bool NEOX, bool KEEP>
+__global__ __launch_bounds__(kI8Threads) void rerotate_int8_lanes_kernel(RerotArgs a) {
+  constexpr int TL = 16 - 2 * H;
+  constexpr int NR = (2 * H + 3) / 4;  // words of the rotary codes (per half under NeoX)
+  constexpr int NT = TL > 0 ? (TL + 3) / 4 : 1;
+  extern __shared__ float s_tab[];
+  const int half = a.to.rotary_dim / 2;
+  const ChunkRows c = chunk_rows(a);
+  float *s_cs = s_tab, *s_sn = s_tab + c.np * half;
+  turn_table(a, c.pa, c.np, s_cs, s_sn);
   const int r = a.to.rotary_dim;
   const int L = a.D / 16;
-  const int npos = min(kPT, a.rows_T - t0);
-  const int items = npos * a.Hkv * L;  // a multiple of L: a row's lanes are always active together
-  const int neox = a.to.neox;
+  const int rr = threadIdx.x / L, q = threadIdx.x - rr * L;
+  // rows past the layer's end turn zeros and store nothing; a row's lanes share that state
+  const bool live = rr < c.nrows;
+  const int tab = ((c.r0 + (live ? rr : 0)) / a.Hkv - c.pa) * half + q * H;
   const long layer_rows = (long)a.rows_T * a.Hkv;
-  int8_t *kc = (int8_t *)a.k;
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int rr = it / L, q = it % L;
-    const float *cs = &s_cs[(rr / a.Hkv) * half + q * H];
-    const float *sn = &s_sn[(rr / a.Hkv) * half + q * H];
-    const long row0 = (long)t0 * a.Hkv + rr;
-    for (int l0 = 0; l0 < a.n_layers; l0 += U) {
-      uint32_t wr[U][NR], wr2[U][NR], wt[U][NT];
-      float sco[U];
+  int8_t *rp = (int8_t *)a.k + (c.row0 + rr) * a.D;
+  float *sp = a.scale + c.row0 + rr;
+  for (int l = 0; l < c.nl; ++l, rp += layer_rows * a.D, sp += layer_rows) {
+  uint32_t w1[NR], w2[NR], wt[NT];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+  for (int i = 0; i < NR; ++i) w1[i] = w2[i] = 0u;
 #pragma unroll
-        for (int i = 0; i < NR; ++i) wr[u][i] = wr2[u][i] = 0u;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) wt[u][i] = 0u;
-        sco[u] = 0.f;
-        if (l0 + u < a.n_layers) {
-          const long row = (l0 + u) * layer_rows + row0;
-          const int8_t *rp = kc + row * a.D;
-          sco[u] = a.scale[row];
-          if (neox) {
-            ld_n<H>(wr[u], rp + q * H);
-            ld_n<H>(wr2[u], rp + half + q * H);
-          } else {
-            ld_n<2 * H>(wr[u], rp + 2 * q * H);
-          }
-          if constexpr (TL > 0) ld_n<TL>(wt[u], rp + r + q * TL);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float y[16];
-#pragma unroll
-        for (int e = 0; e < H; ++e) {
-          float x1, x2;
-          if (neox) {
-            x1 = code_at(wr[u], e) * sco[u];
-            x2 = code_at(wr2[u], e) * sco[u];
-          } else {
-            x1 = code_at(wr[u], 2 * e) * sco[u];
-            x2 = code_at(wr[u], 2 * e + 1) * sco[u];
-          }
-          y[2 * e] = (x1 * cs[e] - x2 * sn[e]) * gain;
-          y[2 * e + 1] = (x2 * cs[e] + x1 * sn[e]) * gain;
-        }
-#pragma unroll
-        for (int e = 0; e < TL; ++e) y[2 * H + e] = code_at(wt[u], e) * sco[u];
-        bool keep = false;
-        float inv = 0.f, amax = 0.f;
-        if (a.keep_scale) {
-          const float inv_old = sco[u] > 0.f ? 1.0f / sco[u] : 0.f;
-          float mx = 0.f;
-#pragma unroll
-          for (int e = 0; e < 2 * H; ++e) mx = fmaxf(mx, fabsf(rintf(y[e] * inv_old)));
-          keep = row_keeps_scale(mx, L);
-          inv = inv_old;
-        }
-        if (!keep) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(y[e]));
-          for (int m = L >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-          inv = amax > 0.f ? 127.0f / amax : 0.f;
-        }
-        uint32_t o1[NR], o2[NR], ot[NT];
-        if (neox) {
-          uint32_t c1[H], c2[H];
-#pragma unroll
-          for (int e = 0; e < H; ++e) {
-            c1[e] = code_bits(y[2 * e], inv);
-            c2[e] = code_bits(y[2 * e + 1], inv);
-          }
-          pack_codes<H>(o1, c1);
-          pack_codes<H>(o2, c2);
-        } else {
-          uint32_t c1[2 * H];
-#pragma unroll
-          for (int e = 0; e < 2 * H; ++e) c1[e] = code_bits(y[e], inv);
-          pack_codes<2 * H>(o1, c1);
-        }
-        if constexpr (TL > 0) {
-          uint32_t ct[TL];
-#pragma unroll
-          for (int e = 0; e < TL; ++e) ct[e] = code_bits(y[2 * H + e], inv);
-          pack_codes<TL>(ot, ct);
-        }
-        if (l0 + u < a.n_layers) {
-          const long row = (l0 + u) * layer_rows + row0;
-          int8_t *rp = kc + row * a.D;
-          if (neox) {
-            st_n<H>(rp + q * H, o1);
-            st_n<H>(rp + half + q * H, o2);
-          } else {
-            st_n<2 * H>(rp + 2 * q * H, o1);
-          }
-          if constexpr (TL > 0) {
-            if (!keep) st_n<TL>(rp + r + q * TL, ot);
-          }
-          if (q == 0 && !keep) a.scale[row] = amax / 127.0f;
-        }
-      }
+  for (int i = 0; i < NT; ++i) wt[i] = 0u;
+  float sco = 0.f;
+  if (live) {
+    sco = *sp;
+    if constexpr (NEOX) {
+      ld_n<H>(w1, rp + q * H);
+      ld_n<H>(w2, rp + half + q * H);
+    } else {
+      ld_n<2 * H>(w1, rp + 2 * q * H);
     }
+    if constexpr (TL > 0) ld_n<TL>(wt, rp + r + q * TL);
+  }
+  float y[2 * H];  // turned rotary values: y[2e], y[2e + 1] = pair e
+  float mrot = 0.f, mtail = 0.f;
+#pragma unroll
+  for (int e = 0; e < H; ++e) {
+    const float cs = s_cs[tab + e], sn = s_sn[tab + e];
+    const float x1 = NEOX ? code_at(w1, e) : code_at(w1, 2 * e);
+    const float x2 = NEOX ? code_at(w2, e) : code_at(w1, 2 * e + 1);
+    y[2 * e] = x1 * cs - x2 * sn;
+    y[2 * e + 1] = x2 * cs + x1 * sn;
+    mrot = fmaxf(mrot, fmaxf(fabsf(y[2 * e]), fabsf(y[2 * e + 1])));
+  }
+  float yt[TL > 0 ? TL : 1];
+#pragma unroll
+  for (int e = 0; e < TL; ++e) {
+    yt[e] = code_at(wt, e);
+    mtail = fmaxf(mtail, fabsf(yt[e]));
+  }
+  for (int m = L >> 1; m >= 1; m >>= 1) {
+    mrot = fmaxf(mrot, __shfl_xor(mrot, m));
+    if constexpr (TL > 0) mtail = fmaxf(mtail, __shfl_xor(mtail, m));
+  }
+  const bool keep = KEEP && mrot < 127.5f;
+  const float amax = fmaxf(mrot, mtail);
+  const float inv = keep ? 1.0f : (amax > 0.f && sco > 0.f ? 127.0f * __builtin_amdgcn_rcpf(amax) : 0.f);
+  if (!live) continue;
+  uint32_t c1[NEOX ? H : 2 * H], c2[H];
+#pragma unroll
+  for (int e = 0; e < H; ++e) {
+    if constexpr (NEOX) {
+      c1[e] = code_fma(y[2 * e], inv);
+      c2[e] = code_fma(y[2 * e + 1], inv);
+    } else {
+      c1[2 * e] = code_fma(y[2 * e], inv);
+      c1[2 * e + 1] = code_fma(y[2 * e + 1], inv);
+    }
+  }
+  uint32_t p1[NR], p2[NR];
+  if constexpr (NEOX) {
+    pack_codes<H>(p1, c1);
+    pack_codes<H>(p2, c2);
+    st_n<H>(rp + q * H, p1);
+    st_n<H>(rp + half + q * H, p2);
+  } else {
+    pack_codes<2 * H>(p1, c1);
+    st_n<2 * H>(rp + 2 * q * H, p1);
+  }
+  if (!keep) {
+    if constexpr (TL > 0) {
+      uint32_t ct[TL], pt[NT];
+#pragma unroll
+      for (int e = 0; e < TL; ++e) ct[e] = code_fma(yt[e], inv);
+      pack_codes<TL>(pt, ct);
+      st_n<TL>(rp + r + q * TL, pt);
+    }
+    if (q == 0) *sp = inv > 0.f ? sco * amax * (1.0f / 127.0f) : 0.f;
+  }
   }
 }
 
@@ -389,9 +424,8 @@ __global__ __launch_bounds__(256) void rerotate_int8_lanes_kernel(RerotArgs a) {
 // are exchanged by shuffles.
 __global__ __launch_bounds__(256) void rerotate_int8_kernel(RerotArgs a) {
   __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
-  __shared__ double s_dw[256];
   const int t0 = blockIdx.x * kPT;
-  const float gain = angle_setup(a, t0, s_cs, s_sn, s_dw);
+  const float gain = angle_setup(a, t0, s_cs, s_sn);
   const int half = a.to.rotary_dim / 2;
   const int r = a.to.rotary_dim;
   const int lpr = a.D / 16;               // lanes per row (power of two, <= 64)
@@ -511,9 +545,8 @@ __device__ __forceinline__ void fwht_lane32(float (&x)[32], int q, int L) {
 
 __global__ __launch_bounds__(256) void rerotate_int8_hadamard_kernel(RerotArgs a) {
   __shared__ float s_cs[kPT * 256], s_sn[kPT * 256];
-  __shared__ double s_dw[256];
   const int t0 = blockIdx.x * kPT;
-  const float gain = angle_setup(a, t0, s_cs, s_sn, s_dw);
+  const float gain = angle_setup(a, t0, s_cs, s_sn);
   const int half = a.to.rotary_dim / 2;
   const int r = a.to.rotary_dim;
   const int L = a.D / 32;                // lanes per row (power of two, 2..16)
@@ -731,8 +764,25 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
   a.pos0 = c.pos0;
   a.n_layers = n_layers;
   a.keep_scale = (c.k_int8_mode & ROPEKV_I8_KEEP_SCALE) != 0;
-  dim3 grid((c.capacity + kPT - 1) / kPT);
   const int half = to.rotary_dim / 2;
+  if (half > 256) return hipErrorInvalidValue;
+  // per-pair frequency change and gain, fp64 on the host (the same formulas as the table kernel)
+  a.gain = params_mscale(to) / params_mscale(from);
+  for (int i = 0; i < 256; ++i) a.dw[i] = i < half ? rope_omega(to, i) - rope_omega(from, i) : 0.0;
+  dim3 grid((c.capacity + kPT - 1) / kPT);
+  // one-shot grids: rpb rows per workgroup, layer-major
+  const long layer_rows = (long)c.capacity * c.num_kv_heads;
+  const long max_rpb_chunks = ((layer_rows + 255) / 256) * 256;  // chunks of the smallest rpb, rounded up
+  if (max_rpb_chunks * n_layers > 0x7fffffffL) return hipErrorInvalidValue;
+  a.lg = 1;
+  auto one_shot = [&](int rpb, size_t &shm1) -> dim3 {
+    a.rpb = rpb;
+    a.chunks = (int)((layer_rows + rpb - 1) / rpb);
+    const int np = (rpb - 1) / a.Hkv + 2;  // positions a chunk of rpb rows can span
+    shm1 = (size_t)np * half * 2 * sizeof(float);
+    return dim3((unsigned)((long)a.chunks * ((n_layers + a.lg - 1) / a.lg)));
+  };
+  size_t shm1 = 0;
   switch (c.kv_dtype) {
     case ROPEKV_I8: {
       if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {
@@ -743,33 +793,51 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
       const int L = c.head_dim / 16;
       const int H = (half % L == 0) ? half / L : 0;
       const bool tail_ok = ((c.head_dim - to.rotary_dim) % L) == 0;
-      if (tail_ok && H == 8)
-        hipLaunchKernelGGL(rerotate_int8_lanes_kernel<8>, grid, dim3(256), 0, s, a);
-      else if (tail_ok && H == 4)
-        hipLaunchKernelGGL(rerotate_int8_lanes_kernel<4>, grid, dim3(256), 0, s, a);
-      else if (tail_ok && H == 2)
-        hipLaunchKernelGGL(rerotate_int8_lanes_kernel<2>, grid, dim3(256), 0, s, a);
-      else
+      const bool nx = to.neox != 0, kp = a.keep_scale != 0;
+      if (tail_ok && (H == 8 || H == 4 || H == 2)) {
+        a.lg = kI8Layers;
+        const dim3 g1 = one_shot(kI8Threads / L, shm1);
+        auto pick = [&](auto h) {
+          constexpr int HH = decltype(h)::value;
+          if (nx && kp) hipLaunchKernelGGL((rerotate_int8_lanes_kernel<HH, true, true>), g1, dim3(kI8Threads), shm1, s, a);
+          else if (nx) hipLaunchKernelGGL((rerotate_int8_lanes_kernel<HH, true, false>), g1, dim3(kI8Threads), shm1, s, a);
+          else if (kp) hipLaunchKernelGGL((rerotate_int8_lanes_kernel<HH, false, true>), g1, dim3(kI8Threads), shm1, s, a);
+          else hipLaunchKernelGGL((rerotate_int8_lanes_kernel<HH, false, false>), g1, dim3(kI8Threads), shm1, s, a);
+        };
+        if (H == 8) pick(std::integral_constant<int, 8>());
+        else if (H == 4) pick(std::integral_constant<int, 4>());
+        else pick(std::integral_constant<int, 2>());
+      } else {
         hipLaunchKernelGGL(rerotate_int8_kernel, grid, dim3(256), 0, s, a);
+      }
       break;
     }
     case ROPEKV_F16:
-      if (half % 8 == 0)
-        hipLaunchKernelGGL((rerotate_float_kernel<f16_t, 8>), grid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((rerotate_float_kernel<f16_t, 1>), grid, dim3(256), 0, s, a);
+      if (half % 8 == 0) {
+        const dim3 g1 = one_shot(256 / (half / 8), shm1);
+        hipLaunchKernelGGL((rerotate_float_kernel<f16_t, 8>), g1, dim3(256), shm1, s, a);
+      } else {
+        const dim3 g1 = one_shot(256 / half, shm1);
+        hipLaunchKernelGGL((rerotate_float_kernel<f16_t, 1>), g1, dim3(256), shm1, s, a);
+      }
       break;
     case ROPEKV_BF16:
-      if (half % 8 == 0)
-        hipLaunchKernelGGL((rerotate_float_kernel<bf16_t, 8>), grid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((rerotate_float_kernel<bf16_t, 1>), grid, dim3(256), 0, s, a);
+      if (half % 8 == 0) {
+        const dim3 g1 = one_shot(256 / (half / 8), shm1);
+        hipLaunchKernelGGL((rerotate_float_kernel<bf16_t, 8>), g1, dim3(256), shm1, s, a);
+      } else {
+        const dim3 g1 = one_shot(256 / half, shm1);
+        hipLaunchKernelGGL((rerotate_float_kernel<bf16_t, 1>), g1, dim3(256), shm1, s, a);
+      }
       break;
     case ROPEKV_F32:
-      if (half % 4 == 0)
-        hipLaunchKernelGGL((rerotate_float_kernel<float, 4>), grid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((rerotate_float_kernel<float, 1>), grid, dim3(256), 0, s, a);
+      if (half % 4 == 0) {
+        const dim3 g1 = one_shot(256 / (half / 4), shm1);
+        hipLaunchKernelGGL((rerotate_float_kernel<float, 4>), g1, dim3(256), shm1, s, a);
+      } else {
+        const dim3 g1 = one_shot(256 / half, shm1);
+        hipLaunchKernelGGL((rerotate_float_kernel<float, 1>), g1, dim3(256), shm1, s, a);
+      }
       break;
     default: return hipErrorInvalidValue;
   }
