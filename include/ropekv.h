@@ -240,7 +240,8 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
  * I8 rows are dequantised, turned and requantised with a new per-row scale.
  * cache: CONTIG, kv_dtype F16 / BF16 / F32 / I8, n_layers layers back to back
  * (FP8: ROPEKV_EDTYPE).
- * Angles and their reduction in fp64, the rotation in fp32.
+ * The angle p (w_to,i - w_from,i) and its reduction modulo 2 pi in fp64; cos and sin of the
+ * reduced angle, and the rotation, in fp32 (cos and sin within a few 1e-7 of the exact values).
  * from / to must agree on head_dim, rotary_dim and neox. */
 int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to,
                     const ropekv_kv_cache *cache, int32_t n_layers, ropekv_stream_t stream);
