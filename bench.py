@@ -218,7 +218,7 @@ def main():
         tot_bytes, tot_ms = 0, 0.0
         for layer in range(3):
             r = WL.RingDecode(R, torch, dev, seed=3000 + 10 * layer)
-            ms = timed(torch, r.decode, 20)
+            ms = timed(torch, r.decode, 200, warmup=10)
             rows[f"decode_ring_w4096_b32_layer{layer}"] = {"ms": round(ms, 4),
                                                            "GBps": round(r.decode_bytes() / ms / 1e6, 1)}
             tot_bytes += r.decode_bytes()
@@ -233,7 +233,7 @@ def main():
                     R.shift_keys(scfg, r.desc, flip[0])
                     flip[0] = -flip[0]
 
-                ms_sh = timed(torch, shift, 20)
+                ms_sh = timed(torch, shift, 200, warmup=10)
                 sh_bytes = 2 * r.B * r.Hkv * r.W * r.d * 2  # rotary slice (r = d) of every ring row, read + write
                 rows["shift_keys_ring_w4096_b32"] = {"ms": round(ms_sh, 4), "GBps": round(sh_bytes / ms_sh / 1e6, 1)}
             del r
@@ -259,7 +259,7 @@ def main():
         assert pf.int_state[3].item() == 0
         rows["rope_append_prefill_t8192"] = {"ms": round(ms_app, 4), "GBps": round(pf.append_bytes() / ms_app / 1e6, 1)}
         wd = WL.WindowedPagedDecode(R, torch, dev)
-        ms_wd = timed(torch, wd.decode, 20)
+        ms_wd = timed(torch, wd.decode, 50, warmup=5)
         rows["decode_windowed_b256_h64"] = {"ms": round(ms_wd, 4), "GBps": round(wd.decode_bytes() / ms_wd / 1e6, 1)}
         assert wd.err.item() == 0
         # one mixed step: the prefill chunk and the decode batch on two streams (default priority)
