@@ -641,6 +641,7 @@ struct ShiftArgs {
   const int32_t *head, *count;
   long rows;
   int D;
+  float cs[256], sn[256];  // cos / sin of delta * w_i per rotary pair (fp64, rounded once), set on the host
 };
 
 template <typename T, int PP>
@@ -648,32 +649,27 @@ __global__ __launch_bounds__(256) void shift_kernel(ShiftArgs a) {
   constexpr int EB = sizeof(T);
   constexpr int NB = PP * EB;
   constexpr int NW = (NB + 3) / 4;
-  __shared__ float s_cs[256], s_sn[256];
   const int half = a.p.rotary_dim / 2;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    double sn, cs;
-    sincos((double)a.delta * rope_omega(a.p, i), &sn, &cs);
-    s_cs[i] = (float)cs;
-    s_sn[i] = (float)sn;
-  }
-  __syncthreads();
   const int tpr = half / PP;
   const long items = a.rows * tpr;
   const int neox = a.p.neox;
   char *kb = (char *)a.k;
-  for (long it = (long)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (long)gridDim.x * blockDim.x) {
+  // one item per thread: read, turn and write back right away (the fastest in-place shape here)
+  {
+    const long it = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (it >= items) return;
     const long row = it / tpr;
     const int q = (int)(it - row * tpr);
     if (a.ring) {
       const int slot = (int)(row % a.C);
       const int b = (int)(row / a.C) / a.Hkv;
-      if (slot < a.S) continue;
+      if (slot < a.S) return;
       const int cnt = min(max(a.count[b], 0), a.W);
       int oldest = (a.head[b] - cnt) % a.W;
       if (oldest < 0) oldest += a.W;
       int rel = (slot - a.S - oldest) % a.W;
       if (rel < 0) rel += a.W;
-      if (rel >= cnt) continue;
+      if (rel >= cnt) return;
     }
     const int j0 = q * PP;
     char *p1 = kb + (row * a.D + (neox ? j0 : 2 * j0)) * EB;
@@ -681,8 +677,8 @@ __global__ __launch_bounds__(256) void shift_kernel(ShiftArgs a) {
     uint32_t w1[NW], w2[NW];
     vld<NB>(w1, p1);
     vld<NB>(w2, p2);
-    const float *cs = &s_cs[j0];
-    const float *sn = &s_sn[j0];
+    const float *cs = &a.cs[j0];
+    const float *sn = &a.sn[j0];
     if constexpr (PP % 2 == 0) {
       if (neox) {
 #pragma unroll
@@ -717,9 +713,9 @@ hipError_t launch_shift_t(const ShiftArgs &a, hipStream_t s) {
   const int half = a.p.rotary_dim / 2;
   const bool wide = half % (16 / (int)sizeof(T)) == 0;
   const long items = a.rows * (wide ? half / (16 / (int)sizeof(T)) : half);
-  long blocks = (items + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  if (blocks < 1) blocks = 1;
+  const long blocks = (items + 255) / 256;
+  if (blocks < 1) return hipSuccess;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   if (wide)
     hipLaunchKernelGGL((shift_kernel<T, 16 / sizeof(T)>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
@@ -743,6 +739,13 @@ hipError_t launch_shift_keys(const RopeParams &p, const ropekv_kv_cache &c, int 
   a.count = c.ring_count;
   a.rows = a.ring ? (long)c.batch * c.num_kv_heads * c.capacity : (long)n_layers * c.capacity * c.num_kv_heads;
   a.D = c.head_dim;
+  const int half = p.rotary_dim / 2;
+  if (half > 256) return hipErrorInvalidValue;
+  for (int i = 0; i < 256; ++i) {
+    const double ang = i < half ? (double)delta * rope_omega(p, i) : 0.0;
+    a.cs[i] = (float)cos(ang);
+    a.sn[i] = (float)sin(ang);
+  }
   switch (c.kv_dtype) {
     case ROPEKV_F32: return launch_shift_t<float>(a, s);
     case ROPEKV_BF16: return launch_shift_t<bf16_t>(a, s);
