@@ -16,9 +16,14 @@
 //
 // Per tile and wave:  S^T[16 keys x 16 cols] = K . Q^T on MFMA (the n_rep
 // query heads fill the first columns, the rest are zero), scores scaled into
-// the log2 domain, masked, online softmax per query head; P and the
-// correction factors go through a small per-wave LDS slot to the layout in
-// which each lane holds 4 keys x (d/16) dims of V, and O += P V in fp32.
+// the log2 domain, masked, online softmax per query head.  bf16 caches:
+// O^T += V^T . P^T on MFMA (16x16x16): the S^T fragment a lane holds (keys
+// 4 grp + j, head col) is the B operand once rounded to bf16, and the lane's
+// V pieces (keys 4 grp + j, dims E col .. E col + E - 1, E = d / 16) give, dim
+// by dim, the A operand of E MFMAs (block mt covers dims E i + mt, i = 0..15).  fp32 caches
+// keep P in fp32: P and the correction factors go through a small per-wave LDS
+// slot to the layout in which each lane holds 4 keys x (d/16) dims of V, and
+// O += P V on the VALU.
 #include <stdlib.h>
 
 #include "decode_common.hpp"
@@ -58,6 +63,8 @@ __device__ __forceinline__ f32x4 qk_tile(const uint32_t *kw, const uint32_t *qw)
   return acc;
 }
 
+typedef short short4v __attribute__((ext_vector_type(4)));
+
 // K and V pieces of one tile held by one lane, plus which of its 4 V keys are visible.
 template <int QB, int VB>
 struct TileFrag {
@@ -67,7 +74,7 @@ struct TileFrag {
 };
 
 template <typename T, int D, int NREP>
-__global__ __launch_bounds__(256) void decode_split_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
+__global__ __launch_bounds__(256, 3) void decode_split_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
                                                            float sl2, float *__restrict__ ws, int tps, int splits) {
   using TR = ElemTraits<T>;
   constexpr int QB = (D / 4) * TR::kBytes;   // bytes of a lane's K / Q quarter-row
@@ -155,12 +162,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
     return ok;
   };
 
+  constexpr bool kMfmaPV = sizeof(T) == 2;
   float m_run = kNegBig, l_run = 0.f;
-  float acc[NREP][E];
+  float acc[kMfmaPV ? 1 : NREP][E];      // VALU path: head h, dims col * E + e
+  f32x4 oacc[kMfmaPV ? D / 16 : 1];     // MFMA path: O^T block mt, dims E (4 grp + r) + mt, head col
 #pragma unroll
-  for (int h = 0; h < NREP; ++h)
+  for (int h = 0; h < (kMfmaPV ? 1 : NREP); ++h)
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < (kMfmaPV ? D / 16 : 1); ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   bool bad_tile = false;
   int tile = t_begin + wave;
@@ -193,10 +204,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
       }
       l_run = l_run * corr + psum;
       m_run = m_new;
-      if (col < NREP) {
-        *(float4 *)&s_p[wave][col][4 * grp] = make_float4(pj[0], pj[1], pj[2], pj[3]);
-        if (grp == 0) s_corr[wave][col] = corr;
-      }
       // invisible keys have p = 0, but their rows may hold anything: zero them once
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -204,32 +211,58 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
 #pragma unroll
           for (int w = 0; w < VB / 4; ++w) cur.vw[j][w] = 0u;
         }
-      float vf[4][E];
+      if constexpr (kMfmaPV) {
+        // rescale this lane's column (its head) when its running maximum moved
+        if (__any(corr != 1.f)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < E; ++e) vf[j][e] = TR::get(cur.vw[j], e);
-      wave_lds_sync();
-      // V layout: this lane holds keys 4*grp + j, dims [col*E, col*E + E)
-#pragma unroll
-      for (int h = 0; h < NREP; ++h) {
-        const float ch = s_corr[wave][h];  // the same value in every lane: a uniform branch
-        const float4 ph = *(const float4 *)&s_p[wave][h][4 * grp];
-        if (ch != 1.f) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[h][e] *= ch;
+          for (int mt = 0; mt < D / 16; ++mt) oacc[mt] *= corr;
         }
+        // B = P^T (keys 4 grp + j, head col) in bf16; columns beyond NREP stay zero
+        const float pc[4] = {col < NREP ? pj[0] : 0.f, col < NREP ? pj[1] : 0.f, col < NREP ? pj[2] : 0.f,
+                             col < NREP ? pj[3] : 0.f};
+        const short4v pb = __builtin_bit_cast(short4v, (uint2){pack2_bf16_rne(pc[0], pc[1]), pack2_bf16_rne(pc[2], pc[3])});
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          float a = acc[h][e];
-          a = fmaf(ph.x, vf[0][e], a);
-          a = fmaf(ph.y, vf[1][e], a);
-          a = fmaf(ph.z, vf[2][e], a);
-          a = fmaf(ph.w, vf[3][e], a);
-          acc[h][e] = a;
+        for (int mt = 0; mt < D / 16; ++mt) {
+          // A = V^T rows E i + mt: element mt of this lane's E dims, from each of its 4 keys
+          const int w = mt >> 1;
+          const uint32_t sel = (mt & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two words
+          const uint32_t a01 = __builtin_amdgcn_perm(cur.vw[1][w], cur.vw[0][w], sel);
+          const uint32_t a23 = __builtin_amdgcn_perm(cur.vw[3][w], cur.vw[2][w], sel);
+          const short4v av = __builtin_bit_cast(short4v, (uint2){a01, a23});
+          oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, oacc[mt], 0, 0, 0);
         }
+      } else {
+        if (col < NREP) {
+          *(float4 *)&s_p[wave][col][4 * grp] = make_float4(pj[0], pj[1], pj[2], pj[3]);
+          if (grp == 0) s_corr[wave][col] = corr;
+        }
+        float vf[4][E];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < E; ++e) vf[j][e] = TR::get(cur.vw[j], e);
+        wave_lds_sync();
+        // V layout: this lane holds keys 4*grp + j, dims [col*E, col*E + E)
+#pragma unroll
+        for (int h = 0; h < (kMfmaPV ? 1 : NREP); ++h) {
+          const float ch = s_corr[wave][h];  // the same value in every lane: a uniform branch
+          const float4 ph = *(const float4 *)&s_p[wave][h][4 * grp];
+          if (ch != 1.f) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] *= ch;
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            float a = acc[h][e];
+            a = fmaf(ph.x, vf[0][e], a);
+            a = fmaf(ph.y, vf[1][e], a);
+            a = fmaf(ph.z, vf[2][e], a);
+            a = fmaf(ph.w, vf[3][e], a);
+            acc[h][e] = a;
+          }
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
     }
     cur = nxt;
     cur_ok = nxt_ok;
@@ -239,23 +272,37 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void *__restric
   // merge the 4 lane groups of this wave (they share m per query head)
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-  for (int h = 0; h < NREP; ++h)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float a = acc[h][e];
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      acc[h][e] = a;
-    }
-  if (grp == 0) {
-#pragma unroll
-    for (int h = 0; h < NREP; ++h)
-#pragma unroll
-      for (int e = 0; e < E; ++e) s_acc[wave][h][col * E + e] = acc[h][e];
+  if constexpr (kMfmaPV) {
+    // the MFMAs summed over all 16 keys of each tile: lanes hold distinct (dim, head) entries
     if (col < NREP) {
-      s_m[wave][col] = m_run;
-      s_l[wave][col] = l_run;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_acc[wave][col][E * (4 * grp + r) + mt] = oacc[mt][r];
+      if (grp == 0) {
+        s_m[wave][col] = m_run;
+        s_l[wave][col] = l_run;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < (kMfmaPV ? 1 : NREP); ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float a = acc[h][e];
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        acc[h][e] = a;
+      }
+    if (grp == 0) {
+#pragma unroll
+      for (int h = 0; h < (kMfmaPV ? 1 : NREP); ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s_acc[wave][h][col * E + e] = acc[h][e];
+      if (col < NREP) {
+        s_m[wave][col] = m_run;
+        s_l[wave][col] = l_run;
+      }
     }
   }
   __syncthreads();
