@@ -336,7 +336,7 @@ hipError_t launch_decode_t(const void *q, int batch, const ropekv_kv_cache &c, f
                      pl.splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, NREP>), dim3(c.num_kv_heads * NREP, batch), dim3(128), 0, s, c,
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, NREP>), dim3(c.num_kv_heads, batch), dim3(256), 0, s, c,
                      ws, sinks, out, pl.tiles_per_split, pl.splits);
   return hipGetLastError();
 }

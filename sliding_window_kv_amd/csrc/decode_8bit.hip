@@ -387,7 +387,7 @@ hipError_t launch_decode_8bit_t(const void *q, int batch, const ropekv_kv_cache 
   hipError_t e = c.kv_dtype == ROPEKV_FP8 ? launch_split_8bit<D, NREP, ROPEKV_FP8>(q, batch, c, sl2, ws, pl, s)
                                           : launch_split_8bit<D, NREP, ROPEKV_I8>(q, batch, c, sl2, ws, pl, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<bf16_t, D, NREP>), dim3(c.num_kv_heads * NREP, batch), dim3(128), 0, s,
+  hipLaunchKernelGGL((decode_combine_kernel<bf16_t, D, NREP>), dim3(c.num_kv_heads, batch), dim3(256), 0, s,
                      c, ws, sinks, out, pl.tiles_per_split, pl.splits);
   return hipGetLastError();
 }

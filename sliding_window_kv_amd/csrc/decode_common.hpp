@@ -131,58 +131,51 @@ struct ElemTraits<bf16_t> {
 
 constexpr int kMaxTps = 256;  // tiles per split (block-table entries staged in LDS)
 
-// Merge the split partials of one (sequence, query head): weights exp2(m_s - m)
-// computed once per split, then one coalesced pass over the partial rows.
+// Merge the split partials of one (sequence, KV head) for its n_rep query heads:
+// one wave per query head finds the global maximum and the split weights
+// exp2(m_s - m) (into LDS) and the total weight l, then all threads make one
+// coalesced pass over the partial rows.
 constexpr int kMaxSplits = 1024;
 
 template <typename T, int D, int NREP>
-__global__ __launch_bounds__(128) void decode_combine_kernel(ropekv_kv_cache c, const float *__restrict__ ws,
+__global__ __launch_bounds__(256) void decode_combine_kernel(ropekv_kv_cache c, const float *__restrict__ ws,
                                                              const float *__restrict__ sinks, void *__restrict__ out,
                                                              int tps, int splits) {
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_red[128];
-  const int h = blockIdx.x, b = blockIdx.y;
+  __shared__ float s_w[NREP][kMaxSplits];
+  __shared__ float s_inv[NREP];
+  const int g = blockIdx.x, b = blockIdx.y;
   const int Hkv = c.num_kv_heads;
-  const int g = h / NREP, hh = h % NREP;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const SeqTiles st = seq_tiles(c, b);
   const int used = min(min((st.ntiles + tps - 1) / tps, splits), kMaxSplits);
-  const long obase = ((long)b * Hkv * NREP + h) * D;
-  const float *src = ws + (((long)(b * Hkv + g) * splits) * NREP + hh) * (D + 2);
+  const float *src = ws + ((long)(b * Hkv + g) * splits) * NREP * (D + 2);  // [split][n_rep][D + 2]
   const long sstride = (long)NREP * (D + 2);
-  // global max over splits
-  float m = kNegBig;
-  for (int s = threadIdx.x; s < used; s += blockDim.x) m = fmaxf(m, src[s * sstride + D]);
-  s_red[threadIdx.x] = m;
-  __syncthreads();
-  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) s_red[threadIdx.x] = fmaxf(s_red[threadIdx.x], s_red[threadIdx.x + w]);
-    __syncthreads();
+  for (int hh = wave; hh < NREP; hh += 4) {
+    const float *sh = src + hh * (D + 2);
+    float m = kNegBig;
+    for (int s = lane; s < used; s += 64) m = fmaxf(m, sh[s * sstride + D]);
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    // a learned sink logit joins the normaliser (log2 units like the partial maxima)
+    const float sink2 = sinks ? sinks[g * NREP + hh] * kLog2e : -INFINITY;
+    if (used > 0) m = fmaxf(m, sink2);
+    float l = 0.f;
+    for (int s = lane; s < used; s += 64) {
+      const float w = exp2f(sh[s * sstride + D] - m);
+      s_w[hh][s] = w;
+      l += w * sh[s * sstride + D + 1];
+    }
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    if (sinks && used > 0) l += exp2f(sink2 - m);
+    if (lane == 0) s_inv[hh] = l > 0.f ? 1.f / l : 0.f;
   }
-  m = s_red[0];
-  // a learned sink logit joins the normaliser (log2 units like the partial maxima)
-  const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
-  if (used > 0) m = fmaxf(m, sink2);
   __syncthreads();
-  // per-split weights and the total weight l
-  float l = 0.f;
-  for (int s = threadIdx.x; s < used; s += blockDim.x) {
-    const float w = exp2f(src[s * sstride + D] - m);
-    s_w[s] = w;
-    l += w * src[s * sstride + D + 1];
-  }
-  s_red[threadIdx.x] = l;
-  __syncthreads();
-  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) s_red[threadIdx.x] += s_red[threadIdx.x + w];
-    __syncthreads();
-  }
-  l = s_red[0];
-  if (sinks && used > 0) l += exp2f(sink2 - m);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
+  const long obase = ((long)b * Hkv + g) * NREP * D;
+  for (int idx = threadIdx.x; idx < NREP * D; idx += 256) {
+    const int hh = idx / D, dd = idx - hh * D;
+    const float *sh = src + hh * (D + 2) + dd;
     float a = 0.f;
-    for (int s = 0; s < used; ++s) a = fmaf(s_w[s], src[s * sstride + dd], a);
-    ElemTraits<T>::put(out, obase + dd, a * inv);
+    for (int s = 0; s < used; ++s) a = fmaf(s_w[hh][s], sh[s * sstride], a);
+    ElemTraits<T>::put(out, obase + idx, a * s_inv[hh]);
   }
 }
 
