@@ -250,7 +250,7 @@ def main():
         # ---------------- mixed: 8192-token prefill chunk + 256-sequence windowed decode
         log("setup: mixed prefill + decode")
         pf = WL.Prefill(R, torch, dev)
-        ms = timed(torch, pf.run, 5)
+        ms = timed(torch, pf.run, 30, warmup=10)
         tflops = pf.flops() / (ms * 1e-3) / 1e12
         rows["prefill_t8192_h64_w4096"] = {"ms": round(ms, 4), "TFLOPs": round(tflops, 2),
                                            "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4),
@@ -274,7 +274,7 @@ def main():
             cur.wait_stream(s1)
             cur.wait_stream(s2)
 
-        ms_mix = timed(torch, mixed, 10)
+        ms_mix = timed(torch, mixed, 20, warmup=5)
         rows["mixed_prefill_decode_two_streams"] = {"ms": round(ms_mix, 4), "alone_sum_ms": round(ms + ms_wd, 4),
                                                     "overlap_gain": round((ms + ms_wd) / ms_mix, 3)}
         del pf, wd

@@ -19,7 +19,8 @@ namespace {
 
 constexpr int kPT = 16;  // positions per workgroup
 constexpr int kI8Threads = 256;  // int8 lane kernel: threads per workgroup
-constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup (1: 16.4 ms, 2: 14.4, 4: 15.3 on
+constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup
+constexpr int kHadLayers = 2;    // Hadamard head_dim-128 kernel: layers per workgroup (1: 20.8 ms, 2: 20.0) (1: 16.4 ms, 2: 14.4, 4: 15.3 on
                                  // the 64-layer int8 switch; the float kernel is fastest at 1)
 
 struct RerotArgs {
@@ -631,6 +632,130 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard_kernel(RerotArgs a
   }
 }
 
+// Hadamard-rotated int8 keys at head_dim 128: two lanes per row, lane q holding
+// the 64 consecutive dims [64 q, 64 q + 64), so six butterfly stages of each
+// transform stay in the lane and the seventh is one exchange with the
+// neighbouring lane (a DPP move, no LDS traffic).  Chunked workgroups of 128
+// rows like the lane kernel; the turn runs in code units of H c (the first
+// transform of integer codes is exact in fp32) with the gain in the cos / sin
+// table, and the two unnormalised transforms' factor 1 / 128 goes into the scale.
+// RN: NeoX rotary_dim (64: pairs (e, e + 32) inside lane 0; 128: pair e is dim e
+// of lane 0 with dim e of lane 1); 0: GPT-J, pairs (2i, 2i + 1) of dims < r.
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+}
+
+// unnormalised Walsh-Hadamard transform over 128 dims held as 64 per lane in lane
+// pairs; sgn = +1 on the lower lane, -1 on the upper one
+__device__ __forceinline__ void fwht128(float (&x)[64], float sgn) {
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+      if ((j & h) == 0) {
+        const float u = x[j], v = x[j + h];
+        x[j] = u + v;
+        x[j + h] = u - v;
+      }
+#pragma unroll
+  for (int j = 0; j < 64; ++j) x[j] = fmaf(sgn, x[j], dpp_xor1(x[j]));  // lower: x + p, upper: p - x
+}
+
+template <int RN>
+__global__ __launch_bounds__(256) void rerotate_int8_hadamard128_kernel(RerotArgs a) {
+  extern __shared__ float s_tab[];
+  const int half = a.to.rotary_dim / 2;
+  const int r = a.to.rotary_dim;
+  const ChunkRows c = chunk_rows(a);
+  float *s_cs = s_tab, *s_sn = s_tab + c.np * half;
+  turn_table(a, c.pa, c.np, s_cs, s_sn);
+  const int rr = threadIdx.x >> 1, q = threadIdx.x & 1;
+  // rows past the layer's end turn zeros and store nothing; both lanes of a row share that state
+  const bool live = rr < c.nrows;
+  const int tab = ((c.r0 + (live ? rr : 0)) / a.Hkv - c.pa) * half;
+  const long layer_rows = (long)a.rows_T * a.Hkv;
+  int8_t *rp = (int8_t *)a.k + (c.row0 + rr) * 128 + 64 * q;
+  float *sp = a.scale + c.row0 + rr;
+  const float sgn = q ? -1.f : 1.f;
+  for (int l = 0; l < c.nl; ++l, rp += layer_rows * 128, sp += layer_rows) {
+    uint32_t w[16];
+    float sco = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0u;
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = ((const uint4 *)rp)[i];
+        w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      }
+      sco = *sp;
+    }
+    float x[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) x[e] = code_at(w, e);
+    fwht128(x, sgn);
+    // the turn, 8 pairs at a time: the scheduling fences keep the cos / sin reads of
+    // one group from being hoisted over the others (which would hold 128 more registers)
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (RN == 64) {
+#pragma unroll
+      for (int e0 = 0; e0 < 32; e0 += 8) {
+#pragma unroll
+        for (int e = e0; e < e0 + 8; ++e) {
+          const float cl = s_cs[tab + e], sl = s_sn[tab + e];  // read by both lanes, used by lane 0
+          const float cs = q ? 1.f : cl, sn = q ? 0.f : sl;
+          const float x1 = x[e], x2 = x[e + 32];
+          x[e] = x1 * cs - x2 * sn;
+          x[e + 32] = x2 * cs + x1 * sn;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (RN == 128) {
+#pragma unroll
+      for (int e0 = 0; e0 < 64; e0 += 8) {
+#pragma unroll
+        for (int e = e0; e < e0 + 8; ++e) {
+          const float p = dpp_xor1(x[e]);
+          x[e] = x[e] * s_cs[tab + e] - sgn * p * s_sn[tab + e];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int i0 = 0; i0 < 32; i0 += 8) {
+#pragma unroll
+        for (int i = i0; i < i0 + 8; ++i) {
+          const int d = 64 * q + 2 * i;
+          const bool rot = d < r;
+          const int ti = tab + (rot ? d / 2 : 0);
+          const float cl = s_cs[ti], sl = s_sn[ti];
+          const float cs = rot ? cl : 1.f, sn = rot ? sl : 0.f;
+          const float x1 = x[2 * i], x2 = x[2 * i + 1];
+          x[2 * i] = x1 * cs - x2 * sn;
+          x[2 * i + 1] = x2 * cs + x1 * sn;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    fwht128(x, sgn);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = fmaxf(amax, dpp_xor1(amax));
+    const float inv = amax > 0.f && sco > 0.f ? 127.0f * __builtin_amdgcn_rcpf(amax) : 0.f;
+    uint32_t out[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      out[i] = pack4_codes(code_fma(x[4 * i], inv), code_fma(x[4 * i + 1], inv), code_fma(x[4 * i + 2], inv),
+                           code_fma(x[4 * i + 3], inv));
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ((uint4 *)rp)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+      if (q == 0) *sp = inv > 0.f ? sco * amax * (1.0f / (127.0f * 128.0f)) : 0.f;
+    }
+  }
+}
+
 // Uniform shift of cached keys by delta positions (local-position windows).
 struct ShiftArgs {
   RopeParams p;
@@ -789,7 +914,18 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
   switch (c.kv_dtype) {
     case ROPEKV_I8: {
       if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {
-        hipLaunchKernelGGL(rerotate_int8_hadamard_kernel, grid, dim3(256), 0, s, a);
+        if (c.head_dim == 128 && (!to.neox || to.rotary_dim == 64 || to.rotary_dim == 128)) {
+          a.lg = kHadLayers;
+          const dim3 g1 = one_shot(128, shm1);
+          if (!to.neox)
+            hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<0>, g1, dim3(256), shm1, s, a);
+          else if (to.rotary_dim == 64)
+            hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<64>, g1, dim3(256), shm1, s, a);
+          else
+            hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<128>, g1, dim3(256), shm1, s, a);
+        } else {
+          hipLaunchKernelGGL(rerotate_int8_hadamard_kernel, grid, dim3(256), 0, s, a);
+        }
         break;
       }
       // lane-local pairs when each lane's 16 codes split into whole pairs and tail: H = half / (D / 16)
