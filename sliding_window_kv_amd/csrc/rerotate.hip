@@ -19,9 +19,9 @@ namespace {
 
 constexpr int kPT = 16;  // positions per workgroup
 constexpr int kI8Threads = 256;  // int8 lane kernel: threads per workgroup
-constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup
-constexpr int kHadLayers = 2;    // Hadamard head_dim-128 kernel: layers per workgroup (1: 20.8 ms, 2: 20.0) (1: 16.4 ms, 2: 14.4, 4: 15.3 on
-                                 // the 64-layer int8 switch; the float kernel is fastest at 1)
+constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup (1: 16.4 ms, 2: 14.4, 4: 15.3 on the
+                                 // 64-layer int8 switch; the float kernel is fastest at 1)
+constexpr int kHadLayers = 2;    // Hadamard head_dim-128 kernel: layers per workgroup (1: 20.8 ms, 2: 20.0)
 
 struct RerotArgs {
   RopeParams from, to;
