@@ -88,14 +88,16 @@ def test_keep_scale_rerotate_vs_oracle(env, r, neox):
     assert s1[0, 5, 2] == 0 and np.all(c1[0, 5, 2] == 0)
 
 
-@pytest.mark.parametrize("r,neox", [(64, True), (128, True), (64, False), (48, False)])
-def test_hadamard_rerotate_vs_oracle(env, r, neox):
+@pytest.mark.parametrize("r,neox,d", [(64, True, 128), (128, True, 128), (64, False, 128), (48, False, 128),
+                                      (64, True, 64), (128, True, 256), (64, False, 256)])
+def test_hadamard_rerotate_vs_oracle(env, r, neox, d):
+    # head_dim 128 runs the two-lanes-per-row kernel, other head dims the general one
     R, torch, dev = env
-    L, T, Hkv, d = 2, 48, 4, 128
+    L, T, Hkv = 2, 48, 4
     ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144, neox=neox)
     cb = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.625, orig_max_pos=262144, neox=neox)
     pos0 = 300007
-    c0, s0 = _seeded_rows(torch, dev, (L, T, Hkv, d), 1300 + r, r, 127)
+    c0, s0 = _seeded_rows(torch, dev, (L, T, Hkv, d), 1300 + r + d, r, 127)
     codes = torch.from_numpy(c0).to(dev)
     scale = torch.from_numpy(s0).to(dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
