@@ -380,8 +380,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][TB];
 
   const ropekv_kv_cache &c = a.c;
-  const int g = blockIdx.y;
-  const int t0 = blockIdx.x * BM;
+  // consecutive workgroups (which the dispatcher spreads over the XCDs round-robin) take
+  // consecutive KV heads, so each XCD walks one head's positions in order and the K / V
+  // tiles its workgroups share stay in that XCD's L2
+  const int bid = blockIdx.x + blockIdx.y * gridDim.x;
+  const int g = bid % c.num_kv_heads;
+  const int t0 = (bid / c.num_kv_heads) * BM;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
