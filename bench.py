@@ -5,7 +5,9 @@
 The headline step is one decode step of a Llama-3-8B-shaped full-attention
 layer over a paged cache (batch 64, 32 query / 8 KV heads, d 128, bf16,
 context 32768 per sequence, 16-token blocks, random block table): rope +
-append of each sequence's new token, then split-K decode attention.
+append of each sequence's new token, then split-K decode attention, its
+launches captured once in a HIP graph and replayed (the eager step is
+reported beside it).
 `value` is the decode's algorithmic KV bytes per step time (GB/s).  The other
 hot-path rows (windowed decode at 128k, mixed prefill + decode, K re-rotation
 at a YaRN switch, table build) are timed in the same run and reported under
@@ -154,17 +156,31 @@ def main():
     log("setup: paged decode B=64 ctx=32768")
     wl = WL.PagedDecode(R, torch, dev)
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
+    # the step's launches (seq_len reset, rope + append, split-K decode and merge) captured once
+    # in a HIP graph and replayed, as a serving loop would; the eager step is timed too
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
         wl.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wl.step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(args.steps):
-        wl.step()
+        graph.replay()
     b.record()
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / args.steps
+    assert wl.err.item() == 0, f"device error word {wl.err.item()}"
+    ms_step_eager = timed(torch, wl.step, args.steps, warmup=args.warmup)
     assert wl.err.item() == 0, f"device error word {wl.err.item()}"
     dec_bytes = wl.decode_bytes()
     value = dec_bytes / (ms_step * 1e-3) / 1e9
@@ -179,6 +195,8 @@ def main():
                 "algorithmic_bytes_per_launch": dec_bytes}
     rows["decode_b64_ctx32768"] = {"ms": round(ms_dec, 4), "GBps": round(achieved, 1),
                                    "frac_hbm": round(achieved / HBM_PEAK_GBS, 4)}
+    rows["decode_step_b64_graph"] = {"ms": round(ms_step, 4), "GBps": round(value, 1)}
+    rows["decode_step_b64_eager"] = {"ms": round(ms_step_eager, 4), "GBps": round(dec_bytes / ms_step_eager / 1e6, 1)}
     rows["rope_append_b64"] = {"ms": round(ms_app, 4)}
     sinks = torch.linspace(-2.0, 6.0, wl.Hq, device=dev)
     ms_dsk = timed(torch, lambda: R.decode_attn(wl.q, wl.B, wl.Hq, wl.desc, 0.0, wl.out, wl.ws, wl.ws_bytes,
@@ -337,7 +355,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "paged decode step (rope+append, split-K decode), Llama-3-8B-shaped layer: "
+        "config": {"workload": "paged decode step (rope+append, split-K decode; launches replayed from a HIP graph), "
+                               "Llama-3-8B-shaped layer: "
                                "batch 64, 32 q / 8 kv heads, d 128, context 32768, 16-token blocks, random table",
                    "global_batch": 64, "seq_len": 32768, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
