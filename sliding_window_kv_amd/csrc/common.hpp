@@ -152,6 +152,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
 
+// max / sum of a value over lanes l and l ^ 16 (l ^ 32) by the gfx950 lane swaps, no LDS
+// round trip: with the same value in both operands the two results are v[l] and v[l ^ 16]
+// (v[l ^ 32]) in some order, which is all a symmetric reduction needs.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Direct global -> LDS loads: the 64 lanes' N-byte reads land at LDS [m0 + N * lane]
 // (m0 = the wave-uniform LDS base).  Issued as inline assembly so the compiler adds
 // no waits of its own on them: callers wait with wait_vmcnt before reading the LDS

@@ -467,8 +467,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     for (int n = 0; n < NI; ++n) dma16(vsrc[n], &v_lds[buf][(4 * n + wave) * 1024]);
   };
 
-  float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
+  float m_run[2] = {kNegBig, kNegBig};
   f32x4 o[2][D / 16];
+  // row sums of P on the MFMA: a block of ones as the A operand gives sum_k P[k][row] in every
+  // element of lsum (the same bf16 P as the numerator)
+  f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const short8 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80};
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -545,8 +549,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[rt][st][j]);
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
+      mx = max_xor32(max_xor16(mx));
       const float m_tile = mx * a.sl2;  // sl2 > 0: the max commutes with the scale; -inf if all masked
       corr[rt] = 1.f;
       if (m_tile > m_run[rt] + kLazy) {
@@ -554,22 +557,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         m_run[rt] = m_tile;
         raised = true;
       }
-      float ps = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[rt][st][j], a.sl2, -m_run[rt]));
-          sc[rt][st][j] = p;
-          ps += p;
-        }
-      l_run[rt] = l_run[rt] * corr[rt] + ps;
+        for (int j = 0; j < 4; ++j) sc[rt][st][j] = __builtin_amdgcn_exp2f(fmaf(sc[rt][st][j], a.sl2, -m_run[rt]));
     }
     if (__any(raised)) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) o[rt][mt] *= corr[rt];
+        lsum[rt] *= corr[rt];
+      }
     }
 
     __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority: the SIMD keeps issuing them
@@ -582,6 +581,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         const f32x4 p0 = sc[rt][2 * u], p1 = sc[rt][2 * u + 1];
         pb[rt] = u32x4{pack_bf16(p0[0], p0[1]), pack_bf16(p0[2], p0[3]), pack_bf16(p1[0], p1[1]),
                        pack_bf16(p1[2], p1[3])};
+        lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones),
+                                                           __builtin_bit_cast(bf16x8, pb[rt]), lsum[rt], 0, 0, 0);
       }
       // lane (grp, col) addresses V[32u + 4grp + col/4 (+16)][16 mt + 4 (col % 4)]
       const int vrow = 32 * u + 4 * grp + (col >> 2);
@@ -610,9 +611,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // ---- normalise and store: lane holds O^T[16 mt + 4 grp + j][its row]
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float l = l_run[rt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = lsum[rt][0];
     float inv = l > 0.f ? 1.f / l : 0.f;
     if (a.sinks) {
       const float sink2 = a.sinks[head[rt]] * kLog2e;
