@@ -337,6 +337,40 @@ def test_decode_paged_random_table(env, n_rep, d):
         assert_bf16_close(got[b], ref)
 
 
+@pytest.mark.parametrize("B,Hkv,n", [(1, 8, 19999), (2, 2, 5003)])
+def test_decode_paged_few_long_sequences(env, B, Hkv, n):
+    # a small batch spreads each sequence over many splits (the plan keeps ~512 workgroups):
+    # 64 splits of 20 tiles for one sequence of 8 KV heads, up to 128 splits for 2 x 2
+    R, torch, dev = env
+    n_rep, d = 4, 128
+    Hq = Hkv * n_rep
+    max_blocks = (n + 15) // 16 + 3
+    num_blocks = B * max_blocks + 5
+    table = synth.block_table_permutation(B, max_blocks, num_blocks, 51 + n)
+    cache = DevPaged(R, torch, dev, torch.bfloat16, B, Hkv, d, 0, 0, table, num_blocks)
+    _fill(torch, cache.k, 52)
+    _fill(torch, cache.v, 53)
+    lens = [n - 7 * b for b in range(B)]
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev), 54)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    kp = to_np64(cache.k)
+    vp = to_np64(cache.v)
+    qq = to_np64(q)
+    got = to_np64(out)
+    for b, nb in enumerate(lens):
+        rows = np.array([table[b, j // 16] for j in range(nb)])
+        slots = np.arange(nb) % 16
+        K = kp[rows, :, slots]
+        V = vp[rows, :, slots]
+        ref = O.decode_attention(qq[b], lambda j: K[j], lambda j: V[j], nb, 0, 0, Hkv)
+        assert_bf16_close(got[b], ref)
+
+
 def test_decode_paged_window_with_null_blocks(env):
     # sink + window paged decode where every block below the window edge is null (-1):
     # the kernel must never touch them and must still see the sinks in block 0.
