@@ -467,6 +467,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     for (int n = 0; n < NI; ++n) dma16(vsrc[n], &v_lds[buf][(4 * n + wave) * 1024]);
   };
 
+  // byte offsets of this lane's transposing V reads, block mt of rows 4 grp + col / 4 (+16, +32:
+  // the same swizzle, so those are immediates): chunk (2 mt + (col % 4) / 2) ^ swizzle
+  int voff[D / 16];
+  {
+    const int vrow = 4 * grp + (col >> 2);
+    const int vx = vswz<D>(vrow);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+      voff[mt] = (vrow * CPR + ((2 * mt + ((col & 3) >> 1)) ^ vx)) * 16 + (col & 1) * 8;
+  }
   float m_run[2] = {kNegBig, kNegBig};
   f32x4 o[2][D / 16];
   // row sums of P on the MFMA: a block of ones as the A operand gives sum_k P[k][row] in every
@@ -585,16 +595,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
                                                            __builtin_bit_cast(bf16x8, pb[rt]), lsum[rt], 0, 0, 0);
       }
       // lane (grp, col) addresses V[32u + 4grp + col/4 (+16)][16 mt + 4 (col % 4)]
-      const int vrow = 32 * u + 4 * grp + (col >> 2);
-      const int vx = vswz<D>(vrow);  // the same for vrow + 16
-      const int half = (col & 1) * 8;
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt) {
-        const int ch = (2 * mt + ((col & 3) >> 1)) ^ vx;
         typedef __attribute__((address_space(3))) short4v lds_s4;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vl + (vrow * CPR + ch) * 16 + half));
-        const short4v hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vl + ((vrow + 16) * CPR + ch) * 16 + half));
+        const uint8_t *vp = vl + voff[mt] + 32 * u * CPR * 16;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)vp);
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vp + 16 * CPR * 16));
         const short8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
