@@ -177,6 +177,13 @@ __device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0)
                    : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base (an SGPR pair) and a 32-bit per-lane byte offset:
+// no per-lane address arithmetic when only the base moves.
+__device__ __forceinline__ void dma16_so(const void *sbase, uint32_t voff, const void *lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                   : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void *gsrc, const void *lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(m0)

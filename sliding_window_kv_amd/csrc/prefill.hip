@@ -430,6 +430,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     vch_n[n] = ((p % CPR) ^ vswz<D>(row_n[n])) * 16;
   }
   const long chunk_row_bytes = (long)c.num_kv_heads * D * 2;  // one position of the chunk's k / v
+  // per-lane byte offsets of the direct loads within a tile of the chunk's k / v (fast path)
+  uint32_t koff_n[NI], voff_n[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    koff_n[n] = (uint32_t)(row_n[n] * chunk_row_bytes + kch_n[n]);
+    voff_n[n] = (uint32_t)(row_n[n] * chunk_row_bytes + vch_n[n]);
+  }
   bool lost = false;
   auto issue = [&](int kt, int buf) {
     const int kb = kt < nst ? kt : first + (kt - nst);
@@ -437,12 +444,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     if (j0 >= a.pos0 && j0 + kBN <= a.pos0 + a.T) {
       // every key of the tile is in the chunk: rows are (j - pos0, g) of k and v
       const long tb = (long)(j0 - a.pos0) * chunk_row_bytes + (long)g * D * 2;
+      const char *kt = (const char *)a.k + tb;  // wave-uniform tile bases
+      const char *vt = (const char *)a.v + tb;
 #pragma unroll
-      for (int n = 0; n < NI; ++n)
-        dma16((const char *)a.k + tb + row_n[n] * chunk_row_bytes + kch_n[n], &k_lds[buf][(4 * n + wave) * 1024]);
+      for (int n = 0; n < NI; ++n) dma16_so(kt, koff_n[n], &k_lds[buf][(4 * n + wave) * 1024]);
 #pragma unroll
-      for (int n = 0; n < NI; ++n)
-        dma16((const char *)a.v + tb + row_n[n] * chunk_row_bytes + vch_n[n], &v_lds[buf][(4 * n + wave) * 1024]);
+      for (int n = 0; n < NI; ++n) dma16_so(vt, voff_n[n], &v_lds[buf][(4 * n + wave) * 1024]);
       return;
     }
     const char *ksrc[NI];
