@@ -119,6 +119,51 @@ def cpu_baseline(R, torch, wl, budget_s=12.0):
     }
 
 
+def rerotate_rows(R, torch, WL, dev, rows, kinds):
+    """K re-rotation at a YaRN switch (1 <-> 1.125), 64 layers x 524288 positions x 8 heads."""
+    for kind in kinds:
+        log(f"setup: rerotate {kind}")
+        rr = WL.Rerotate(R, torch, dev, kind=kind)
+        flip = [1.0, 1.125]
+
+        def one(rr=rr, flip=flip):
+            rr.run(flip[0], flip[1])
+            flip.reverse()
+
+        kept = None
+        if kind == "i8_keep":
+            before = rr.scale.clone()
+            one()
+            torch.cuda.synchronize()
+            kept = round(float((rr.scale == before).float().mean().item()), 4)  # rows that kept their scale
+            del before
+        ms = timed(torch, one, 4, warmup=1)
+        rows[f"rerotate_{kind}_L64_T524288"] = {"ms": round(ms, 3), "GBps": round(rr.bytes() / ms / 1e6, 1),
+                                                "frac_hbm": round(rr.bytes() / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                                "algorithmic_bytes": rr.bytes()}
+        if kept is not None:
+            rows[f"rerotate_{kind}_L64_T524288"]["rows_kept_scale"] = kept
+        if kind == "f16":
+            tcfg = rr.cfg(2.0)
+            tab = torch.empty(524288, 64, dtype=torch.float32, device=dev)
+            rows["table_build_524288x64"] = {"ms": round(timed(torch, lambda: R.build_table(tcfg, 524288, tab), 5), 4)}
+            del tab
+        assert rr.err.item() == 0
+        del rr
+        torch.cuda.empty_cache()
+
+
+def prefill_rows(R, torch, WL, dev, rows):
+    """The 8192-token chunk over the sink(4) + window(4096) mask, 64 q / 8 kv heads; returns the workload."""
+    pf = WL.Prefill(R, torch, dev)
+    ms = timed(torch, pf.run, 30, warmup=10)
+    tflops = pf.flops() / (ms * 1e-3) / 1e12
+    rows["prefill_t8192_h64_w4096"] = {"ms": round(ms, 4), "TFLOPs": round(tflops, 2),
+                                       "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4),
+                                       "algorithmic_flops": pf.flops()}
+    return pf, ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +171,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="run only these rows and print them (for counter runs): prefill, rerotate_f16, "
+                         "rerotate_i8, rerotate_i8_keep, rerotate_i8_hadamard (comma separated)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 2 GiB device copy 5 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -151,6 +199,16 @@ def main():
 
     dev = torch.device("cuda:0")
     rows = {}
+    if args.only:
+        for part in args.only.split(","):
+            if part == "prefill":
+                prefill_rows(R, torch, WL, dev, rows)
+            elif part.startswith("rerotate_"):
+                rerotate_rows(R, torch, WL, dev, rows, (part[len("rerotate_"):],))
+            else:
+                raise SystemExit(f"unknown row {part!r}")
+        print(json.dumps({"rows": rows}))
+        return
 
     # ---------------- headline: paged decode step, batch 64 x 32768
     log("setup: paged decode B=64 ctx=32768")
@@ -267,12 +325,7 @@ def main():
 
         # ---------------- mixed: 8192-token prefill chunk + 256-sequence windowed decode
         log("setup: mixed prefill + decode")
-        pf = WL.Prefill(R, torch, dev)
-        ms = timed(torch, pf.run, 30, warmup=10)
-        tflops = pf.flops() / (ms * 1e-3) / 1e12
-        rows["prefill_t8192_h64_w4096"] = {"ms": round(ms, 4), "TFLOPs": round(tflops, 2),
-                                           "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4),
-                                           "algorithmic_flops": pf.flops()}
+        pf, ms = prefill_rows(R, torch, WL, dev, rows)
         ms_app = timed(torch, pf.append, 10)
         assert pf.int_state[3].item() == 0
         rows["rope_append_prefill_t8192"] = {"ms": round(ms_app, 4), "GBps": round(pf.append_bytes() / ms_app / 1e6, 1)}
@@ -299,35 +352,7 @@ def main():
         torch.cuda.empty_cache()
 
         # ---------------- K re-rotation at a YaRN switch, 64 layers x 524288 x 8 heads
-        for kind in ("f16", "i8", "i8_keep", "i8_hadamard"):
-            log(f"setup: rerotate {kind}")
-            rr = WL.Rerotate(R, torch, dev, kind=kind)
-            flip = [1.0, 1.125]
-
-            def one(rr=rr, flip=flip):
-                rr.run(flip[0], flip[1])
-                flip.reverse()
-
-            kept = None
-            if kind == "i8_keep":
-                before = rr.scale.clone()
-                one()
-                torch.cuda.synchronize()
-                kept = round(float((rr.scale == before).float().mean().item()), 4)  # rows that kept their scale
-                del before
-            ms = timed(torch, one, 4, warmup=1)
-            rows[f"rerotate_{kind}_L64_T524288"] = {"ms": round(ms, 3), "GBps": round(rr.bytes() / ms / 1e6, 1),
-                                                    "frac_hbm": round(rr.bytes() / ms / 1e6 / HBM_PEAK_GBS, 4)}
-            if kept is not None:
-                rows[f"rerotate_{kind}_L64_T524288"]["rows_kept_scale"] = kept
-            if kind == "f16":
-                tcfg = rr.cfg(2.0)
-                tab = torch.empty(524288, 64, dtype=torch.float32, device=dev)
-                rows["table_build_524288x64"] = {"ms": round(timed(torch, lambda: R.build_table(tcfg, 524288, tab),
-                                                                   5), 4)}
-                del tab
-            del rr
-            torch.cuda.empty_cache()
+        rerotate_rows(R, torch, WL, dev, rows, ("f16", "i8", "i8_keep", "i8_hadamard"))
 
     if not args.no_extras:
         # practical HBM ceilings of plain streams on this device (torch's own elementwise kernels):
