@@ -346,10 +346,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 // Same workgroup and tile walk as above.  K and V tiles are copied into LDS
 // with direct loads (no staging registers, the next tile in flight while the
 // current one is computed) in rows of D / 8 16-byte chunks, chunk c of row r
-// stored at c ^ kswz(r) (K) or c ^ vswz(r) (V).  The swizzles make the MFMA
-// operand reads conflict-free: the 16 lanes reading a K chunk of 16 different
-// rows hit 16 different 16-byte bank groups, and the 32 lanes of a transposing
-// V read (8 rows x 4 column groups) hit 32 different 8-byte bank slots.
+// stored at c ^ kswz(r) (K) or c ^ vswz(r) (V).  The 32 lanes of a transposing
+// V read (8 rows x 4 column groups) hit 32 different 8-byte bank slots and
+// time as fast as linear reads.  The K swizzle gives the 16 lanes reading one
+// chunk column 16 different 16-byte bank groups, yet on gfx950 those 16-byte
+// reads still meet two-way bank conflicts (the lane grouping of such reads is
+// not documented; counters show half of the K read cycles as conflicts).  A
+// conflict-free order exists (bit reversal of r mod 16, found by timing XOR
+// patterns) but ran this kernel 2 % slower, as LDS bandwidth is not what
+// bounds it, so the simpler swizzle stays.
 //
 // The running maximum is raised only when a tile's maximum exceeds it by more
 // than kLazy (log2 units): in between, p = exp2(s - m) stays below 2^kLazy,
