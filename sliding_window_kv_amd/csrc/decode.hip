@@ -74,7 +74,7 @@ struct TileFrag {
 };
 
 template <typename T, int D, int NREP>
-__global__ __launch_bounds__(256, 3) void decode_split_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void decode_split_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
                                                            float sl2, float *__restrict__ ws, int tps, int splits) {
   using TR = ElemTraits<T>;
   constexpr int QB = (D / 4) * TR::kBytes;   // bytes of a lane's K / Q quarter-row
