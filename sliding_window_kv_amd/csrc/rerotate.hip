@@ -21,7 +21,7 @@ constexpr int kPT = 16;  // positions per workgroup
 constexpr int kI8Threads = 256;  // int8 lane kernel: threads per workgroup
 constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup (1: 16.4 ms, 2: 14.4, 4: 15.3 on the
                                  // 64-layer int8 switch; the float kernel is fastest at 1)
-constexpr int kHadLayers = 2;    // Hadamard head_dim-128 kernel: layers per workgroup (1: 20.8 ms, 2: 20.0)
+constexpr int kHadLayers = 4;    // Hadamard head_dim-128 kernels: layers per workgroup (r 64: 1: 16.2 ms, 2: 15.7, 4: 15.2, 8: 15.1)
 
 struct RerotArgs {
   RopeParams from, to;
@@ -639,8 +639,9 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard_kernel(RerotArgs a
 // rows like the lane kernel; the turn runs in code units of H c (the first
 // transform of integer codes is exact in fp32) with the gain in the cos / sin
 // table, and the two unnormalised transforms' factor 1 / 128 goes into the scale.
-// RN: NeoX rotary_dim (64: pairs (e, e + 32) inside lane 0; 128: pair e is dim e
-// of lane 0 with dim e of lane 1); 0: GPT-J, pairs (2i, 2i + 1) of dims < r.
+// RN: 128 for NeoX over all dims (pair e is dim e of lane 0 with dim e of lane 1);
+// 0: GPT-J, pairs (2i, 2i + 1) of dims < r.  NeoX with r = 64 has a kernel of its own
+// below that transforms half rows.
 __device__ __forceinline__ float dpp_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
 }
@@ -697,20 +698,7 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_kernel(RerotArg
     // the turn, 8 pairs at a time: the scheduling fences keep the cos / sin reads of
     // one group from being hoisted over the others (which would hold 128 more registers)
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (RN == 64) {
-#pragma unroll
-      for (int e0 = 0; e0 < 32; e0 += 8) {
-#pragma unroll
-        for (int e = e0; e < e0 + 8; ++e) {
-          const float cl = s_cs[tab + e], sl = s_sn[tab + e];  // read by both lanes, used by lane 0
-          const float cs = q ? 1.f : cl, sn = q ? 0.f : sl;
-          const float x1 = x[e], x2 = x[e + 32];
-          x[e] = x1 * cs - x2 * sn;
-          x[e + 32] = x2 * cs + x1 * sn;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else if constexpr (RN == 128) {
+    if constexpr (RN == 128) {
 #pragma unroll
       for (int e0 = 0; e0 < 64; e0 += 8) {
 #pragma unroll
@@ -751,6 +739,121 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_kernel(RerotArg
     if (live) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ((uint4 *)rp)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+      if (q == 0) *sp = inv > 0.f ? sco * amax * (1.0f / (127.0f * 128.0f)) : 0.f;
+    }
+  }
+}
+
+// Hadamard-rotated int8 keys at head_dim 128 whose rotary dims lie in the leading 64
+// (NeoX with r = 64: pairs (e, e + 32); GPT-J with r <= 64: pairs (2i, 2i + 1) of
+// dims < r).  With H the unnormalised Sylvester-ordered transform of
+// order 128 (H = [[H64, H64], [H64, -H64]]) the key in code units is x = H c, and
+// the turn R (gain included) moves x[0..63] only, so
+//   H R H c = 128 c + H [D; 0],  D = (R - I) x[0..63],  x[0..63] = H64 (c_lo + c_hi),
+//   H [D; 0] = [H64 D; H64 D]    (c_lo, c_hi: codes 0..63 and 64..127).
+// Two 64-point transforms on half a row replace two 128-point ones on the whole row.
+// Lane q of a row's pair holds codes 32 q .. 32 q + 31 of each half, so its half of
+// u = c_lo + c_hi is lane-local, the 64-point transforms run five stages in the lane
+// and the top one across the pair, NeoX partners x[e] and x[e + 32] sit at the same
+// index of the two lanes (GPT-J partners share a lane), and 128 c + H64 D needs only
+// the lane's own indices.  The
+// factor 1 / 128 of the two transforms goes into the scale as in the kernel above.
+__device__ __forceinline__ void fwht64_pair(float (&x)[32], float sgn) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if ((j & h) == 0) {
+        const float u = x[j], v = x[j + h];
+        x[j] = u + v;
+        x[j + h] = u - v;
+      }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = fmaf(sgn, x[j], dpp_xor1(x[j]));  // lower: x + p, upper: p - x
+}
+
+template <bool NEOX>
+__global__ __launch_bounds__(256) void rerotate_int8_hadamard128_r64_kernel(RerotArgs a) {
+  extern __shared__ float s_tab[];
+  const int half = a.to.rotary_dim / 2;
+  const int r = a.to.rotary_dim;
+  const ChunkRows c = chunk_rows(a);
+  float *s_cs = s_tab, *s_sn = s_tab + c.np * half;
+  turn_table(a, c.pa, c.np, s_cs, s_sn);
+  const int rr = threadIdx.x >> 1, q = threadIdx.x & 1;
+  // rows past the layer's end turn zeros and store nothing; both lanes of a row share that state
+  const bool live = rr < c.nrows;
+  const int tab = ((c.r0 + (live ? rr : 0)) / a.Hkv - c.pa) * half;
+  const long layer_rows = (long)a.rows_T * a.Hkv;
+  int8_t *rp = (int8_t *)a.k + (c.row0 + rr) * 128 + 32 * q;  // + 64: the same lane's upper half
+  float *sp = a.scale + c.row0 + rr;
+  const float sgn = q ? -1.f : 1.f;
+  for (int l = 0; l < c.nl; ++l, rp += layer_rows * 128, sp += layer_rows) {
+    uint32_t w[16];  // words 0..7: codes 32 q + (0..31); 8..15: codes 64 + 32 q + (0..31)
+    float sco = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0u;
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = ((const uint4 *)(rp + 64 * (i >> 1)))[i & 1];
+        w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      }
+      sco = *sp;
+    }
+    float x[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = code_at(w, e) + code_at(w, 32 + e);
+    fwht64_pair(x, sgn);  // x[e] = x[32 q + e] of H64 (c_lo + c_hi): integers, exact
+    // D = (R - I) x
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEOX) {  // lane 0 holds the first of each pair, lane 1 the second
+#pragma unroll
+      for (int e0 = 0; e0 < 32; e0 += 8) {
+#pragma unroll
+        for (int e = e0; e < e0 + 8; ++e) {
+          const float cs = s_cs[tab + e], sl = s_sn[tab + e];
+          const float sn = q ? sl : -sl;
+          const float p = dpp_xor1(x[e]);
+          x[e] = fmaf(p, sn, fmaf(x[e], cs, -x[e]));  // lane 0: x1 (cs - 1) - x2 sn; lane 1: x2 (cs - 1) + x1 sn
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {  // pair (2i, 2i + 1) = lane-local (e, e + 1) at dim 32 q + e; no turn from dim r on
+#pragma unroll
+      for (int e0 = 0; e0 < 32; e0 += 8) {
+#pragma unroll
+        for (int e = e0; e < e0 + 8; e += 2) {
+          const int d = 32 * q + e;
+          const bool rot = d < r;
+          const int ti = tab + (rot ? d / 2 : 0);
+          const float cl = s_cs[ti], sl = s_sn[ti];
+          const float cs = rot ? cl : 1.f, sn = rot ? sl : 0.f;
+          const float x1 = x[e], x2 = x[e + 1];
+          x[e] = fmaf(-x2, sn, fmaf(x1, cs, -x1));
+          x[e + 1] = fmaf(x1, sn, fmaf(x2, cs, -x2));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    fwht64_pair(x, sgn);  // x[e] = (H64 D)[32 q + e]
+    float y[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) y[e] = fmaf(code_at(w, e), 128.f, x[e & 31]);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    amax = fmaxf(amax, dpp_xor1(amax));
+    const float inv = amax > 0.f && sco > 0.f ? 127.0f * __builtin_amdgcn_rcpf(amax) : 0.f;
+    uint32_t out[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      out[i] = pack4_codes(code_fma(y[4 * i], inv), code_fma(y[4 * i + 1], inv), code_fma(y[4 * i + 2], inv),
+                           code_fma(y[4 * i + 3], inv));
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ((uint4 *)(rp + 64 * (i >> 1)))[i & 1] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
       if (q == 0) *sp = inv > 0.f ? sco * amax * (1.0f / (127.0f * 128.0f)) : 0.f;
     }
   }
@@ -917,10 +1020,12 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
         if (c.head_dim == 128 && (!to.neox || to.rotary_dim == 64 || to.rotary_dim == 128)) {
           a.lg = kHadLayers;
           const dim3 g1 = one_shot(128, shm1);
-          if (!to.neox)
+          if (!to.neox && to.rotary_dim <= 64)
+            hipLaunchKernelGGL(rerotate_int8_hadamard128_r64_kernel<false>, g1, dim3(256), shm1, s, a);
+          else if (!to.neox)
             hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<0>, g1, dim3(256), shm1, s, a);
           else if (to.rotary_dim == 64)
-            hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<64>, g1, dim3(256), shm1, s, a);
+            hipLaunchKernelGGL(rerotate_int8_hadamard128_r64_kernel<true>, g1, dim3(256), shm1, s, a);
           else
             hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<128>, g1, dim3(256), shm1, s, a);
         } else {
