@@ -140,7 +140,7 @@ def test_prefill_t8192_sampled_rows(env):
         assert_bf16_close(out[t], ref)
 
 
-@pytest.mark.parametrize("kind", ["f16", "i8"])
+@pytest.mark.parametrize("kind", ["f16", "i8", "i8_keep", "i8_hadamard"])
 def test_rerotate_l64_t524288_sampled_rows(env, kind):
     R, torch, dev, WL = env
     rr = WL.Rerotate(R, torch, dev, kind=kind)
@@ -148,7 +148,7 @@ def test_rerotate_l64_t524288_sampled_rows(env, kind):
     flat = rr.k.view(-1, rr.d)
     idx = torch.from_numpy(rows).to(dev)
     before = flat[idx].cpu().numpy()
-    sc_before = rr.scale.view(-1)[idx].cpu().numpy() if kind == "i8" else None
+    sc_before = rr.scale.view(-1)[idx].cpu().numpy() if kind != "f16" else None
     rr.run(1.0, 1.125)
     torch.cuda.synchronize()
     after = flat[idx].cpu().numpy()
@@ -159,8 +159,21 @@ def test_rerotate_l64_t524288_sampled_rows(env, kind):
         unit = np.maximum(np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64), 1e-6)
         assert np.all(np.abs(after.astype(np.float64) - ref) <= unit)
         assert np.array_equal(after[:, rr.r:], before[:, rr.r:])
+    elif kind == "i8_keep":
+        # the keep decision is taken in fp32 on both sides: it may differ only for a row whose largest
+        # turned code sits at the rounding edge, so nearly all rows agree
+        codes, scale, over = O.rerotate_int8_keep_scale_rows(before, sc_before, positions, ca, cb)
+        sc_after = rr.scale.view(-1)[idx].cpu().numpy()
+        kept = sc_after == sc_before
+        agree = kept == ~over
+        assert agree.mean() > 0.99 and kept[agree].any()
+        assert np.array_equal(after[agree & kept, rr.r:], before[agree & kept, rr.r:])  # tail bitwise
+        np.testing.assert_allclose(sc_after[agree], scale[agree], rtol=1e-5)
+        assert np.max(np.abs(after[agree].astype(np.int32) - codes[agree].astype(np.int32))) <= 1
+        assert np.mean(after[agree] != codes[agree]) < 0.01
     else:
-        codes, scale = O.rerotate_int8_rows(before, sc_before, positions, ca, cb)
+        rot = O.rerotate_int8_hadamard_rows if kind == "i8_hadamard" else O.rerotate_int8_rows
+        codes, scale = rot(before, sc_before, positions, ca, cb)
         sc_after = rr.scale.view(-1)[idx].cpu().numpy()
         np.testing.assert_allclose(sc_after, scale, rtol=1e-5)
         # codes decided in fp32 on both sides from rotations done in different precision: off by at most one
