@@ -416,10 +416,6 @@ DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c) {
   splits = max(splits, (max_tiles + kMaxTps - 1) / kMaxTps);
   splits = min(splits, max_tiles);
   int tps = (max_tiles + splits - 1) / splits;
-  if (const char *e = getenv("ROPEKV_DECODE_TPS")) {
-    const int v = atoi(e);
-    if (v >= 1 && v <= kMaxTps) tps = v;
-  }
   while ((max_tiles + tps - 1) / tps > kMaxSplits && tps < kMaxTps) tps = min(2 * tps, kMaxTps);
   pl.max_tiles = max_tiles;
   pl.tiles_per_split = tps;
