@@ -86,7 +86,7 @@ def test_table_factor_one_is_plain(env):
     assert torch.equal(a, b)
 
 
-# ------------------------------------------------------------------ ring: config-1 end to end
+# ------------------------------------------------------------------ ring: 16-slot cache (S 4 + W 12) end to end
 
 def _ring_end_to_end(env, neox, dtype_name, chunks):
     R, torch, dev = env
@@ -180,7 +180,7 @@ def _ring_end_to_end(env, neox, dtype_name, chunks):
 
 
 @pytest.mark.parametrize("neox", [True, False])
-def test_ring_config1_prefill_then_decode(env, neox):
+def test_ring_c16_prefill_then_decode(env, neox):
     # the tiny fp32 case: prefill 0..63, then 16 decode steps
     _ring_end_to_end(env, neox, "f32", [64] + [1] * 16)
 
@@ -289,7 +289,7 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
 
 
 @pytest.mark.parametrize("S,W", [(4, 12), (0, 20), (4, 0), (3, 33)])
-def test_paged_config1_shape(env, S, W):
+def test_paged_small_shapes(env, S, W):
     _paged_end_to_end(env, "f32", S, W, B=3, Hq=8, Hkv=4, d=64, rounds=14, seed=7 + S + W)
 
 
@@ -307,7 +307,8 @@ def _fill(torch, t, seed):
 @pytest.mark.parametrize("n_rep,d,dt", [(4, 128, "bf16"), (8, 128, "bf16"), (2, 64, "bf16"), (1, 128, "bf16"),
                                          (1, 128, "f32"), (4, 128, "f32"), (8, 128, "f32")])
 def test_decode_paged_random_table(env, n_rep, d, dt):
-    # config-2-shaped: paged 16-token blocks, random block table, ragged lengths incl. 1 and block edges;
+    # Llama-3-8B-layer-shaped heads (8 KV heads): paged 16-token blocks, random block table, ragged
+    # lengths incl. 1 and block edges;
     # fp32 caches at d 128 run the kernels whose P . V is on the VALU (the largest register use)
     R, torch, dev = env
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -416,7 +417,7 @@ def test_decode_paged_window_with_null_blocks(env):
 
 
 def test_decode_ring_random_head(env):
-    # config-3-shaped windowed layer: full ring (count = W), head at a random offset, long positions
+    # a sink + window ring layer (S 4, W 300): full ring (count = W), head at a random offset, long positions
     R, torch, dev = env
     Hkv, n_rep, d, S, W = 8, 4, 128, 4, 300
     Hq = Hkv * n_rep
@@ -509,7 +510,7 @@ def test_prefill_ring_prefix_lost_is_flagged(env):
     assert cache.err.item() & R.DEV_PREFIX_LOST
 
 
-# ------------------------------------------------------------------ rerotation (fp16 / int8), config-4-shaped
+# ------------------------------------------------------------------ rerotation (fp16 / int8), d 128 / r 64 caches
 
 def _contig_write(R, torch, dev, cfg, table, raw_dev, kv_dtype, L, T, Hkv, d, pos0):
     """Write raw keys for positions pos0.. into a CONTIG cache via apply_append (one call per layer)."""
