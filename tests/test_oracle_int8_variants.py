@@ -84,6 +84,38 @@ def test_hadamard_rerotation_within_pages_bounds(fa, fb):
     assert ratio_a > 10
 
 
+@pytest.mark.parametrize("neox,r", [(True, 64), (False, 64), (False, 48)])
+def test_hadamard_turn_of_leading_half_by_half_transforms(neox, r):
+    # The half-row form a kernel may use when the turn R moves only dims < 64 of a 128-dim row:
+    # with the unnormalised Sylvester H of order 128, H R H c = 128 c + [H64 D; H64 D],
+    # D = (R - I) H64 (c_lo + c_hi).  Checked in fp64 against the oracle's orthonormal transform
+    # (H = sqrt(n) * O.hadamard) and a direct turn of the pairs.
+    rng = synth.rng(2200 + r + neox)
+    c = rng.integers(-127, 128, size=(9, 128)).astype(np.float64)
+    ang = rng.uniform(-4.0, 4.0, size=(9, r // 2))
+    g = 1.07
+    cs, sn = g * np.cos(ang), g * np.sin(ang)
+
+    def turn(x):
+        y = np.array(x, copy=True)
+        for i in range(r // 2):
+            a, b = (i, i + r // 2) if neox else (2 * i, 2 * i + 1)
+            y[:, a] = x[:, a] * cs[:, i] - x[:, b] * sn[:, i]
+            y[:, b] = x[:, b] * cs[:, i] + x[:, a] * sn[:, i]
+        return y
+
+    h128 = lambda x: O.hadamard(x) * math.sqrt(128)
+    h64 = lambda x: O.hadamard(x) * 8.0
+    full = h128(turn(h128(c)))
+    x = np.zeros_like(c)
+    x[:, :64] = h64(c[:, :64] + c[:, 64:])
+    dd = (turn(x) - x)[:, :64]
+    assert np.all(dd[:, r:] == 0)  # dims past r do not move
+    h = h64(dd)
+    half = 128 * c + np.concatenate([h, h], axis=1)
+    np.testing.assert_allclose(half, full, rtol=0, atol=1e-9 * np.max(np.abs(full)))
+
+
 def test_hadamard_rerotation_identity_turn():
     c = _cfg(1.5)
     pos = synth.uniform_ints(200, 0, 500000, 920)
