@@ -40,6 +40,8 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 
 // The four codes of a word (byte b = code b) as exact floats: int8 by sign
 // extension, E4M3 by the hardware's fp8 -> fp32 conversion (two per instruction).
+// The E4M3 operands of the products skip the floats: fp8x2_bf16 below converts two
+// codes straight to a packed bf16 word.
 template <int KVDT>
 __device__ __forceinline__ void codes4(uint32_t w, float *f) {
   if constexpr (KVDT == ROPEKV_FP8) {
@@ -53,6 +55,13 @@ __device__ __forceinline__ void codes4(uint32_t w, float *f) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) f[b] = (float)(int8_t)(w >> (8 * b));
   }
+}
+
+// two E4M3 codes (the low or the high half of w) -> one packed bf16 word, exactly (every finite
+// E4M3 value is a bf16 value; unit scale)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // two floats -> one packed bf16 word (round to nearest even; exact for codes)
@@ -252,11 +261,17 @@ __global__ __launch_bounds__(256) void decode_split_8bit_kernel(const void *__re
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int tt = 2 * i + h;  // MFMA step: local elements 8 tt .. 8 tt + 7
-        float kf[8];
-        codes4<KVDT>(kp[2 * h], kf);
-        codes4<KVDT>(kp[2 * h + 1], kf + 4);
-        const u32x4_t av = {pack2_bf16(kf[0], kf[1]), pack2_bf16(kf[2], kf[3]), pack2_bf16(kf[4], kf[5]),
-                            pack2_bf16(kf[6], kf[7])};
+        u32x4_t av;
+        if constexpr (KVDT == ROPEKV_FP8) {
+          av = u32x4_t{fp8x2_bf16<false>(kp[2 * h]), fp8x2_bf16<true>(kp[2 * h]), fp8x2_bf16<false>(kp[2 * h + 1]),
+                       fp8x2_bf16<true>(kp[2 * h + 1])};
+        } else {
+          float kf[8];
+          codes4<KVDT>(kp[2 * h], kf);
+          codes4<KVDT>(kp[2 * h + 1], kf + 4);
+          av = u32x4_t{pack2_bf16(kf[0], kf[1]), pack2_bf16(kf[2], kf[3]), pack2_bf16(kf[4], kf[5]),
+                       pack2_bf16(kf[6], kf[7])};
+        }
         const u32x4_t bv = {qw[4 * tt], qw[4 * tt + 1], qw[4 * tt + 2], qw[4 * tt + 3]};
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
                                                        sacc, 0, 0, 0);
@@ -309,16 +324,32 @@ __global__ __launch_bounds__(256) void decode_split_8bit_kernel(const void *__re
         vw[j][0] = *(const uint32_t *)src;
       }
     }
-    float vf[4][E];
+    if constexpr (KVDT == ROPEKV_FP8) {
+      // bytes (key 0, key 1) and (key 2, key 3) of dims e, e + 1 gathered into one word each, then
+      // converted two at a time straight to bf16
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int e = 0; e < E; e += 2) {
+        const int w = e / 4;
+        const uint32_t sel = (e % 4) ? 0x07030602u : 0x05010400u;
+        const uint32_t p01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], sel);
+        const short4_t vb0 = __builtin_bit_cast(short4_t, (uint2){fp8x2_bf16<false>(p01), fp8x2_bf16<false>(p23)});
+        const short4_t vb1 = __builtin_bit_cast(short4_t, (uint2){fp8x2_bf16<true>(p01), fp8x2_bf16<true>(p23)});
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb0, acc[e], 0, 0, 0);
+        acc[e + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb1, acc[e + 1], 0, 0, 0);
+      }
+    } else {
+      float vf[4][E];
 #pragma unroll
-      for (int w = 0; w < E / 4; ++w) codes4<KVDT>(vw[j][w], vf[j] + 4 * w);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const short4_t vb = __builtin_bit_cast(
-          short4_t, (uint2){pack2_bf16(vf[0][e], vf[1][e]), pack2_bf16(vf[2][e], vf[3][e])});
-      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[e], 0, 0, 0);
+        for (int w = 0; w < E / 4; ++w) codes4<KVDT>(vw[j][w], vf[j] + 4 * w);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const short4_t vb = __builtin_bit_cast(
+            short4_t, (uint2){pack2_bf16(vf[0][e], vf[1][e]), pack2_bf16(vf[2][e], vf[3][e])});
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[e], 0, 0, 0);
+      }
     }
   };
   for (int k0 = 0; k0 < nk; k0 += NST) {
