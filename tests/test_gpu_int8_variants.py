@@ -89,9 +89,11 @@ def test_keep_scale_rerotate_vs_oracle(env, r, neox):
 
 
 @pytest.mark.parametrize("r,neox,d", [(64, True, 128), (128, True, 128), (64, False, 128), (48, False, 128),
+                                      (16, False, 128), (32, False, 128), (96, False, 128),
                                       (64, True, 64), (128, True, 256), (64, False, 256)])
 def test_hadamard_rerotate_vs_oracle(env, r, neox, d):
-    # head_dim 128 runs the two-lanes-per-row kernel, other head dims the general one
+    # head_dim 128 runs the two-lanes-per-row kernels (half rows when the turn stays in dims < 64), other
+    # head dims the general one
     R, torch, dev = env
     L, T, Hkv = 2, 48, 4
     ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144, neox=neox)
