@@ -13,8 +13,10 @@
  *
  * Conventions for every entry point:
  *   - Pointers named *_dev or documented as "device" point to device memory
- *     the caller allocated (e.g. with torch); the library never allocates,
- *     frees or keeps device memory, and keeps no state between calls.
+ *     the caller allocated (e.g. with torch); the library never allocates or
+ *     frees device memory and keeps no state between calls, except the one
+ *     fixed device array of ropekv_decode_attn_noalloc (loaded with the
+ *     library's code, one per GPU).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     default stream).  No call synchronises the host.
  *   - Arguments are validated on the host before any launch; a failing check
@@ -217,6 +219,20 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
 int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads,
                        const ropekv_kv_cache *cache, float scale, const float *sink_logits,
                        void *out, void *ws, size_t ws_bytes, ropekv_stream_t stream);
+
+/* ropekv_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation): the split-K partials go to a 64 MiB device array inside
+ * the library, one per GPU, set up on the first call on each device and held
+ * until the process ends.  Nothing is allocated per call.  Same arguments,
+ * kernels and results as ropekv_decode_attn.  A batch and cache whose partials
+ * (ropekv_decode_workspace_size) exceed 64 MiB return ROPEKV_ENOSPACE and
+ * launch nothing.  All calls on one GPU share the array: calls that overlap in
+ * time on one GPU (different streams, or different host threads) race and
+ * must be ordered by the caller. */
+int ropekv_decode_attn_noalloc(const void *q, int32_t batch, int32_t n_q_heads,
+                               const ropekv_kv_cache *cache, float scale,
+                               const float *sink_logits, void *out, ropekv_stream_t stream);
 
 /* Prefill attention for one sequence's chunk ([GOSS] 5.5 mask alignment):
  * queries t < T at positions pos0 + t see keys j <= pos0 + t with j < S or

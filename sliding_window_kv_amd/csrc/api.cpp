@@ -157,6 +157,27 @@ int check_attention_shape(const ropekv_kv_cache *c, int n_q_heads, bool int8_ok)
   return ROPEKV_OK;
 }
 
+// Checks shared by both decode entry points; on success *pl is the launch plan.
+int check_decode(const void *q, int batch, int n_q_heads, const ropekv_kv_cache *cache, float scale,
+                 const void *out, DecodePlan *pl) {
+  int e = check_cache(cache);
+  if (e) return e;
+  if (cache->layout != ROPEKV_RING && cache->layout != ROPEKV_PAGED)
+    return fail(ROPEKV_ELAYOUT, "decode needs a RING or PAGED cache");
+  e = check_attention_shape(cache, n_q_heads, true);
+  if (e) return e;
+  if (cache->layout == ROPEKV_PAGED && cache->block_size != 16)
+    return fail(ROPEKV_EINVAL, "decode needs block_size 16");
+  if (batch < 1 || batch > cache->batch) return fail(ROPEKV_EINVAL, "batch %d outside [1, %d]", batch, cache->batch);
+  if (!q || !out) return fail(ROPEKV_EINVAL, "q and out are required");
+  if (!aligned16(q) || !aligned16(out)) return fail(ROPEKV_EINVAL, "q and out must be 16-byte aligned");
+  if (!(scale >= 0.f) || !isfinite(scale)) return fail(ROPEKV_EINVAL, "scale must be finite and >= 0");
+  *pl = plan_decode(batch, n_q_heads, *cache);
+  if (pl->splits > kMaxDecodeSplits)
+    return fail(ROPEKV_ERANGE, "cache too long for one decode call (%d splits)", pl->splits);
+  return ROPEKV_OK;
+}
+
 float resolve_scale(float scale, int d) { return scale == 0.f ? 1.0f / sqrtf((float)d) : scale; }
 
 }  // namespace
@@ -239,23 +260,30 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
 
 int ropekv_decode_attn(const void *q, int32_t batch, int32_t n_q_heads, const ropekv_kv_cache *cache, float scale,
                        const float *sink_logits, void *out, void *ws, size_t ws_bytes, ropekv_stream_t stream) {
-  int e = check_cache(cache);
+  DecodePlan pl;
+  int e = check_decode(q, batch, n_q_heads, cache, scale, out, &pl);
   if (e) return e;
-  if (cache->layout != ROPEKV_RING && cache->layout != ROPEKV_PAGED)
-    return fail(ROPEKV_ELAYOUT, "decode needs a RING or PAGED cache");
-  e = check_attention_shape(cache, n_q_heads, true);
-  if (e) return e;
-  if (cache->layout == ROPEKV_PAGED && cache->block_size != 16)
-    return fail(ROPEKV_EINVAL, "decode needs block_size 16");
-  if (batch < 1 || batch > cache->batch) return fail(ROPEKV_EINVAL, "batch %d outside [1, %d]", batch, cache->batch);
-  if (!q || !out || !ws) return fail(ROPEKV_EINVAL, "q, out and ws are required");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(ws))
-    return fail(ROPEKV_EINVAL, "q, out and ws must be 16-byte aligned");
-  if (!(scale >= 0.f) || !isfinite(scale)) return fail(ROPEKV_EINVAL, "scale must be finite and >= 0");
-  const DecodePlan pl = plan_decode(batch, n_q_heads, *cache);
+  if (!ws) return fail(ROPEKV_EINVAL, "ws is required");
+  if (!aligned16(ws)) return fail(ROPEKV_EINVAL, "ws must be 16-byte aligned");
   if (ws_bytes < pl.ws_bytes)
     return fail(ROPEKV_ENOSPACE, "workspace %zu bytes < %zu needed", ws_bytes, pl.ws_bytes);
-  if (pl.splits > 1024) return fail(ROPEKV_ERANGE, "cache too long for one decode call (%d splits)", pl.splits);
+  return hip_status(launch_decode(q, batch, n_q_heads, *cache, resolve_scale(scale, cache->head_dim), sink_logits,
+                                  out, ws, pl, (hipStream_t)stream),
+                    "decode launch");
+}
+
+int ropekv_decode_attn_noalloc(const void *q, int32_t batch, int32_t n_q_heads, const ropekv_kv_cache *cache,
+                               float scale, const float *sink_logits, void *out, ropekv_stream_t stream) {
+  DecodePlan pl;
+  int e = check_decode(q, batch, n_q_heads, cache, scale, out, &pl);
+  if (e) return e;
+  if (pl.ws_bytes > kDecodeScratchBytes)
+    return fail(ROPEKV_ENOSPACE, "split-K partials need %zu bytes, more than the %zu-byte scratch of the "
+                "allocation-free decode (use ropekv_decode_attn with a workspace)",
+                pl.ws_bytes, kDecodeScratchBytes);
+  float *ws = nullptr;
+  e = hip_status(decode_scratch(&ws), "decode scratch address");
+  if (e) return e;
   return hip_status(launch_decode(q, batch, n_q_heads, *cache, resolve_scale(scale, cache->head_dim), sink_logits,
                                   out, ws, pl, (hipStream_t)stream),
                     "decode launch");

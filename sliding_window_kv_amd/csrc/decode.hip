@@ -26,9 +26,18 @@
 // O += P V on the VALU.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "decode_common.hpp"
 
 namespace ropekv {
+
+// Split-K partials of the allocation-free decode call: one copy of this array
+// per GPU, loaded with the library's code object and held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host the
+// name is a stand-in, not a device address); it asks for each device's address
+// once (decode_scratch) and passes that.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
 
 namespace {
 
@@ -440,6 +449,26 @@ hipError_t launch_decode(const void *q, int batch, int n_q_heads, const ropekv_k
     return launch_decode_8bit(q, batch, c, sl2, sinks, out, w, pl, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t decode_scratch(float **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = (float *)p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_visible_slots(const ropekv_kv_cache &c, int seq, int32_t *pos_out, int64_t *off_out, int max_out,

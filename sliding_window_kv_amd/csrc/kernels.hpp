@@ -18,6 +18,13 @@ struct DecodePlan {
 
 DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c);
 
+// The allocation-free decode keeps its split-K partials in a file-scope device
+// array of this size (one copy per GPU); decode_scratch gives the current
+// device's address of it, looked up once per device.
+constexpr int kMaxDecodeSplits = 1024;  // splits one combine workgroup merges
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(float **ptr);
+
 hipError_t launch_build_table(const RopeParams &rp, int max_pos, float *out, float *mscale_dev,
                               hipStream_t s);
 

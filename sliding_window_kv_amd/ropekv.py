@@ -32,6 +32,7 @@ EXPORTS = [
     "ropekv_apply_append",
     "ropekv_decode_workspace_size",
     "ropekv_decode_attn",
+    "ropekv_decode_attn_noalloc",
     "ropekv_prefill_attn",
     "ropekv_rerotate",
     "ropekv_shift_keys",
@@ -105,6 +106,7 @@ def _load():
     lib.ropekv_decode_workspace_size.argtypes = [I32, I32, KC]
     lib.ropekv_decode_workspace_size.restype = SZ
     lib.ropekv_decode_attn.argtypes = [P, I32, I32, KC, ctypes.c_float, P, P, P, SZ, P]
+    lib.ropekv_decode_attn_noalloc.argtypes = [P, I32, I32, KC, ctypes.c_float, P, P, P]
     lib.ropekv_prefill_attn.argtypes = [P, P, P, I32, I32, I32, KC, I32, ctypes.c_float, P, P, P]
     lib.ropekv_rerotate.argtypes = [RC, RC, KC, I32, P]
     lib.ropekv_shift_keys.argtypes = [RC, KC, I32, I32, P]
@@ -193,6 +195,12 @@ def decode_attn(q, batch: int, n_q_heads: int, cache: KVCache, scale: float, out
                 stream=None, sink_logits=None) -> int:
     return _check(LIB.ropekv_decode_attn(_ptr(q), batch, n_q_heads, ctypes.byref(cache), scale, _ptr(sink_logits),
                                          _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def decode_attn_noalloc(q, batch: int, n_q_heads: int, cache: KVCache, scale: float, out, stream=None,
+                       sink_logits=None) -> int:
+    return _check(LIB.ropekv_decode_attn_noalloc(_ptr(q), batch, n_q_heads, ctypes.byref(cache), scale,
+                                                 _ptr(sink_logits), _ptr(out), _stream(stream)))
 
 
 def prefill_attn(q, k, v, T: int, pos0: int, n_q_heads: int, cache: KVCache, seq_id: int, scale: float, out,

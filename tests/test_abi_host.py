@@ -170,6 +170,28 @@ def test_attention_argument_errors():
     assert pre(FAKE, FAKE, FAKE, 0, 0, 8, ctypes.byref(c), 0, 0.0, None, FAKE, None) == R.OK
 
 
+def test_decode_noalloc_argument_errors():
+    # the allocation-free decode shares the workspace call's checks and refuses plans whose
+    # split-K partials exceed its fixed 64 MiB array, all before any launch
+    from sliding_window_kv_amd import ropekv as R
+
+    f = R.raw("ropekv_decode_attn_noalloc")
+    c = _ring()
+    assert f(FAKE, 1, 6, ctypes.byref(c), 0.0, None, FAKE, None) == R.EINVAL      # 6 % 4
+    assert f(FAKE, 1, 64, ctypes.byref(c), 0.0, None, FAKE, None) == R.ERANGE     # n_rep 16
+    assert f(FAKE, 2, 8, ctypes.byref(c), 0.0, None, FAKE, None) == R.EINVAL      # batch > cache batch
+    assert f(FAKE + 2, 1, 8, ctypes.byref(c), 0.0, None, FAKE, None) == R.EINVAL  # q alignment
+    assert f(FAKE, 1, 8, ctypes.byref(c), float("inf"), None, FAKE, None) == R.EINVAL
+    assert f(FAKE, 1, 8, ctypes.byref(c), 0.0, None, None, None) == R.EINVAL      # out missing
+    contig = R.kv_cache(R.CONTIG, R.F32, 4, 64, FAKE, capacity=10, err_word=FAKE)
+    assert f(FAKE, 1, 8, ctypes.byref(contig), 0.0, None, FAKE, None) == R.ELAYOUT
+    big = R.kv_cache(R.PAGED, R.BF16, 8, 128, FAKE, FAKE, batch=256, max_blocks=8192, num_blocks=1 << 21,
+                     block_table=FAKE, seq_len=FAKE, err_word=FAKE)
+    assert R.decode_workspace_size(256, 32, big) > 64 << 20
+    assert f(FAKE, 256, 32, ctypes.byref(big), 0.0, None, FAKE, None) == R.ENOSPACE
+    assert "scratch" in R.last_error()
+
+
 def test_workspace_size_formula():
     from sliding_window_kv_amd import ropekv as R
 
