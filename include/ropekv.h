@@ -184,10 +184,10 @@ int ropekv_build_table(const ropekv_rope_cfg *cfg, int32_t max_pos, float *cos_s
  *   nothing is freed.
  * CONTIG: row t = p - pos0.
  * Stored dtype: F32 / BF16 / F16 round the fp32 result to nearest; I8 stores
- *   per-row codes rne(x * (127 / max|x|)) with scale = max|x| / 127 (keys
- *   after rotation, values as given; an all-zero row has scale 0).  FP8 stores
- *   the E4M3 code nearest (ties to even) to x * (448 / max|x|), computed in
- *   fp32 and clamped to [-448, 448], with scale = max|x| / 448. */
+ *   per-row codes clamp(rne(x / scale), -127, 127) with scale = max|x| / 127,
+ *   both IEEE fp32 divisions (keys after rotation, values as given; an
+ *   all-zero row has scale 0).  FP8 stores the E4M3 code nearest (ties to
+ *   even) to x / scale clamped to [-448, 448], with scale = max|x| / 448. */
 int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_t table_len,
                         void *q, int32_t n_q_heads, void *k, const void *v, int32_t act_dtype,
                         int32_t n_tokens, const int32_t *positions, const int32_t *seq_ids,
@@ -253,7 +253,10 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
  * the cached keys follow a change; [SINK] R_a R_b = R_{a+b}): every pair i of
  * the row at position p turns by p (w_to,i - w_from,i) and is scaled by
  * mscale_to / mscale_from; dims r..d-1 are untouched (bitwise for F16/BF16/F32).
- * I8 rows are dequantised, turned and requantised with a new per-row scale.
+ * I8 rows are dequantised, turned and requantised with a new per-row scale
+ * max|y| / 127, codes rne(y * (127 / max|y|)) with the reciprocal correctly
+ * rounded and the product rounded once (within one fp32 rounding of y / scale);
+ * a row the turn leaves unchanged keeps its codes and scale bit for bit.
  * cache: CONTIG, kv_dtype F16 / BF16 / F32 / I8, n_layers layers back to back
  * (FP8: ROPEKV_EDTYPE).
  * The angle p (w_to,i - w_from,i) and its reduction modulo 2 pi in fp64; cos and sin of the

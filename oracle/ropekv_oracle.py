@@ -7,9 +7,10 @@ imports or calls it, and this module imports nothing from the product path.
 
 Everything here is written for a reader to check against the pages by eye:
 no blocking, no fusion, no reordering beyond what each definition states.
-All floating point is numpy float64 unless a function says otherwise (the
-quantisers take their integer decisions in float32, the precision the
-kernels decide them in).
+All floating point is numpy float64 unless a function says otherwise.  The
+8-bit quantisers take their integer decisions in float32 (the stored scales
+are float32 and the pages fix no other precision), by the plain definition
+code = rne(x / scale) with the quotient rounded once to float32.
 
 Sources (cited by page title and section):
   [RoPE]   "RoPE, scaling, sliding window, attention sinks" (mlinterviewnotes,
@@ -270,7 +271,8 @@ def visible_positions(p: int, sinks: int, window: int) -> list[int]:
 
 
 # --------------------------------------------------------------------------
-# Quantisers (integer decisions taken in float32, as the kernels take them)
+# Quantisers   ([DYN] "What it does": cached K is dequantised, turned and
+# requantised; config 4 keeps one fp32 scale per row)
 # --------------------------------------------------------------------------
 
 
@@ -288,23 +290,44 @@ def round_f16(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
-def quant_int8_rows(x: np.ndarray):
-    """Per-row symmetric int8: amax = max|x|, scale = amax / 127, code = clamp(rne(x * (127 / amax)), -127, 127).
+def _row_scale(x: np.ndarray, qmax: float) -> np.ndarray:
+    """scale = max|x| / qmax over the last axis, rounded once to float32 (the stored precision)."""
+    amax = np.max(np.abs(np.asarray(x, dtype=np.float64)), axis=-1)
+    return (amax / qmax).astype(np.float32)
 
-    The pages fix only "dequantise, rotate, requantise" with a per-row scale;
-    the integer decision is taken in float32 with the reciprocal 127 / amax
-    (the row is rounded to float32 first), the precision and form the kernels
-    use.  An all-zero row gets scale 0 and codes 0.
+
+def _quotients32(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """x / scale per row, rounded once to float32; rows with scale 0 give 0.  For float32
+    operands this is the IEEE float32 quotient (a float64 quotient rounded to float32 is
+    correctly rounded)."""
+    s = np.asarray(scale, dtype=np.float64)
+    safe = np.where(s > 0, s, 1.0)
+    q = (np.asarray(x, dtype=np.float64) / safe[..., None]).astype(np.float32)
+    return np.where(s[..., None] > 0, q, np.float32(0.0)).astype(np.float32)
+
+
+def quant_int8_rows(x: np.ndarray):
+    """Per-row symmetric int8: scale = max|x| / 127, code = clamp(rne(x / scale), -127, 127).
+
+    One scale per row of d dims (config 4: per-row fp32 scale).  The scale is
+    max|x| / 127 rounded to float32, the precision it is stored in; each code
+    rounds (to nearest, ties to even) the quotient x / scale taken against that
+    stored scale and rounded to float32: the code whose multiple of the stored
+    scale is nearest to x.  An all-zero row gets scale 0 and codes 0.
     Returns (codes int8 [..., d], scale float32 [...]).
     """
-    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
-    amax = np.max(np.abs(x32), axis=-1).astype(np.float32)
-    scale = (amax / np.float32(127.0)).astype(np.float32)
-    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
-    inv = np.where(amax > 0, (np.float32(127.0) / safe).astype(np.float32), np.float32(0.0)).astype(np.float32)
-    q = np.rint((x32 * inv[..., None]).astype(np.float32))
-    q = np.clip(q, -127, 127)
+    x = np.asarray(x, dtype=np.float64)
+    scale = _row_scale(x, 127.0)
+    q = np.clip(np.rint(_quotients32(x, scale)), -127, 127)
     return q.astype(np.int8), scale
+
+
+def row_quotients(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """x / scale per row in float64: the exact value a code rounds, for locating rounding edges."""
+    x = np.asarray(x, dtype=np.float64)
+    s = np.asarray(scale, dtype=np.float64)
+    safe = np.where(s > 0, s, 1.0)
+    return np.where(s[..., None] > 0, x / safe[..., None], 0.0)
 
 
 def dequant_int8_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
@@ -349,20 +372,18 @@ def round_e4m3(y) -> np.ndarray:
 
 
 def quant_fp8_rows(x: np.ndarray):
-    """Per-row E4M3: amax = max|x|, scale = amax / 448, code = round_e4m3(x * (448 / amax)).
+    """Per-row E4M3: scale = max|x| / 448, code = round_e4m3(x / scale).
 
-    As for the int8 rows, the row is rounded to float32 first and the product is taken
-    in float32 with the float32 reciprocal (the precision and form the kernels use),
-    clamped to [-448, 448].  An all-zero row gets scale 0 (its codes are zeros).
+    The same reading as the int8 rows with 448, the largest E4M3 value, in place
+    of 127: scale and quotient rounded once to float32, the quotient clamped to
+    [-448, 448] and rounded to the nearest E4M3 value (ties to the even
+    mantissa).  An all-zero row gets scale 0 (its
+    codes are zeros).
     Returns (codes uint8 [..., d], scale float32 [...]).
     """
-    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
-    amax = np.max(np.abs(x32), axis=-1).astype(np.float32)
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
-    inv = np.where(amax > 0, (np.float32(E4M3_MAX) / safe).astype(np.float32), np.float32(0.0)).astype(np.float32)
-    y = (x32 * inv[..., None]).astype(np.float32)
-    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    x = np.asarray(x, dtype=np.float64)
+    scale = _row_scale(x, E4M3_MAX)
+    y = np.clip(_quotients32(x, scale), np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     return round_e4m3(y.astype(np.float64)), scale
 
 
@@ -642,22 +663,20 @@ def rerotate_int8_keep_scale_rows(codes: np.ndarray, scale: np.ndarray, position
     leaves the dims past the rotary slice (codes and scales) bitwise as they
     were written.  With one scale per row that holds only if the scale stays:
     dequantise, turn the rotary pairs, and re-code the rotary dims with the old
-    scale (code = rne(x * (1 / scale)), decided in float32 like the row
-    quantiser); the tail codes and the scale are kept.  If any re-coded value
-    leaves [-127, 127] (the turn can grow a pair's larger component up to
+    scale (code = rne(y / scale), the quotient rounded to float32 as in
+    quant_int8_rows); the tail codes and the scale are kept.  If any re-coded
+    value leaves [-127, 127] (the turn can grow a pair's larger component up to
     sqrt(2) times, and the gain mscale_to / mscale_from may exceed 1), the row
     is re-quantised whole as in rerotate_int8_rows.  A zero scale (all-zero
     row) stays zero.
+    Returns (codes, scale, overflow) with overflow True for the re-quantised rows.
     """
     codes = np.asarray(codes)
     scale = np.asarray(scale, dtype=np.float32)
     x = dequant_int8_rows(codes, scale)
     y = rerotate_rows(x, positions, cfg_from, cfg_to)
     r = cfg_to.rotary_dim
-    inv = np.where(scale > 0, (np.float32(1.0) / np.where(scale > 0, scale, np.float32(1.0))).astype(np.float32),
-                   np.float32(0.0)).astype(np.float32)
-    y32 = y[..., :r].astype(np.float32)
-    cand = np.rint((y32 * inv[..., None]).astype(np.float32))
+    cand = np.rint(_quotients32(y[..., :r], scale))
     overflow = np.any(np.abs(cand) > 127, axis=-1)
     out_codes = codes.astype(np.int8).copy()
     out_scale = scale.copy()

@@ -44,10 +44,11 @@ __device__ inline int run_last(const AppendArgs &a, int t, int p, int seq) {
   return lo;
 }
 
-// One 8-bit code of y = x * (qmax / max|x|) (qmax 127 for int8, 448 for E4M3):
-// int8 rounds to nearest even and clamps to [-127, 127]; E4M3 clamps to
-// [-448, 448] and takes the nearest code, ties to even, by the hardware's
-// fp32 -> fp8 conversion (the OCP format on this chip).
+// One 8-bit code of the quotient y = x / scale, scale = max|x| / qmax (qmax 127
+// for int8, 448 for E4M3; both IEEE fp32 divisions): int8 rounds to nearest
+// even and clamps to [-127, 127]; E4M3 clamps to [-448, 448] and takes the
+// nearest code, ties to even, by the hardware's fp32 -> fp8 conversion (the
+// OCP format on this chip).
 __device__ __forceinline__ uint8_t code8(float y, int kvdt) {
   if (kvdt == ROPEKV_FP8)
     return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(y, -448.f), 448.f), 0.f, 0, false) & 0xff);
@@ -310,14 +311,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             for (int e = lane; e < d; e += 64) x[e] *= norm;
             wave_lds_sync();
           }
-          // per-row symmetric codes: scale = max|x| / qmax, code = code8(x * (qmax / max|x|))
+          // per-row symmetric codes: scale = max|x| / qmax, code = code8(x / scale)
           float amax = 0.f;
           for (int e = lane; e < d; e += 64) amax = fmaxf(amax, fabsf(rowbuf[wave][e]));
           for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);
           const float scale = amax / qmax;
-          const float inv = amax > 0.f ? qmax / amax : 0.f;
           uint8_t *kc = (uint8_t *)c.k;
-          for (int e = lane; e < d; e += 64) kc[coff + e] = code8(rowbuf[wave][e] * inv, kvdt);
+          for (int e = lane; e < d; e += 64)
+            kc[coff + e] = code8(scale > 0.f ? rowbuf[wave][e] / scale : 0.f, kvdt);
           if (lane == 0) c.k_scale[coff / d] = scale;
           wave_lds_sync();
         }
@@ -337,10 +338,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
           }
           for (int m = 32; m >= 1; m >>= 1) amax = wave_max_xor(amax, m);
           wave_lds_sync();
-          const float inv = amax > 0.f ? qmax / amax : 0.f;
+          const float scale = amax / qmax;
           uint8_t *vc = (uint8_t *)c.v;
-          for (int e = lane; e < d; e += 64) vc[coff + e] = code8(rowbuf[wave][e] * inv, kvdt);
-          if (lane == 0) c.v_scale[coff / d] = amax / qmax;
+          for (int e = lane; e < d; e += 64)
+            vc[coff + e] = code8(scale > 0.f ? rowbuf[wave][e] / scale : 0.f, kvdt);
+          if (lane == 0) c.v_scale[coff / d] = scale;
           wave_lds_sync();
         } else {
           for (int e = lane; e < d; e += 64) store_elem(c.v, coff + e, kvdt, load_elem(a.v, voff + e, act));

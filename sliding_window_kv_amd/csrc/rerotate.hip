@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void rerotate_float_kernel(RerotArgs a) {
 // TL = 16 - 2H tail codes [r + q TL, ...); GPT-J lane q holds the 2H
 // interleaved codes of the same pairs.  No lane exchange is needed to turn a
 // pair; the row's absmax is a reduction over its L lanes.  Codes are
-// requantised as rne(y * (127 / max|y|)).
+// requantised as rne(y * (127 / max|y|)), the reciprocal correctly rounded.
 template <int N>
 __device__ __forceinline__ void ld_n(uint32_t *w, const int8_t *p) {
   if constexpr (N == 16) {
@@ -309,7 +309,9 @@ __device__ inline void gain_table(const RerotArgs &a, int t0, float *s_cs, float
 // int8 keys turned in code units.  A row x = c * sc (codes c, row scale sc) turns
 // into y * sc with y = R c (the pair turn with the gain folded into cos / sin),
 // so the requantised row needs only the codes: amax = max|y| over the row (tail
-// codes included), new codes rne(y * 127 / amax), new scale sc * amax / 127.
+// codes included), new codes rne(y * (127 / amax)) with 127 / amax correctly
+// rounded and the product rounded once, new scale sc * (amax / 127) (a row that
+// does not move keeps its codes and scale bit for bit).
 // Keep-scale: the row keeps sc (tail codes untouched) when every turned rotary
 // value re-codes within [-127, 127], i.e. max|y| < 127.5, and stores rne(y).
 // A row with sc = 0 becomes all zero with scale 0, as its dequantised values are.
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(kI8Threads) void rerotate_int8_lanes_kernel(RerotAr
   }
   const bool keep = KEEP && mrot < 127.5f;
   const float amax = fmaxf(mrot, mtail);
-  const float inv = keep ? 1.0f : (amax > 0.f && sco > 0.f ? 127.0f * __builtin_amdgcn_rcpf(amax) : 0.f);
+  const float inv = keep ? 1.0f : (amax > 0.f && sco > 0.f ? 127.0f / amax : 0.f);
   if (!live) continue;
   uint32_t c1[NEOX ? H : 2 * H], c2[H];
 #pragma unroll
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(kI8Threads) void rerotate_int8_lanes_kernel(RerotAr
       pack_codes<TL>(pt, ct);
       st_n<TL>(rp + r + q * TL, pt);
     }
-    if (q == 0) *sp = inv > 0.f ? sco * amax * (1.0f / 127.0f) : 0.f;
+    if (q == 0) *sp = inv > 0.f ? sco * (amax / 127.0f) : 0.f;
   }
   }
 }
@@ -730,7 +732,7 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_kernel(RerotArg
 #pragma unroll
     for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(x[e]));
     amax = fmaxf(amax, dpp_xor1(amax));
-    const float inv = amax > 0.f && sco > 0.f ? 127.0f * __builtin_amdgcn_rcpf(amax) : 0.f;
+    const float inv = amax > 0.f && sco > 0.f ? 127.0f / amax : 0.f;
     uint32_t out[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_r64_kernel(Rero
 #pragma unroll
     for (int e = 0; e < 64; ++e) amax = fmaxf(amax, fabsf(y[e]));
     amax = fmaxf(amax, dpp_xor1(amax));
-    const float inv = amax > 0.f && sco > 0.f ? 127.0f * __builtin_amdgcn_rcpf(amax) : 0.f;
+    const float inv = amax > 0.f && sco > 0.f ? 127.0f / amax : 0.f;
     uint32_t out[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)

@@ -93,3 +93,111 @@ class DevPaged:
         self.desc = R.kv_cache(R.PAGED, kvdt, Hkv, d, self.k, self.v, batch=B, sinks=S, window=W, block_size=bs,
                                max_blocks=table.shape[1], num_blocks=num_blocks, block_table=self.table,
                                seq_len=self.seq_len, err_word=self.err, k_scale=self.k_scale, v_scale=self.v_scale)
+
+
+# ------------------------------------------------------------------ 8-bit codes: rounding-edge validity
+#
+# A kernel and the oracle decide an 8-bit code from the same quotient x / scale but by different
+# float32 arithmetic: the kernels rotate in float32 with a float32 table (the oracle in fp64) and
+# re-quantise turned rows by a product with the correctly rounded reciprocal 127 / max (the oracle
+# divides).  So a kernel code may land on the other side of a rounding boundary.  It may differ from
+# the oracle's code only by one step, and only where the oracle's exact fp64 quotient lies within
+# eps of the boundary between the two codes.  Values that are never rotated (the appended V rows)
+# go through the same IEEE float32 division on both sides and are compared bit for bit instead.
+#
+# eps, in quotient units (code steps for int8):
+#   append of a rotated key: float32 table entries (2^-24 relative each) and three float32
+#     roundings of a pair, |pair| <= sqrt(2) max|x|, scaled by 127 / max|x|:
+#     127 (2 + 3 sqrt(2)) 2^-24 ~ 4.7e-5 for int8; 448 x the same ~ 1.7e-4 for E4M3.
+#     eps = 2.5e-4 (int8), 1e-3 (E4M3): about 5x margin.
+#   re-rotation of int8 rows in code units: cos / sin of the reduced angle within 5e-7 (the
+#     re-rotation's stated accuracy), gain <= 1.1, |c| <= 127, three float32 roundings, then the
+#     new unit 127 / max|y| <= sqrt(2) per old unit: sqrt(2) (127 * 2 * 5e-7 * 1.1 + 3 * 127 * 2^-24)
+#     ~ 2.3e-4.  eps = 1e-3.
+#   Hadamard rows: the second transform of the turned row runs in float32 (7 butterfly levels over
+#     values up to sqrt(128) * 127): about 1e-3 code steps at worst.  eps = 4e-3.
+EPS_APPEND_I8 = 2.5e-4
+EPS_APPEND_FP8 = 1e-3
+EPS_TURN_I8 = 1e-3
+EPS_TURN_HADAMARD = 4e-3
+
+
+def assert_int8_codes_valid(got, want, quot, eps):
+    """got, want: int8 codes; quot: the oracle's exact quotients (same shape).  Returns the number
+    of codes that differ (each one step, at a rounding edge)."""
+    g = np.asarray(got).astype(np.int32)
+    w = np.asarray(want).astype(np.int32)
+    diff = g - w
+    assert int(np.max(np.abs(diff), initial=0)) <= 1, "a code differs by more than one step"
+    bad = diff != 0
+    if bad.any():
+        edge = (g[bad] + w[bad]) / 2.0
+        dist = np.abs(np.asarray(quot, dtype=np.float64)[bad] - edge)
+        assert float(dist.max()) <= eps, (
+            f"{int(bad.sum())} codes differ; worst is {float(dist.max()):.3e} from its rounding edge (eps {eps})")
+    return int(bad.sum())
+
+
+def _e4m3_ordinal(codes):
+    u = np.asarray(codes).view(np.uint8).astype(np.int32)
+    return np.where(u & 0x80, -(u & 0x7F), u)
+
+
+def assert_fp8_codes_valid(got, want, quot, eps):
+    """As assert_int8_codes_valid for E4M3 bytes: neighbouring values (ordinal step one), the
+    oracle's quotient within eps of the midpoint of the two values (+0 and -0 count as equal)."""
+    og, ow = _e4m3_ordinal(got), _e4m3_ordinal(want)
+    diff = og - ow
+    assert int(np.max(np.abs(diff), initial=0)) <= 1, "an E4M3 code differs by more than one step"
+    bad = diff != 0
+    if bad.any():
+        mid = (O.e4m3_value(np.asarray(got)[bad]) + O.e4m3_value(np.asarray(want)[bad])) / 2.0
+        q = np.clip(np.asarray(quot, dtype=np.float64)[bad], -O.E4M3_MAX, O.E4M3_MAX)
+        dist = np.abs(q - mid)
+        assert float(dist.max()) <= eps, (
+            f"{int(bad.sum())} codes differ; worst is {float(dist.max()):.3e} from its rounding edge (eps {eps})")
+    return int(bad.sum())
+
+
+def int8_turn_quotients(kind, codes, scale, positions, cfg_from, cfg_to, new_scale, kept=None):
+    """The oracle's exact quotients behind re-rotated int8 codes: the fp64 turned row (in the H
+    domain for Hadamard rows) over the scale the codes are taken against (the new one, or the
+    old one for rows that keep their scale)."""
+    x = O.dequant_int8_rows(codes, scale)
+    if kind == "i8_hadamard":
+        y = O.hadamard(O.rerotate_rows(O.hadamard(x), positions, cfg_from, cfg_to))
+    else:
+        y = O.rerotate_rows(x, positions, cfg_from, cfg_to)
+    s = np.asarray(new_scale, dtype=np.float32)
+    if kept is not None:
+        s = np.where(kept, np.asarray(scale, dtype=np.float32), s)
+    return O.row_quotients(y, s)
+
+
+def check_keep_scale_rows(before, sc_before, after, sc_after, positions, cfg_from, cfg_to):
+    """Keep-scale re-rotation of int8 rows, checked row by row against the branch the kernel took.
+
+    A row the kernel kept (scale unchanged) must have its tail codes bit for bit and rotary codes
+    valid against rne(y / old scale); a row it re-quantised must match the oracle's whole-row
+    quantiser of y (scale to 5e-6, codes valid).  The kernel's decision may differ from the
+    oracle's only where the row's largest turned rotary quotient at the old scale sits at the
+    re-coding edge 127.5.  Returns (rows kept, rows re-quantised)."""
+    r = cfg_to.rotary_dim
+    codes_o, scale_o, over_o = O.rerotate_int8_keep_scale_rows(before, sc_before, positions, cfg_from, cfg_to)
+    y = O.rerotate_rows(O.dequant_int8_rows(before, sc_before), positions, cfg_from, cfg_to)
+    kept = np.asarray(sc_after) == np.asarray(sc_before)
+    q_old = O.row_quotients(y[:, :r], sc_before)
+    dis = kept == over_o
+    if dis.any():
+        edge = np.max(np.abs(q_old[dis]), axis=1)
+        assert np.all(np.abs(edge - 127.5) <= EPS_TURN_I8), edge
+    if kept.any():
+        assert np.array_equal(after[kept, r:], before[kept, r:])
+        want = np.rint(q_old[kept].astype(np.float32)).astype(np.int32)
+        assert_int8_codes_valid(after[kept, :r], want, q_old[kept], EPS_TURN_I8)
+    req = ~kept
+    if req.any():
+        full_c, full_s = O.quant_int8_rows(y[req])
+        np.testing.assert_allclose(sc_after[req], full_s, rtol=5e-6)
+        assert_int8_codes_valid(after[req], full_c, O.row_quotients(y[req], full_s), EPS_TURN_I8)
+    return int(kept.sum()), int(req.sum())

@@ -3,16 +3,18 @@ Hadamard-rotated keys (append, decode, re-rotation), against the oracle.
 
 Inputs are seeded codes and scales (or seeded raw keys for the append); the
 expected values come from the oracle only.  A turned code may sit on the other
-side of a rounding boundary (fp32 kernel math vs the oracle's fp64 turn rounded
-to fp32), so codes may differ by one step in a small fraction of places; scales
-agree to 1e-5 relative; kept scales and kept tail codes are bitwise.
+side of a rounding boundary (fp32 kernel math vs the oracle's fp64 turn), so a
+code may differ by one step, and only where the oracle's exact quotient lies at
+that boundary; scales agree to 1e-5 relative; kept scales and kept tail codes
+are bitwise, and a keep / re-quantise decision may differ only at its edge.
 """
 import numpy as np
 import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import DevPaged, assert_bf16_close, oracle_cfg, to_np64, torch_dev
+from tests.gpu_util import (EPS_TURN_HADAMARD, DevPaged, assert_bf16_close, assert_int8_codes_valid,
+                            check_keep_scale_rows, int8_turn_quotients, oracle_cfg, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,11 +27,6 @@ def env():
     from sliding_window_kv_amd import ropekv as R
 
     return R, torch, dev
-
-
-def _codes_close(got, want):
-    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
-    assert diff.max() <= 1 and diff.mean() < 0.01, (diff.max(), diff.mean())
 
 
 def _seeded_rows(torch, dev, shape, seed, rot_dims, rot_amp):
@@ -67,23 +64,10 @@ def test_keep_scale_rerotate_vs_oracle(env, r, neox):
     pos = np.repeat(np.arange(pos0, pos0 + T), Hkv)
     n_keep = n_over = 0
     for layer in range(L):
-        wc, ws_, over = O.rerotate_int8_keep_scale_rows(c0[layer].reshape(-1, d), s0[layer].reshape(-1), pos,
-                                                       oracle_cfg(ca), oracle_cfg(cb))
-        gc, gs = c1[layer].reshape(-1, d), s1[layer].reshape(-1)
-        kept = gs == s0[layer].reshape(-1)
-        for i in np.nonzero(kept != ~over)[0]:
-            # a decision may only differ on a row whose largest turned code sits at the rounding edge
-            y = O.rerotate_rows(O.dequant_int8_rows(c0[layer].reshape(-1, d)[i:i + 1], s0[layer].reshape(-1)[i:i + 1]),
-                                pos[i:i + 1], oracle_cfg(ca), oracle_cfg(cb))
-            edge = np.max(np.abs(y[0, :r])) / float(s0[layer].reshape(-1)[i])
-            assert abs(edge - 127.5) < 1e-3, (i, edge)
-        agree = kept == ~over
-        keep_rows = agree & kept
-        n_keep += int(keep_rows.sum())
-        n_over += int((agree & ~kept).sum())
-        assert np.array_equal(gc[keep_rows, r:], c0[layer].reshape(-1, d)[keep_rows, r:])  # tail bitwise
-        _codes_close(gc[agree], wc[agree])
-        np.testing.assert_allclose(gs[agree], ws_[agree], rtol=1e-5)
+        k_, o_ = check_keep_scale_rows(c0[layer].reshape(-1, d), s0[layer].reshape(-1), c1[layer].reshape(-1, d),
+                                       s1[layer].reshape(-1), pos, oracle_cfg(ca), oracle_cfg(cb))
+        n_keep += k_
+        n_over += o_
     assert n_keep > 20 and n_over > 20  # both branches exercised
     assert s1[0, 5, 2] == 0 and np.all(c1[0, 5, 2] == 0)
 
@@ -110,10 +94,11 @@ def test_hadamard_rerotate_vs_oracle(env, r, neox, d):
     c1, s1 = codes.cpu().numpy(), scale.cpu().numpy()
     pos = np.repeat(np.arange(pos0, pos0 + T), Hkv)
     for layer in range(L):
-        wc, ws_ = O.rerotate_int8_hadamard_rows(c0[layer].reshape(-1, d), s0[layer].reshape(-1), pos,
-                                                oracle_cfg(ca), oracle_cfg(cb))
-        _codes_close(c1[layer].reshape(-1, d), wc)
+        cl, sl = c0[layer].reshape(-1, d), s0[layer].reshape(-1)
+        wc, ws_ = O.rerotate_int8_hadamard_rows(cl, sl, pos, oracle_cfg(ca), oracle_cfg(cb))
         np.testing.assert_allclose(s1[layer].reshape(-1), ws_, rtol=1e-5)
+        quot = int8_turn_quotients("i8_hadamard", cl, sl, pos, oracle_cfg(ca), oracle_cfg(cb), ws_)
+        assert_int8_codes_valid(c1[layer].reshape(-1, d), wc, quot, EPS_TURN_HADAMARD)
 
 
 def test_hadamard_rerotate_bounds_from_append(env):
@@ -153,7 +138,7 @@ def test_hadamard_rerotate_bounds_from_append(env):
         key_a = np.stack([O.rotate_by_angle(rawn[l], np.outer(pos, O.inv_freq(oa))[:, None, :], r, True, O.mscale(oa))
                           for l in range(L)])
         wc, ws_ = O.quant_int8_hadamard_rows(key_a)
-        _codes_close(ka.cpu().numpy(), wc)
+        assert_int8_codes_valid(ka.cpu().numpy(), wc, O.row_quotients(O.hadamard(key_a), ws_), EPS_TURN_HADAMARD)
         np.testing.assert_allclose(sa.cpu().numpy(), ws_, rtol=1e-5)
         R.rerotate(ca, cb, desc_a, L)
         torch.cuda.synchronize()
@@ -237,7 +222,7 @@ def test_hadamard_paged_append_then_decode(env):
     kc, ks = cache.k.cpu().numpy(), cache.k_scale.cpu().numpy()
     got_c = np.stack([kc[table[b, p // bs], :, p % bs] for b, p in toks]).reshape(B, n_tok, Hkv, d)
     got_s = np.stack([ks[table[b, p // bs], :, p % bs] for b, p in toks]).reshape(B, n_tok, Hkv)
-    _codes_close(got_c, kc_want)
+    assert_int8_codes_valid(got_c, kc_want, O.row_quotients(O.hadamard(krot), ks_want), EPS_TURN_HADAMARD)
     np.testing.assert_allclose(got_s, ks_want, rtol=1e-5)
     qd = torch.from_numpy(qrot[:, n_tok - 1]).to(dev, bf)
     out = torch.empty(B, Hq, d, dtype=bf, device=dev)

@@ -2,20 +2,21 @@
 per-row quantised K and V in apply_append, decode over codes x scales.
 
 Reference values: the oracle's row quantisers (scale = max|x| / qmax with qmax
-127 for int8 and 448 for E4M3, codes decided in float32 with the reciprocal
-qmax / max|x|, the precision the kernels use) applied to the oracle's fp64
-rotation, and the oracle's decode over the dequantised rows.  Values are not
-rotated, so their codes and scales must match bit for bit; a rotated key may
-land on the other side of a rounding boundary (float32 vs fp64 rotation), so
-its code may be the neighbouring one.  Decode outputs (bf16) meet
-|gpu - ref| <= 2e-2 + 1e-2 |ref|.
+127 for int8 and 448 for E4M3, code = the nearest code to x / scale, decided in
+float32) applied to the oracle's fp64 rotation, and the oracle's decode over the
+dequantised rows.  Values are not rotated, so their codes and scales must match
+bit for bit; a rotated key may land on the other side of a rounding boundary
+(float32 vs fp64 rotation), so its code may be the neighbouring one, and then
+only where the oracle's exact quotient sits at that boundary.  Decode outputs
+(bf16) meet |gpu - ref| <= 2e-2 + 1e-2 |ref|.
 """
 import numpy as np
 import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import DevPaged, DevRing, assert_bf16_close, oracle_cfg, to_np64, torch_dev
+from tests.gpu_util import (EPS_APPEND_FP8, EPS_APPEND_I8, DevPaged, DevRing, assert_bf16_close,
+                            assert_fp8_codes_valid, assert_int8_codes_valid, oracle_cfg, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,33 +134,27 @@ def test_kv8_decode_ring(env, kind, n_rep, d):
         assert_bf16_close(got[b], ref)
 
 
-def _ordinal(kind, codes):
-    """Codes as integers in value order (neighbouring values differ by 1; E4M3 +0 and -0 are both 0)."""
-    c = np.asarray(codes)
-    if kind == "i8":
-        return c.astype(np.int32)
-    u = c.view(np.uint8).astype(np.int32)
-    return np.where(u & 0x80, -(u & 0x7F), u)
-
-
-def _check_rows(kind, got_codes, got_scale, want_codes, want_scale, rotated):
-    """Codes / scales of cached rows against the oracle quantiser."""
-    if rotated:
-        diff = np.abs(_ordinal(kind, got_codes) - _ordinal(kind, want_codes))
-        assert int(diff.max()) <= 1
-        assert float(np.mean(diff)) <= 1e-2
+def _check_rows(kind, got_codes, got_scale, want_codes, want_scale, quot=None):
+    """Codes / scales of cached rows against the oracle quantiser: bit for bit for values
+    (quot None), rounding-edge validity for rotated keys (quot = the oracle's exact quotients)."""
+    if quot is not None:
+        if kind == "i8":
+            assert_int8_codes_valid(got_codes, want_codes, quot, EPS_APPEND_I8)
+        else:
+            assert_fp8_codes_valid(got_codes, want_codes, quot, EPS_APPEND_FP8)
         np.testing.assert_allclose(got_scale, want_scale, rtol=1e-6, atol=0)
     else:
-        assert np.array_equal(got_codes, want_codes)
+        assert np.array_equal(np.asarray(got_codes).view(np.uint8), np.asarray(want_codes).view(np.uint8))
         assert np.array_equal(got_scale, want_scale)
 
 
 def _oracle_quant(kind, rows):
+    """(codes, scale, dequantised rows, exact quotients) of the oracle's quantiser."""
     if kind == "i8":
         codes, scale = O.quant_int8_rows(rows)
-        return codes, scale, O.dequant_int8_rows(codes, scale)
+        return codes, scale, O.dequant_int8_rows(codes, scale), O.row_quotients(rows, scale)
     codes, scale = O.quant_fp8_rows(rows)
-    return codes, scale, O.dequant_fp8_rows(codes, scale)
+    return codes, scale, O.dequant_fp8_rows(codes, scale), O.row_quotients(rows, scale)
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -184,8 +179,8 @@ def test_kv8_paged_append_and_decode(env, kind):
     vall = to_np64(torch.from_numpy(synth.normal((B, max_len, Hkv, d), 504)).to(bf))
     krot = np.stack([O.rope_apply(kall[b], np.arange(max_len), otab, d, True) for b in range(B)])
     qrot = np.stack([O.rope_apply(qall[b], np.arange(max_len), otab, d, True) for b in range(B)])
-    kq_codes, kq_scale, kdeq = _oracle_quant(kind, krot)
-    vq_codes, vq_scale, vdeq = _oracle_quant(kind, vall)
+    kq_codes, kq_scale, kdeq, kquot = _oracle_quant(kind, krot)
+    vq_codes, vq_scale, vdeq, _ = _oracle_quant(kind, vall)
     n = [0] * B
     freed_dev = torch.full((B * max_blocks,), -7, dtype=torch.int32, device=dev)
     nfreed = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -218,18 +213,18 @@ def test_kv8_paged_append_and_decode(env, kind):
         kc, ks = cache.k.cpu().numpy(), cache.k_scale.cpu().numpy()
         vc, vs = cache.v.cpu().numpy(), cache.v_scale.cpu().numpy()
         # rows written by this step (rows of freed blocks may be reused later and are not checked)
-        gk, gks, wk, wks, gv, gvs, wv, wvs = [], [], [], [], [], [], [], []
+        gk, gks, wk, wks, wq, gv, gvs, wv, wvs = [], [], [], [], [], [], [], [], []
         for b, p in toks:
             bid = otable[b][p // bs]
             if bid < 0:
                 continue
             gk.append(kc[bid, :, p % bs]), gks.append(ks[bid, :, p % bs])
-            wk.append(kq_codes[b, p]), wks.append(kq_scale[b, p])
+            wk.append(kq_codes[b, p]), wks.append(kq_scale[b, p]), wq.append(kquot[b, p])
             gv.append(vc[bid, :, p % bs]), gvs.append(vs[bid, :, p % bs])
             wv.append(vq_codes[b, p]), wvs.append(vq_scale[b, p])
         if gk:
-            _check_rows(kind, np.stack(gk), np.stack(gks), np.stack(wk), np.stack(wks), rotated=True)
-            _check_rows(kind, np.stack(gv), np.stack(gvs), np.stack(wv), np.stack(wvs), rotated=False)
+            _check_rows(kind, np.stack(gk), np.stack(gks), np.stack(wk), np.stack(wks), np.stack(wq))
+            _check_rows(kind, np.stack(gv), np.stack(gvs), np.stack(wv), np.stack(wvs))
         qd = torch.from_numpy(np.stack([qrot[b, max(n[b] - 1, 0)] for b in range(B)])).to(dev, bf)
         out = torch.empty(B, Hq, d, dtype=bf, device=dev)
         R.decode_attn(qd, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
@@ -261,8 +256,8 @@ def test_kv8_ring_append_and_decode(env, kind, chunks):
     vd = torch.from_numpy(synth.normal((n_total, Hkv, d), 513)).to(dev, bf)
     qrot = O.rope_apply(to_np64(qd), np.arange(n_total), otab, d, True)
     krot = O.rope_apply(to_np64(kd), np.arange(n_total), otab, d, True)
-    kq_codes, kq_scale, kdeq = _oracle_quant(kind, krot)
-    vq_codes, vq_scale, vdeq = _oracle_quant(kind, to_np64(vd))
+    kq_codes, kq_scale, kdeq, kquot = _oracle_quant(kind, krot)
+    vq_codes, vq_scale, vdeq, _ = _oracle_quant(kind, to_np64(vd))
     cache = DevRing(R, torch, dev, _store(torch, kind), B, Hkv, d, S, W)
     oring = O.RingSeq(sinks=S, window=W)
     out = torch.empty(1, Hq, d, dtype=bf, device=dev)
@@ -283,8 +278,8 @@ def test_kv8_ring_append_and_decode(env, kind, chunks):
         vc, vs = cache.v[0].cpu().numpy(), cache.v_scale[0].cpu().numpy()
         slots = sorted(oring.slot_pos)
         ps = [oring.slot_pos[s] for s in slots]
-        _check_rows(kind, kc[:, slots].transpose(1, 0, 2), ks[:, slots].T, kq_codes[ps], kq_scale[ps], rotated=True)
-        _check_rows(kind, vc[:, slots].transpose(1, 0, 2), vs[:, slots].T, vq_codes[ps], vq_scale[ps], rotated=False)
+        _check_rows(kind, kc[:, slots].transpose(1, 0, 2), ks[:, slots].T, kq_codes[ps], kq_scale[ps], kquot[ps])
+        _check_rows(kind, vc[:, slots].transpose(1, 0, 2), vs[:, slots].T, vq_codes[ps], vq_scale[ps])
         R.decode_attn(q[T - 1:T], 1, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
         torch.cuda.synchronize()
         ref = O.decode_attention(qrot[p0 + T - 1], lambda j: kdeq[j], lambda j: vdeq[j], p0 + T, S, W, Hkv)

@@ -14,8 +14,8 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (DevPaged, DevRing, assert_bf16_close, normwise, oracle_cfg, rowwise, to_np64,
-                            torch_dev)
+from tests.gpu_util import (EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_int8_codes_valid,
+                            int8_turn_quotients, normwise, oracle_cfg, rowwise, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -619,6 +619,27 @@ def test_rerotate_identity_and_oracle_parity(env):
                 assert_bf16_close(to_np64(k2), ref2, atol=2e-2, rtol=1e-2)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_rerotate_int8_identity(env, mode):
+    # A -> A over rows the append quantised (row max 127 codes): codes and scales bit for bit, for the
+    # requantising turn (mode 0) and the keep-scale turn (mode 1); the oracle's turn is the identity too
+    R, torch, dev = env
+    L, T, Hkv, d, r = 2, 96, 8, 128, 64
+    ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.375, orig_max_pos=262144)
+    P = 524288
+    ta = _table(R, torch, dev, ca, P)
+    raw = torch.from_numpy(synth.normal((L, T, Hkv, d), 98)).to(dev, torch.float16)
+    kc, sc, desc = _contig_write(R, torch, dev, ca, ta, raw, R.I8, L, T, Hkv, d, 400000)
+    desc.k_int8_mode = mode
+    c0, s0 = kc.cpu().numpy(), sc.cpu().numpy()
+    R.rerotate(ca, ca, desc, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), c0) and np.array_equal(sc.cpu().numpy(), s0)
+    pos = np.repeat(np.arange(400000, 400000 + T), Hkv)
+    wc, ws_ = O.rerotate_int8_rows(c0[0].reshape(-1, d), s0[0].reshape(-1), pos, oracle_cfg(ca), oracle_cfg(ca))
+    assert np.array_equal(wc, c0[0].reshape(-1, d)) and np.array_equal(ws_, s0[0].reshape(-1))
+
+
 @pytest.mark.parametrize("r,neox", [(128, True), (32, True), (96, True), (64, False), (32, False), (64, True)])
 def test_rerotate_int8_shapes_vs_oracle(env, r, neox):
     # every int8 code path (lane-local pairs with 2, 4 or 8 codes per half, GPT-J, and the
@@ -642,10 +663,11 @@ def test_rerotate_int8_shapes_vs_oracle(env, r, neox):
     c1, s1 = codes.cpu().numpy(), scale.cpu().numpy()
     pos = np.repeat(np.arange(pos0, pos0 + T), Hkv)
     for l in range(L):
-        wc, ws_ = O.rerotate_int8_rows(c0[l].reshape(-1, d), s0[l].reshape(-1), pos, oracle_cfg(ca), oracle_cfg(cb))
-        np.testing.assert_allclose(s1[l].reshape(-1), ws_, rtol=1e-5)
-        diff = np.abs(c1[l].reshape(-1, d).astype(np.int32) - wc.astype(np.int32))
-        assert diff.max() <= 1 and diff.mean() < 0.01, (diff.max(), diff.mean())
+        cl, sl = c0[l].reshape(-1, d), s0[l].reshape(-1)
+        wc, ws_ = O.rerotate_int8_rows(cl, sl, pos, oracle_cfg(ca), oracle_cfg(cb))
+        np.testing.assert_allclose(s1[l].reshape(-1), ws_, rtol=5e-6)
+        quot = int8_turn_quotients("i8", cl, sl, pos, oracle_cfg(ca), oracle_cfg(cb), ws_)
+        assert_int8_codes_valid(c1[l].reshape(-1, d), wc, quot, EPS_TURN_I8)
     assert s1[0, 3, 1] == 0 and np.all(c1[0, 3, 1] == 0)
 
 
