@@ -201,3 +201,66 @@ def check_keep_scale_rows(before, sc_before, after, sc_after, positions, cfg_fro
         np.testing.assert_allclose(sc_after[req], full_s, rtol=5e-6)
         assert_int8_codes_valid(after[req], full_c, O.row_quotients(y[req], full_s), EPS_TURN_I8)
     return int(kept.sum()), int(req.sum())
+
+
+# ------------------------------------------------------------------ needles: full-size attention parity with power
+#
+# With N(0, 1) queries, keys and values, an attention output over n keys is a mean of ~n / e
+# values and only ~1/sqrt(n) in size: at full size it sits below the bf16 tolerance
+# 2e-2 + 1e-2 |ref|, so a dropped sink, an off-by-one window edge or a wrong block would pass.
+# These helpers plant needles.  The tested queries get a component beta * u_g along a unit
+# direction u_g of their KV head g (beta = sqrt(d)), and keys at chosen positions are set to
+# alpha * u_g: a needle scores alpha (1 + N(0, 1) / sqrt(d)) ~ 16 nats, the background keys
+# N(0, 2), so the visible needles carry > 99 % of the softmax mass even over 131072 keys.  Their
+# values are distinct N(0, gamma^2) rows (gamma 4), so the output is about the mean of the visible
+# needles' values and a needle wrongly dropped or admitted moves it by O(1).  Each test also checks
+# that the oracle over a wrong visible set (shifted window, no sinks, a dropped block...) fails the
+# same tolerance: the comparison has the power to see that mistake.
+NEEDLE_ALPHA = 16.0
+NEEDLE_GAMMA = 4.0
+
+
+def needle_dirs(Hkv, d, seed):
+    """One unit direction per KV head, float64 [Hkv, d]."""
+    from sliding_window_kv_amd import synth
+
+    u = synth.normal((Hkv, d), seed).astype(np.float64)
+    return u / np.linalg.norm(u, axis=1, keepdims=True)
+
+
+def plant_queries_(torch, q, u):
+    """q: device tensor [..., Hq, d]; adds sqrt(d) u_g to every query head of KV head g, in place."""
+    Hq, d = q.shape[-2], q.shape[-1]
+    n_rep = Hq // u.shape[0]
+    add = torch.from_numpy(np.repeat(u, n_rep, axis=0) * np.sqrt(d)).to(q.device, torch.float32)
+    q.copy_((q.float() + add).to(q.dtype))
+
+
+def needle_kv(u, n, seed):
+    """n needle rows: keys alpha u_g, values N(0, gamma^2); float64 [n, Hkv, d] each."""
+    from sliding_window_kv_amd import synth
+
+    K = np.broadcast_to(NEEDLE_ALPHA * u, (n,) + u.shape).copy()
+    V = NEEDLE_GAMMA * synth.normal((n,) + u.shape, seed).astype(np.float64)
+    return K, V
+
+
+def excess(gpu, ref, atol=2e-2, rtol=1e-2):
+    """max(|gpu - ref| - (atol + rtol |ref|)): > 0 means the bf16 comparison fails."""
+    return float(np.max(np.abs(gpu - ref) - (atol + rtol * np.abs(ref))))
+
+
+def attend_set(q, K, V, idx, Hkv):
+    """The oracle's attention of q [Hq, d] over the rows idx of K, V [n, Hkv, d] (a wrong visible
+    set for a negative control, or the true one)."""
+    import math
+
+    Hq, d = q.shape
+    n_rep = Hq // Hkv
+    idx = np.asarray(idx)
+    out = np.empty((Hq, d))
+    for g in range(Hkv):
+        Kg, Vg = K[idx, g], V[idx, g]
+        for h in range(g * n_rep, (g + 1) * n_rep):
+            out[h] = O.attend(q[h], Kg, Vg, 1.0 / math.sqrt(d))
+    return out

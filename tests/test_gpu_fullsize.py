@@ -3,7 +3,10 @@
 Sampled outputs are checked one by one against the fp64 oracle: whole
 sequences for decode, single query rows for prefill, random rows for the
 re-rotation.  Inputs are the seeded device buffers of the workload (filled by
-torch's generator), read back to the host for the oracle.
+torch's generator), read back to the host for the oracle.  The attention
+checks plant needle keys (tests/gpu_util.py) at sinks, window edges, 16-key
+block and split boundaries, and show with negative controls that the oracle
+over a wrong visible set fails the same tolerance.
 """
 import numpy as np
 import pytest
@@ -11,8 +14,9 @@ import pytest
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
 from tests.gpu_util import (EPS_APPEND_FP8, EPS_APPEND_I8, EPS_TURN_HADAMARD, EPS_TURN_I8, assert_bf16_close,
-                            assert_fp8_codes_valid, assert_int8_codes_valid, check_keep_scale_rows,
-                            int8_turn_quotients, oracle_cfg, to_np64, torch_dev)
+                            assert_fp8_codes_valid, assert_int8_codes_valid, attend_set, check_keep_scale_rows,
+                            excess, int8_turn_quotients, needle_dirs, needle_kv, oracle_cfg, plant_queries_,
+                            to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +30,57 @@ def env():
     from sliding_window_kv_amd import workloads as WL
 
     return R, torch, dev, WL
+
+
+def _split_keys(R, wl, max_tiles):
+    """Keys per split of the decode plan (the plan is read back from the workspace size)."""
+    n_rep = wl.Hq // wl.Hkv
+    splits = wl.ws_bytes // (wl.B * wl.Hkv * n_rep * (wl.d + 2) * 4)
+    return 16 * ((max_tiles + splits - 1) // splits)
+
+
+def _paged_full_needles(R, torch, wl, seqs, seed):
+    """Full-attention paged decode with needles, in the workload's own launch: needles at the first
+    and last keys, 16-key block edges, split edges and mid-sequence; negative controls drop key 0,
+    the last key, the block after the first split edge, or shift the set by 64."""
+    n, d, Hkv = wl.ctx, wl.d, wl.Hkv
+    sp = _split_keys(R, wl, wl.max_blocks)
+    pos = sorted({0, 15, 16, sp - 1, sp, n // 2 - 1, n // 2, n - sp - 1, n - sp, n - 2, n - 1})
+    u = needle_dirs(Hkv, d, seed)
+    Kn, Vn = needle_kv(u, len(pos), seed + 1)
+    planted = [(wl.k, Kn, wl.k_scale), (wl.v, Vn, wl.v_scale)]
+    if wl.kv8:  # 8-bit caches: the needle rows as the oracle quantises them (codes + row scales)
+        quant = O.quant_int8_rows if wl.kv8 == "i8" else O.quant_fp8_rows
+        planted = [(buf, quant(rows), sc) for buf, rows, sc in planted]
+    for b in seqs:
+        blk = torch.tensor([int(wl.table_host[b, j // 16]) for j in pos], device=wl.k.device)
+        slot = torch.tensor([j % 16 for j in pos], device=wl.k.device)
+        for buf, rows, sc in planted:
+            if wl.kv8:
+                codes, scale = rows
+                buf[blk, :, slot] = torch.from_numpy(codes.view(np.uint8)).to(buf.device).view(buf.dtype)
+                sc[blk, :, slot] = torch.from_numpy(scale).to(buf.device)
+            else:
+                buf[blk, :, slot] = torch.from_numpy(rows).to(buf.device, buf.dtype)
+        plant_queries_(torch, wl.q[b], u)
+    wl.decode()
+    torch.cuda.synchronize()
+    assert wl.err.item() == 0
+    out, q = to_np64(wl.out), to_np64(wl.q)
+    for b in seqs:
+        if wl.kv8:
+            dequant = O.dequant_int8_rows if wl.kv8 == "i8" else O.dequant_fp8_rows
+            kc, ks, vc, vs = wl.codes_of(b)
+            K, V = dequant(kc, ks), dequant(vc, vs)
+        else:
+            K, V = wl.kv_of(b)
+        ref = O.decode_attention(q[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
+        assert_bf16_close(out[b], ref)
+        assert np.max(np.abs(ref)) > 1.0  # the needles carry the output
+        every = np.arange(n)
+        wrong = [every[1:], every[:-1], np.r_[every[:sp], every[sp + 16:]], every[:-64]]
+        for idx in wrong:
+            assert excess(attend_set(q[b], K, V, idx, Hkv), ref) > 0
 
 
 def test_paged_decode_b64_ctx32768(env):
@@ -52,6 +107,16 @@ def test_paged_decode_b64_ctx32768(env):
         assert np.array_equal(v[p], v_raw[b])
         ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
         assert_bf16_close(out[b], ref)
+    # needles: the same layer decoded again with planted keys and queries
+    _paged_full_needles(R, torch, wl, (0, 37, 63), 2100)
+
+
+def test_paged_decode_b32_ctx131072(env):
+    # the full-attention layer of the windowed 128k stack: 32 sequences of 131072 keys, 8192 blocks each
+    R, torch, dev, WL = env
+    wl = WL.PagedDecode(R, torch, dev, B=32, ctx=131072, seed=3100)
+    wl.seq_len.fill_(wl.ctx)
+    _paged_full_needles(R, torch, wl, (0, 31), 3150)
 
 
 @pytest.mark.parametrize("kind", ["i8", "fp8"])
@@ -87,18 +152,33 @@ def test_paged_decode_b64_ctx32768_8bit(env, kind):
         v = dequant(vc, vs)
         ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
         assert_bf16_close(out[b], ref)
+    _paged_full_needles(R, torch, wl, (0, 63), 2200 + len(kind))
 
 
 def test_ring_decode_128k(env):
+    # one ring layer (head at a random offset, full ring): needles in the sink slots, the first and
+    # last ring slots, tile edges and the split edge; every ring slot is visible, so the negative
+    # controls drop the sinks, the tile after the split edge or the last slot
     R, torch, dev, WL = env
     r = WL.RingDecode(R, torch, dev)
+    C = r.C
+    sp = _split_keys(R, r, (C + 15) // 16)
+    slots = sorted({0, 3, 4, 15, 16, sp - 1, sp, 1000, 1001, C - 17, C - 16, C - 1})
+    u = needle_dirs(r.Hkv, r.d, 3050)
+    Kn, Vn = needle_kv(u, len(slots), 3051)
+    seqs = (0, 17, 31)
+    sl = torch.tensor(slots, device=r.k.device)
+    for b in seqs:
+        r.k[b][:, sl] = torch.from_numpy(Kn.transpose(1, 0, 2).copy()).to(r.k.device, r.k.dtype)
+        r.v[b][:, sl] = torch.from_numpy(Vn.transpose(1, 0, 2).copy()).to(r.k.device, r.k.dtype)
+        plant_queries_(torch, r.q[b], u)
     r.decode()
     torch.cuda.synchronize()
     assert r.err.item() == 0
     heads = r.head.cpu().numpy()
     out = to_np64(r.out)
     q = to_np64(r.q)
-    for b in (0, 17, 31):
+    for b in seqs:
         kc = to_np64(r.k[b])
         vc = to_np64(r.v[b])
         ring = O.RingSeq(sinks=r.S, window=r.W, head=int(heads[b]), count=r.W, seq_len=r.n)
@@ -106,39 +186,113 @@ def test_ring_decode_128k(env):
         ref = O.decode_attention(q[b], lambda j: kc[:, slot_of[j]], lambda j: vc[:, slot_of[j]], r.n, r.S, r.W,
                                  r.Hkv)
         assert_bf16_close(out[b], ref)
+        assert np.max(np.abs(ref)) > 1.0
+        K, V = kc.transpose(1, 0, 2), vc.transpose(1, 0, 2)  # by slot
+        every = np.arange(C)
+        for idx in (every[r.S:], np.r_[every[:sp], every[sp + 16:]], every[:-1]):
+            assert excess(attend_set(q[b], K, V, idx, r.Hkv), ref) > 0
 
 
 def test_windowed_paged_decode_b256(env):
+    # 256 sequences of the sink + window layer, lengths in [1k, 128k], blocks outside sinks and window
+    # null: needles at the sinks, at key 4 (inside the pinned sink block, invisible), at the key just
+    # outside the window (its block is live when it shares a block with the first visible key), the
+    # first visible key, block edges in the window and the newest key
     R, torch, dev, WL = env
     wd = WL.WindowedPagedDecode(R, torch, dev)
+    S, W = wd.S, wd.W
+    shares = [b for b in range(wd.B) if (int(wd.lens[b]) - W) % 16 != 0 and int(wd.lens[b]) > W + 40]
+    seqs = sorted({0, 100, 255, shares[0], shares[1]})
+    u = needle_dirs(wd.Hkv, wd.d, 5050)
+    planted = {}
+    for i, b in enumerate(seqs):
+        n = int(wd.lens[b])
+        p = n - 1
+        cand = {0, 3, 4, 5, p - W, p - W + 1, p - W + 16 - (p - W + 1) % 16, p - 16, p - 1, p}
+        row = wd.table_host[b]
+        pos = sorted(j for j in cand if 0 <= j <= p and row[j // 16] >= 0)
+        Kn, Vn = needle_kv(u, len(pos), 5051 + i)
+        blk = torch.tensor([int(row[j // 16]) for j in pos], device=wd.k.device)
+        slot = torch.tensor([j % 16 for j in pos], device=wd.k.device)
+        wd.k[blk, :, slot] = torch.from_numpy(Kn).to(wd.k.device, wd.k.dtype)
+        wd.v[blk, :, slot] = torch.from_numpy(Vn).to(wd.k.device, wd.k.dtype)
+        plant_queries_(torch, wd.q[b], u)
+        planted[b] = pos
     wd.decode()
     torch.cuda.synchronize()
     assert wd.err.item() == 0
     out, q = to_np64(wd.out), to_np64(wd.q)
     kp, vp = wd.k, wd.v
-    for b in (0, 100, 255):
+    n_outside = checked = 0
+    for b in seqs:
         n = int(wd.lens[b])
+        p = n - 1
         row = wd.table_host[b]
-        vis = O.visible_positions(n - 1, wd.S, wd.W)
-        blocks = sorted({row[j // 16] for j in vis})
-        idx = torch.tensor(blocks, dtype=torch.long, device=kp.device)
-        kb = dict(zip(blocks, to_np64(kp[idx])))
-        vb = dict(zip(blocks, to_np64(vp[idx])))
-        ref = O.decode_attention(q[b], lambda j: kb[row[j // 16]][:, j % 16], lambda j: vb[row[j // 16]][:, j % 16],
-                                 n, wd.S, wd.W, wd.Hkv)
+        live = sorted({int(x) for x in row if x >= 0})
+        idx = torch.tensor(live, dtype=torch.long, device=kp.device)
+        kb = dict(zip(live, to_np64(kp[idx])))
+        vb = dict(zip(live, to_np64(vp[idx])))
+
+        def kf(j, row=row):
+            return kb[int(row[j // 16])][:, j % 16]
+
+        def vf(j, row=row):
+            return vb[int(row[j // 16])][:, j % 16]
+
+        ref = O.decode_attention(q[b], kf, vf, n, S, W, wd.Hkv)
         assert_bf16_close(out[b], ref)
+        assert np.max(np.abs(ref)) > 1.0
+        # negative controls: the oracle's visible set with no sinks, one sink more (admits key 4), the
+        # window one shorter (drops the first visible key) and, when its block is live, one longer;
+        # each one that changes which needles are visible must fail the tolerance
+        needles = set(planted[b])
+        vis = set(O.visible_positions(p, S, W)) & needles
+        controls = [(0, W), (S + 1, W), (S, W - 1)]
+        if p >= W and row[(p - W) // 16] >= 0:
+            controls.append((S, W + 1))
+            n_outside += 1
+        for s2, w2 in controls:
+            if set(O.visible_positions(p, s2, w2)) & needles != vis:
+                bad = O.decode_attention(q[b], kf, vf, n, s2, w2, wd.Hkv)
+                assert excess(bad, ref) > 0, (b, s2, w2)
+                checked += 1
+    assert n_outside >= 2  # the key just outside the window was planted in a live block
+    assert checked >= 10
 
 
 def test_prefill_t8192_sampled_rows(env):
+    # the 8192-token chunk over sink(4) + window(4096): the sampled rows get planted query components,
+    # and needle keys sit at the sinks, keys 4 and 5 (the first to leave the window, at rows 4100 and
+    # 4101), 64-key tile edges, the window edges of the last row (4095 | 4096) and the newest keys
     R, torch, dev, WL = env
     pf = WL.Prefill(R, torch, dev)
+    S, W = pf.S, pf.W
+    rows = (0, 1, 15, 16, 63, 64, 4095, 4096, 4097, 4099, 4100, 4101, 5000, 8190, 8191)
+    keys = [0, 3, 4, 5, 63, 64, 127, 128, 904, 4095, 4096, 4097, 8190, 8191]
+    u = needle_dirs(pf.Hkv, pf.d, 6050)
+    Kn, Vn = needle_kv(u, len(keys), 6051)
+    kk = torch.tensor(keys, device=pf.k.device)
+    pf.k[kk] = torch.from_numpy(Kn).to(pf.k.device, pf.k.dtype)
+    pf.v[kk] = torch.from_numpy(Vn).to(pf.k.device, pf.k.dtype)
+    for t in rows:
+        plant_queries_(torch, pf.q[t], u)
     pf.run()
     torch.cuda.synchronize()
     assert pf.int_state[3].item() == 0
     q, k, v, out = to_np64(pf.q), to_np64(pf.k), to_np64(pf.v), to_np64(pf.out)
-    for t in (0, 1, 15, 16, 63, 64, 4095, 4099, 4100, 4101, 5000, 8191):
-        ref = O.decode_attention(q[t], lambda j: k[j], lambda j: v[j], t + 1, pf.S, pf.W, pf.Hkv)
+    needles = set(keys)
+    checked = 0
+    for t in rows:
+        ref = O.decode_attention(q[t], lambda j: k[j], lambda j: v[j], t + 1, S, W, pf.Hkv)
         assert_bf16_close(out[t], ref)
+        assert np.max(np.abs(ref)) > 1.0
+        vis = set(O.visible_positions(t, S, W))
+        for s2, w2 in ((0, W), (S + 1, W), (S, W - 1), (S, W + 1)):
+            if set(O.visible_positions(t, s2, w2)) & needles != vis & needles:
+                bad = O.decode_attention(q[t], lambda j: k[j], lambda j: v[j], t + 1, s2, w2, pf.Hkv)
+                assert excess(bad, ref) > 0, (t, s2, w2)
+                checked += 1
+    assert checked >= 16
 
 
 @pytest.mark.parametrize("kind", ["f16", "i8", "i8_keep", "i8_hadamard"])

@@ -14,8 +14,9 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_int8_codes_valid,
-                            int8_turn_quotients, normwise, oracle_cfg, rowwise, to_np64, torch_dev)
+from tests.gpu_util import (EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_int8_codes_valid, attend_set,
+                            excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
+                            plant_queries_, rowwise, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -360,8 +361,23 @@ def test_decode_paged_few_long_sequences(env, B, Hkv, n):
     lens = [n - 7 * b for b in range(B)]
     cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
     q = _fill(torch, torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev), 54)
+    ws_bytes = R.decode_workspace_size(B, Hq, cache.desc)
+    # needles at the first and last keys and on both sides of every split edge
+    splits = ws_bytes // (B * Hkv * n_rep * (d + 2) * 4)
+    sp = 16 * ((max_blocks + splits - 1) // splits)
+    u = needle_dirs(Hkv, d, 55)
+    for b, nb in enumerate(lens):
+        edges = list(range(sp, nb, sp))
+        edges = sorted({edges[0], edges[1], edges[len(edges) // 2], edges[-1]})
+        pos = sorted({0, nb - 1} | {e + o for e in edges for o in (-1, 0)})
+        Kn, Vn = needle_kv(u, len(pos), 56 + b)
+        blk = torch.tensor([int(table[b, j // 16]) for j in pos], device=dev)
+        slot = torch.tensor([j % 16 for j in pos], device=dev)
+        cache.k[blk, :, slot] = torch.from_numpy(Kn).to(dev, torch.bfloat16)
+        cache.v[blk, :, slot] = torch.from_numpy(Vn).to(dev, torch.bfloat16)
+        plant_queries_(torch, q[b], u)
     out = torch.empty_like(q)
-    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    ws = torch.empty(ws_bytes // 4 + 1, dtype=torch.float32, device=dev)
     R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
     torch.cuda.synchronize()
     assert cache.err.item() == 0
@@ -376,6 +392,12 @@ def test_decode_paged_few_long_sequences(env, B, Hkv, n):
         V = vp[rows, :, slots]
         ref = O.decode_attention(qq[b], lambda j: K[j], lambda j: V[j], nb, 0, 0, Hkv)
         assert_bf16_close(got[b], ref)
+        assert np.max(np.abs(ref)) > 1.0
+        every = np.arange(nb)
+        # negative controls: drop the block after the middle needle split edge, or the last key
+        e = edges[len(edges) // 2]
+        for idx in (np.r_[every[:e], every[e + 16:]], every[:-1]):
+            assert excess(attend_set(qq[b], K, V, idx, Hkv), ref) > 0
 
 
 def test_decode_paged_window_with_null_blocks(env):
