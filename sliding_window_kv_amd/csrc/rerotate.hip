@@ -87,6 +87,37 @@ __device__ inline void turn_table(const RerotArgs &a, int pa, int np, float *s_c
   __syncthreads();
 }
 
+// As turn_table, with the frequency change w_to,i - w_from,i of this thread's pair i =
+// threadIdx.x % half read by the caller up front (own_dw): the change sits in the kernel
+// arguments and is read with a vector load, which the caller issues before its own global
+// loads, so that waiting for it does not also wait for those.  When the workgroup size is a
+// multiple of half, every entry a thread computes has that pair; otherwise later entries read
+// their own change.
+__device__ __forceinline__ double own_dw(const RerotArgs &a) {
+  return a.dw[threadIdx.x % (a.to.rotary_dim / 2)];
+}
+__device__ inline void turn_table_w(const RerotArgs &a, int pa, int np, float *s_cs, float *s_sn, double dwt,
+                                    float *s_nsn = nullptr) {
+  const int half = a.to.rotary_dim / 2;
+  const float gain = (float)a.gain;
+  const bool same_pair = blockDim.x % half == 0;
+  for (int idx = threadIdx.x; idx < np * half; idx += blockDim.x) {
+    const int pt = idx / half, i = idx - pt * half;
+    const double th = (double)(a.pos0 + pa + pt) * (same_pair || idx == (int)threadIdx.x ? dwt : a.dw[i]);
+    const double k = rint(th * 0.15915494309189535);                  // turns of 2 pi
+    const double rd = fma(-k, 2.4492935982947064e-16, fma(-k, 6.283185307179586, th));
+    float sf, cf;
+    sincosf((float)rd, &sf, &cf);
+    s_cs[idx] = cf * gain;
+    s_sn[idx] = sf * gain;
+    if (s_nsn) s_nsn[idx] = -(sf * gain);
+  }
+  // the table is LDS-only: wait for this wave's LDS writes, then the workgroup barrier, without
+  // the wait on outstanding global loads a __syncthreads() fence would add (the memory clobber
+  // keeps the compiler from moving the table's reads above the barrier)
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Keep-scale decision for one int8 row: every turned rotary value of the row must
 // re-code within [-127, 127] at the row's old scale (decided like the quantiser, in
 // fp32 with the reciprocal of the scale).  `mx` is this lane's largest such code,
@@ -419,6 +450,365 @@ __global__ __launch_bounds__(kI8Threads) void rerotate_int8_lanes_kernel(RerotAr
     }
     if (q == 0) *sp = inv > 0.f ? sco * (amax / 127.0f) : 0.f;
   }
+  }
+}
+
+// ---- Chunk kernels: one 16-byte chunk of a row per thread.
+//
+// On this part an in-place stream of 16-byte chunks runs fastest in small one-shot
+// workgroups (128 threads, one layer each) whose loads and stores stream past the
+// caches (sc0 sc1 nt): a probe over a 32 GiB buffer moved 6.5 TB/s both for whole
+// rows and for the rotary half of 256-byte fp16 rows (read + write counted), against
+// 5.3 TB/s for the same half rows with cached loads and stores in 256-thread
+// workgroups.  A row's chunks sit in adjacent lanes; under NeoX pairing the chunks of
+// the first half of the rotary slice hold the first members of pairs and the chunks
+// of the second half the partners, R / 2 lanes away (R rotary chunks per row, R / 2 a
+// power of two), so a pair's partner comes from one lane exchange.  GPT-J pairs
+// (2i, 2i + 1) lie inside a chunk.
+
+// The value of lane l ^ M for M = 1, 2, 4, 8 (lane groups inside rows of 16 lanes) by DPP lane
+// moves, no LDS round trip; larger M by a cross-lane permute.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm 1, 0, 3, 2
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm 2, 3, 0, 1
+  } else if constexpr (M == 4 || M == 8) {
+    // row_shl:M reads lane l + M, row_shr:M lane l - M; a lane keeps the one inside its row
+    const uint32_t up = __builtin_amdgcn_mov_dpp(v, 0x100 + M, 0xF, 0xF, true);
+    const uint32_t dn = __builtin_amdgcn_mov_dpp(v, 0x110 + M, 0xF, 0xF, true);
+    return (__lane_id() & M) ? dn : up;
+  } else {
+    return (uint32_t)__shfl_xor((int)v, M);
+  }
+}
+template <int M>
+__device__ __forceinline__ float xor_lane_f(float v) {
+  return __uint_as_float(xor_lane<M>(__float_as_uint(v)));
+}
+// max over the aligned group of G lanes (G a power of two <= 64)
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (G >= 2) v = fmaxf(v, xor_lane_f<1>(v));
+  if constexpr (G >= 4) v = fmaxf(v, xor_lane_f<2>(v));
+  if constexpr (G >= 8) v = fmaxf(v, xor_lane_f<4>(v));
+  if constexpr (G >= 16) v = fmaxf(v, xor_lane_f<8>(v));
+  if constexpr (G >= 32) v = fmaxf(v, xor_lane_f<16>(v));
+  if constexpr (G >= 64) v = fmaxf(v, xor_lane_f<32>(v));
+  return v;
+}
+
+constexpr int kChunkThreads = 128;
+constexpr int kI8Chunks = 4;  // int8 chunk kernel: row blocks (chunks per thread) per workgroup
+constexpr int kFloatChunks = 1;  // float chunk kernel: row blocks per workgroup
+constexpr int kI8HalfChunks = 1;  // int8 half-rotary kernel: row blocks per workgroup
+constexpr int kStream = 19;  // buffer cache policy: sc0 | nt | sc1
+
+typedef decltype(__builtin_amdgcn_raw_buffer_load_b128(__amdgpu_buffer_rsrc_t(), 0, 0, 0)) b128_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(void *base, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void chunk_load(uint32_t *w, __amdgpu_buffer_rsrc_t r, int off) {
+  const b128_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
+  w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+}
+__device__ __forceinline__ void chunk_store(const uint32_t *w, __amdgpu_buffer_rsrc_t r, int off) {
+  b128_t v;
+  v[0] = w[0]; v[1] = w[1]; v[2] = w[2]; v[3] = w[3];
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStream);
+}
+
+// Float keys: R = r * sizeof(T) / 16 rotary chunks per row (R a power of two, R <= 32); a
+// workgroup owns NCH blocks of kChunkThreads / R consecutive rows of one layer, each thread one
+// chunk of every block, all loads issued before the first turn; chunk c sits at byte 16 c of
+// its row.  Rows past the layer's end lie beyond the buffer resource's extent: their loads
+// return zeros without touching memory and they store nothing.
+template <typename T, int R, int NCH, bool NEOX>
+__global__ __launch_bounds__(kChunkThreads) void rerotate_float_chunk_kernel(RerotArgs a) {
+  constexpr int EB = sizeof(T);
+  constexpr int CPE = 16 / EB;  // elements per chunk
+  constexpr int RB = kChunkThreads / R;  // rows per block
+  extern __shared__ float s_tab[];
+  const int half = a.to.rotary_dim / 2;
+  const ChunkRows c = chunk_rows(a);
+  const int rr = threadIdx.x / R, ch = threadIdx.x % R;
+  const int rowb = a.D * EB;
+  const __amdgpu_buffer_rsrc_t rs = span_rsrc((char *)a.k + c.row0 * rowb, (long)c.nrows * rowb);
+  const double dwt = own_dw(a);
+  uint32_t w[NCH][4];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) chunk_load(w[k], rs, (rr + k * RB) * rowb + 16 * ch);  // in flight during the table
+  float *s_cs = s_tab, *s_sn = s_tab + c.np * half;
+  turn_table_w(a, c.pa, c.np, s_cs, s_sn, dwt);
+  // pair base of this chunk
+  const int pb = NEOX ? CPE * (ch % (R / 2)) : CPE / 2 * ch;
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int row = rr + k * RB;
+    const bool live = row < c.nrows;
+    const float *cs = &s_cs[((c.r0 + (live ? row : 0)) / a.Hkv - c.pa) * half + pb];
+    const float *sn = &s_sn[((c.r0 + (live ? row : 0)) / a.Hkv - c.pa) * half + pb];
+    uint32_t *v = w[k];
+    if constexpr (NEOX) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = xor_lane<R / 2>(v[i]);
+      const bool first = ch < R / 2;  // holds first members (x1), the partner holds x2
+#pragma unroll
+      for (int e = 0; e < CPE; e += 2) {
+        const float own0 = vget<T>(v, e), own1 = vget<T>(v, e + 1);
+        const float par0 = vget<T>(pw, e), par1 = vget<T>(pw, e + 1);
+        const float y0 = first ? own0 * cs[e] - par0 * sn[e] : own0 * cs[e] + par0 * sn[e];
+        const float y1 = first ? own1 * cs[e + 1] - par1 * sn[e + 1] : own1 * cs[e + 1] + par1 * sn[e + 1];
+        vput2<T>(v, e, y0, y1);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPE; e += 2) {
+        const float x1 = vget<T>(v, e), x2 = vget<T>(v, e + 1);
+        vput2<T>(v, e, x1 * cs[e / 2] - x2 * sn[e / 2], x2 * cs[e / 2] + x1 * sn[e / 2]);
+      }
+    }
+    if (live) chunk_store(v, rs, row * rowb + 16 * ch);
+  }
+}
+
+// int8 keys with a per-row fp32 scale, turned in code units (see the lane kernel below):
+// L = D / 16 lanes per row with 16 codes each, RC = r / 16 rotary chunks (NeoX: RC / 2 a
+// power of two).  A workgroup owns NCH blocks of kChunkThreads / L consecutive rows of one
+// layer and each thread one chunk of every block: all the blocks' loads are issued before
+// any of them is turned, so one wait for memory serves NCH chunks (workgroups are short-lived
+// and their lifetime is the memory wait plus the turn).  Every lane runs the same
+// instructions: a lane of the tail turns by the identity (cos 1, sin 0, from a constant block
+// of the table), and the NeoX sign of the partner term comes from a negated copy of the sine
+// rows, so no lane waits while its row's other lanes take another branch.  The row's turned
+// rotary maximum and overall maximum are reductions over its L lanes.
+// Table layout (dynamic LDS, floats): cos [np][half], sin [np][half], -sin [np][half], then 16
+// ones and 16 zeros.
+template <int L, bool NEOX, bool KEEP>
+__device__ __forceinline__ void turn_i8_chunk(const uint32_t *w, float sco, bool live, bool rot, int hc,
+                                              const float *cs, const float *sn, __amdgpu_buffer_rsrc_t rs,
+                                              __amdgpu_buffer_rsrc_t rsc, int off, int soff, bool lead) {
+  uint32_t pw[4] = {0u, 0u, 0u, 0u};
+  if constexpr (NEOX) {
+    // partner chunk hc = RC / 2 lanes away, a power of two <= L / 2 (checked on the host); tail
+    // lanes exchange too and multiply the partner by zero (uniform branch on the rotary width)
+    switch (hc) {
+      case 1:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[i] = xor_lane<1>(w[i]);
+        break;
+      case 2:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[i] = xor_lane<2>(w[i]);
+        break;
+      case 4:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[i] = xor_lane<4>(w[i]);
+        break;
+      default:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[i] = xor_lane<8>(w[i]);
+        break;
+    }
+  }
+  float y[16];
+  float m = 0.f;
+  if constexpr (NEOX) {
+    // 16 cos and 16 sin, 16-byte reads (every table row and block starts 64-byte aligned)
+    float4 c4[4], s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c4[i] = ((const float4 *)cs)[i];
+      s4[i] = ((const float4 *)sn)[i];
+    }
+    const float *cv = (const float *)c4, *sv = (const float *)s4;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      y[e] = fmaf(code_at(pw, e), sv[e], code_at(w, e) * cv[e]);
+      m = fmaxf(m, fabsf(y[e]));
+    }
+  } else {
+    float4 c4[2], s4[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      c4[i] = ((const float4 *)cs)[i];
+      s4[i] = ((const float4 *)sn)[i];
+    }
+    const float *cv = (const float *)c4, *sv = (const float *)s4;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float x1 = code_at(w, e), x2 = code_at(w, e + 1);
+      y[e] = x1 * cv[e / 2] - x2 * sv[e / 2];
+      y[e + 1] = x2 * cv[e / 2] + x1 * sv[e / 2];
+      m = fmaxf(m, fmaxf(fabsf(y[e]), fabsf(y[e + 1])));
+    }
+  }
+  const float amax = group_max<L>(m);
+  bool keep = false;
+  if constexpr (KEEP) keep = group_max<L>(rot ? m : 0.f) < 127.5f;
+  const float inv = keep ? 1.0f : (amax > 0.f && sco > 0.f ? 127.0f / amax : 0.f);
+  if (!live || (keep && !rot)) return;
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    out[i] = pack4_codes(code_fma(y[4 * i], inv), code_fma(y[4 * i + 1], inv), code_fma(y[4 * i + 2], inv),
+                         code_fma(y[4 * i + 3], inv));
+  chunk_store(out, rs, off);
+  if (!keep && lead)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, inv > 0.f ? sco * (amax / 127.0f) : 0.f), rsc,
+                                          soff, 0, kStream);
+}
+
+template <int L, int NCH, bool NEOX, bool KEEP>
+__global__ __launch_bounds__(kChunkThreads) void rerotate_int8_chunk_kernel(RerotArgs a) {
+  constexpr int RB = kChunkThreads / L;  // rows per block
+  extern __shared__ float s_tab[];
+  const int half = a.to.rotary_dim / 2;
+  const ChunkRows c = chunk_rows(a);
+  const int rr = threadIdx.x / L, ch = threadIdx.x % L;
+  const __amdgpu_buffer_rsrc_t rs = span_rsrc((char *)a.k + c.row0 * a.D, (long)c.nrows * a.D);
+  const __amdgpu_buffer_rsrc_t rsc = span_rsrc(a.scale + c.row0, (long)c.nrows * 4);
+  const double dwt = own_dw(a);
+  // every block's chunk and scale in flight while the turn table is built; rows past the
+  // layer's end lie beyond the buffer resources' extents, so their loads return zeros without
+  // touching memory
+  uint32_t w[NCH][4];
+  float sco[NCH];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    chunk_load(w[k], rs, (rr + k * RB) * a.D + 16 * ch);
+    sco[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * (rr + k * RB), 0, kStream));
+  }
+  const int nt = c.np * half;
+  float *s_cs = s_tab, *s_sn = s_tab + nt, *s_nsn = s_tab + 2 * nt, *s_id = s_tab + 3 * nt;
+  if (threadIdx.x < 32) s_id[threadIdx.x] = threadIdx.x < 16 ? 1.0f : 0.0f;
+  turn_table_w(a, c.pa, c.np, s_cs, s_sn, dwt, s_nsn);
+  // this lane's table columns (the same in every block) and rows (one per position)
+  const int RC = a.to.rotary_dim / 16, hc = RC >> 1;
+  const bool rot = ch < RC;
+  const int col = NEOX ? 16 * (ch & (hc - 1)) : 8 * ch;
+  const float *cs0 = rot ? s_cs + col : s_id;
+  const float *sn0 = rot ? (NEOX && ch < hc ? s_nsn : s_sn) + col : s_id + 16;  // NeoX first members: x1 cos - x2 sin
+  const int rstep = rot ? half : 0;  // tail lanes stay on the identity block
+  const int pos_r = (c.r0 + rr) / a.Hkv - c.pa;
+  const bool even = RB % a.Hkv == 0;  // blocks start at whole positions: positions step by RB / Hkv
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int row = rr + k * RB;
+    const bool live = row < c.nrows;
+    const int pr = even ? pos_r + k * (RB / a.Hkv) : (c.r0 + (live ? row : 0)) / a.Hkv - c.pa;
+    const int prow = (live ? pr : 0) * rstep;
+    turn_i8_chunk<L, NEOX, KEEP>(w[k], sco[k], live, rot, hc, cs0 + prow, sn0 + prow, rs, rsc, row * a.D + 16 * ch,
+                                 4 * row, ch == 0);
+  }
+}
+
+// int8 keys whose rotary slice is half the row (r = D / 2): H = D / 32 lanes per row, lane q
+// holding rotary chunk q (codes 16 q ..) and tail chunk q (codes r + 16 q ..), so every lane
+// turns 16 codes and requantises 32 with no lane idle; NeoX partners sit RC / 2 = H / 2 lanes
+// away.  A workgroup owns NCH blocks of kChunkThreads / H rows of one layer, all loads issued
+// before the first turn (as the chunk kernel above).  Table layout as the chunk kernel's,
+// without the identity block.
+template <int H, int NCH, bool NEOX, bool KEEP>
+__global__ __launch_bounds__(kChunkThreads) void rerotate_int8_half_kernel(RerotArgs a) {
+  constexpr int RB = kChunkThreads / H;  // rows per block
+  extern __shared__ float s_tab[];
+  const int half = a.to.rotary_dim / 2;  // = 8 H pairs
+  const ChunkRows c = chunk_rows(a);
+  const int rr = threadIdx.x / H, q = threadIdx.x % H;
+  const __amdgpu_buffer_rsrc_t rs = span_rsrc((char *)a.k + c.row0 * a.D, (long)c.nrows * a.D);
+  const __amdgpu_buffer_rsrc_t rsc = span_rsrc(a.scale + c.row0, (long)c.nrows * 4);
+  const double dwt = own_dw(a);
+  uint32_t wr[NCH][4], wt[NCH][4];
+  float sco[NCH];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int o = (rr + k * RB) * a.D + 16 * q;
+    chunk_load(wr[k], rs, o);
+    chunk_load(wt[k], rs, o + a.to.rotary_dim);
+    sco[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * (rr + k * RB), 0, kStream));
+  }
+  const int nt = c.np * half;
+  float *s_cs = s_tab, *s_sn = s_tab + nt, *s_nsn = s_tab + 2 * nt;
+  turn_table_w(a, c.pa, c.np, s_cs, s_sn, dwt, s_nsn);
+  constexpr int HC = H / 2;  // NeoX: partner lane distance
+  const int col = NEOX ? 16 * (q & (HC - 1)) : 8 * q;
+  const float *cs0 = s_cs + col;
+  const float *sn0 = (NEOX && q < HC ? s_nsn : s_sn) + col;  // NeoX first members: x1 cos - x2 sin
+  const int pos_r = (c.r0 + rr) / a.Hkv - c.pa;
+  const bool even = RB % a.Hkv == 0;
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int row = rr + k * RB;
+    const bool live = row < c.nrows;
+    const int pr = even ? pos_r + k * (RB / a.Hkv) : (c.r0 + (live ? row : 0)) / a.Hkv - c.pa;
+    const float *cs = cs0 + (live ? pr : 0) * half;
+    const float *sn = sn0 + (live ? pr : 0) * half;
+    const uint32_t *w = wr[k];
+    float y[16], t[16];
+    float mr = 0.f, mt = 0.f;
+    if constexpr (NEOX) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = xor_lane<HC>(w[i]);
+      float4 c4[4], s4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c4[i] = ((const float4 *)cs)[i];
+        s4[i] = ((const float4 *)sn)[i];
+      }
+      const float *cv = (const float *)c4, *sv = (const float *)s4;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        y[e] = fmaf(code_at(pw, e), sv[e], code_at(w, e) * cv[e]);
+        mr = fmaxf(mr, fabsf(y[e]));
+      }
+    } else {
+      float4 c4[2], s4[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        c4[i] = ((const float4 *)cs)[i];
+        s4[i] = ((const float4 *)sn)[i];
+      }
+      const float *cv = (const float *)c4, *sv = (const float *)s4;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float x1 = code_at(w, e), x2 = code_at(w, e + 1);
+        y[e] = x1 * cv[e / 2] - x2 * sv[e / 2];
+        y[e + 1] = x2 * cv[e / 2] + x1 * sv[e / 2];
+        mr = fmaxf(mr, fmaxf(fabsf(y[e]), fabsf(y[e + 1])));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      t[e] = code_at(wt[k], e);
+      mt = fmaxf(mt, fabsf(t[e]));
+    }
+    mr = group_max<H>(mr);
+    const float amax = fmaxf(mr, group_max<H>(mt));
+    const bool keep = KEEP && mr < 127.5f;
+    const float inv = keep ? 1.0f : (amax > 0.f && sco[k] > 0.f ? 127.0f / amax : 0.f);
+    if (!live) continue;
+    const int o = row * a.D + 16 * q;
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[i] = pack4_codes(code_fma(y[4 * i], inv), code_fma(y[4 * i + 1], inv), code_fma(y[4 * i + 2], inv),
+                           code_fma(y[4 * i + 3], inv));
+    chunk_store(out, rs, o);
+    if (!keep) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[i] = pack4_codes(code_fma(t[4 * i], inv), code_fma(t[4 * i + 1], inv), code_fma(t[4 * i + 2], inv),
+                             code_fma(t[4 * i + 3], inv));
+      chunk_store(out, rs, o + a.to.rotary_dim);
+      if (q == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, inv > 0.f ? sco[k] * (amax / 127.0f) : 0.f),
+                                              rsc, 4 * row, 0, kStream);
+    }
   }
 }
 
@@ -1016,6 +1406,76 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
     return dim3((unsigned)((long)a.chunks * ((n_layers + a.lg - 1) / a.lg)));
   };
   size_t shm1 = 0;
+  // chunk kernels (one 16-byte chunk per thread) where the row shape allows them
+  {
+    auto pow2 = [](int x) { return x > 0 && (x & (x - 1)) == 0; };
+    const bool nx = to.neox != 0;
+    if (c.kv_dtype == ROPEKV_F16 || c.kv_dtype == ROPEKV_BF16 || c.kv_dtype == ROPEKV_F32) {
+      const int eb = c.kv_dtype == ROPEKV_F32 ? 4 : 2;
+      const int R = to.rotary_dim * eb / 16;
+      if ((to.rotary_dim * eb) % 16 == 0 && pow2(R) && R >= 2 && R <= 32) {
+        a.lg = 1;
+        const dim3 g1 = one_shot(kFloatChunks * kChunkThreads / R, shm1);
+        auto go = [&](auto tag, auto rtag) {
+          using T = decltype(tag);
+          constexpr int RR = decltype(rtag)::value, NC = kFloatChunks;
+          if (nx) hipLaunchKernelGGL((rerotate_float_chunk_kernel<T, RR, NC, true>), g1, dim3(kChunkThreads), shm1, s, a);
+          else hipLaunchKernelGGL((rerotate_float_chunk_kernel<T, RR, NC, false>), g1, dim3(kChunkThreads), shm1, s, a);
+        };
+        auto by_r = [&](auto tag) {
+          switch (R) {
+            case 2: go(tag, std::integral_constant<int, 2>()); break;
+            case 4: go(tag, std::integral_constant<int, 4>()); break;
+            case 8: go(tag, std::integral_constant<int, 8>()); break;
+            case 16: go(tag, std::integral_constant<int, 16>()); break;
+            default: go(tag, std::integral_constant<int, 32>()); break;
+          }
+        };
+        if (c.kv_dtype == ROPEKV_F16) by_r(f16_t());
+        else if (c.kv_dtype == ROPEKV_BF16) by_r(bf16_t());
+        else by_r(float());
+        return hipGetLastError();
+      }
+    } else if (c.kv_dtype == ROPEKV_I8 && !(c.k_int8_mode & ROPEKV_I8_HADAMARD)) {
+      const int L = c.head_dim / 16, RC = to.rotary_dim / 16;
+      if (a.keep_scale && c.head_dim % 32 == 0 && 2 * to.rotary_dim == c.head_dim && (L == 8 || L == 16)) {
+        // keep-scale with the rotary slice half the row: one rotary and one tail chunk per lane
+        // (measured on the 64-layer switch: 5.2 TB/s against 4.9 for the chunk kernel, which
+        // stays ahead for the requantising turn, 5.6 against 5.3)
+        a.lg = 1;
+        const int H = L / 2;
+        const dim3 g1 = one_shot(kI8HalfChunks * kChunkThreads / H, shm1);
+        shm1 = shm1 / 2 * 3;  // cos, sin, -sin planes
+        auto go = [&](auto htag) {
+          constexpr int HH = decltype(htag)::value, NC = kI8HalfChunks;
+          if (nx) hipLaunchKernelGGL((rerotate_int8_half_kernel<HH, NC, true, true>), g1, dim3(kChunkThreads), shm1, s, a);
+          else hipLaunchKernelGGL((rerotate_int8_half_kernel<HH, NC, false, true>), g1, dim3(kChunkThreads), shm1, s, a);
+        };
+        if (H == 4) go(std::integral_constant<int, 4>());
+        else go(std::integral_constant<int, 8>());
+        return hipGetLastError();
+      }
+      const bool shape_ok = c.head_dim % 16 == 0 && (L == 4 || L == 8 || L == 16) && to.rotary_dim % 16 == 0 &&
+                            (!nx || (RC % 2 == 0 && pow2(RC / 2)));
+      if (shape_ok) {
+        a.lg = 1;
+        const dim3 g1 = one_shot(kI8Chunks * kChunkThreads / L, shm1);
+        shm1 = shm1 / 2 * 3 + 32 * sizeof(float);  // cos, sin, -sin planes and the identity block
+        const bool kp = a.keep_scale != 0;
+        auto go = [&](auto ltag) {
+          constexpr int LL = decltype(ltag)::value, NC = kI8Chunks;
+          if (nx && kp) hipLaunchKernelGGL((rerotate_int8_chunk_kernel<LL, NC, true, true>), g1, dim3(kChunkThreads), shm1, s, a);
+          else if (nx) hipLaunchKernelGGL((rerotate_int8_chunk_kernel<LL, NC, true, false>), g1, dim3(kChunkThreads), shm1, s, a);
+          else if (kp) hipLaunchKernelGGL((rerotate_int8_chunk_kernel<LL, NC, false, true>), g1, dim3(kChunkThreads), shm1, s, a);
+          else hipLaunchKernelGGL((rerotate_int8_chunk_kernel<LL, NC, false, false>), g1, dim3(kChunkThreads), shm1, s, a);
+        };
+        if (L == 4) go(std::integral_constant<int, 4>());
+        else if (L == 8) go(std::integral_constant<int, 8>());
+        else go(std::integral_constant<int, 16>());
+        return hipGetLastError();
+      }
+    }
+  }
   switch (c.kv_dtype) {
     case ROPEKV_I8: {
       if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {

@@ -290,12 +290,15 @@ class Rerotate:
     def run(self, s_from: float, s_to: float):
         self.R.rerotate(self.cfg(s_from), self.cfg(s_to), self.desc, self.L)
 
-    def bytes(self) -> int:
-        """fp16: the rotary slice read and written.  int8: the row and its scale read and written
-        (keep-scale: the row read, the rotary codes written; rows that overflow write more, uncounted)."""
+    def bytes(self, kept_fraction=None) -> int:
+        """fp16: the rotary slice read and written.  int8: the row and its scale read and written.
+        Keep-scale: every row and scale read; a row that keeps its scale writes its rotary codes,
+        one that overflows writes the whole row and its scale (kept_fraction: the measured share of
+        rows that kept their scale; None counts every row as kept)."""
         rows = self.L * self.T * self.Hkv
         if self.kind == "f16":
             return 2 * rows * self.r * 2
         if self.kind == "i8_keep":
-            return rows * (self.d + 4 + self.r)
+            kept = rows if kept_fraction is None else int(round(rows * kept_fraction))
+            return rows * (self.d + 4) + kept * self.r + (rows - kept) * (self.d + 4)
         return 2 * rows * (self.d + 4)
