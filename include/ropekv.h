@@ -195,7 +195,10 @@ int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_
                         int32_t freed_capacity, int32_t *n_freed, ropekv_stream_t stream);
 
 /* Bytes of fp32 workspace ropekv_decode_attn needs for this batch and cache
- * (split-K partials [batch, Hkv, splits, n_rep, d + 2]).  0 on bad input. */
+ * (split-K partials [batch, Hkv, splits, n_rep, d + 2]).  0 on bad input, and 0
+ * for plans without partials: F32 / BF16 caches with at least 256 (sequence, KV
+ * head) units of at most 512 16-row tiles each get one workgroup per unit that
+ * writes its output directly. */
 size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const ropekv_kv_cache *cache);
 
 /* Decode attention ([SINK] the incremental path; [GOSS] 4.3 decode, 4.4 GQA):
@@ -203,7 +206,9 @@ size_t ropekv_decode_workspace_size(int32_t batch, int32_t n_q_heads, const rope
  * out[b][h] = softmax(q[b][h] . K_j * scale) V_j over the keys j visible to
  * position n - 1, with K / V of KV head h / (n_q_heads / Hkv).  The keys are
  * read in place (no gather, no repeat of KV heads).  Split-K partials go to
- * ws; a second launch combines them.  n == 0 gives a zero row.
+ * ws and a second launch combines them, unless the plan has one workgroup per
+ * (sequence, KV head) (see ropekv_decode_workspace_size).  n == 0 gives a zero
+ * row.
  *   q   [batch, n_q_heads, d] kv_dtype (rotated), out same shape and dtype
  *   scale: 0 means 1/sqrt(d)
  *   sink_logits: NULL, or device fp32 [n_q_heads] learned sink logits ([RoPE]

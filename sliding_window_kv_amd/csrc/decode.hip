@@ -82,19 +82,27 @@ struct TileFrag {
   bool vis[4];
 };
 
-template <typename T, int D, int NREP>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void decode_split_kernel(const void *__restrict__ qp, ropekv_kv_cache c,
-                                                           float sl2, float *__restrict__ ws, int tps, int splits) {
+// NW waves per workgroup, each taking every NW-th tile of the workgroup's run.  Split mode
+// (out == nullptr): the merged partial (acc, m, l) goes to ws for the combine launch.  Direct
+// mode (one split per sequence and KV head): the workgroup merges its waves, adds the learned
+// sink logit and writes the normalised output itself, so no partial leaves the chip and no
+// second launch runs.
+template <typename T, int D, int NREP, int NW>
+__global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 3 : 2) void decode_split_kernel(
+    const void *__restrict__ qp, ropekv_kv_cache c, float sl2, float *__restrict__ ws, int tps, int splits,
+    const float *__restrict__ sinks, void *__restrict__ out) {
   using TR = ElemTraits<T>;
+  constexpr int NT = 64 * NW;                // threads
   constexpr int QB = (D / 4) * TR::kBytes;   // bytes of a lane's K / Q quarter-row
   constexpr int E = D / 16;                  // V dims per lane per key
   constexpr int VB = E * TR::kBytes;         // bytes of a lane's V piece per key
   using Frag = TileFrag<QB, VB>;
-  __shared__ float s_p[4][NREP][kTile];
-  __shared__ float s_corr[4][NREP];
-  __shared__ float s_m[4][NREP], s_l[4][NREP];
-  __shared__ float s_acc[4][NREP][D];
-  __shared__ int s_bid[kMaxTps];
+  constexpr bool kMfmaPV = sizeof(T) == 2;
+  __shared__ float s_p[kMfmaPV ? 1 : NW][NREP][kTile];
+  __shared__ float s_corr[kMfmaPV ? 1 : NW][NREP];
+  __shared__ float s_m[NW][NREP], s_l[NW][NREP];
+  __shared__ float s_acc[NW][NREP][D];
+  __shared__ int s_bid[kMaxDirectTiles];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -104,12 +112,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void decode_split_kern
   // a length the planned splits cannot cover (table too short for seq_len) is flagged, not read
   if (split == splits - 1 && threadIdx.x == 0 && st.ntiles > splits * tps) dev_error(c.err_word, ROPEKV_DEV_BLOCK_RANGE);
   const int t_begin = split * tps;
-  if (t_begin >= st.ntiles) return;
+  if (t_begin >= st.ntiles) {
+    if (out != nullptr) {  // direct mode, empty sequence: a zero row
+      const long obase = ((long)b * Hkv + g) * NREP * D;
+      for (int idx = threadIdx.x; idx < NREP * D; idx += NT) TR::put(out, obase + idx, 0.f);
+    }
+    return;
+  }
   const int t_end = min(st.ntiles, t_begin + tps);
 
   // stage this split's block ids (paged) so no tile waits on a dependent table load
   if (c.layout == ROPEKV_PAGED) {
-    for (int i = threadIdx.x; i < t_end - t_begin; i += 256) {
+    for (int i = threadIdx.x; i < t_end - t_begin; i += NT) {
       const int tile = t_begin + i;
       const int blk = tile < st.nsb ? tile : st.fr + (tile - st.nsb);
       s_bid[i] = (blk < c.max_blocks) ? c.block_table[(long)b * c.max_blocks + blk] : -1;
@@ -171,7 +185,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void decode_split_kern
     return ok;
   };
 
-  constexpr bool kMfmaPV = sizeof(T) == 2;
   float m_run = kNegBig, l_run = 0.f;
   float acc[kMfmaPV ? 1 : NREP][E];      // VALU path: head h, dims col * E + e
   f32x4 oacc[kMfmaPV ? D / 16 : 1];     // MFMA path: O^T block mt, dims E (4 grp + r) + mt, head col
@@ -186,9 +199,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void decode_split_kern
   int tile = t_begin + wave;
   Frag cur, nxt;
   bool cur_ok = tile < t_end ? load_tile(cur, tile) : false;
-  for (; tile < t_end; tile += 4) {
+  for (; tile < t_end; tile += NW) {
     bool nxt_ok = false;
-    if (tile + 4 < t_end) nxt_ok = load_tile(nxt, tile + 4);
+    if (tile + NW < t_end) nxt_ok = load_tile(nxt, tile + NW);
     if (!cur_ok) {
       bad_tile = true;
     } else {
@@ -315,24 +328,44 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 2) void decode_split_kern
     }
   }
   __syncthreads();
-  // merge the 4 waves and write this split's partial
-  const int nwaves = min(4, t_end - t_begin);
-  float *dst = ws + (((long)(b * Hkv + g) * splits + split) * NREP) * (D + 2);
-  for (int idx = threadIdx.x; idx < NREP * D; idx += 256) {
-    const int h = idx / D, dd = idx % D;
-    float m = kNegBig;
-    for (int w = 0; w < nwaves; ++w) m = fmaxf(m, s_m[w][h]);
-    float a = 0.f, l = 0.f;
-    for (int w = 0; w < nwaves; ++w) {
-      const float f = exp2f(s_m[w][h] - m);
-      a += f * s_acc[w][h][dd];
-      l += f * s_l[w][h];
+  // merge the waves: this split's partial, or (direct mode) the normalised output
+  const int nwaves = min(NW, t_end - t_begin);
+  if (out == nullptr) {
+    float *dst = ws + (((long)(b * Hkv + g) * splits + split) * NREP) * (D + 2);
+    for (int idx = threadIdx.x; idx < NREP * D; idx += NT) {
+      const int h = idx / D, dd = idx % D;
+      float m = kNegBig;
+      for (int w = 0; w < nwaves; ++w) m = fmaxf(m, s_m[w][h]);
+      float a = 0.f, l = 0.f;
+      for (int w = 0; w < nwaves; ++w) {
+        const float f = exp2f(s_m[w][h] - m);
+        a += f * s_acc[w][h][dd];
+        l += f * s_l[w][h];
+      }
+      float *o = dst + (long)h * (D + 2);
+      o[dd] = a;
+      if (dd == 0) {
+        o[D] = m;
+        o[D + 1] = l;
+      }
     }
-    float *o = dst + (long)h * (D + 2);
-    o[dd] = a;
-    if (dd == 0) {
-      o[D] = m;
-      o[D + 1] = l;
+  } else {
+    const long obase = ((long)b * Hkv + g) * NREP * D;
+    for (int idx = threadIdx.x; idx < NREP * D; idx += NT) {
+      const int h = idx / D, dd = idx % D;
+      float m = kNegBig;
+      for (int w = 0; w < nwaves; ++w) m = fmaxf(m, s_m[w][h]);
+      // a learned sink logit joins the normaliser (log2 units like the running maxima)
+      const float sink2 = sinks ? sinks[g * NREP + h] * kLog2e : -INFINITY;
+      m = fmaxf(m, sink2);
+      float a = 0.f, l = 0.f;
+      for (int w = 0; w < nwaves; ++w) {
+        const float f = exp2f(s_m[w][h] - m);
+        a += f * s_acc[w][h][dd];
+        l += f * s_l[w][h];
+      }
+      if (sinks) l += exp2f(sink2 - m);
+      TR::put(out, obase + idx, l > 0.f ? a * (1.f / l) : 0.f);
     }
   }
 }
@@ -341,8 +374,14 @@ template <typename T, int D, int NREP>
 hipError_t launch_decode_t(const void *q, int batch, const ropekv_kv_cache &c, float sl2, const float *sinks,
                            void *out, float *ws, const DecodePlan &pl, hipStream_t s) {
   dim3 grid(pl.splits, c.num_kv_heads, batch);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, NREP>), grid, dim3(256), 0, s, q, c, sl2, ws, pl.tiles_per_split,
-                     pl.splits);
+  if (pl.direct) {
+    constexpr int NWD = sizeof(T) == 2 ? kDirectWaves : kDirectWavesF32;
+    hipLaunchKernelGGL((decode_split_kernel<T, D, NREP, NWD>), grid, dim3(64 * NWD), 0, s, q, c, sl2, ws,
+                       pl.tiles_per_split, pl.splits, sinks, out);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_split_kernel<T, D, NREP, 4>), grid, dim3(256), 0, s, q, c, sl2, ws, pl.tiles_per_split,
+                     pl.splits, (const float *)nullptr, (void *)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D, NREP>), dim3(c.num_kv_heads, batch), dim3(256), 0, s, c,
@@ -421,6 +460,17 @@ DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c) {
   // ring-window layer 2 splits of 129 tiles run 12% faster than 9 of 29, and the batch-64 x
   // 32768 and batch-32 x 131072 layers gain 1-3% over 128-tile splits.
   const long units = (long)batch * c.num_kv_heads;
+  pl.direct = false;
+  if ((c.kv_dtype == ROPEKV_BF16 || c.kv_dtype == ROPEKV_F32) && units >= 256 && max_tiles <= kMaxDirectTiles) {
+    // enough (sequence, KV head) units to give every CU a workgroup, and short runs: one wide
+    // workgroup per unit writes its output directly (no partials, no combine launch)
+    pl.direct = true;
+    pl.max_tiles = max_tiles;
+    pl.tiles_per_split = max_tiles;
+    pl.splits = 1;
+    pl.ws_bytes = 0;
+    return pl;
+  }
   int splits = (int)((512 + units - 1) / units);
   splits = max(splits, (max_tiles + kMaxTps - 1) / kMaxTps);
   splits = min(splits, max_tiles);

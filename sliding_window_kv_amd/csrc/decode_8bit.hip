@@ -201,16 +201,16 @@ __global__ __launch_bounds__(256) void decode_split_8bit_kernel(const void *__re
       const int p = 64 * n + lane;
       const int r = p / CPR;
       const int ch = (p % CPR) ^ kswz<D>(r);
-      dma16(kbase + row_of(t, r) * D + ch * 16, S.k + 1024 * n);
+      dma16_stream(kbase + row_of(t, r) * D + ch * 16, S.k + 1024 * n);
     }
 #pragma unroll
     for (int n = 0; n < KI; ++n) {
       const int p = 64 * n + lane;
-      dma16(vbase + row_of(t, p / CPR) * D + (p % CPR) * 16, S.v + 1024 * n);
+      dma16_stream(vbase + row_of(t, p / CPR) * D + (p % CPR) * 16, S.v + 1024 * n);
     }
     if (lane < 32) {
       const float *src = (lane < 16 ? c.k_scale : c.v_scale) + row_of(t, lane & 15);
-      dma4(src, S.sc);
+      dma4_stream(src, S.sc);
     }
   };
   auto visible = [&](const TileAt &t, int r) -> bool {

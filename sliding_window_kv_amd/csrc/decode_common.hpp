@@ -129,7 +129,10 @@ struct ElemTraits<bf16_t> {
   static __device__ __forceinline__ void put(void *p, long i, float v) { ((uint16_t *)p)[i] = f_to_bf16(v); }
 };
 
-constexpr int kMaxTps = 256;  // tiles per split (block-table entries staged in LDS)
+constexpr int kMaxTps = 256;  // tiles per split of a split plan
+constexpr int kMaxDirectTiles = 512;  // tiles of a direct-plan workgroup (block-table entries staged in LDS)
+constexpr int kDirectWaves = 12;      // waves of a direct-plan workgroup (16-bit caches: 3 per SIMD)
+constexpr int kDirectWavesF32 = 8;    // fp32 caches run at 2 waves per SIMD
 
 // Merge the split partials of one (sequence, KV head) for its n_rep query heads:
 // one wave per query head finds the global maximum and the split weights

@@ -14,6 +14,7 @@ struct DecodePlan {
   int tiles_per_split;  // tiles handled by one workgroup
   int splits;           // workgroups per (sequence, KV head)
   size_t ws_bytes;
+  bool direct;          // one wide workgroup per (sequence, KV head) writes the output (no combine)
 };
 
 DecodePlan plan_decode(int batch, int n_q_heads, const ropekv_kv_cache &c);

@@ -33,9 +33,13 @@ def env():
 
 
 def _split_keys(R, wl, max_tiles):
-    """Keys per split of the decode plan (the plan is read back from the workspace size)."""
+    """Keys per split of the decode plan (read back from the workspace size).  A plan without
+    partials (one workgroup per sequence and KV head, its waves taking tiles in turn) has no split
+    edge: a tile edge in the middle of the run stands in for it."""
     n_rep = wl.Hq // wl.Hkv
     splits = wl.ws_bytes // (wl.B * wl.Hkv * n_rep * (wl.d + 2) * 4)
+    if splits == 0:
+        return 16 * (max_tiles // 2)
     return 16 * ((max_tiles + splits - 1) // splits)
 
 

@@ -364,7 +364,7 @@ def test_decode_paged_few_long_sequences(env, B, Hkv, n):
     ws_bytes = R.decode_workspace_size(B, Hq, cache.desc)
     # needles at the first and last keys and on both sides of every split edge
     splits = ws_bytes // (B * Hkv * n_rep * (d + 2) * 4)
-    sp = 16 * ((max_blocks + splits - 1) // splits)
+    sp = 16 * ((max_blocks + splits - 1) // splits) if splits else 16 * (max_blocks // 2)
     u = needle_dirs(Hkv, d, 55)
     for b, nb in enumerate(lens):
         edges = list(range(sp, nb, sp))
@@ -726,6 +726,67 @@ def test_decode_learned_sink_logits(env, dtype_name, n_rep, d):
                                  lambda j: vp[table[b, j // 16], :, j % 16], n, 4, 200, Hkv, sink_logits=sk)
         if dtype_name == "f32":
             assert rowwise(got[b], ref) <= 1e-5
+        else:
+            assert_bf16_close(got[b], ref)
+
+
+@pytest.mark.parametrize("dtype_name,layout,sinks_on", [("f32", "paged", True), ("bf16", "paged", False),
+                                                        ("f32", "ring", False), ("bf16", "ring", True)])
+def test_decode_direct_plan(env, dtype_name, layout, sinks_on):
+    # 32 sequences x 8 KV heads = 256 units with short visible runs: the plan gives each
+    # (sequence, KV head) one wide workgroup that writes its output directly (no workspace, no
+    # combine); ragged lengths incl. an empty sequence and runs shorter than the workgroup's waves
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
+    B, Hkv, n_rep, d, S, W = 32, 8, 4, 128, 4, 300
+    Hq = Hkv * n_rep
+    lens = [0, 1, 2, 5, 17, 100, 303, 304, 305, 1000] + [int(x) for x in synth.uniform_ints(B - 10, 1, 5000, 130)]
+    if layout == "paged":
+        max_blocks = 5000 // 16 + 2
+        table = synth.block_table_permutation(B, max_blocks, B * max_blocks, 131)
+        cache = DevPaged(R, torch, dev, dtype, B, Hkv, d, S, W, table, B * max_blocks)
+    else:
+        cache = DevRing(R, torch, dev, dtype, B, Hkv, d, S, W)
+        heads = synth.uniform_ints(B, 0, W, 132)
+        # a full ring for sequences past the window, a partly filled one (head = count) below it
+        count = [min(max(n - S, 0), W) for n in lens]
+        cache.head.copy_(torch.tensor([int(h) if c == W else c % W for h, c in zip(heads, count)], dtype=torch.int32))
+        cache.count.copy_(torch.tensor(count, dtype=torch.int32))
+    _fill(torch, cache.k, 133)
+    _fill(torch, cache.v, 134)
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    assert R.decode_workspace_size(B, Hq, cache.desc) == 0  # the direct plan needs no partials
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=dtype, device=dev), 135)
+    sinks = torch.from_numpy(synth.normal((Hq,), 136) * 3.0).to(dev) if sinks_on else None
+    out = torch.full_like(q, float("nan"))
+    ws = torch.empty(1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, 4, sink_logits=sinks)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    kc, vc, qq, got = to_np64(cache.k), to_np64(cache.v), to_np64(q), to_np64(out)
+    sk = sinks.cpu().numpy().astype(np.float64) if sinks_on else None
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0)
+            continue
+        if layout == "paged":
+            def kf(j, b=b):
+                return kc[table[b, j // 16], :, j % 16]
+
+            def vf(j, b=b):
+                return vc[table[b, j // 16], :, j % 16]
+        else:
+            ring = O.RingSeq(sinks=S, window=W, head=int(cache.head[b].item()), count=count[b], seq_len=n)
+            slot_of = dict(zip(O.visible_positions(n - 1, S, W), ring.chronological_slots()))
+
+            def kf(j, b=b, slot_of=slot_of):
+                return kc[b, :, slot_of[j]]
+
+            def vf(j, b=b, slot_of=slot_of):
+                return vc[b, :, slot_of[j]]
+        ref = O.decode_attention(qq[b], kf, vf, n, S, W, Hkv, sink_logits=sk)
+        if dtype_name == "f32":
+            assert rowwise(got[b], ref) <= 1e-5, b
         else:
             assert_bf16_close(got[b], ref)
 

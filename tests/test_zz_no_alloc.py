@@ -105,6 +105,26 @@ def test_noalloc_ring_after_paged(env):
     assert torch.equal(a, b)
 
 
+def test_noalloc_direct_plan(env):
+    # 256 (sequence, KV head) units with short runs: a plan without partials (each unit's workgroup
+    # writes its output); the allocation-free call takes it too
+    R, torch, dev = env
+    B, Hkv, n_rep, d, S, W = 32, 8, 4, 128, 4, 500
+    Hq = Hkv * n_rep
+    ring = DevRing(R, torch, dev, torch.bfloat16, B, Hkv, d, S, W)
+    synth.device_normal_(ring.k, 101)
+    synth.device_normal_(ring.v, 102)
+    ring.head.copy_(torch.from_numpy(synth.uniform_ints(B, 0, W, 103)))
+    ring.count.fill_(W)
+    ring.seq_len.copy_(torch.from_numpy(synth.uniform_ints(B, W + S, 200000, 104)))
+    assert R.decode_workspace_size(B, Hq, ring.desc) == 0
+    q = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    synth.device_normal_(q, 105)
+    a, b = _both(R, torch, dev, q, B, Hq, ring)
+    assert torch.equal(a, b)
+    assert bool(torch.isfinite(b.float()).all())
+
+
 def test_noalloc_refuses_plans_beyond_its_array(env):
     # 256 sequences of a full-attention layer of 8192 blocks need 32 splits x 256 x 8 KV heads x
     # 4 heads x 130 floats = 136 MB of partials, more than the 64 MiB array: refused, nothing launched
