@@ -195,7 +195,10 @@ int ropekv_apply_append(const ropekv_rope_cfg *cfg, const float *cos_sin, int32_
                         int32_t freed_capacity, int32_t *n_freed, ropekv_stream_t stream);
 
 /* Bytes of fp32 workspace ropekv_decode_attn needs for this batch and cache
- * (split-K partials [batch, Hkv, splits, n_rep, d + 2]).  0 on bad input, and 0
+ * (the split-K partials of the decode plan: decode is bound by streaming the
+ * KV cache, [GOSS] 4.3, so one long sequence is spread over many workgroups
+ * whose partial softmax sums are then merged: [batch, Hkv, splits, n_rep,
+ * d + 2]).  0 on bad input, and 0
  * for plans without partials: F32 / BF16 caches with at least 256 (sequence, KV
  * head) units of at most 512 16-row tiles each get one workgroup per unit that
  * writes its output directly. */
@@ -286,13 +289,19 @@ int ropekv_shift_keys(const ropekv_rope_cfg *cfg, const ropekv_kv_cache *cache, 
 /* Test-facing: the visible logical positions of sequence seq's next query
  * (position seq_len - 1) and the element offset of each key row in the
  * cache's k buffer, in chronological order, as the attention kernels address
- * them.  positions_out / offsets_out: device int32 / int64 [max_out];
+ * them.  The visible set is the one [SINK] "可见集合与容量定义" defines (the
+ * S sinks and the W most recent positions, capacity C = S + W); the order is
+ * the chronological read-out of [GOSS] "5.3 get" (sinks, then the ring from
+ * its oldest entry).  positions_out / offsets_out: device int32 / int64 [max_out];
  * n_out: device int32 receiving the count (entries beyond max_out dropped). */
 int ropekv_visible_slots(const ropekv_kv_cache *cache, int32_t seq, int32_t *positions_out,
                          int64_t *offsets_out, int32_t max_out, int32_t *n_out,
                          ropekv_stream_t stream);
 
-/* The message of the last failing call on this thread ("" if none). */
+/* The message of the last failing call on this thread ("" if none).  Calls
+ * fail loudly with a reason where the engines [RoPE] compares either read
+ * past the cos/sin table or grow it silently with the unscaled base (the
+ * passage on what happens when a position exceeds the table). */
 const char *ropekv_last_error(void);
 
 #ifdef __cplusplus
