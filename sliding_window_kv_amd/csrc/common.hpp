@@ -191,11 +191,6 @@ __device__ __forceinline__ void dma16_stream(const void *gsrc, const void *lds_b
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc0 sc1 nt" ::"v"(gsrc), "s"(m0)
                    : "memory", "m0");
 }
-__device__ __forceinline__ void dma4_stream(const void *gsrc, const void *lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off sc0 sc1 nt" ::"v"(gsrc), "s"(m0)
-                   : "memory", "m0");
-}
 __device__ __forceinline__ void dma4(const void *gsrc, const void *lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(m0)
