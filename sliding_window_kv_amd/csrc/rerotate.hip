@@ -504,14 +504,19 @@ constexpr int kI8Chunks = 4;  // int8 chunk kernel: row blocks (chunks per threa
 constexpr int kFloatChunks = 1;  // float chunk kernel: row blocks per workgroup
 constexpr int kI8HalfChunks = 1;  // int8 half-rotary kernel: row blocks per workgroup
 constexpr int kStream = 19;  // buffer cache policy: sc0 | nt | sc1
+// Row scales go through the caches: a wave writes the 4-byte scales of 8 rows (32 bytes of a
+// 128-byte line, the rest from other waves and blocks); streamed, those partial lines cost the
+// int8 pass 6 % (13.25 -> 12.49 ms on the 64-layer switch)
+constexpr int kScalePolicy = 0;
 
 typedef decltype(__builtin_amdgcn_raw_buffer_load_b128(__amdgpu_buffer_rsrc_t(), 0, 0, 0)) b128_t;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(void *base, long bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
 }
+template <int POLICY = kStream>
 __device__ __forceinline__ void chunk_load(uint32_t *w, __amdgpu_buffer_rsrc_t r, int off) {
-  const b128_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
+  const b128_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
   w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
 }
 __device__ __forceinline__ void chunk_store(const uint32_t *w, __amdgpu_buffer_rsrc_t r, int off) {
@@ -659,7 +664,7 @@ __device__ __forceinline__ void turn_i8_chunk(const uint32_t *w, float sco, bool
   chunk_store(out, rs, off);
   if (!keep && lead)
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, inv > 0.f ? sco * (amax / 127.0f) : 0.f), rsc,
-                                          soff, 0, kStream);
+                                          soff, 0, kScalePolicy);
 }
 
 template <int L, int NCH, bool NEOX, bool KEEP>
@@ -680,7 +685,7 @@ __global__ __launch_bounds__(kChunkThreads) void rerotate_int8_chunk_kernel(Rero
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     chunk_load(w[k], rs, (rr + k * RB) * a.D + 16 * ch);
-    sco[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * (rr + k * RB), 0, kStream));
+    sco[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * (rr + k * RB), 0, kScalePolicy));
   }
   const int nt = c.np * half;
   float *s_cs = s_tab, *s_sn = s_tab + nt, *s_nsn = s_tab + 2 * nt, *s_id = s_tab + 3 * nt;
@@ -727,9 +732,11 @@ __global__ __launch_bounds__(kChunkThreads) void rerotate_int8_half_kernel(Rerot
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     const int o = (rr + k * RB) * a.D + 16 * q;
-    chunk_load(wr[k], rs, o);
-    chunk_load(wt[k], rs, o + a.to.rotary_dim);
-    sco[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * (rr + k * RB), 0, kStream));
+    // the two 64-byte halves of a row's line come from separate loads, which run faster through
+    // the caches than streamed past them (measured: streamed, the keep-scale pass takes 6 % longer)
+    chunk_load<0>(wr[k], rs, o);
+    chunk_load<0>(wt[k], rs, o + a.to.rotary_dim);
+    sco[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * (rr + k * RB), 0, kScalePolicy));
   }
   const int nt = c.np * half;
   float *s_cs = s_tab, *s_sn = s_tab + nt, *s_nsn = s_tab + 2 * nt;
@@ -807,7 +814,7 @@ __global__ __launch_bounds__(kChunkThreads) void rerotate_int8_half_kernel(Rerot
       chunk_store(out, rs, o + a.to.rotary_dim);
       if (q == 0)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, inv > 0.f ? sco[k] * (amax / 127.0f) : 0.f),
-                                              rsc, 4 * row, 0, kStream);
+                                              rsc, 4 * row, 0, kScalePolicy);
     }
   }
 }
