@@ -34,6 +34,22 @@ def rowwise(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.max(np.abs(g - r), axis=1) / den))
 
 
+def assert_bf16_rounded(gpu: np.ndarray, ref: np.ndarray, rel_fp32=1e-6):
+    """gpu is the exact value ref, computed in fp32 and rounded once to bf16 (round to nearest):
+    |gpu - ref| <= ulp(gpu) / 2 + e, with ulp(g) = 2^(floor(log2 |g|) - 7) (8 significant bits) and
+    e = rel_fp32 * (the row's largest |ref|) a bound on the fp32 arithmetic before the rounding (a
+    few fp32 roundings of products of the inputs and the cos / sin table, ~1e-7).  A value one
+    bf16 step off fails unless ref lies within e of the midpoint between the two."""
+    g = gpu.reshape(-1, gpu.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    e = rel_fp32 * np.max(np.abs(r), axis=1, keepdims=True)
+    _, ex = np.frexp(g)  # g = m 2^ex, 0.5 <= |m| < 1: ulp = 2^(ex - 8)
+    half = np.where(g == 0, 0.0, np.ldexp(1.0, ex - 9))
+    excess = np.abs(g - r) - (half + e)
+    assert float(np.max(excess)) <= 0.0, (
+        f"max excess {float(np.max(excess)):.3e} over half a bf16 ulp, max abs err {float(np.max(np.abs(g - r))):.3e}")
+
+
 def assert_bf16_close(gpu: np.ndarray, ref: np.ndarray, atol=2e-2, rtol=1e-2):
     err = np.abs(gpu - ref) - (atol + rtol * np.abs(ref))
     assert float(np.max(err)) <= 0.0, f"max excess {float(np.max(err)):.3e}, max abs err {float(np.max(np.abs(gpu-ref))):.3e}"

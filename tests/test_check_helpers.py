@@ -1,0 +1,85 @@
+"""The GPU tests' comparison helpers, pinned on the CPU: each accepts what it must accept and
+rejects a planted mistake one unit beyond its bound (no GPU, no kernel involved)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ropekv_oracle as O
+from tests.gpu_util import (assert_bf16_close, assert_bf16_rounded, assert_fp8_codes_valid,
+                            assert_int8_codes_valid, excess)
+
+
+def _bf16(x):
+    """round to nearest bf16 (torch's conversion), back to fp64"""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _bf16_step(x, away):
+    """the bf16 neighbour of bf16 values x one step toward (away=False) or away from zero"""
+    b = torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16)
+    return (b + (1 if away else -1)).view(torch.bfloat16).double().numpy()
+
+
+def test_bf16_rounded_accepts_round_to_nearest_and_rejects_one_step():
+    rng = np.random.default_rng(7)
+    ref = rng.standard_normal((6, 128)) * np.exp(rng.uniform(-6, 6, (6, 1)))
+    got = _bf16(ref)
+    assert_bf16_rounded(got, ref)
+    # the fp32 result of a short computation, then one rounding: still within the bound
+    assert_bf16_rounded(_bf16((ref * (1 + 3e-7)).astype(np.float32)), ref)
+    _, ex = np.frexp(got)
+    ulp = np.ldexp(1.0, ex - 8)
+    # elements whose exact value is at most 0.4 ulp from the rounded one: either neighbour fails
+    picks = np.argwhere((np.abs(got - ref) < 0.4 * ulp) & (np.abs(got) > 0))[:6]
+    assert len(picks) == 6
+    for i, j in picks:
+        for away in (False, True):
+            bad = got.copy()
+            bad[i, j] = _bf16_step(got[i, j], away)
+            with pytest.raises(AssertionError):
+                assert_bf16_rounded(bad, ref)
+
+
+def test_bf16_close_bound_and_signed_excess():
+    ref = np.array([[0.0, 1.0, -2.0, 10.0]])
+    ok = ref + np.array([[0.0199, 0.0299, -0.0399, 0.1199]])  # just inside atol 2e-2 + rtol 1e-2 |ref|
+    assert_bf16_close(ok, ref)
+    assert -2e-4 < excess(ok, ref) < 0
+    bad = ok.copy()
+    bad[0, 3] += 1e-3
+    with pytest.raises(AssertionError):
+        assert_bf16_close(bad, ref)
+    assert excess(bad, ref) > 0
+    assert excess(ref, ref) < 0  # the margin is reported signed
+
+
+def test_int8_validity_accepts_edge_flips_only():
+    want = np.array([3, -7, 10, 0], dtype=np.int8)
+    quot = np.array([3.4996, -6.5004, 10.2, 0.0])  # two quotients sit within 5e-4 of an edge
+    got = want.copy()
+    got[0] = 4  # 3.4996 is 4e-4 from the 3 / 4 edge
+    got[1] = -6  # -6.5004 is 4e-4 from the -7 / -6 edge
+    assert assert_int8_codes_valid(got, want, quot, 1e-3) == 2
+    with pytest.raises(AssertionError):  # the same flips need more than a 1e-4 margin
+        assert_int8_codes_valid(got, want, quot, 1e-4)
+    far = want.copy()
+    far[2] = 11  # 10.2 is 0.3 from the 10 / 11 edge
+    with pytest.raises(AssertionError):
+        assert_int8_codes_valid(far, want, quot, 1e-3)
+    two = want.copy()
+    two[3] = 2  # two steps
+    with pytest.raises(AssertionError):
+        assert_int8_codes_valid(two, want, quot, 1e-3)
+
+
+def test_fp8_validity_accepts_neighbour_at_midpoint_only():
+    # E4M3 values 1.0 and 1.125 are neighbours (bytes 0x38, 0x39); their midpoint is 1.0625
+    want = np.array([0x38, 0x38], dtype=np.uint8).view(np.int8)
+    got = np.array([0x39, 0x38], dtype=np.uint8).view(np.int8)
+    assert O.e4m3_value(np.array([0x38], dtype=np.uint8).view(np.int8))[0] == 1.0
+    assert assert_fp8_codes_valid(got, want, np.array([1.0624, 1.0]), 1e-3) == 1
+    with pytest.raises(AssertionError):
+        assert_fp8_codes_valid(got, want, np.array([1.05, 1.0]), 1e-3)
+    skip = np.array([0x3A, 0x38], dtype=np.uint8).view(np.int8)  # two steps (1.25)
+    with pytest.raises(AssertionError):
+        assert_fp8_codes_valid(skip, want, np.array([1.0624, 1.0]), 1e-3)

@@ -13,7 +13,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (EPS_APPEND_FP8, EPS_APPEND_I8, EPS_TURN_HADAMARD, EPS_TURN_I8, assert_bf16_close,
+from tests.gpu_util import (EPS_APPEND_FP8, EPS_APPEND_I8, EPS_TURN_HADAMARD, EPS_TURN_I8, assert_bf16_close, assert_bf16_rounded,
                             assert_fp8_codes_valid, assert_int8_codes_valid, attend_set, check_keep_scale_rows,
                             excess, int8_turn_quotients, needle_dirs, needle_kv, oracle_cfg, plant_queries_,
                             to_np64, torch_dev)
@@ -104,10 +104,10 @@ def test_paged_decode_b64_ctx32768(env):
     for b in (0, 37, 63):
         p = wl.ctx - 1
         want_q = O.rope_apply(q_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
-        assert_bf16_close(q_rot[b], want_q, atol=1e-2, rtol=1e-2)
+        assert_bf16_rounded(q_rot[b], want_q)
         k, v = wl.kv_of(b)
         want_k = O.rope_apply(k_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
-        assert_bf16_close(k[p], want_k, atol=1e-2, rtol=1e-2)
+        assert_bf16_rounded(k[p], want_k)
         assert np.array_equal(v[p], v_raw[b])
         ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
         assert_bf16_close(out[b], ref)
