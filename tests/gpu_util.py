@@ -55,6 +55,33 @@ def assert_bf16_close(gpu: np.ndarray, ref: np.ndarray, atol=2e-2, rtol=1e-2):
     assert float(np.max(err)) <= 0.0, f"max excess {float(np.max(err)):.3e}, max abs err {float(np.max(np.abs(gpu-ref))):.3e}"
 
 
+def assert_bf16_attention(gpu: np.ndarray, ref: np.ndarray, ref_abs: np.ndarray):
+    """The bound a bf16 attention output's own roundings imply.  The kernels round each weight P_j
+    once to bf16 (relative error <= 2^-8) and sum in fp32, which moves the weighted average by at
+    most 2^-8 (A + |out|), A = sum_j w_j |v_j| (the same attention over |V|, ref_abs); the output's
+    rounding to bf16 adds half an ulp <= 2^-8 |out|.  The 5 % and 1e-5 A margins cover the fp32
+    score and exp2 arithmetic (relative ~1e-4 at the needle rows' scores)."""
+    g = gpu.reshape(-1, gpu.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    a = ref_abs.reshape(-1, ref_abs.shape[-1])
+    bound = 1.05 * 2.0 ** -8 * (a + 2.0 * np.abs(r)) + 1e-5 * np.max(a, axis=1, keepdims=True)
+    excess_ = np.abs(g - r) - bound
+    assert float(np.max(excess_)) <= 0.0, (
+        f"max excess {float(np.max(excess_)):.3e} over the bf16 rounding bound (max abs err "
+        f"{float(np.max(np.abs(g - r))):.3e})")
+
+
+def bf16_attention_ref(gpu: np.ndarray, attention, q, kfn, vfn, *args, **kw):
+    """ref = attention(q, kfn, vfn, *args, **kw), an oracle attention; gpu is checked against it at
+    the stated bf16 tolerance (2e-2 + 1e-2 |ref|) and at the tighter bound of its roundings
+    (assert_bf16_attention, with the same attention over |V|).  Returns ref."""
+    ref = attention(q, kfn, vfn, *args, **kw)
+    ref_abs = attention(q, kfn, lambda j: np.abs(vfn(j)), *args, **kw)
+    assert_bf16_close(gpu, ref)
+    assert_bf16_attention(gpu, ref, ref_abs)
+    return ref
+
+
 def oracle_cfg(cfg) -> O.RopeCfg:
     """The oracle's view of a ctypes RopeCfg (same numbers)."""
     types = {0: "yarn", 1: "linear", 2: "ntk", 3: "dynamic_ntk", 4: "llama3"}

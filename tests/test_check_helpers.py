@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from oracle import ropekv_oracle as O
-from tests.gpu_util import (assert_bf16_close, assert_bf16_rounded, assert_fp8_codes_valid,
+from tests.gpu_util import (assert_bf16_attention, assert_bf16_close, assert_bf16_rounded, assert_fp8_codes_valid,
                             assert_int8_codes_valid, excess)
 
 
@@ -83,3 +83,54 @@ def test_fp8_validity_accepts_neighbour_at_midpoint_only():
     skip = np.array([0x3A, 0x38], dtype=np.uint8).view(np.int8)  # two steps (1.25)
     with pytest.raises(AssertionError):
         assert_fp8_codes_valid(skip, want, np.array([1.0624, 1.0]), 1e-3)
+
+
+def _attention_with_rounded_weights(q, K, V, Hkv, sign=None):
+    """q [Hq, d], K, V [n, Hkv, d]: softmax weights rounded to bf16 one by one (or, with sign, moved
+    by a full 2^-8 each in the direction sign), fp64 sums, the result rounded to bf16: the roundings
+    a bf16 attention kernel makes, written out for one small case."""
+    Hq, d = q.shape
+    out = np.empty((Hq, d))
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        s = K[:, g, :] @ q[h] / np.sqrt(d)
+        p = np.exp(s - s.max())
+        if sign is None:
+            pr = _bf16(p)
+            out[h] = (pr @ V[:, g, :]) / pr.sum()
+        else:  # worst case per output dim: each weight pushed 2^-8 toward that dim's outliers
+            for c in range(d):
+                o = (p @ V[:, g, c]) / p.sum()
+                pr = p * (1 + 2.0 ** -8 * np.sign(V[:, g, c] - o))
+                out[h, c] = (pr @ V[:, g, c]) / pr.sum()
+    return _bf16(out)
+
+
+@pytest.mark.parametrize("worst", [False, True])
+def test_bf16_attention_bound_holds_for_rounded_weights_and_catches_a_dropped_key(worst):
+    rng = np.random.default_rng(11)
+    n, Hkv, Hq, d = 120, 2, 8, 64
+    q = _bf16(rng.standard_normal((Hq, d)))
+    K = _bf16(rng.standard_normal((n, Hkv, d)))
+    V = _bf16(rng.standard_normal((n, Hkv, d)))
+    ref = O.decode_attention(q, lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
+    ref_abs = O.decode_attention(q, lambda j: K[j], lambda j: np.abs(V[j]), n, 0, 0, Hkv)
+    got = _attention_with_rounded_weights(q, K, V, Hkv, sign=True if worst else None)
+    assert_bf16_attention(got, ref, ref_abs)
+    # each key's largest effect on an output: w_hj |v_j - out_h| over heads and dims
+    eff = np.zeros(n)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        s = K[:, g, :] @ q[h] / np.sqrt(d)
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        eff = np.maximum(eff, np.max(w[:, None] * np.abs(V[:, g, :] - ref[h]), axis=1))
+    # a key whose loss moves some output by 0.006-0.017: inside 2e-2 + 1e-2 |ref|, well outside the
+    # rounding bound (~0.0035 here)
+    j = int(np.argmin(np.abs(eff - 0.012)))
+    assert 0.006 < eff[j] < 0.017
+    keep = np.r_[0:j, j + 1:n]
+    dropped = _attention_with_rounded_weights(q, K[keep], V[keep], Hkv)
+    assert_bf16_close(dropped, ref)
+    with pytest.raises(AssertionError):
+        assert_bf16_attention(dropped, ref, ref_abs)

@@ -13,7 +13,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (EPS_APPEND_FP8, EPS_APPEND_I8, EPS_TURN_HADAMARD, EPS_TURN_I8, assert_bf16_close, assert_bf16_rounded,
+from tests.gpu_util import (bf16_attention_ref, EPS_APPEND_FP8, EPS_APPEND_I8, EPS_TURN_HADAMARD, EPS_TURN_I8, assert_bf16_close, assert_bf16_rounded,
                             assert_fp8_codes_valid, assert_int8_codes_valid, attend_set, check_keep_scale_rows,
                             excess, int8_turn_quotients, needle_dirs, needle_kv, oracle_cfg, plant_queries_,
                             to_np64, torch_dev)
@@ -78,8 +78,7 @@ def _paged_full_needles(R, torch, wl, seqs, seed):
             K, V = dequant(kc, ks), dequant(vc, vs)
         else:
             K, V = wl.kv_of(b)
-        ref = O.decode_attention(q[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
-        assert_bf16_close(out[b], ref)
+        ref = bf16_attention_ref(out[b], O.decode_attention, q[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
         assert np.max(np.abs(ref)) > 1.0  # the needles carry the output
         every = np.arange(n)
         wrong = [every[1:], every[:-1], np.r_[every[:sp], every[sp + 16:]], every[:-64]]
@@ -109,8 +108,7 @@ def test_paged_decode_b64_ctx32768(env):
         want_k = O.rope_apply(k_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
         assert_bf16_rounded(k[p], want_k)
         assert np.array_equal(v[p], v_raw[b])
-        ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
-        assert_bf16_close(out[b], ref)
+        ref = bf16_attention_ref(out[b], O.decode_attention, q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
     # needles: the same layer decoded again with planted keys and queries
     _paged_full_needles(R, torch, wl, (0, 37, 63), 2100)
 
@@ -154,8 +152,7 @@ def test_paged_decode_b64_ctx32768_8bit(env, kind):
         assert np.array_equal(vc[p].view(np.uint8), wv_codes.view(np.uint8)) and np.array_equal(vs[p], wv_scale)
         k = dequant(kc, ks)
         v = dequant(vc, vs)
-        ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
-        assert_bf16_close(out[b], ref)
+        ref = bf16_attention_ref(out[b], O.decode_attention, q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
     _paged_full_needles(R, torch, wl, (0, 63), 2200 + len(kind))
 
 
@@ -187,9 +184,8 @@ def test_ring_decode_128k(env):
         vc = to_np64(r.v[b])
         ring = O.RingSeq(sinks=r.S, window=r.W, head=int(heads[b]), count=r.W, seq_len=r.n)
         slot_of = dict(zip(O.visible_positions(r.n - 1, r.S, r.W), ring.chronological_slots()))
-        ref = O.decode_attention(q[b], lambda j: kc[:, slot_of[j]], lambda j: vc[:, slot_of[j]], r.n, r.S, r.W,
+        ref = bf16_attention_ref(out[b], O.decode_attention, q[b], lambda j: kc[:, slot_of[j]], lambda j: vc[:, slot_of[j]], r.n, r.S, r.W,
                                  r.Hkv)
-        assert_bf16_close(out[b], ref)
         assert np.max(np.abs(ref)) > 1.0
         K, V = kc.transpose(1, 0, 2), vc.transpose(1, 0, 2)  # by slot
         every = np.arange(C)
@@ -243,8 +239,7 @@ def test_windowed_paged_decode_b256(env):
         def vf(j, row=row):
             return vb[int(row[j // 16])][:, j % 16]
 
-        ref = O.decode_attention(q[b], kf, vf, n, S, W, wd.Hkv)
-        assert_bf16_close(out[b], ref)
+        ref = bf16_attention_ref(out[b], O.decode_attention, q[b], kf, vf, n, S, W, wd.Hkv)
         assert np.max(np.abs(ref)) > 1.0
         # negative controls: the oracle's visible set with no sinks, one sink more (admits key 4), the
         # window one shorter (drops the first visible key) and, when its block is live, one longer;
@@ -287,8 +282,7 @@ def test_prefill_t8192_sampled_rows(env):
     needles = set(keys)
     checked = 0
     for t in rows:
-        ref = O.decode_attention(q[t], lambda j: k[j], lambda j: v[j], t + 1, S, W, pf.Hkv)
-        assert_bf16_close(out[t], ref)
+        ref = bf16_attention_ref(out[t], O.decode_attention, q[t], lambda j: k[j], lambda j: v[j], t + 1, S, W, pf.Hkv)
         assert np.max(np.abs(ref)) > 1.0
         vis = set(O.visible_positions(t, S, W))
         for s2, w2 in ((0, W), (S + 1, W), (S, W - 1), (S, W + 1)):

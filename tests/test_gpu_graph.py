@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import ropekv_oracle as O
-from tests.gpu_util import assert_bf16_close, assert_bf16_rounded, oracle_cfg, to_np64, torch_dev
+from tests.gpu_util import bf16_attention_ref, assert_bf16_close, assert_bf16_rounded, oracle_cfg, to_np64, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -72,5 +72,4 @@ def test_graph_replays_match_eager_step(env, kv8):
             k, v = wl.kv_of(b)
             want_k = O.rope_apply(to_np64(k0)[b:b + 1], [p], otab, wl.d, True)[0]
             assert_bf16_rounded(k[p], want_k)
-            ref = O.decode_attention(q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
-            assert_bf16_close(out[b], ref)
+            ref = bf16_attention_ref(out[b], O.decode_attention, q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)

@@ -13,7 +13,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (EPS_TURN_HADAMARD, DevPaged, assert_bf16_close, assert_int8_codes_valid,
+from tests.gpu_util import (bf16_attention_ref, EPS_TURN_HADAMARD, DevPaged, assert_bf16_close, assert_int8_codes_valid,
                             check_keep_scale_rows, int8_turn_quotients, oracle_cfg, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -180,9 +180,8 @@ def test_hadamard_decode_paged(env, n_rep, d):
     vd = O.dequant_int8_rows(cache.v.cpu().numpy(), cache.v_scale.cpu().numpy())
     qq, got = to_np64(q), to_np64(out)
     for b, n in enumerate(lens):
-        ref = O.decode_attention(qq[b], lambda j, b=b: kd[table[b, j // 16], :, j % 16],
+        ref = bf16_attention_ref(got[b], O.decode_attention, qq[b], lambda j, b=b: kd[table[b, j // 16], :, j % 16],
                                  lambda j, b=b: vd[table[b, j // 16], :, j % 16], n, S, W, Hkv)
-        assert_bf16_close(got[b], ref)
 
 
 def test_hadamard_paged_append_then_decode(env):
@@ -231,5 +230,4 @@ def test_hadamard_paged_append_then_decode(env):
     torch.cuda.synchronize()
     got, qused = to_np64(out), to_np64(qd)
     for b in range(B):
-        ref = O.decode_attention(qused[b], lambda j, b=b: kplain[b, j], lambda j, b=b: vdeq[b, j], n_tok, S, W, Hkv)
-        assert_bf16_close(got[b], ref)
+        ref = bf16_attention_ref(got[b], O.decode_attention, qused[b], lambda j, b=b: kplain[b, j], lambda j, b=b: vdeq[b, j], n_tok, S, W, Hkv)

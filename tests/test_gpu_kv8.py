@@ -15,7 +15,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (EPS_APPEND_FP8, EPS_APPEND_I8, DevPaged, DevRing, assert_bf16_close,
+from tests.gpu_util import (bf16_attention_ref, EPS_APPEND_FP8, EPS_APPEND_I8, DevPaged, DevRing, assert_bf16_close,
                             assert_fp8_codes_valid, assert_int8_codes_valid, oracle_cfg, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -98,8 +98,7 @@ def test_kv8_decode_paged(env, kind, n_rep, d, S, W, sinks):
         def vb(j, b=b):
             return vd[table[b, j // 16], :, j % 16]
 
-        ref = O.decode_attention(qq[b], kb, vb, n, S, W, Hkv, sink_logits=slh)
-        assert_bf16_close(got[b], ref)
+        ref = bf16_attention_ref(got[b], O.decode_attention, qq[b], kb, vb, n, S, W, Hkv, sink_logits=slh)
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -129,9 +128,8 @@ def test_kv8_decode_ring(env, kind, n_rep, d):
     for b in range(B):
         ring = O.RingSeq(sinks=S, window=W, head=int(heads[b]), count=W, seq_len=lens[b])
         slot_of = dict(zip(O.visible_positions(lens[b] - 1, S, W), ring.chronological_slots()))
-        ref = O.decode_attention(qq[b], lambda j: kd[b, :, slot_of[j]], lambda j: vd[b, :, slot_of[j]], lens[b], S,
+        ref = bf16_attention_ref(got[b], O.decode_attention, qq[b], lambda j: kd[b, :, slot_of[j]], lambda j: vd[b, :, slot_of[j]], lens[b], S,
                                  W, Hkv)
-        assert_bf16_close(got[b], ref)
 
 
 def _check_rows(kind, got_codes, got_scale, want_codes, want_scale, quot=None):
@@ -235,8 +233,7 @@ def test_kv8_paged_append_and_decode(env, kind):
             if n[b] == 0:
                 assert np.all(got[b] == 0)
                 continue
-            ref = O.decode_attention(qused[b], lambda j: kdeq[b, j], lambda j: vdeq[b, j], n[b], S, W, Hkv)
-            assert_bf16_close(got[b], ref)
+            ref = bf16_attention_ref(got[b], O.decode_attention, qused[b], lambda j: kdeq[b, j], lambda j: vdeq[b, j], n[b], S, W, Hkv)
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -282,6 +279,5 @@ def test_kv8_ring_append_and_decode(env, kind, chunks):
         _check_rows(kind, vc[:, slots].transpose(1, 0, 2), vs[:, slots].T, vq_codes[ps], vq_scale[ps])
         R.decode_attn(q[T - 1:T], 1, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
         torch.cuda.synchronize()
-        ref = O.decode_attention(qrot[p0 + T - 1], lambda j: kdeq[j], lambda j: vdeq[j], p0 + T, S, W, Hkv)
-        assert_bf16_close(to_np64(out[0]), ref)
+        ref = bf16_attention_ref(to_np64(out[0]), O.decode_attention, qrot[p0 + T - 1], lambda j: kdeq[j], lambda j: vdeq[j], p0 + T, S, W, Hkv)
         p0 += T

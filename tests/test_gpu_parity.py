@@ -15,7 +15,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, attend_set,
+from tests.gpu_util import (bf16_attention_ref, EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, attend_set,
                             excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
                             plant_queries_, rowwise, to_np64, torch_dev)
 
@@ -391,8 +391,7 @@ def test_decode_paged_few_long_sequences(env, B, Hkv, n):
         slots = np.arange(nb) % 16
         K = kp[rows, :, slots]
         V = vp[rows, :, slots]
-        ref = O.decode_attention(qq[b], lambda j: K[j], lambda j: V[j], nb, 0, 0, Hkv)
-        assert_bf16_close(got[b], ref)
+        ref = bf16_attention_ref(got[b], O.decode_attention, qq[b], lambda j: K[j], lambda j: V[j], nb, 0, 0, Hkv)
         assert np.max(np.abs(ref)) > 1.0
         every = np.arange(nb)
         # negative controls: drop the block after the middle needle split edge, or the last key
@@ -435,8 +434,7 @@ def test_decode_paged_window_with_null_blocks(env):
         def vb(j, b=b):
             return vp[table[b, j // 16], :, j % 16]
 
-        ref = O.decode_attention(qq[b], kb, vb, n, S, W, Hkv)
-        assert_bf16_close(got[b], ref)
+        ref = bf16_attention_ref(got[b], O.decode_attention, qq[b], kb, vb, n, S, W, Hkv)
 
 
 def test_decode_ring_random_head(env):
@@ -464,9 +462,8 @@ def test_decode_ring_random_head(env):
         slots = ring.chronological_slots()
         vis = O.visible_positions(lens[b] - 1, S, W)
         slot_of = dict(zip(vis, slots))
-        ref = O.decode_attention(qq[b], lambda j: kc[b, :, slot_of[j]], lambda j: vc[b, :, slot_of[j]], lens[b], S,
+        ref = bf16_attention_ref(got[b], O.decode_attention, qq[b], lambda j: kc[b, :, slot_of[j]], lambda j: vc[b, :, slot_of[j]], lens[b], S,
                                  W, Hkv)
-        assert_bf16_close(got[b], ref)
 
 
 # ------------------------------------------------------------------ prefill (bf16 MFMA)
@@ -487,8 +484,7 @@ def test_prefill_chunk_from_zero(env, T, S, W, n_rep, d):
     torch.cuda.synchronize()
     assert cache.err.item() == 0
     qq, kk, vv = to_np64(q), to_np64(k), to_np64(v)
-    ref = O.prefill_attention(qq, lambda j: kk[j], lambda j: vv[j], 0, S, W, Hkv)
-    assert_bf16_close(to_np64(out), ref)
+    ref = bf16_attention_ref(to_np64(out), O.prefill_attention, qq, lambda j: kk[j], lambda j: vv[j], 0, S, W, Hkv)
 
 
 def test_prefill_with_paged_prefix_equals_one_shot(env):
@@ -514,8 +510,7 @@ def test_prefill_with_paged_prefix_equals_one_shot(env):
     torch.cuda.synchronize()
     assert cache.err.item() == 0
     qq, kk, vv = to_np64(q), to_np64(k), to_np64(v)
-    ref = O.prefill_attention(qq[pos0:], lambda j: kk[j], lambda j: vv[j], pos0, S, W, Hkv)
-    assert_bf16_close(to_np64(out), ref)
+    ref = bf16_attention_ref(to_np64(out), O.prefill_attention, qq[pos0:], lambda j: kk[j], lambda j: vv[j], pos0, S, W, Hkv)
 
 
 def test_prefill_ring_prefix_lost_is_flagged(env):
