@@ -163,21 +163,21 @@ def _ring_end_to_end(env, neox, dtype_name, chunks):
             present = set(oring.slot_pos.values())
             if needed <= present:
                 assert cache.err.item() == 0
-                ref = O.prefill_attention(qrot[p0:p0 + T], lambda j: kbp[j], lambda j: vraw[j], p0, S, W, Hkv)
+                args = (qrot[p0:p0 + T], lambda j: kbp[j], lambda j: vraw[j], p0, S, W, Hkv)
                 if tol:
-                    assert rowwise(to_np64(o), ref) <= tol
+                    assert rowwise(to_np64(o), O.prefill_attention(*args)) <= tol
                 else:
-                    assert_bf16_close(to_np64(o), ref)
+                    bf16_attention_ref(to_np64(o), O.prefill_attention, *args)
             else:
                 assert cache.err.item() & R.DEV_PREFIX_LOST
                 cache.err.zero_()
         R.decode_attn(q[T - 1:T], 1, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
         torch.cuda.synchronize()
-        ref = O.decode_attention(qrot[p0 + T - 1], lambda j: kbp[j], lambda j: vraw[j], p0 + T, S, W, Hkv)
+        args = (qrot[p0 + T - 1], lambda j: kbp[j], lambda j: vraw[j], p0 + T, S, W, Hkv)
         if tol:
-            assert rowwise(to_np64(out[0]), ref) <= tol
+            assert rowwise(to_np64(out[0]), O.decode_attention(*args)) <= tol
         else:
-            assert_bf16_close(to_np64(out[0]), ref)
+            bf16_attention_ref(to_np64(out[0]), O.decode_attention, *args)
         p0 += T
 
 
@@ -283,11 +283,11 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
             if n[b] == 0:
                 assert np.all(got[b] == 0)
                 continue
-            ref = O.decode_attention(qused[b], lambda j: krot[b, j], lambda j: vall[b, j], n[b], S, W, Hkv)
+            args = (qused[b], lambda j: krot[b, j], lambda j: vall[b, j], n[b], S, W, Hkv)
             if dtype_name == "f32":
-                assert rowwise(got[b], ref) <= 1e-5
+                assert rowwise(got[b], O.decode_attention(*args)) <= 1e-5
             else:
-                assert_bf16_close(got[b], ref)
+                bf16_attention_ref(got[b], O.decode_attention, *args)
 
 
 @pytest.mark.parametrize("S,W", [(4, 12), (0, 20), (4, 0), (3, 33)])
@@ -339,11 +339,11 @@ def test_decode_paged_random_table(env, n_rep, d, dt):
         rows = [table[b, j // 16] for j in range(n)]
         K = np.stack([kp[rows[j], :, j % 16] for j in range(n)])
         V = np.stack([vp[rows[j], :, j % 16] for j in range(n)])
-        ref = O.decode_attention(qq[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
+        args = (qq[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
         if dt == "bf16":
-            assert_bf16_close(got[b], ref)
+            bf16_attention_ref(got[b], O.decode_attention, *args)
         else:
-            assert rowwise(got[b], ref) <= 1e-5
+            assert rowwise(got[b], O.decode_attention(*args)) <= 1e-5
 
 
 @pytest.mark.parametrize("B,Hkv,n", [(1, 8, 19999), (2, 2, 5003)])
@@ -718,12 +718,12 @@ def test_decode_learned_sink_logits(env, dtype_name, n_rep, d):
         if n == 0:
             assert np.all(got[b] == 0)
             continue
-        ref = O.decode_attention(qq[b], lambda j: kp[table[b, j // 16], :, j % 16],
-                                 lambda j: vp[table[b, j // 16], :, j % 16], n, 4, 200, Hkv, sink_logits=sk)
+        args = (qq[b], lambda j: kp[table[b, j // 16], :, j % 16], lambda j: vp[table[b, j // 16], :, j % 16], n,
+                4, 200, Hkv)
         if dtype_name == "f32":
-            assert rowwise(got[b], ref) <= 1e-5
+            assert rowwise(got[b], O.decode_attention(*args, sink_logits=sk)) <= 1e-5
         else:
-            assert_bf16_close(got[b], ref)
+            bf16_attention_ref(got[b], O.decode_attention, *args, sink_logits=sk)
 
 
 @pytest.mark.parametrize("dtype_name,layout,sinks_on", [("f32", "paged", True), ("bf16", "paged", False),
@@ -780,11 +780,10 @@ def test_decode_direct_plan(env, dtype_name, layout, sinks_on):
 
             def vf(j, b=b, slot_of=slot_of):
                 return vc[b, :, slot_of[j]]
-        ref = O.decode_attention(qq[b], kf, vf, n, S, W, Hkv, sink_logits=sk)
         if dtype_name == "f32":
-            assert rowwise(got[b], ref) <= 1e-5, b
+            assert rowwise(got[b], O.decode_attention(qq[b], kf, vf, n, S, W, Hkv, sink_logits=sk)) <= 1e-5, b
         else:
-            assert_bf16_close(got[b], ref)
+            bf16_attention_ref(got[b], O.decode_attention, qq[b], kf, vf, n, S, W, Hkv, sink_logits=sk)
 
 
 @pytest.mark.parametrize("dtype_name", ["bf16", "f32"])
@@ -803,12 +802,12 @@ def test_prefill_learned_sink_logits(env, dtype_name):
     torch.cuda.synchronize()
     assert cache.err.item() == 0
     qq, kk, vv = to_np64(q), to_np64(k), to_np64(v)
-    ref = O.prefill_attention(qq, lambda j: kk[j], lambda j: vv[j], 0, S, W, Hkv,
-                              sink_logits=sinks.cpu().numpy().astype(np.float64))
+    args = (qq, lambda j: kk[j], lambda j: vv[j], 0, S, W, Hkv)
+    sl = sinks.cpu().numpy().astype(np.float64)
     if dtype_name == "f32":
-        assert rowwise(to_np64(out), ref) <= 1e-5
+        assert rowwise(to_np64(out), O.prefill_attention(*args, sink_logits=sl)) <= 1e-5
     else:
-        assert_bf16_close(to_np64(out), ref)
+        bf16_attention_ref(to_np64(out), O.prefill_attention, *args, sink_logits=sl)
 
 
 # ------------------------------------------------------------------ local-position key shift
