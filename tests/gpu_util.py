@@ -20,6 +20,14 @@ def to_np64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def bf16_round(x) -> np.ndarray:
+    """x rounded to the nearest bf16 on the host (what a bf16 tensor holds for the exact value x),
+    back in fp64: the oracle's rotated q and k as the bf16 activations and cache store them."""
+    import torch
+
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
 def normwise(gpu: np.ndarray, ref: np.ndarray) -> float:
     """max |gpu - ref| / max |ref| over the whole tensor."""
     den = float(np.max(np.abs(ref)))

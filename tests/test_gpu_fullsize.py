@@ -13,7 +13,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (bf16_attention_ref, EPS_APPEND_FP8, EPS_APPEND_I8, EPS_TURN_HADAMARD, EPS_TURN_I8, assert_bf16_close, assert_bf16_rounded,
+from tests.gpu_util import (bf16_attention_ref, bf16_round, EPS_APPEND_FP8, EPS_APPEND_I8, EPS_TURN_HADAMARD, EPS_TURN_I8, assert_bf16_close, assert_bf16_rounded,
                             assert_fp8_codes_valid, assert_int8_codes_valid, attend_set, check_keep_scale_rows,
                             excess, int8_turn_quotients, needle_dirs, needle_kv, oracle_cfg, plant_queries_,
                             to_np64, torch_dev)
@@ -108,7 +108,12 @@ def test_paged_decode_b64_ctx32768(env):
         want_k = O.rope_apply(k_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
         assert_bf16_rounded(k[p], want_k)
         assert np.array_equal(v[p], v_raw[b])
-        ref = bf16_attention_ref(out[b], O.decode_attention, q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
+        # the attention over the oracle's own values: its rotated q and new key as bf16 holds them,
+        # the seeded cache rows before them
+        k_ref = k.copy()
+        k_ref[p] = bf16_round(want_k)
+        bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k_ref[j], lambda j: v[j], wl.ctx,
+                           0, 0, wl.Hkv)
     # needles: the same layer decoded again with planted keys and queries
     _paged_full_needles(R, torch, wl, (0, 37, 63), 2100)
 
@@ -150,9 +155,17 @@ def test_paged_decode_b64_ctx32768_8bit(env, kind):
         np.testing.assert_allclose(ks[p], wk_scale, rtol=1e-6, atol=0)
         wv_codes, wv_scale = quant(v_raw[b])
         assert np.array_equal(vc[p].view(np.uint8), wv_codes.view(np.uint8)) and np.array_equal(vs[p], wv_scale)
-        k = dequant(kc, ks)
+        # the attention over the oracle's own values: its rotated q as bf16, its codes of the new
+        # key and value, the seeded code rows before them
+        kc_ref = kc.copy()
+        ks_ref = ks.copy()
+        kc_ref[p], ks_ref[p] = wk_codes, wk_scale
+        k = dequant(kc_ref, ks_ref)
         v = dequant(vc, vs)
-        ref = bf16_attention_ref(out[b], O.decode_attention, q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
+        want_q = O.rope_apply(q_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
+        assert_bf16_rounded(q_rot[b], want_q)
+        bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k[j], lambda j: v[j], wl.ctx, 0,
+                           0, wl.Hkv)
     _paged_full_needles(R, torch, wl, (0, 63), 2200 + len(kind))
 
 

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import ropekv_oracle as O
-from tests.gpu_util import bf16_attention_ref, assert_bf16_close, assert_bf16_rounded, oracle_cfg, to_np64, torch_dev
+from tests.gpu_util import bf16_attention_ref, bf16_round, assert_bf16_close, assert_bf16_rounded, oracle_cfg, to_np64, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -71,5 +71,12 @@ def test_graph_replays_match_eager_step(env, kv8):
         for b in (0, wl.B - 1):
             k, v = wl.kv_of(b)
             want_k = O.rope_apply(to_np64(k0)[b:b + 1], [p], otab, wl.d, True)[0]
+            want_q = O.rope_apply(to_np64(q0)[b:b + 1], [p], otab, wl.d, True)[0]
             assert_bf16_rounded(k[p], want_k)
-            ref = bf16_attention_ref(out[b], O.decode_attention, q_rot[b], lambda j: k[j], lambda j: v[j], wl.ctx, 0, 0, wl.Hkv)
+            assert_bf16_rounded(q_rot[b], want_q)
+            # the attention over the oracle's own rotated q and new key (as bf16 holds them) and the
+            # seeded cache rows before them
+            k_ref = k.copy()
+            k_ref[p] = bf16_round(want_k)
+            bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k_ref[j], lambda j: v[j],
+                               wl.ctx, 0, 0, wl.Hkv)

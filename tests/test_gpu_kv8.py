@@ -15,7 +15,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (bf16_attention_ref, EPS_APPEND_FP8, EPS_APPEND_I8, DevPaged, DevRing, assert_bf16_close,
+from tests.gpu_util import (bf16_attention_ref, bf16_round, EPS_APPEND_FP8, EPS_APPEND_I8, DevPaged, DevRing, assert_bf16_close,
                             assert_fp8_codes_valid, assert_int8_codes_valid, oracle_cfg, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -279,5 +279,7 @@ def test_kv8_ring_append_and_decode(env, kind, chunks):
         _check_rows(kind, vc[:, slots].transpose(1, 0, 2), vs[:, slots].T, vq_codes[ps], vq_scale[ps])
         R.decode_attn(q[T - 1:T], 1, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
         torch.cuda.synchronize()
-        ref = bf16_attention_ref(to_np64(out[0]), O.decode_attention, qrot[p0 + T - 1], lambda j: kdeq[j], lambda j: vdeq[j], p0 + T, S, W, Hkv)
+        # the oracle's rotated query as the bf16 activation holds it, the oracle's codes of the keys
+        bf16_attention_ref(to_np64(out[0]), O.decode_attention, bf16_round(qrot[p0 + T - 1]), lambda j: kdeq[j],
+                           lambda j: vdeq[j], p0 + T, S, W, Hkv)
         p0 += T

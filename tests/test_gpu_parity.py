@@ -15,7 +15,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (bf16_attention_ref, EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, attend_set,
+from tests.gpu_util import (bf16_attention_ref, bf16_round, EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, attend_set,
                             excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
                             plant_queries_, rowwise, to_np64, torch_dev)
 
@@ -90,11 +90,11 @@ def test_table_factor_one_is_plain(env):
 
 # ------------------------------------------------------------------ ring: 16-slot cache (S 4 + W 12) end to end
 
-def _ring_end_to_end(env, neox, dtype_name, chunks):
+def _ring_end_to_end(env, neox, dtype_name, chunks, S=4, W=12):
     R, torch, dev = env
     dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
     act = {"f32": R.F32, "bf16": R.BF16}[dtype_name]
-    B, Hq, Hkv, d, S, W = 1, 8, 4, 64, 4, 12
+    B, Hq, Hkv, d = 1, 8, 4, 64
     n_total = sum(chunks)
     cfg = R.rope_cfg(d, d, rope_theta=1e4, neox=neox)
     ocfg = oracle_cfg(cfg)
@@ -153,7 +153,10 @@ def _ring_end_to_end(env, neox, dtype_name, chunks):
         assert vp[:nv].cpu().tolist() == want_pos
         want_slots = oring.chronological_slots()
         assert (vo[:nv].cpu().numpy() // d).tolist() == want_slots
-        kbp = {j: krot[j] for j in range(n_total)}
+        # the attention reads the oracle's rotated keys and queries as the cache and activations
+        # hold them (rounded once to bf16; fp32 holds them to 1e-7)
+        kbp = {j: krot[j] if tol else bf16_round(krot[j]) for j in range(n_total)}
+        qref = qrot if tol else bf16_round(qrot)
         if T > 1:
             o = torch.empty(T, Hq, d, dtype=dtype, device=dev)
             R.prefill_attn(q, k, v, T, p0, Hq, cache.desc, 0, 0.0, o)
@@ -163,7 +166,7 @@ def _ring_end_to_end(env, neox, dtype_name, chunks):
             present = set(oring.slot_pos.values())
             if needed <= present:
                 assert cache.err.item() == 0
-                args = (qrot[p0:p0 + T], lambda j: kbp[j], lambda j: vraw[j], p0, S, W, Hkv)
+                args = (qref[p0:p0 + T], lambda j: kbp[j], lambda j: vraw[j], p0, S, W, Hkv)
                 if tol:
                     assert rowwise(to_np64(o), O.prefill_attention(*args)) <= tol
                 else:
@@ -173,7 +176,7 @@ def _ring_end_to_end(env, neox, dtype_name, chunks):
                 cache.err.zero_()
         R.decode_attn(q[T - 1:T], 1, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
         torch.cuda.synchronize()
-        args = (qrot[p0 + T - 1], lambda j: kbp[j], lambda j: vraw[j], p0 + T, S, W, Hkv)
+        args = (qref[p0 + T - 1], lambda j: kbp[j], lambda j: vraw[j], p0 + T, S, W, Hkv)
         if tol:
             assert rowwise(to_np64(out[0]), O.decode_attention(*args)) <= tol
         else:
@@ -195,6 +198,13 @@ def test_ring_chunked_appends(env, chunks):
 
 def test_ring_bf16(env):
     _ring_end_to_end(env, True, "bf16", [40, 1, 1, 1, 5])
+
+
+@pytest.mark.parametrize("S,dtype_name", [(2, "f32"), (0, "f32"), (3, "bf16")])
+def test_ring_window_of_one(env, S, dtype_name):
+    # the degenerate window W = 1: every query sees the sinks and itself; each token overwrites the
+    # single ring slot, chunks longer than the ring keep only their last token
+    _ring_end_to_end(env, True, dtype_name, [5, 1, 1, 3, 1, 2], S=S, W=1)
 
 
 # ------------------------------------------------------------------ paged append + freeing + decode
@@ -278,19 +288,20 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
         torch.cuda.synchronize()
         assert cache.err.item() == 0
         got = to_np64(out)
-        qused = to_np64(qd)
+        qused = to_np64(qd)  # the oracle's rotated queries, rounded to the activation dtype by torch
+        kref = krot if dtype_name == "f32" else bf16_round(krot)  # the rotated keys as the cache holds them
         for b in range(B):
             if n[b] == 0:
                 assert np.all(got[b] == 0)
                 continue
-            args = (qused[b], lambda j: krot[b, j], lambda j: vall[b, j], n[b], S, W, Hkv)
+            args = (qused[b], lambda j: kref[b, j], lambda j: vall[b, j], n[b], S, W, Hkv)
             if dtype_name == "f32":
                 assert rowwise(got[b], O.decode_attention(*args)) <= 1e-5
             else:
                 bf16_attention_ref(got[b], O.decode_attention, *args)
 
 
-@pytest.mark.parametrize("S,W", [(4, 12), (0, 20), (4, 0), (3, 33)])
+@pytest.mark.parametrize("S,W", [(4, 12), (0, 20), (4, 0), (3, 33), (2, 1), (0, 1)])
 def test_paged_small_shapes(env, S, W):
     _paged_end_to_end(env, "f32", S, W, B=3, Hq=8, Hkv=4, d=64, rounds=14, seed=7 + S + W)
 
@@ -469,7 +480,8 @@ def test_decode_ring_random_head(env):
 # ------------------------------------------------------------------ prefill (bf16 MFMA)
 
 @pytest.mark.parametrize("T,S,W,n_rep,d", [(300, 4, 100, 8, 128), (200, 0, 0, 4, 128), (129, 4, 64, 2, 64),
-                                           (77, 3, 1000, 1, 128), (333, 4, 65, 8, 64)])
+                                           (77, 3, 1000, 1, 128), (333, 4, 65, 8, 64), (150, 2, 1, 4, 128),
+                                           (70, 0, 1, 8, 64)])
 def test_prefill_chunk_from_zero(env, T, S, W, n_rep, d):
     R, torch, dev = env
     Hkv = 8 if n_rep > 1 else 4
