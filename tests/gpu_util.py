@@ -189,6 +189,35 @@ def assert_int8_codes_valid(got, want, quot, eps):
     return int(bad.sum())
 
 
+def decode_int8(codes, scale) -> np.ndarray:
+    """Rows of an int8 cache read back for comparison: codes x the row's fp32 scale, float64
+    (Hadamard rows stay in the transformed domain their codes live in)."""
+    return np.asarray(codes).astype(np.float64) * np.asarray(scale).astype(np.float64)[..., None]
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """E4M3 bytes read back for comparison, decoded by torch's float8_e4m3fn (bias 7, no
+    infinities, largest finite 448), float64."""
+    import torch
+
+    u8 = np.ascontiguousarray(np.asarray(codes).view(np.uint8))
+    return torch.from_numpy(u8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def oracle_written(kind, key):
+    """A key as a cache written directly at its factor holds it, by the oracle's storage: fp16
+    rounding to nearest ("f16"), or the oracle's row quantiser ("i8", "i8_keep"; for "i8_hadamard"
+    the codes of H key, and the values stay in the H domain).  Returns (values, unit): the unit is an
+    fp16 ulp of the row's largest stored value, or the row's quantisation step."""
+    key = np.asarray(key, dtype=np.float64)
+    if kind == "f16":
+        vals = key.astype(np.float16).astype(np.float64)
+        rowmax = np.max(np.abs(vals), axis=-1, keepdims=True)
+        return vals, np.spacing(rowmax.astype(np.float16)).astype(np.float64)
+    codes, scale = O.quant_int8_hadamard_rows(key) if kind == "i8_hadamard" else O.quant_int8_rows(key)
+    return O.dequant_int8_rows(codes, scale), np.asarray(scale, dtype=np.float64)[..., None]
+
+
 def _e4m3_ordinal(codes):
     u = np.asarray(codes).view(np.uint8).astype(np.int32)
     return np.where(u & 0x80, -(u & 0x7F), u)
@@ -202,7 +231,7 @@ def assert_fp8_codes_valid(got, want, quot, eps):
     assert int(np.max(np.abs(diff), initial=0)) <= 1, "an E4M3 code differs by more than one step"
     bad = diff != 0
     if bad.any():
-        mid = (O.e4m3_value(np.asarray(got)[bad]) + O.e4m3_value(np.asarray(want)[bad])) / 2.0
+        mid = (decode_e4m3(np.asarray(got)[bad]) + decode_e4m3(np.asarray(want)[bad])) / 2.0
         q = np.clip(np.asarray(quot, dtype=np.float64)[bad], -O.E4M3_MAX, O.E4M3_MAX)
         dist = np.abs(q - mid)
         assert float(dist.max()) <= eps, (

@@ -6,7 +6,7 @@ import torch
 
 from oracle import ropekv_oracle as O
 from tests.gpu_util import (assert_bf16_attention, assert_bf16_close, assert_bf16_rounded, assert_fp8_codes_valid,
-                            assert_int8_codes_valid, excess)
+                            assert_int8_codes_valid, decode_e4m3, decode_int8, excess, oracle_written)
 
 
 def _bf16(x):
@@ -83,6 +83,31 @@ def test_fp8_validity_accepts_neighbour_at_midpoint_only():
     skip = np.array([0x3A, 0x38], dtype=np.uint8).view(np.int8)  # two steps (1.25)
     with pytest.raises(AssertionError):
         assert_fp8_codes_valid(skip, want, np.array([1.0624, 1.0]), 1e-3)
+
+
+def test_host_decoders_agree_with_the_oracle_storage():
+    # decode_e4m3 (torch's float8_e4m3fn) and the oracle's E4M3 table agree on every byte but the two
+    # NaNs; decode_int8 is codes x the row scale
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    assert np.array_equal(decode_e4m3(codes), O.e4m3_value(codes))
+    assert decode_e4m3(np.array([0x7E], dtype=np.uint8))[0] == 448.0
+    c = np.array([[127, -3, 0], [1, 2, -127]], dtype=np.int8)
+    assert np.array_equal(decode_int8(c, np.array([0.5, 0.25], dtype=np.float32)),
+                          [[63.5, -1.5, 0.0], [0.25, 0.5, -31.75]])
+
+
+def test_oracle_written_is_one_storage_rounding():
+    rng = np.random.default_rng(11)
+    key = rng.standard_normal((5, 4, 128))
+    vals, unit = oracle_written("f16", key)
+    assert np.all(np.abs(vals - key) <= unit / 2)  # one fp16 rounding, at most half the row max's ulp
+    assert np.array_equal(vals, key.astype(np.float16).astype(np.float64))
+    vals, unit = oracle_written("i8", key)
+    assert np.all(np.abs(vals - key) <= unit / 2 * (1 + 1e-6)) and np.all(unit[..., 0] > 0)
+    assert np.allclose(np.max(np.abs(vals), axis=-1), 127 * unit[..., 0])  # the row max takes code 127
+    hv, hunit = oracle_written("i8_hadamard", key)  # H domain: within half a step of H key
+    assert np.all(np.abs(hv - O.hadamard(key)) <= hunit / 2 * (1 + 1e-6))
+    assert not np.allclose(hv, vals)
 
 
 def _attention_with_rounded_weights(q, K, V, Hkv, sign=None):

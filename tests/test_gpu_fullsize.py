@@ -52,6 +52,9 @@ def _paged_full_needles(R, torch, wl, seqs, seed):
     pos = sorted({0, 15, 16, sp - 1, sp, n // 2 - 1, n // 2, n - sp - 1, n - sp, n - 2, n - 1})
     u = needle_dirs(Hkv, d, seed)
     Kn, Vn = needle_kv(u, len(pos), seed + 1)
+    # fresh seeded queries (a step before this one rotated the workload's queries in place); the last
+    # key, the one a step appends, is among the planted rows
+    synth.device_normal_(wl.q, seed + 2)
     planted = [(wl.k, Kn, wl.k_scale), (wl.v, Vn, wl.v_scale)]
     if wl.kv8:  # 8-bit caches: the needle rows as the oracle quantises them (codes + row scales)
         quant = O.quant_int8_rows if wl.kv8 == "i8" else O.quant_fp8_rows
@@ -109,11 +112,11 @@ def test_paged_decode_b64_ctx32768(env):
         assert_bf16_rounded(k[p], want_k)
         assert np.array_equal(v[p], v_raw[b])
         # the attention over the oracle's own values: its rotated q and new key as bf16 holds them,
-        # the seeded cache rows before them
-        k_ref = k.copy()
-        k_ref[p] = bf16_round(want_k)
-        bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k_ref[j], lambda j: v[j], wl.ctx,
-                           0, 0, wl.Hkv)
+        # the seeded new value, the seeded cache rows before them
+        k_ref, v_ref = k.copy(), v.copy()
+        k_ref[p], v_ref[p] = bf16_round(want_k), v_raw[b]
+        bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k_ref[j], lambda j: v_ref[j],
+                           wl.ctx, 0, 0, wl.Hkv)
     # needles: the same layer decoded again with planted keys and queries
     _paged_full_needles(R, torch, wl, (0, 37, 63), 2100)
 
@@ -157,11 +160,11 @@ def test_paged_decode_b64_ctx32768_8bit(env, kind):
         assert np.array_equal(vc[p].view(np.uint8), wv_codes.view(np.uint8)) and np.array_equal(vs[p], wv_scale)
         # the attention over the oracle's own values: its rotated q as bf16, its codes of the new
         # key and value, the seeded code rows before them
-        kc_ref = kc.copy()
-        ks_ref = ks.copy()
+        kc_ref, ks_ref, vc_ref, vs_ref = kc.copy(), ks.copy(), vc.copy(), vs.copy()
         kc_ref[p], ks_ref[p] = wk_codes, wk_scale
+        vc_ref[p], vs_ref[p] = wv_codes, wv_scale
         k = dequant(kc_ref, ks_ref)
-        v = dequant(vc, vs)
+        v = dequant(vc_ref, vs_ref)
         want_q = O.rope_apply(q_raw[b:b + 1], [p], otab_row, wl.d, True)[0]
         assert_bf16_rounded(q_rot[b], want_q)
         bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k[j], lambda j: v[j], wl.ctx, 0,
@@ -310,16 +313,26 @@ def test_prefill_t8192_sampled_rows(env):
 def test_rerotate_l64_t524288_sampled_rows(env, kind):
     R, torch, dev, WL = env
     rr = WL.Rerotate(R, torch, dev, kind=kind)
-    rows = synth.rng(77).integers(0, rr.L * rr.T * rr.Hkv, 512)
+    rows = np.unique(synth.rng(77).integers(0, rr.L * rr.T * rr.Hkv, 512))
     flat = rr.k.view(-1, rr.d)
     idx = torch.from_numpy(rows).to(dev)
-    before = flat[idx].cpu().numpy()
-    sc_before = rr.scale.view(-1)[idx].cpu().numpy() if kind != "f16" else None
+    positions = (rows // rr.Hkv) % rr.T
+    ca, cb = oracle_cfg(rr.cfg(1.0)), oracle_cfg(rr.cfg(1.125))
+    if kind in ("i8_keep", "i8_hadamard"):
+        # the sampled rows hold the oracle's own codes of seeded keys rotated at factor 1 (the rest of
+        # the cache was written by the append kernel, as in the benchmark), uploaded by a torch copy
+        raw = synth.normal((len(rows), rr.d), 78)
+        krot = O.rotate_by_angle(raw, np.outer(positions, O.inv_freq(ca)), rr.r, True, O.mscale(ca))
+        codes0, sc0 = O.quant_int8_hadamard_rows(krot) if kind == "i8_hadamard" else O.quant_int8_rows(krot)
+        flat[idx] = torch.from_numpy(codes0).to(dev)
+        rr.scale.view(-1)[idx] = torch.from_numpy(np.asarray(sc0, dtype=np.float32)).to(dev)
+        before, sc_before = codes0, np.asarray(sc0, dtype=np.float32)
+    else:  # seeded device fills
+        before = flat[idx].cpu().numpy()
+        sc_before = rr.scale.view(-1)[idx].cpu().numpy() if kind != "f16" else None
     rr.run(1.0, 1.125)
     torch.cuda.synchronize()
     after = flat[idx].cpu().numpy()
-    positions = (rows // rr.Hkv) % rr.T
-    ca, cb = oracle_cfg(rr.cfg(1.0)), oracle_cfg(rr.cfg(1.125))
     if kind == "f16":
         ref = O.rerotate_rows(before.astype(np.float64), positions, ca, cb)
         unit = np.maximum(np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64), 1e-6)

@@ -74,9 +74,10 @@ def test_graph_replays_match_eager_step(env, kv8):
             want_q = O.rope_apply(to_np64(q0)[b:b + 1], [p], otab, wl.d, True)[0]
             assert_bf16_rounded(k[p], want_k)
             assert_bf16_rounded(q_rot[b], want_q)
-            # the attention over the oracle's own rotated q and new key (as bf16 holds them) and the
-            # seeded cache rows before them
-            k_ref = k.copy()
-            k_ref[p] = bf16_round(want_k)
-            bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k_ref[j], lambda j: v[j],
+            # the attention over the oracle's own rotated q and new key (as bf16 holds them), the seeded
+            # new value and the seeded cache rows before them
+            assert np.array_equal(v[p], to_np64(v0)[b])
+            k_ref, v_ref = k.copy(), v.copy()
+            k_ref[p], v_ref[p] = bf16_round(want_k), to_np64(v0)[b]
+            bf16_attention_ref(out[b], O.decode_attention, bf16_round(want_q), lambda j: k_ref[j], lambda j: v_ref[j],
                                wl.ctx, 0, 0, wl.Hkv)

@@ -14,7 +14,8 @@ import pytest
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
 from tests.gpu_util import (bf16_attention_ref, EPS_TURN_HADAMARD, DevPaged, assert_bf16_close, assert_int8_codes_valid,
-                            check_keep_scale_rows, int8_turn_quotients, oracle_cfg, to_np64, torch_dev)
+                            check_keep_scale_rows, decode_int8, int8_turn_quotients, oracle_cfg, oracle_written, to_np64,
+                            torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +104,8 @@ def test_hadamard_rerotate_vs_oracle(env, r, neox, d):
 
 def test_hadamard_rerotate_bounds_from_append(env):
     # raw keys written at A by apply_append into Hadamard-rotated int8 rows, turned to B, compared with
-    # the fp64 key at B in the H domain; the key written directly at B is the yardstick
+    # the fp64 key at B in the H domain; the key written directly at B, as the oracle's Hadamard
+    # quantiser stores it, is the yardstick
     R, torch, dev = env
     L, T, Hkv, d, r = 2, 256, 8, 128, 64
     kw = dict(rope_theta=5e5, orig_max_pos=262144)
@@ -111,44 +113,44 @@ def test_hadamard_rerotate_bounds_from_append(env):
     for fa, fb in ((1.0, 2.0), (2.0, 1.0)):
         ca, cb = R.rope_cfg(d, r, yarn_factor=fa, **kw), R.rope_cfg(d, r, yarn_factor=fb, **kw)
         ta = torch.empty(P, r, dtype=torch.float32, device=dev)
-        tb = torch.empty(P, r, dtype=torch.float32, device=dev)
         R.build_table(ca, P, ta)
-        R.build_table(cb, P, tb)
         pos0 = 262144 - T // 2
         raw = torch.from_numpy(synth.normal((L, T, Hkv, d), 1400)).to(dev, torch.float16)
-        out = []
-        for cfg, tab in ((ca, ta), (cb, tb)):
-            kc = torch.zeros(L, T, Hkv, d, dtype=torch.int8, device=dev)
-            sc = torch.zeros(L, T, Hkv, dtype=torch.float32, device=dev)
-            err = torch.zeros(1, dtype=torch.int32, device=dev)
-            pos = torch.arange(pos0, pos0 + T, dtype=torch.int32, device=dev)
-            for layer in range(L):
-                dl = R.kv_cache(R.CONTIG, R.I8, Hkv, d, kc[layer], capacity=T, pos0=pos0, k_scale=sc[layer],
-                                err_word=err, k_int8_mode=R.I8_HADAMARD)
-                R.apply_append(cfg, tab, P, None, 0, raw[layer].clone(), None, R.F16, T, pos, None, dl)
-            torch.cuda.synchronize()
-            assert err.item() == 0
-            out.append((kc, sc, R.kv_cache(R.CONTIG, R.I8, Hkv, d, kc, capacity=T, pos0=pos0, k_scale=sc,
-                                           err_word=err, k_int8_mode=R.I8_HADAMARD)))
-        (ka, sa, desc_a), (kb, sb, _) = out
+        ka = torch.zeros(L, T, Hkv, d, dtype=torch.int8, device=dev)
+        sa = torch.zeros(L, T, Hkv, dtype=torch.float32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        pos_d = torch.arange(pos0, pos0 + T, dtype=torch.int32, device=dev)
+        for layer in range(L):
+            dl = R.kv_cache(R.CONTIG, R.I8, Hkv, d, ka[layer], capacity=T, pos0=pos0, k_scale=sa[layer],
+                            err_word=err, k_int8_mode=R.I8_HADAMARD)
+            R.apply_append(ca, ta, P, None, 0, raw[layer].clone(), None, R.F16, T, pos_d, None, dl)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        desc_a = R.kv_cache(R.CONTIG, R.I8, Hkv, d, ka, capacity=T, pos0=pos0, k_scale=sa, err_word=err,
+                            k_int8_mode=R.I8_HADAMARD)
         rawn = to_np64(raw)
         pos = np.arange(pos0, pos0 + T)
         oa, ob = oracle_cfg(ca), oracle_cfg(cb)
+
+        def key_at(o):
+            return np.stack([O.rotate_by_angle(rawn[l], np.outer(pos, O.inv_freq(o))[:, None, :], r, True, O.mscale(o))
+                             for l in range(L)])
+
         # the append's rows against the oracle's Hadamard quantiser of the fp64 key at A
-        key_a = np.stack([O.rotate_by_angle(rawn[l], np.outer(pos, O.inv_freq(oa))[:, None, :], r, True, O.mscale(oa))
-                          for l in range(L)])
+        key_a = key_at(oa)
         wc, ws_ = O.quant_int8_hadamard_rows(key_a)
         assert_int8_codes_valid(ka.cpu().numpy(), wc, O.row_quotients(O.hadamard(key_a), ws_), EPS_TURN_HADAMARD)
         np.testing.assert_allclose(sa.cpu().numpy(), ws_, rtol=1e-5)
         R.rerotate(ca, cb, desc_a, L)
         torch.cuda.synchronize()
-        truth = O.hadamard(np.stack([O.rotate_by_angle(rawn[l], np.outer(pos, O.inv_freq(ob))[:, None, :], r, True,
-                                                       O.mscale(ob)) for l in range(L)]))
-        turned = O.dequant_int8_rows(ka.cpu().numpy(), sa.cpu().numpy())
-        written = O.dequant_int8_rows(kb.cpu().numpy(), sb.cpu().numpy())
+        assert err.item() == 0
+        key_b = key_at(ob)
+        truth = O.hadamard(key_b)
+        written, unit = oracle_written("i8_hadamard", key_b)  # H domain
+        turned = decode_int8(ka.cpu().numpy(), sa.cpu().numpy())
         et, ew = turned - truth, written - truth
         ratio = float(np.sqrt(np.mean(et * et)) / np.sqrt(np.mean(ew * ew)))
-        worst = float(np.max(np.abs(et) / sb.cpu().numpy().astype(np.float64)[..., None]))
+        worst = float(np.max(np.abs(et) / unit))
         assert ratio <= 1.6 and worst <= 3.0, (fa, fb, ratio, worst)
 
 

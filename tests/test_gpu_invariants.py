@@ -9,7 +9,9 @@
   written key's error variance, so after k turns the RMS bound is
   sqrt(1 + 1.56 k) (1.6 at k = 1), and each further turn adds at most one
   rounding to the worst element: w1 + (k - 1) u (u = 1 ulp / 1 step / 1.5
-  steps).
+  steps).  The written key is the fp64 key at the target factor as the
+  oracle's storage holds it (fp16 rounding to nearest, or the oracle's row
+  quantiser), so no yardstick comes from the kernels under test.
 - q . k depends only on m - n through apply_append ("RoPE, scaling, sliding
   window, attention sinks", "A worked number": q at 5 against k at 3 equals q
   at 105 against k at 103, both cos(0.2) = 0.9800666 for pair 16 at b = 1e4),
@@ -24,7 +26,8 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import DevPaged, DevRing, assert_bf16_close, oracle_cfg, rowwise, to_np64, torch_dev
+from tests.gpu_util import (DevPaged, DevRing, assert_bf16_close, decode_int8, oracle_cfg, oracle_written, rowwise,
+                            to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,20 +68,10 @@ def _write(R, torch, dev, cfg, table, raw, kind, pos0):
 
 
 def _values(kind, kc, sc):
-    """The keys a cache holds, float64; Hadamard rows back in the plain domain."""
+    """The keys a cache holds, read back as float64 (Hadamard rows in the H domain of their codes)."""
     if kind == "f16":
         return to_np64(kc)
-    x = O.dequant_int8_rows(kc.cpu().numpy(), sc.cpu().numpy())
-    return O.hadamard(x) if kind == "i8_hadamard" else x
-
-
-def _unit(kind, written, sc_written):
-    """The error unit of the key written directly at the target: an fp16 ulp of the row's largest
-    value, or the quantisation step of its row (with the Hadamard, in the transformed domain)."""
-    if kind == "f16":
-        rowmax = np.max(np.abs(written), axis=-1, keepdims=True)
-        return np.spacing(rowmax.astype(np.float16)).astype(np.float64)
-    return sc_written.cpu().numpy().astype(np.float64)[..., None]
+    return decode_int8(kc.cpu().numpy(), sc.cpu().numpy())
 
 
 W1 = {"f16": 3.0, "i8": 2.0, "i8_keep": 2.0, "i8_hadamard": 3.0}
@@ -91,10 +84,11 @@ WSTEP = {"f16": 1.0, "i8": 1.0, "i8_keep": 1.0, "i8_hadamard": 1.5}
 
 
 def _stats(kind, turned, written, truth, unit):
-    """RMS(turned - truth) / RMS(written - truth) and the worst |turned - truth| in units (Hadamard
-    rows compared in the transformed domain, where their codes live)."""
+    """RMS(turned - truth) / RMS(written - truth) and the worst |turned - truth| in units; turned and
+    written as the cache holds them (Hadamard rows in the transformed domain, where their codes
+    live), truth the plain fp64 key."""
     if kind == "i8_hadamard":
-        turned, written, truth = O.hadamard(turned), O.hadamard(written), O.hadamard(truth)
+        truth = O.hadamard(truth)
     ratio = float(np.sqrt(np.mean((turned - truth) ** 2)) / np.sqrt(np.mean((written - truth) ** 2)))
     worst = float(np.max(np.abs(turned - truth) / unit))
     return ratio, worst
@@ -112,27 +106,25 @@ def _cfg(R, s):
 @pytest.mark.parametrize("kind", ["f16", "i8", "i8_keep", "i8_hadamard"])
 @pytest.mark.parametrize("fa,fb", [(1.0, 2.0), (1.5, 1.125)])
 def test_rerotate_round_trip(env, kind, fa, fb):
-    # keys written at A, turned A -> B -> A, against the fp64 key at A; the key written at A is the
-    # yardstick; two turns
+    # keys written at A by apply_append, turned A -> B -> A, against the fp64 key at A; the key as
+    # the oracle's storage holds it written directly at A (or B, after one turn) is the yardstick
     R, torch, dev = env
     T, Hkv, d = 512, 8, 128
     P = 524288
     ca, cb = _cfg(R, fa), _cfg(R, fb)
     ta = _table(R, torch, dev, ca, P)
-    tb = _table(R, torch, dev, cb, P)
     for pos0 in (262144 - T // 2, 519999 - T + 1):
         raw = torch.from_numpy(synth.normal((T, Hkv, d), 3000 + pos0 % 89)).to(dev, torch.float16)
         rawn = to_np64(raw)
         pos = np.arange(pos0, pos0 + T)
         kc, sc, desc, err = _write(R, torch, dev, ca, ta, raw, kind, pos0)
-        written = _values(kind, kc, sc)
-        unit = _unit(kind, written, sc)
+        truth_a, truth_b = _truth(rawn, pos, ca), _truth(rawn, pos, cb)
+        written, unit = oracle_written(kind, truth_a)
         # there: one turn, against the key written directly at B
         R.rerotate(ca, cb, desc, 1)
         torch.cuda.synchronize()
-        wb, sb, _, _ = _write(R, torch, dev, cb, tb, raw, kind, pos0)
-        written_b = _values(kind, wb, sb)
-        r1, w1 = _stats(kind, _values(kind, kc, sc), written_b, _truth(rawn, pos, cb), _unit(kind, written_b, sb))
+        written_b, unit_b = oracle_written(kind, truth_b)
+        r1, w1 = _stats(kind, _values(kind, kc, sc), written_b, truth_b, unit_b)
         assert r1 <= 1.6 and w1 <= W1[kind], (pos0, r1, w1)
         # and back: two turns, against the key written at A
         R.rerotate(cb, ca, desc, 1)
@@ -140,7 +132,7 @@ def test_rerotate_round_trip(env, kind, fa, fb):
         assert err.item() == 0
         if kind == "f16":  # dims past the rotary slice never move
             assert torch.equal(kc[..., 64:], raw.to(torch.float16)[..., 64:])
-        ratio, worst = _stats(kind, _values(kind, kc, sc), written, _truth(rawn, pos, ca), unit)
+        ratio, worst = _stats(kind, _values(kind, kc, sc), written, truth_a, unit)
         k = 2
         print(f"round trip {kind} {fa}->{fb}->{fa} pos0 {pos0}: one turn {r1:.3f}x {w1:.2f}; back {ratio:.3f}x {worst:.2f}")
         assert ratio <= rms_bound(k), (pos0, ratio)
@@ -151,7 +143,8 @@ def test_rerotate_round_trip(env, kind, fa, fb):
 def test_rerotate_factor_sequence(env, kind):
     # one cache written at factor 1, turned 1 -> 1.125 -> ... -> 2, then 2 -> 1 and 1 -> 2 (the
     # growing dialog of the page's band runs); after every switch, against the fp64 key at that
-    # factor with the key written directly at it as the yardstick, k turns so far
+    # factor with the key written directly at it (by the oracle's storage) as the yardstick, k turns
+    # so far
     R, torch, dev = env
     T, Hkv, d, P = 512, 8, 128, 524288
     pos0 = 519999 - T + 1
@@ -169,10 +162,9 @@ def test_rerotate_factor_sequence(env, kind):
         assert err.item() == 0
         if kind == "i8_keep":
             kept.append(float((sc == before).float().mean().item()))
-        wk, ws_, _, _ = _write(R, torch, dev, _cfg(R, fb), _table(R, torch, dev, _cfg(R, fb), P), raw, kind, pos0)
-        written = _values(kind, wk, ws_)
-        ratio, worst = _stats(kind, _values(kind, kc, sc), written, _truth(rawn, pos, _cfg(R, fb)),
-                              _unit(kind, written, ws_))
+        truth = _truth(rawn, pos, _cfg(R, fb))
+        written, unit = oracle_written(kind, truth)
+        ratio, worst = _stats(kind, _values(kind, kc, sc), written, truth, unit)
         print(f"sequence {kind} step {k} {fa}->{fb}: {ratio:.3f}x (bound {rms_bound(k):.3f}), "
               f"worst {worst:.2f} (bound {W1[kind] + (k - 1) * WSTEP[kind]:.1f})"
               + (f", kept {kept[-1]:.4f}" if kept else ""))

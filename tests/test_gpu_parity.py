@@ -16,8 +16,8 @@ import pytest
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
 from tests.gpu_util import (bf16_attention_ref, bf16_round, EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, attend_set,
-                            excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
-                            plant_queries_, rowwise, to_np64, torch_dev)
+                            decode_int8, excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
+                            oracle_written, plant_queries_, rowwise, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -575,8 +575,9 @@ def _turn_stats(turned, written, truth, unit):
 @pytest.mark.parametrize("fa,fb", [(1.0, 2.0), (1.5, 2.0), (2.0, 1.0), (1.0, 1.125)])
 def test_rerotate_bounds(env, kind, fa, fb):
     # keys written at factor A by apply_append, turned to B, compared with the fp64 key at B;
-    # the error of a key written directly at B is the yardstick (RMS <= 1.6x; worst <= 3 fp16
-    # ulps of the row max, or <= 2 int8 steps of B's row scale).
+    # the error of the key written directly at B (as the oracle's storage holds it: fp16 rounding or
+    # its row quantiser) is the yardstick (RMS <= 1.6x; worst <= 3 fp16 ulps of the row max, or
+    # <= 2 int8 steps of B's row scale).
     R, torch, dev = env
     L, T, Hkv, d, r = 2, 512, 8, 128, 64
     base_kw = dict(rope_theta=5e5, orig_max_pos=262144)
@@ -584,12 +585,10 @@ def test_rerotate_bounds(env, kind, fa, fb):
     oa, ob = oracle_cfg(ca), oracle_cfg(cb)
     P = 524288
     ta = _table(R, torch, dev, ca, P)
-    tb = _table(R, torch, dev, cb, P)
     kv_dtype = R.F16 if kind == "f16" else R.I8
     for pos0 in (262144 - T // 2, 519999 - T + 1):
         raw = torch.from_numpy(synth.normal((L, T, Hkv, d), 90 + pos0 % 97)).to(dev, torch.float16)
         kc, sc, desc = _contig_write(R, torch, dev, ca, ta, raw, kv_dtype, L, T, Hkv, d, pos0)
-        kw, sw, _ = _contig_write(R, torch, dev, cb, tb, raw, kv_dtype, L, T, Hkv, d, pos0)  # written at B
         before = kc.clone()
         R.rerotate(ca, cb, desc, L)
         torch.cuda.synchronize()
@@ -597,15 +596,12 @@ def test_rerotate_bounds(env, kind, fa, fb):
         pos = np.arange(pos0, pos0 + T)
         truth = np.stack([O.rotate_by_angle(rawn[l].reshape(T, Hkv, d), np.outer(pos, O.inv_freq(ob))[:, None, :],
                                             r, True, O.mscale(ob)) for l in range(L)])
+        written, unit = oracle_written(kind, truth)
         if kind == "f16":
-            turned, written = to_np64(kc), to_np64(kw)
-            rowmax = np.max(np.abs(written), axis=-1, keepdims=True)
-            unit = np.spacing(rowmax.astype(np.float16)).astype(np.float64)
+            turned = to_np64(kc)
             assert np.array_equal(kc[..., r:].cpu().numpy(), before[..., r:].cpu().numpy())  # tail bitwise
         else:
-            turned = kc.cpu().numpy().astype(np.float64) * sc.cpu().numpy().astype(np.float64)[..., None]
-            written = kw.cpu().numpy().astype(np.float64) * sw.cpu().numpy().astype(np.float64)[..., None]
-            unit = sw.cpu().numpy().astype(np.float64)[..., None]
+            turned = decode_int8(kc.cpu().numpy(), sc.cpu().numpy())
         ratio, worst = _turn_stats(turned, written, truth, unit)
         assert ratio <= 1.6, ratio
         assert worst <= (3.0 if kind == "f16" else 2.0), worst
@@ -651,17 +647,22 @@ def test_rerotate_identity_and_oracle_parity(env):
 
 @pytest.mark.parametrize("mode", [0, 1])
 def test_rerotate_int8_identity(env, mode):
-    # A -> A over rows the append quantised (row max 127 codes): codes and scales bit for bit, for the
-    # requantising turn (mode 0) and the keep-scale turn (mode 1); the oracle's turn is the identity too
+    # A -> A over quantised keys (the oracle's codes of seeded keys rotated at A: a row's largest code
+    # is +-127): codes and scales bit for bit, for the requantising turn (mode 0) and the keep-scale
+    # turn (mode 1); the oracle's turn is the identity too
     R, torch, dev = env
     L, T, Hkv, d, r = 2, 96, 8, 128, 64
     ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.375, orig_max_pos=262144)
-    P = 524288
-    ta = _table(R, torch, dev, ca, P)
-    raw = torch.from_numpy(synth.normal((L, T, Hkv, d), 98)).to(dev, torch.float16)
-    kc, sc, desc = _contig_write(R, torch, dev, ca, ta, raw, R.I8, L, T, Hkv, d, 400000)
-    desc.k_int8_mode = mode
-    c0, s0 = kc.cpu().numpy(), sc.cpu().numpy()
+    oa = oracle_cfg(ca)
+    raw = synth.normal((L, T, Hkv, d), 98)
+    angles = np.outer(np.arange(400000, 400000 + T), O.inv_freq(oa))[:, None, :]
+    key = np.stack([O.rotate_by_angle(raw[l], angles, r, True, O.mscale(oa)) for l in range(L)])
+    c0, s0 = O.quant_int8_rows(key)
+    s0 = np.asarray(s0, dtype=np.float32)
+    kc, sc = torch.from_numpy(c0).to(dev), torch.from_numpy(s0).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    desc = R.kv_cache(R.CONTIG, R.I8, Hkv, d, kc, capacity=T, pos0=400000, k_scale=sc, err_word=err,
+                      k_int8_mode=mode)
     R.rerotate(ca, ca, desc, L)
     torch.cuda.synchronize()
     assert np.array_equal(kc.cpu().numpy(), c0) and np.array_equal(sc.cpu().numpy(), s0)
