@@ -22,6 +22,7 @@ constexpr int kI8Threads = 256;  // int8 lane kernel: threads per workgroup
 constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup (1: 16.4 ms, 2: 14.4, 4: 15.3 on the
                                  // 64-layer int8 switch; the float kernel is fastest at 1)
 constexpr int kHadLayers = 4;    // Hadamard head_dim-128 kernels: layers per workgroup (r 64: 1: 16.2 ms, 2: 15.7, 4: 15.2, 8: 15.1)
+constexpr int kHadNeoxLayers = 8;  // the staged NeoX r = 64 Hadamard kernel (64-layer switch: 2: 14.2 ms, 4: 13.6, 8: 13.5)
 
 struct RerotArgs {
   RopeParams from, to;
@@ -1258,6 +1259,247 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_r64_kernel(Rero
   }
 }
 
+// NeoX r = 64 over Hadamard rows, with fewer vector instructions per row than the kernel
+// above (same lane layout: lane q of a row's pair holds codes 32 q .. 32 q + 31 of each half).
+//  * The first transform is exact integer arithmetic: u = c_lo + c_hi lies in [-256, 254]
+//    and its 32-point transform within 32 x 256 = 8192, so it runs two values per
+//    instruction on 16-bit halves; the sums of sign-extended code bytes are written
+//    straight into the halves.
+//  * The Sylvester transform splits as H64 = [[H32, H32], [H32, -H32]].  With
+//    s = H32 u[0..31] (lane 0) and t = H32 u[32..63] (lane 1), the top stage of the first
+//    transform, the turn R - I of the NeoX pairs (e, e + 32) and the top stage of the second
+//    transform collapse into one map per pair:
+//      H2 [[cm1, -sn], [sn, cm1]] H2 = 2 [[cm1, sn], [-sn, cm1]],   cm1 = cos - 1,
+//    so (H64 D) / 2 is H32, on each lane, of (cm1 s + sn t, cm1 t - sn s): one partner
+//    exchange replaces the two cross-lane butterfly stages, and sin / -sin come from two
+//    table planes so both lanes run the same instructions.  cm1 is taken as
+//    -2 sin^2(angle / 2) times the gain plus (gain - 1), exact for small angles.
+//  * y / 2 = 64 c + (H64 D) / 2 is requantised against its row maximum; the factor 1 / 64 of
+//    the unnormalised transforms goes into the scale.
+// The table's layout in LDS: per position 36 floats (32 used), and the sin / -sin planes start
+// 16 floats (mod 64) after the cos - 1 plane, so that a read of one entry group by the 8 distinct
+// (plane, position) pairs of a wave falls in 8 distinct 16-byte bank groups.
+__host__ __device__ constexpr int had_plane(int np) { return 36 * np; }
+__host__ __device__ constexpr int had_off_sn(int np) { return (had_plane(np) + 47) / 64 * 64 + 16; }
+__host__ __device__ constexpr int had_off_nsn(int np) { return had_off_sn(np) + (had_plane(np) + 63) / 64 * 64; }
+__host__ __device__ constexpr int had_table_floats(int np) { return had_off_nsn(np) + had_plane(np); }
+__device__ __forceinline__ void hadamard_pair_table(const RerotArgs &a, int pa, int np, float *s_tab, double dwt) {
+  const int half = a.to.rotary_dim / 2;
+  const float gain = (float)a.gain, gm1 = (float)(a.gain - 1.0);
+  const bool same_pair = blockDim.x % half == 0;
+  for (int idx = threadIdx.x; idx < np * half; idx += blockDim.x) {
+    const int pt = idx / half, i = idx - pt * half;
+    const double th = (double)(a.pos0 + pa + pt) * (same_pair || idx == (int)threadIdx.x ? dwt : a.dw[i]);
+    const double k = rint(th * 0.15915494309189535);  // turns of 2 pi
+    const double rd = fma(-k, 2.4492935982947064e-16, fma(-k, 6.283185307179586, th));
+    const float sf = sinf((float)rd), hs = sinf(0.5f * (float)rd);
+    const int o = 36 * pt + i;
+    s_tab[o] = fmaf(-2.f * gain * hs, hs, gm1);
+    s_tab[had_off_sn(np) + o] = sf * gain;
+    s_tab[had_off_nsn(np) + o] = -(sf * gain);
+  }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+// 16-bit halves (sext(a.byte0) + sext(b.byte0), sext(a.byte2) + sext(b.byte2)), and the same
+// for bytes 1 and 3: two byte adds written straight into the halves
+__device__ __forceinline__ uint32_t add_bytes_02(uint32_t a, uint32_t b) {
+  uint32_t r;
+  __asm__("v_add_u32_sdwa %0, sext(%1), sext(%2) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:BYTE_0\n\t"
+          "v_add_u32_sdwa %0, sext(%1), sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2 src1_sel:BYTE_2"
+          : "=&v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t add_bytes_13(uint32_t a, uint32_t b) {
+  uint32_t r;
+  __asm__("v_add_u32_sdwa %0, sext(%1), sext(%2) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:BYTE_1\n\t"
+          "v_add_u32_sdwa %0, sext(%1), sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3 src1_sel:BYTE_3"
+          : "=&v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// (lo, hi) -> (lo + hi, lo - hi) in one packed multiply-add: hi * 1 + lo and hi * 0xffff + lo
+// (mod 2^16); k holds 0xffff0001
+__device__ __forceinline__ uint32_t bfly_halves(uint32_t x, uint32_t k) {
+  uint32_t r;
+  __asm__("v_pk_mad_u16 %0, %1, %2, %1 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(x), "v"(k));
+  return r;
+}
+
+// Row staging for the kernel below: each wave owns 32 rows of the workgroup's 128 and walks the
+// workgroup's layers; a layer's rows come in by direct global -> LDS loads in which every 8 lanes
+// take one whole 128-byte row (full cache lines, streamed), and the results leave the same way.
+// Rows sit 144 bytes apart in the stage (9 slots of 16 bytes, the ninth unused), so that 8
+// consecutive rows start in 8 distinct 16-byte bank groups and each lane reads its half row at
+// fixed offsets from one address (the two lanes of a row read chunks 2 slots apart, which
+// overlaps in banks two ways within 16 lanes).  Reading the rows in place (32 bytes of a row per
+// lane pair and instruction) instead ran at the rate of the same pass with no arithmetic at all.
+// Everything that depends on the lane is derived again in each layer from an opaque copy of the
+// lane index: held across the layer loop, the turn table and the addresses took 150-190
+// registers (3 waves per SIMD).
+// o[e] += x'[e] * b[e] for 8 values, x' = x of the partner lane l ^ 1, as v_fmac_f32 with a DPP
+// lane swap on its first operand (the compiler keeps the swap as a separate move).  The leading
+// s_nop 1 gives the two wait states a DPP read needs after a vector write of its operand; inside
+// the block no instruction reads a register another one writes.
+__device__ __forceinline__ void fmac_partner8(float (&o)[8], const float *x, const float (&b)[8]) {
+  __asm__("s_nop 1\n\t"
+          "v_fmac_f32_dpp %0, %8, %16 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %17 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %18 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %19 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %20 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %21 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %23 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+          : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]), "+v"(o[6]), "+v"(o[7])
+          : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+            "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]));
+}
+
+constexpr int kHadStage = 32 * 9 * 16;  // bytes per wave
+
+__device__ __forceinline__ void had_load_rows(const int8_t *lk, uint8_t *stage, int ln, int nrows, int wrow0) {
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int sl = 64 * jj + ln, r = sl / 9, ch = min(sl - 9 * r, 7);
+    if (jj < 4 || ln < 32) dma16_stream(lk + min(wrow0 + r, nrows - 1) * 128 + 16 * ch, stage + 1024 * jj);
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void rerotate_int8_hadamard128_neox64_kernel(RerotArgs a) {
+  extern __shared__ float s_tab[];  // [3][np][32] table, then one row stage per wave
+  const int half = 32;
+  const double dwt = own_dw(a);
+  const ChunkRows c = chunk_rows(a);
+  const int wv = threadIdx.x >> 6;
+  const int wrow0 = 32 * wv;  // the wave's first row within the workgroup's rows
+  const long layer_rows = (long)a.rows_T * a.Hkv;
+  uint8_t *stage = (uint8_t *)(s_tab + had_table_floats(c.np)) + kHadStage * wv;
+  // stage slot s = 64 j + lane (j < 5; the last load only in lanes < 32) holds chunk s % 9 of
+  // the wave's row s / 9 (the ninth slot repeats chunk 7); rows past the layer's end load the
+  // last live row, whose results are never stored
+  had_load_rows((const int8_t *)a.k + c.row0 * 128, stage, threadIdx.x & 63, c.nrows, wrow0);
+  hadamard_pair_table(a, c.pa, c.np, s_tab, dwt);
+  const float *s_cm1 = s_tab, *s_sn = s_tab + had_off_sn(c.np), *s_nsn = s_tab + had_off_nsn(c.np);
+  const uint32_t kbf = 0xffff0001u;
+  for (int l = 0; l < c.nl; ++l) {
+    int lane = threadIdx.x & 63;
+    __asm__ volatile("" : "+v"(lane));
+    const long lrow = c.row0 + (long)l * layer_rows;  // the workgroup's first row in this layer
+    // computing layout: lane l holds codes 32 q .. 32 q + 31 of each half of row rr = l / 2 (q = l % 2);
+    // out = A x + B x' with x' the partner lane's value and (A, B) = (cm1, sn) on the lower lane
+    // (x = s, x' = t) and (cm1, -sn) on the upper one (x = t, x' = s)
+    const int rr = lane >> 1, q = lane & 1;
+    const int row = wrow0 + rr;
+    const bool live = row < c.nrows;
+    const int tab = ((c.r0 + (live ? row : 0)) / a.Hkv - c.pa) * 36;
+    const float *ta = s_cm1 + tab, *tb = (q ? s_nsn : s_sn) + tab;
+    uint8_t *mine = stage + 16 * (9 * rr + 2 * q);
+    const float sco = a.scale[lrow + (live ? row : 0)];
+    wait_vmcnt<0>();  // this wave's rows of layer l are in its stage
+    uint32_t w[16];  // words 0..7: codes 32 q + (0..31); 8..15: codes 64 + 32 q + (0..31)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = *(const uint4 *)(mine + 16 * ((i & 1) + 4 * (i >> 1)));
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+    // P[2 j + b] holds u[4 j + b] (low half) and u[4 j + 2 + b] (high half), u = c_lo + c_hi
+    uint32_t P[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      P[2 * j] = add_bytes_02(w[j], w[8 + j]);
+      P[2 * j + 1] = add_bytes_13(w[j], w[8 + j]);
+    }
+    // H32 over index bits 0, 2, 3, 4 (register index bits 0..3), then bit 1 inside the registers
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i & m) == 0) {
+          const u16x2 x = as_u16x2(P[i]), y = as_u16x2(P[i | m]);
+          P[i] = as_u32(x + y);
+          P[i | m] = as_u32(x - y);
+        }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) P[i] = bfly_halves(P[i], kbf);
+    float x[32];  // lower lane: s = H32 u[0..31]; upper lane: t = H32 u[32..63]
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t v = P[2 * (e >> 2) + (e & 1)];
+      x[e] = (float)(short)(((e >> 1) & 1) ? (v >> 16) : (v & 0xffffu));
+    }
+    // the collapsed top stages and turn: lower lane cm1 s + sn t, upper lane cm1 t - sn s
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e0 = 0; e0 < 32; e0 += 8) {
+      const float4 a0 = *(const float4 *)(ta + e0), a1 = *(const float4 *)(ta + e0 + 4);
+      const float4 b0 = *(const float4 *)(tb + e0), b1 = *(const float4 *)(tb + e0 + 4);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = x[e0 + e] * av[e];
+      fmac_partner8(o, x + e0, bv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e0 + e] = o[e];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // H32 on each lane: x[e] = (H64 D)[32 q + e] / 2
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if ((j & h) == 0) {
+          const float u = x[j], v = x[j + h];
+          x[j] = u + v;
+          x[j + h] = u - v;
+        }
+    // y / 2 = 64 c + x, in blocks behind scheduling fences so that each x dies as its two y are made
+    float y[64];
+    float amax = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e0 = 0; e0 < 32; e0 += 4) {
+#pragma unroll
+      for (int e = e0; e < e0 + 4; ++e) {
+        y[e] = fmaf(code_at(w, e), 64.f, x[e]);
+        y[32 + e] = fmaf(code_at(w, 32 + e), 64.f, x[e]);
+        amax = fmaxf(amax, fmaxf(fabsf(y[e]), fabsf(y[32 + e])));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    amax = fmaxf(amax, dpp_xor1(amax));
+    const float inv = amax > 0.f && sco > 0.f ? 127.0f / amax : 0.f;
+    uint32_t out[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      out[i] = pack4_codes(code_fma(y[4 * i], inv), code_fma(y[4 * i + 1], inv), code_fma(y[4 * i + 2], inv),
+                           code_fma(y[4 * i + 3], inv));
+    // back into the same slots, then out by whole rows (lane l: row 8 j + l / 8, chunk l % 8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(uint4 *)(mine + 16 * ((i & 1) + 4 * (i >> 1))) = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    __asm__ volatile("" ::: "memory");
+    const __amdgpu_buffer_rsrc_t rs = span_rsrc((int8_t *)a.k + lrow * 128, (long)c.nrows * 128);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 8 * j + (lane >> 3);
+      const uint4 v = *(const uint4 *)(stage + 16 * (9 * r + (lane & 7)));
+      b128_t o;
+      o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+      // rows past the layer's end lie beyond the resource's extent: the store is dropped
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, (wrow0 + r) * 128 + 16 * (lane & 7), 0, kStream);
+    }
+    if (live && q == 0) a.scale[lrow + row] = inv > 0.f ? sco * amax * (1.0f / (127.0f * 64.0f)) : 0.f;
+    if (l + 1 < c.nl) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stage has been read out
+      had_load_rows((const int8_t *)a.k + (lrow + layer_rows) * 128, stage, lane, c.nrows, wrow0);
+    }
+  }
+}
+
 // Uniform shift of cached keys by delta positions (local-position windows).
 struct ShiftArgs {
   RopeParams p;
@@ -1493,8 +1735,12 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
             hipLaunchKernelGGL(rerotate_int8_hadamard128_r64_kernel<false>, g1, dim3(256), shm1, s, a);
           else if (!to.neox)
             hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<0>, g1, dim3(256), shm1, s, a);
-          else if (to.rotary_dim == 64)
-            hipLaunchKernelGGL(rerotate_int8_hadamard128_r64_kernel<true>, g1, dim3(256), shm1, s, a);
+          else if (to.rotary_dim == 64) {
+            a.lg = kHadNeoxLayers;
+            const dim3 g2 = one_shot(128, shm1);
+            shm1 = sizeof(float) * had_table_floats((128 - 1) / c.num_kv_heads + 2) + 4 * kHadStage;  // table, four row stages
+            hipLaunchKernelGGL(rerotate_int8_hadamard128_neox64_kernel, g2, dim3(256), shm1, s, a);
+          }
           else
             hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<128>, g1, dim3(256), shm1, s, a);
         } else {
