@@ -1156,8 +1156,9 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_kernel(RerotArg
 // u = c_lo + c_hi is lane-local, the 64-point transforms run five stages in the lane
 // and the top one across the pair, NeoX partners x[e] and x[e + 32] sit at the same
 // index of the two lanes (GPT-J partners share a lane), and 128 c + H64 D needs only
-// the lane's own indices.  The
-// factor 1 / 128 of the two transforms goes into the scale as in the kernel above.
+// the lane's own indices.  The factor 1 / 128 of the two transforms goes into the scale
+// as in the kernel above.  This kernel serves GPT-J pairs with r <= 64; NeoX r = 64 has
+// the staged kernel below.
 __device__ __forceinline__ void fwht64_pair(float (&x)[32], float sgn) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1)
@@ -1172,7 +1173,6 @@ __device__ __forceinline__ void fwht64_pair(float (&x)[32], float sgn) {
   for (int j = 0; j < 32; ++j) x[j] = fmaf(sgn, x[j], dpp_xor1(x[j]));  // lower: x + p, upper: p - x
 }
 
-template <bool NEOX>
 __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_r64_kernel(RerotArgs a) {
   extern __shared__ float s_tab[];
   const int half = a.to.rotary_dim / 2;
@@ -1207,19 +1207,7 @@ __global__ __launch_bounds__(256) void rerotate_int8_hadamard128_r64_kernel(Rero
     fwht64_pair(x, sgn);  // x[e] = x[32 q + e] of H64 (c_lo + c_hi): integers, exact
     // D = (R - I) x
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEOX) {  // lane 0 holds the first of each pair, lane 1 the second
-#pragma unroll
-      for (int e0 = 0; e0 < 32; e0 += 8) {
-#pragma unroll
-        for (int e = e0; e < e0 + 8; ++e) {
-          const float cs = s_cs[tab + e], sl = s_sn[tab + e];
-          const float sn = q ? sl : -sl;
-          const float p = dpp_xor1(x[e]);
-          x[e] = fmaf(p, sn, fmaf(x[e], cs, -x[e]));  // lane 0: x1 (cs - 1) - x2 sn; lane 1: x2 (cs - 1) + x1 sn
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {  // pair (2i, 2i + 1) = lane-local (e, e + 1) at dim 32 q + e; no turn from dim r on
+    {  // pair (2i, 2i + 1) = lane-local (e, e + 1) at dim 32 q + e; no turn from dim r on
 #pragma unroll
       for (int e0 = 0; e0 < 32; e0 += 8) {
 #pragma unroll
@@ -1732,7 +1720,7 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
           a.lg = kHadLayers;
           const dim3 g1 = one_shot(128, shm1);
           if (!to.neox && to.rotary_dim <= 64)
-            hipLaunchKernelGGL(rerotate_int8_hadamard128_r64_kernel<false>, g1, dim3(256), shm1, s, a);
+            hipLaunchKernelGGL(rerotate_int8_hadamard128_r64_kernel, g1, dim3(256), shm1, s, a);
           else if (!to.neox)
             hipLaunchKernelGGL(rerotate_int8_hadamard128_kernel<0>, g1, dim3(256), shm1, s, a);
           else if (to.rotary_dim == 64) {

@@ -73,14 +73,16 @@ def test_keep_scale_rerotate_vs_oracle(env, r, neox):
     assert s1[0, 5, 2] == 0 and np.all(c1[0, 5, 2] == 0)
 
 
-@pytest.mark.parametrize("r,neox,d", [(64, True, 128), (128, True, 128), (64, False, 128), (48, False, 128),
-                                      (16, False, 128), (32, False, 128), (96, False, 128),
-                                      (64, True, 64), (128, True, 256), (64, False, 256)])
-def test_hadamard_rerotate_vs_oracle(env, r, neox, d):
+@pytest.mark.parametrize("r,neox,d,Hkv", [(64, True, 128, 4), (128, True, 128, 4), (64, False, 128, 4),
+                                          (48, False, 128, 4), (16, False, 128, 4), (32, False, 128, 4),
+                                          (96, False, 128, 4), (64, True, 64, 4), (128, True, 256, 4),
+                                          (64, False, 256, 4), (64, True, 128, 3), (64, True, 128, 5)])
+def test_hadamard_rerotate_vs_oracle(env, r, neox, d, Hkv):
     # head_dim 128 runs the two-lanes-per-row kernels (half rows when the turn stays in dims < 64), other
-    # head dims the general one
+    # head dims the general one; with 3 or 5 KV heads a 128-row chunk starts and ends inside a position,
+    # and the second chunk of each layer is partial; 10 layers span two groups of layers
     R, torch, dev = env
-    L, T, Hkv = 2, 48, 4
+    L, T = (10 if Hkv == 5 else 2), 48
     ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144, neox=neox)
     cb = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.625, orig_max_pos=262144, neox=neox)
     pos0 = 300007
