@@ -131,7 +131,7 @@ struct ElemTraits<bf16_t> {
 
 constexpr int kMaxTps = 256;  // tiles per split of a split plan
 constexpr int kMaxDirectTiles = 512;  // tiles of a direct-plan workgroup (block-table entries staged in LDS)
-constexpr int kDirectWaves = 12;      // waves of a direct-plan workgroup (16-bit caches: 3 per SIMD)
+constexpr int kDirectWaves = 8;       // waves of a direct-plan workgroup, 16-bit caches (2 per SIMD; windowed batch-256 and ring layer: 4: +1 % / +7 %, 6: -3 %, 8: -3 %, 16: +40 % against 12)
 constexpr int kDirectWavesF32 = 8;    // fp32 caches run at 2 waves per SIMD
 
 // Merge the split partials of one (sequence, KV head) for its n_rep query heads:
