@@ -433,6 +433,20 @@ def main():
         rows["ceiling_copy_16GiB"] = {"ms": round(ms, 3), "GBps": round(2 * h * 4 / ms / 1e6, 1)}
         del x
         torch.cuda.empty_cache()
+        # the matrix-core rate a library bf16 GEMM reaches on this chip and clock (torch -> hipBLASLt),
+        # the practical ceiling next to the vendor peak for the prefill's bf16 MFMA work
+        log("mfma ceiling: bf16 GEMM 8192 x 8192 x 8192")
+        n = 8192
+        ga = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gc = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        ms = timed(torch, lambda: torch.matmul(ga, gb, out=gc), 40, warmup=40)
+        rows["ceiling_gemm_bf16_8192"] = {"ms": round(ms, 4), "TFLOPs": round(2 * n ** 3 / ms / 1e9, 1)}
+        del ga, gb, gc
+        torch.cuda.empty_cache()
+        pf = rows.get("prefill_t8192_h64_w4096")
+        if pf:
+            pf["frac_of_gemm_ceiling"] = round(pf["TFLOPs"] / rows["ceiling_gemm_bf16_8192"]["TFLOPs"], 3)
 
     line = {
         "metric": METRIC,
