@@ -1316,17 +1316,6 @@ __device__ __forceinline__ uint32_t bfly_halves(uint32_t x, uint32_t k) {
   return r;
 }
 
-// Row staging for the kernel below: each wave owns 32 rows of the workgroup's 128 and walks the
-// workgroup's layers; a layer's rows come in by direct global -> LDS loads in which every 8 lanes
-// take one whole 128-byte row (full cache lines, streamed), and the results leave the same way.
-// Rows sit 144 bytes apart in the stage (9 slots of 16 bytes, the ninth unused), so that 8
-// consecutive rows start in 8 distinct 16-byte bank groups and each lane reads its half row at
-// fixed offsets from one address (the two lanes of a row read chunks 2 slots apart, which
-// overlaps in banks two ways within 16 lanes).  Reading the rows in place (32 bytes of a row per
-// lane pair and instruction) instead ran at the rate of the same pass with no arithmetic at all.
-// Everything that depends on the lane is derived again in each layer from an opaque copy of the
-// lane index: held across the layer loop, the turn table and the addresses took 150-190
-// registers (3 waves per SIMD).
 // o[e] += x'[e] * b[e] for 8 values, x' = x of the partner lane l ^ 1, as v_fmac_f32 with a DPP
 // lane swap on its first operand (the compiler keeps the swap as a separate move).  The leading
 // s_nop 1 gives the two wait states a DPP read needs after a vector write of its operand; inside
@@ -1346,6 +1335,17 @@ __device__ __forceinline__ void fmac_partner8(float (&o)[8], const float *x, con
             "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]));
 }
 
+// Row staging for the kernel below: each wave owns 32 rows of the workgroup's 128 and walks the
+// workgroup's layers; a layer's rows come in by direct global -> LDS loads in which every 8 lanes
+// take one whole 128-byte row (full cache lines, streamed), and the results leave the same way.
+// Rows sit 144 bytes apart in the stage (9 slots of 16 bytes, the ninth unused), so that 8
+// consecutive rows start in 8 distinct 16-byte bank groups and each lane reads its half row at
+// fixed offsets from one address (the two lanes of a row read chunks 2 slots apart, which
+// overlaps in banks two ways within 16 lanes).  Reading the rows in place (32 bytes of a row per
+// lane pair and instruction) instead ran at the rate of the same pass with no arithmetic at all.
+// Everything that depends on the lane is derived again in each layer from an opaque copy of the
+// lane index: held across the layer loop, the turn table and the addresses took 150-190
+// registers (3 waves per SIMD).
 constexpr int kHadStage = 32 * 9 * 16;  // bytes per wave
 
 __device__ __forceinline__ void had_load_rows(const int8_t *lk, uint8_t *stage, int ln, int nrows, int wrow0) {
