@@ -1454,7 +1454,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void r
       for (int e = e0; e < e0 + 4; ++e) {
         y[e] = fmaf(code_at(w, e), 64.f, x[e]);
         y[32 + e] = fmaf(code_at(w, 32 + e), 64.f, x[e]);
-        amax = fmaxf(amax, fmaxf(fabsf(y[e]), fabsf(y[32 + e])));
+        amax = fmaxf(fmaxf(amax, fabsf(y[e])), fabsf(y[32 + e]));  // one v_max3 per pair
       }
       __builtin_amdgcn_sched_barrier(0);
     }
