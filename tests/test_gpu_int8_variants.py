@@ -104,6 +104,36 @@ def test_hadamard_rerotate_vs_oracle(env, r, neox, d, Hkv):
         assert_int8_codes_valid(c1[layer].reshape(-1, d), wc, quot, EPS_TURN_HADAMARD)
 
 
+@pytest.mark.parametrize("neox,r", [(True, 64), (False, 64), (True, 128)])
+def test_hadamard_rerotate_identity(env, neox, r):
+    # A -> A over Hadamard rows as the quantiser leaves them (a row's largest code +-127): the turn is
+    # the identity, so the codes come back bit for bit and the scale within one float32 rounding;
+    # the oracle's turn is the identity too
+    R, torch, dev = env
+    L, T, Hkv, d = 2, 40, 4, 128
+    ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.375, orig_max_pos=262144, neox=neox)
+    oa = oracle_cfg(ca)
+    pos0 = 250001
+    raw = synth.normal((L, T, Hkv, d), 1350 + r + neox)
+    angles = np.outer(np.arange(pos0, pos0 + T), O.inv_freq(oa))[:, None, :]
+    key = np.stack([O.rotate_by_angle(raw[l], angles, r, neox, O.mscale(oa)) for l in range(L)])
+    c0, s0 = O.quant_int8_hadamard_rows(key)
+    s0 = np.asarray(s0, dtype=np.float32)
+    codes, scale = torch.from_numpy(c0).to(dev), torch.from_numpy(s0).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    desc = R.kv_cache(R.CONTIG, R.I8, Hkv, d, codes, capacity=T, pos0=pos0, k_scale=scale, err_word=err,
+                      k_int8_mode=R.I8_HADAMARD)
+    R.rerotate(ca, ca, desc, L)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(codes.cpu().numpy(), c0)
+    np.testing.assert_allclose(scale.cpu().numpy(), s0, rtol=2.0 ** -23, atol=0)
+    pos = np.repeat(np.arange(pos0, pos0 + T), Hkv)
+    wc, ws_ = O.rerotate_int8_hadamard_rows(c0[0].reshape(-1, d), s0[0].reshape(-1), pos, oa, oa)
+    assert np.array_equal(wc, c0[0].reshape(-1, d))
+    np.testing.assert_allclose(ws_, s0[0].reshape(-1), rtol=1e-12)
+
+
 def test_hadamard_rerotate_bounds_from_append(env):
     # raw keys written at A by apply_append into Hadamard-rotated int8 rows, turned to B, compared with
     # the fp64 key at B in the H domain; the key written directly at B, as the oracle's Hadamard
