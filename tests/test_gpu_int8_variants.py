@@ -87,6 +87,8 @@ def test_hadamard_rerotate_vs_oracle(env, r, neox, d, Hkv):
     cb = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.625, orig_max_pos=262144, neox=neox)
     pos0 = 300007
     c0, s0 = _seeded_rows(torch, dev, (L, T, Hkv, d), 1300 + r + d, r, 127)
+    s0[1, 7, Hkv - 1] = 0.0  # an all-zero row stays all zero with scale 0
+    c0[1, 7, Hkv - 1] = 0
     codes = torch.from_numpy(c0).to(dev)
     scale = torch.from_numpy(s0).to(dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -102,6 +104,7 @@ def test_hadamard_rerotate_vs_oracle(env, r, neox, d, Hkv):
         np.testing.assert_allclose(s1[layer].reshape(-1), ws_, rtol=1e-5)
         quot = int8_turn_quotients("i8_hadamard", cl, sl, pos, oracle_cfg(ca), oracle_cfg(cb), ws_)
         assert_int8_codes_valid(c1[layer].reshape(-1, d), wc, quot, EPS_TURN_HADAMARD)
+    assert s1[1, 7, Hkv - 1] == 0 and np.all(c1[1, 7, Hkv - 1] == 0)
 
 
 @pytest.mark.parametrize("neox,r", [(True, 64), (False, 64), (True, 128)])
