@@ -58,6 +58,31 @@ def assert_bf16_rounded(gpu: np.ndarray, ref: np.ndarray, rel_fp32=1e-6):
         f"max excess {float(np.max(excess)):.3e} over half a bf16 ulp, max abs err {float(np.max(np.abs(g - r))):.3e}")
 
 
+def assert_f16_rounded(gpu: np.ndarray, ref: np.ndarray, rel_fp32=1e-6):
+    """gpu is the exact value ref, computed in fp32 and rounded once to IEEE half (round to
+    nearest): |gpu - ref| <= ulp / 2 + e, with ulp = 2^(max(floor(log2 |g|), -14) - 10) (11
+    significant bits, subnormals below 2^-14 on the fixed 2^-24 grid), and e as for bf16."""
+    g = gpu.reshape(-1, gpu.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    e = rel_fp32 * np.max(np.abs(r), axis=1, keepdims=True)
+    _, ex = np.frexp(g)  # floor(log2 |g|) = ex - 1
+    half = np.ldexp(1.0, np.maximum(ex - 1, -14) - 11)
+    excess = np.abs(g - r) - (half + e)
+    assert float(np.max(excess)) <= 0.0, (
+        f"max excess {float(np.max(excess)):.3e} over half an fp16 ulp, max abs err {float(np.max(np.abs(g - r))):.3e}")
+
+
+def assert_rounded_once(gpu: np.ndarray, ref: np.ndarray, dtype_name: str, rel_fp32=1e-6):
+    """One rounding of the exact value to the stored dtype ("f32", "bf16", "f16"); fp32 stores the
+    fp32 arithmetic itself, within rel_fp32 of the row's largest |ref|."""
+    if dtype_name == "bf16":
+        assert_bf16_rounded(gpu, ref, rel_fp32)
+    elif dtype_name == "f16":
+        assert_f16_rounded(gpu, ref, rel_fp32)
+    else:
+        assert rowwise(gpu, ref) <= rel_fp32, f"fp32 row error {rowwise(gpu, ref):.3e}"
+
+
 def assert_bf16_close(gpu: np.ndarray, ref: np.ndarray, atol=2e-2, rtol=1e-2):
     err = np.abs(gpu - ref) - (atol + rtol * np.abs(ref))
     assert float(np.max(err)) <= 0.0, f"max excess {float(np.max(err)):.3e}, max abs err {float(np.max(np.abs(gpu-ref))):.3e}"

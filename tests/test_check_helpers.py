@@ -5,8 +5,8 @@ import pytest
 import torch
 
 from oracle import ropekv_oracle as O
-from tests.gpu_util import (assert_bf16_attention, assert_bf16_close, assert_bf16_rounded, assert_fp8_codes_valid,
-                            assert_int8_codes_valid, decode_e4m3, decode_int8, excess, oracle_written)
+from tests.gpu_util import (assert_bf16_attention, assert_bf16_close, assert_bf16_rounded, assert_f16_rounded, assert_fp8_codes_valid,
+                            assert_int8_codes_valid, assert_rounded_once, decode_e4m3, decode_int8, excess, oracle_written)
 
 
 def _bf16(x):
@@ -38,6 +38,32 @@ def test_bf16_rounded_accepts_round_to_nearest_and_rejects_one_step():
             bad[i, j] = _bf16_step(got[i, j], away)
             with pytest.raises(AssertionError):
                 assert_bf16_rounded(bad, ref)
+
+
+def test_f16_rounded_accepts_round_to_nearest_and_rejects_one_step():
+    rng = np.random.default_rng(8)
+    # magnitudes from the subnormal range (below 2^-14) to 2^11
+    ref = rng.standard_normal((6, 128)) * np.exp(rng.uniform(-12, 7, (6, 1)))
+    ref[0, :4] = [3e-8, -2e-6, 5.9e-5, 0.0]
+    got = ref.astype(np.float16).astype(np.float64)
+    assert_f16_rounded(got, ref, rel_fp32=0.0)
+    assert_f16_rounded((ref * (1 + 3e-7)).astype(np.float32).astype(np.float16).astype(np.float64), ref)
+    bits = got.astype(np.float16).view(np.int16)
+    ulp = np.abs((bits + 1).view(np.float16).astype(np.float64) - got)
+    picks = np.argwhere((np.abs(got - ref) < 0.4 * ulp) & (np.abs(got) > 0))
+    picks = np.concatenate([picks[:5], [[0, 1]]])  # one subnormal among them
+    for i, j in picks:
+        for step in (1, -1):
+            bad = got.copy()
+            bad[i, j] = (bits[i, j:j + 1] + step).view(np.float16).astype(np.float64)[0]
+            with pytest.raises(AssertionError):
+                assert_f16_rounded(bad, ref, rel_fp32=0.0)
+    # fp32 results: the dtype switch holds them to rel_fp32 of the row's largest value
+    assert_rounded_once(ref.astype(np.float32).astype(np.float64), ref, "f32")
+    bad = ref.copy()
+    bad[2, 5] += 2e-6 * np.max(np.abs(ref[2]))
+    with pytest.raises(AssertionError):
+        assert_rounded_once(bad, ref, "f32")
 
 
 def test_bf16_close_bound_and_signed_excess():

@@ -15,7 +15,7 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import (bf16_attention_ref, bf16_round, EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, attend_set,
+from tests.gpu_util import (bf16_attention_ref, bf16_round, EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, assert_rounded_once, attend_set,
                             decode_int8, excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
                             oracle_written, plant_queries_, rowwise, to_np64, torch_dev)
 
@@ -205,6 +205,98 @@ def test_ring_window_of_one(env, S, dtype_name):
     # the degenerate window W = 1: every query sees the sinks and itself; each token overwrites the
     # single ring slot, chunks longer than the ring keep only their last token
     _ring_end_to_end(env, True, dtype_name, [5, 1, 1, 3, 1, 2], S=S, W=1)
+
+
+# ------------------------------------------------------------------ rope + append over head shapes
+
+APPEND_SHAPES = [
+    # layout, dtype, d, r, neox, Hq, Hkv, unaligned activations, YaRN factor
+    ("ring", "bf16", 512, 512, True, 4, 2, False, 1.0),     # the largest head (16-byte unit path)
+    ("contig", "f32", 512, 128, False, 0, 3, False, 1.0),   # keys only, no q, CONTIG rows from pos0 1000
+    ("ring", "f16", 256, 64, True, 6, 2, False, 4.0),       # partial rotary, YaRN table (mscale != 1)
+    ("ring", "bf16", 128, 36, True, 4, 1, False, 1.0),      # r / 2 = 18: not whole units, element path
+    ("ring", "f32", 34, 18, False, 2, 2, False, 1.0),       # d not a whole number of units
+    ("ring", "f16", 2, 2, True, 1, 1, False, 1.0),          # the smallest head
+    ("contig", "bf16", 6, 4, False, 3, 1, False, 1.0),
+    ("ring", "bf16", 128, 128, True, 8, 2, True, 1.0),      # unit-shaped rows at 2-byte offsets: element path
+    ("ring", "f32", 512, 2, True, 2, 1, False, 1.0),        # one rotary pair in the largest head
+]
+
+
+@pytest.mark.parametrize("layout,dtype_name,d,r,neox,Hq,Hkv,unaligned,yarn", APPEND_SHAPES)
+def test_append_head_shapes(env, layout, dtype_name, d, r, neox, Hq, Hkv, unaligned, yarn):
+    # every head shape the append accepts runs one of two paths (16-byte units when the rotary
+    # halves, the tail and the addresses allow, else element by element); both against the oracle:
+    # q and k rotated in place and the cached k one rounding of the exact rotation, the tail and v
+    # bit for bit, slots past the appended run untouched
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype_name]
+    act = {"f32": R.F32, "bf16": R.BF16, "f16": R.F16}[dtype_name]
+    n = 37
+    pos0 = 1000 if layout == "contig" else 0
+    kw = dict(yarn_factor=yarn, orig_max_pos=16) if yarn > 1.0 else {}
+    cfg = R.rope_cfg(d, r, rope_theta=1e4, neox=neox, **kw)
+    table = _table(R, torch, dev, cfg, pos0 + n)
+    otab = O.build_table(oracle_cfg(cfg), pos0 + n)
+    positions = np.arange(pos0, pos0 + n)
+
+    def upload(shape, seed):
+        host = torch.from_numpy(synth.normal(shape, seed)).to(dtype)
+        if not unaligned:
+            return host.to(dev)
+        buf = torch.empty(host.numel() + 1, dtype=dtype, device=dev)  # one element in: off 16-byte alignment
+        view = buf[1:].view(shape)
+        view.copy_(host.to(dev))
+        return view
+
+    q = upload((n, Hq, d), 301) if Hq else None
+    k = upload((n, Hkv, d), 302)
+    v = upload((n, Hkv, d), 303)
+    q_raw = to_np64(q) if Hq else None
+    k_raw, v_raw = to_np64(k), to_np64(v)
+    pos = torch.from_numpy(positions.astype(np.int32)).to(dev)
+    if layout == "ring":
+        S = 2
+        cache = DevRing(R, torch, dev, dtype, 1, Hkv, d, S, n + 5)
+        desc, err = cache.desc, cache.err
+        seq = torch.zeros(n, dtype=torch.int32, device=dev)
+    else:
+        kc = torch.zeros(n, Hkv, d, dtype=dtype, device=dev)
+        vc = torch.zeros_like(kc) if Hq else None  # the keys-only case has no value cache
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        desc = R.kv_cache(R.CONTIG, act, Hkv, d, kc, vc, capacity=n, pos0=pos0, err_word=err)
+        seq = None
+        if vc is None:
+            v, v_raw = None, None
+    R.apply_append(cfg, table, pos0 + n, q, Hq, k, v, act, n, pos, seq, desc)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    k_want = O.rope_apply(k_raw, positions, otab, r, neox)
+    got_k = to_np64(k)
+    assert_rounded_once(got_k, k_want, dtype_name)
+    assert np.array_equal(got_k[..., r:], k_raw[..., r:])
+    if Hq:
+        got_q = to_np64(q)
+        assert_rounded_once(got_q, O.rope_apply(q_raw, positions, otab, r, neox), dtype_name)
+        assert np.array_equal(got_q[..., r:], q_raw[..., r:])
+    if layout == "ring":
+        # an empty ring takes a run shorter than W at slots p (sinks p < S, then S + p - S)
+        oring = O.RingSeq(sinks=S, window=n + 5)
+        oring.append(n)
+        assert (cache.head.item(), cache.count.item(), cache.seq_len.item()) == (oring.head, oring.count,
+                                                                                  oring.seq_len)
+        assert sorted(oring.slot_pos.items()) == [(s, s) for s in range(n)]  # slot -> position
+        kc_rows = to_np64(cache.k[0].permute(1, 0, 2))  # [C, Hkv, d]
+        vc_rows = to_np64(cache.v[0].permute(1, 0, 2))
+    else:
+        kc_rows = to_np64(kc)
+        vc_rows = to_np64(vc) if vc is not None else None
+    assert_rounded_once(kc_rows[:n], k_want, dtype_name)
+    assert np.array_equal(kc_rows[:n], got_k)  # the cached key is the in-place rotated key
+    assert not np.any(kc_rows[n:])
+    if vc_rows is not None:
+        assert np.array_equal(vc_rows[:n], v_raw)
+        assert not np.any(vc_rows[n:])
 
 
 # ------------------------------------------------------------------ paged append + freeing + decode
