@@ -22,7 +22,9 @@ constexpr int kI8Threads = 256;  // int8 lane kernel: threads per workgroup
 constexpr int kI8Layers = 2;     // int8 lane kernel: layers per workgroup (1: 16.4 ms, 2: 14.4, 4: 15.3 on the
                                  // 64-layer int8 switch; the float kernel is fastest at 1)
 constexpr int kHadLayers = 4;    // Hadamard head_dim-128 kernels: layers per workgroup (r 64: 1: 16.2 ms, 2: 15.7, 4: 15.2, 8: 15.1)
-constexpr int kHadNeoxLayers = 8;  // the staged NeoX r = 64 Hadamard kernel (64-layer switch: 2: 14.2 ms, 4: 13.6, 8: 13.5)
+// layers per workgroup of the staged NeoX r = 64 Hadamard kernel (64-layer switch: 2 layers ran
+// 12.6 ms on one box and 14.2 on another, against 13.0 and 13.5 for 8; 4: 13.6)
+constexpr int kHadNeoxLayers = 8;
 
 struct RerotArgs {
   RopeParams from, to;
@@ -1336,9 +1338,13 @@ __device__ __forceinline__ void fmac_partner8(float (&o)[8], const float *x, con
 }
 
 // Row staging for the kernel below: each wave owns 32 rows of the workgroup's 128 and walks the
-// workgroup's layers; a layer's rows come in by direct global -> LDS loads in which every 8 lanes
-// take one whole 128-byte row (full cache lines, streamed), and the results leave the same way.
-// Rows sit 144 bytes apart in the stage (9 slots of 16 bytes, the ninth unused), so that 8
+// workgroup's layers; every 8 lanes move one whole 128-byte row (full cache lines, streamed) in
+// and out.  The first layer's rows come by direct global -> LDS loads; each later layer's rows
+// are loaded into registers two layers ahead and written into the stage once the layer before
+// has left it.  The pass runs at the rate of its memory traffic, not of its arithmetic (on the
+// 64-layer switch: no arithmetic 13.1 ms, arithmetic with no loads or stores 8.7 ms, the whole
+// pass 13.0-13.5 ms); the two-layer lead takes about 2 % off, one layer or a second LDS stage
+// about 1 %.  Rows sit 144 bytes apart in the stage (9 slots of 16 bytes, the ninth unused), so that 8
 // consecutive rows start in 8 distinct 16-byte bank groups and each lane reads its half row at
 // fixed offsets from one address (the two lanes of a row read chunks 2 slots apart, which
 // overlaps in banks two ways within 16 lanes).  Reading the rows in place (32 bytes of a row per
@@ -1356,7 +1362,7 @@ __device__ __forceinline__ void had_load_rows(const int8_t *lk, uint8_t *stage, 
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void rerotate_int8_hadamard128_neox64_kernel(RerotArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void rerotate_int8_hadamard128_neox64_kernel(RerotArgs a) {
   extern __shared__ float s_tab[];  // [3][np][32] table, then one row stage per wave
   const int half = 32;
   const double dwt = own_dw(a);
@@ -1372,6 +1378,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void r
   hadamard_pair_table(a, c.pa, c.np, s_tab, dwt);
   const float *s_cm1 = s_tab, *s_sn = s_tab + had_off_sn(c.np), *s_nsn = s_tab + had_off_nsn(c.np);
   const uint32_t kbf = 0xffff0001u;
+  // entering layer l: sco_a is its row scale and sco_b layer l + 1's, nxA holds layer l + 1's
+  // rows and nxB takes layer l + 2's (rows past the layer's end lie beyond the resource's
+  // extent and load zeros; their results are never stored)
+  const int prow = min(wrow0 + (int)((threadIdx.x & 63) >> 1), c.nrows - 1);
+  float sco_a = a.scale[c.row0 + prow], sco_b = 0.f;
+  b128_t nxA[4], nxB[4];
+  auto load_rows = [&](b128_t (&dst)[4], int layer) {
+    const __amdgpu_buffer_rsrc_t rn = span_rsrc((int8_t *)a.k + (c.row0 + (long)layer * layer_rows) * 128, (long)c.nrows * 128);
+    const int ln = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rn, (wrow0 + 8 * j + (ln >> 3)) * 128 + 16 * (ln & 7), 0, kStream);
+  };
+  if (c.nl > 1) {
+    load_rows(nxA, 1);
+    sco_b = a.scale[c.row0 + layer_rows + prow];
+  }
   for (int l = 0; l < c.nl; ++l) {
     int lane = threadIdx.x & 63;
     __asm__ volatile("" : "+v"(lane));
@@ -1385,8 +1408,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void r
     const int tab = ((c.r0 + (live ? row : 0)) / a.Hkv - c.pa) * 36;
     const float *ta = s_cm1 + tab, *tb = (q ? s_nsn : s_sn) + tab;
     uint8_t *mine = stage + 16 * (9 * rr + 2 * q);
-    const float sco = a.scale[lrow + (live ? row : 0)];
-    wait_vmcnt<0>();  // this wave's rows of layer l are in its stage
+    const float sco = sco_a;
+    sco_a = sco_b;
+    if (l == 0) wait_vmcnt<0>();  // layer 0's rows came by direct loads
+    if (l + 2 < c.nl) {
+      load_rows(nxB, l + 2);
+      sco_b = a.scale[lrow + 2 * layer_rows + (live ? row : 0)];
+    }
     uint32_t w[16];  // words 0..7: codes 32 q + (0..31); 8..15: codes 64 + 32 q + (0..31)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1483,7 +1511,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void r
     if (live && q == 0) a.scale[lrow + row] = inv > 0.f ? sco * amax * (1.0f / (127.0f * 64.0f)) : 0.f;
     if (l + 1 < c.nl) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stage has been read out
-      had_load_rows((const int8_t *)a.k + (lrow + layer_rows) * 128, stage, lane, c.nrows, wrow0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(uint4 *)(stage + 16 * (9 * (8 * j + (lane >> 3)) + (lane & 7))) = make_uint4(nxA[j][0], nxA[j][1], nxA[j][2], nxA[j][3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nxA[j] = nxB[j];
     }
   }
 }
