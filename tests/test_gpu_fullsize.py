@@ -43,10 +43,11 @@ def _split_keys(R, wl, max_tiles):
     return 16 * ((max_tiles + splits - 1) // splits)
 
 
-def _paged_full_needles(R, torch, wl, seqs, seed):
+def _paged_full_needles(R, torch, wl, seqs, seed, sink_logits=None):
     """Full-attention paged decode with needles, in the workload's own launch: needles at the first
     and last keys, 16-key block edges, split edges and mid-sequence; negative controls drop key 0,
-    the last key, the block after the first split edge, or shift the set by 64."""
+    the last key, the block after the first split edge, or shift the set by 64.  With sink_logits
+    (device fp32 [Hq]) the decode takes them, and the negative control is the oracle without them."""
     n, d, Hkv = wl.ctx, wl.d, wl.Hkv
     sp = _split_keys(R, wl, wl.max_blocks)
     pos = sorted({0, 15, 16, sp - 1, sp, n // 2 - 1, n // 2, n - sp - 1, n - sp, n - 2, n - 1})
@@ -70,10 +71,14 @@ def _paged_full_needles(R, torch, wl, seqs, seed):
             else:
                 buf[blk, :, slot] = torch.from_numpy(rows).to(buf.device, buf.dtype)
         plant_queries_(torch, wl.q[b], u)
-    wl.decode()
+    if sink_logits is None:
+        wl.decode()
+    else:
+        R.decode_attn(wl.q, wl.B, wl.Hq, wl.desc, 0.0, wl.out, wl.ws, wl.ws_bytes, sink_logits=sink_logits)
     torch.cuda.synchronize()
     assert wl.err.item() == 0
     out, q = to_np64(wl.out), to_np64(wl.q)
+    sk = None if sink_logits is None else sink_logits.cpu().numpy().astype(np.float64)
     for b in seqs:
         if wl.kv8:
             dequant = O.dequant_int8_rows if wl.kv8 == "i8" else O.dequant_fp8_rows
@@ -81,8 +86,12 @@ def _paged_full_needles(R, torch, wl, seqs, seed):
             K, V = dequant(kc, ks), dequant(vc, vs)
         else:
             K, V = wl.kv_of(b)
-        ref = bf16_attention_ref(out[b], O.decode_attention, q[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv)
+        ref = bf16_attention_ref(out[b], O.decode_attention, q[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv,
+                                 sink_logits=sk)
         assert np.max(np.abs(ref)) > 1.0  # the needles carry the output
+        if sk is not None:
+            assert excess(O.decode_attention(q[b], lambda j: K[j], lambda j: V[j], n, 0, 0, Hkv), ref) > 0
+            continue
         every = np.arange(n)
         wrong = [every[1:], every[:-1], np.r_[every[:sp], every[sp + 16:]], every[:-64]]
         for idx in wrong:
@@ -119,6 +128,67 @@ def test_paged_decode_b64_ctx32768(env):
                            wl.ctx, 0, 0, wl.Hkv)
     # needles: the same layer decoded again with planted keys and queries
     _paged_full_needles(R, torch, wl, (0, 37, 63), 2100)
+
+
+def test_paged_decode_b64_ctx32768_learned_sinks(env):
+    # the learned-sink decode row's launch: the config-2 decode with one sink logit per query head,
+    # after a step; needles score about 16, and the sink logits run from 14 (a few per cent of the
+    # needles' weight) to 22 (most of it), so the oracle without them fails the same tolerance
+    R, torch, dev, WL = env
+    wl = WL.PagedDecode(R, torch, dev)
+    wl.step()
+    torch.cuda.synchronize()
+    sinks = torch.linspace(14.0, 22.0, wl.Hq, device=dev)
+    _paged_full_needles(R, torch, wl, (0, 37, 63), 2200, sink_logits=sinks)
+
+
+def test_decode_step_graph_b64_ctx32768(env):
+    # the headline step as bench.py times it: seq_len reset, rope + append and the split-K decode
+    # captured in a HIP graph; every replay (eager work and synchronisations between them) gives the
+    # eager step's outputs and rotated q bit for bit, and the eager step matches the oracle
+    R, torch, dev, WL = env
+    wl = WL.PagedDecode(R, torch, dev)
+    q0, k0, v0 = wl.q.clone(), wl.k_new.clone(), wl.v_new.clone()
+
+    def step():
+        wl.q.copy_(q0)
+        wl.k_new.copy_(k0)
+        wl.v_new.copy_(v0)
+        wl.step()
+
+    step()
+    torch.cuda.synchronize()
+    assert wl.err.item() == 0
+    eager_out, eager_q = wl.out.clone(), wl.q.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        wl.out.fill_(float("nan"))
+        torch.randn(1 << 20, device=dev).mul_(2.0).sum().item()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert wl.err.item() == 0
+        assert torch.equal(wl.out, eager_out), f"replay {rep} differs from the eager step"
+        assert torch.equal(wl.q, eager_q)
+    p = wl.ctx - 1
+    otab = O.build_table(oracle_cfg(wl.cfg), wl.ctx)
+    b = 11
+    want_q = O.rope_apply(to_np64(q0)[b:b + 1], [p], otab, wl.d, True)[0]
+    want_k = O.rope_apply(to_np64(k0)[b:b + 1], [p], otab, wl.d, True)[0]
+    assert_bf16_rounded(to_np64(eager_q)[b], want_q)
+    k, v = wl.kv_of(b)
+    assert_bf16_rounded(k[p], want_k)
+    k[p], v[p] = bf16_round(want_k), to_np64(v0)[b]
+    bf16_attention_ref(to_np64(eager_out)[b], O.decode_attention, bf16_round(want_q), lambda j: k[j], lambda j: v[j],
+                       wl.ctx, 0, 0, wl.Hkv)
 
 
 def test_paged_decode_b32_ctx131072(env):
@@ -207,6 +277,33 @@ def test_ring_decode_128k(env):
         every = np.arange(C)
         for idx in (every[r.S:], np.r_[every[:sp], every[sp + 16:]], every[:-1]):
             assert excess(attend_set(q[b], K, V, idx, r.Hkv), ref) > 0
+
+
+def test_shift_keys_ring_w4096_b32(env):
+    # the local-shift row: one ring layer (32 sequences, 8 KV heads, S 4 + W 4096, full ring, head at
+    # a seeded offset) moved back by one position; sampled rows against the oracle's shift (one bf16
+    # rounding), sink rows and all values bitwise unchanged
+    R, torch, dev, WL = env
+    r = WL.RingDecode(R, torch, dev)
+    cfg = R.rope_cfg(r.d, r.d, rope_theta=5e5)
+    rng = synth.rng(3300)
+    n = 40
+    bs = rng.integers(0, r.B, n)
+    hs = rng.integers(0, r.Hkv, n)
+    slots = rng.integers(0, r.C, n)
+    slots[:6] = [0, r.S - 1, r.S, r.S + 1, r.C - 2, r.C - 1]  # sinks, both ends of the ring
+    idx = (torch.from_numpy(bs).to(dev), torch.from_numpy(hs).to(dev), torch.from_numpy(slots).to(dev))
+    before = to_np64(r.k[idx])
+    v0 = r.v.clone()
+    R.shift_keys(cfg, r.desc, -1)
+    torch.cuda.synchronize()
+    after = to_np64(r.k[idx])
+    assert torch.equal(r.v, v0)
+    sink = slots < r.S
+    assert np.array_equal(after[sink], before[sink])
+    want = O.shift_keys(before[~sink], -1, oracle_cfg(cfg))
+    assert_bf16_rounded(after[~sink], want)
+    assert not np.array_equal(after[~sink], before[~sink])
 
 
 def test_windowed_paged_decode_b256(env):
