@@ -406,6 +406,41 @@ def test_prefill_t8192_sampled_rows(env):
     assert checked >= 16
 
 
+def test_rope_append_prefill_t8192(env):
+    # the prefill chunk's rope + append row: 8192 tokens from position 0 into an empty sink(4) +
+    # window(4096) ring; sampled tokens' q and k rotated in place (one bf16 rounding), the ring
+    # state, and sampled slots holding the oracle's rotated key and the raw value of the position
+    # the ring rule puts there (the sinks, then the chunk's last 4096 tokens from slot S on)
+    R, torch, dev, WL = env
+    pf = WL.Prefill(R, torch, dev)
+    S, W, T = pf.S, pf.W, pf.T
+    ring = O.RingSeq(sinks=S, window=W)
+    ring.append(T)
+    slots = sorted({0, 1, S - 1, S, S + 1, S + 63, S + 64, S + W // 2, S + W - 2, S + W - 1}
+                   | {int(x) for x in synth.rng(6100).integers(0, S + W, 20)})
+    toks = sorted({0, 1, S - 1, S, 100, 4095, 4096, 4097, 8000, T - 2, T - 1} | {ring.slot_pos[sl] for sl in slots})
+    ti = torch.tensor(toks, device=dev)
+    q_raw, k_raw, v_raw = to_np64(pf.q[ti]), to_np64(pf.k[ti]), to_np64(pf.v[ti])
+    pf.append()
+    torch.cuda.synchronize()
+    st = pf.int_state.cpu().tolist()
+    assert st[3] == 0
+    assert (st[0], st[1], st[2]) == (ring.head, ring.count, ring.seq_len)
+    otab = O.build_table(oracle_cfg(pf.cfg), T)
+    want_q = O.rope_apply(q_raw, toks, otab, pf.d, True)
+    want_k = O.rope_apply(k_raw, toks, otab, pf.d, True)
+    assert_bf16_rounded(to_np64(pf.q[ti]), want_q)
+    assert_bf16_rounded(to_np64(pf.k[ti]), want_k)
+    row = {t: i for i, t in enumerate(toks)}
+    si = torch.tensor(slots, device=dev)
+    kc = to_np64(pf.kc[0][:, si]).transpose(1, 0, 2)  # [slot, Hkv, d]
+    vc = to_np64(pf.vc[0][:, si]).transpose(1, 0, 2)
+    for i, sl in enumerate(slots):
+        t = ring.slot_pos[sl]
+        assert_bf16_rounded(kc[i], want_k[row[t]])
+        assert np.array_equal(vc[i], v_raw[row[t]])
+
+
 @pytest.mark.parametrize("kind", ["f16", "i8", "i8_keep", "i8_hadamard"])
 def test_rerotate_l64_t524288_sampled_rows(env, kind):
     R, torch, dev, WL = env
