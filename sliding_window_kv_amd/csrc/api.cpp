@@ -330,8 +330,8 @@ int ropekv_rerotate(const ropekv_rope_cfg *from, const ropekv_rope_cfg *to, cons
   if (cache->kv_dtype == ROPEKV_I8) {
     const int d = cache->head_dim, r = to->rotary_dim;
     const int lpr = d / 16;
-    if (d % 16 || lpr > 64 || (lpr & (lpr - 1)))
-      return fail(ROPEKV_ERANGE, "int8 rerotate needs head_dim = 16 * 2^k <= 1024");
+    if (d % 16 || (lpr & (lpr - 1)))
+      return fail(ROPEKV_ERANGE, "int8 rerotate needs head_dim = 16 * 2^k (16 to 512)");
     if (to->neox ? (r % 32) : (r % 16))
       return fail(ROPEKV_ERANGE, "int8 rerotate needs rotary_dim %% %d == 0", to->neox ? 32 : 16);
     if ((cache->k_int8_mode & ROPEKV_I8_HADAMARD) && to->neox && (r < 64 || (r & (r - 1))))

@@ -279,6 +279,21 @@ def int8_turn_quotients(kind, codes, scale, positions, cfg_from, cfg_to, new_sca
     return O.row_quotients(y, s)
 
 
+def seeded_int8_rows(shape, seed, rot_dims, rot_amp):
+    """int8 rows: rotary dims uniform in [-rot_amp, rot_amp], the rest in [-127, 127]; scales U(0.01, 0.03).
+    Odd rows use the full range in the rotary dims too (those rows tend to overflow a turn)."""
+    from sliding_window_kv_amd import synth
+
+    rng = synth.rng(seed)
+    codes = rng.integers(-127, 128, size=shape).astype(np.int8)
+    small = rng.integers(-rot_amp, rot_amp + 1, size=shape[:-1] + (rot_dims,)).astype(np.int8)
+    rows = codes.reshape(-1, shape[-1])
+    srows = small.reshape(-1, rot_dims)
+    rows[0::2, :rot_dims] = srows[0::2]
+    scale = (rng.random(shape[:-1], dtype=np.float32) * 0.02 + 0.01).astype(np.float32)
+    return codes, scale
+
+
 def check_keep_scale_rows(before, sc_before, after, sc_after, positions, cfg_from, cfg_to):
     """Keep-scale re-rotation of int8 rows, checked row by row against the branch the kernel took.
 

@@ -14,7 +14,7 @@ import pytest
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
 from tests.gpu_util import (bf16_attention_ref, EPS_TURN_HADAMARD, DevPaged, assert_bf16_close, assert_int8_codes_valid,
-                            check_keep_scale_rows, decode_int8, int8_turn_quotients, oracle_cfg, oracle_written, to_np64,
+                            check_keep_scale_rows, decode_int8, int8_turn_quotients, oracle_cfg, oracle_written, seeded_int8_rows, to_np64,
                             torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -30,19 +30,6 @@ def env():
     return R, torch, dev
 
 
-def _seeded_rows(torch, dev, shape, seed, rot_dims, rot_amp):
-    """int8 rows: rotary dims uniform in [-rot_amp, rot_amp], the rest in [-127, 127]; scales U(0.01, 0.03).
-    Odd rows use the full range in the rotary dims too (those rows tend to overflow a turn)."""
-    rng = synth.rng(seed)
-    codes = rng.integers(-127, 128, size=shape).astype(np.int8)
-    small = rng.integers(-rot_amp, rot_amp + 1, size=shape[:-1] + (rot_dims,)).astype(np.int8)
-    rows = codes.reshape(-1, shape[-1])
-    srows = small.reshape(-1, rot_dims)
-    rows[0::2, :rot_dims] = srows[0::2]
-    scale = (rng.random(shape[:-1], dtype=np.float32) * 0.02 + 0.01).astype(np.float32)
-    return codes, scale
-
-
 @pytest.mark.parametrize("r,neox", [(64, True), (128, True), (96, True), (64, False), (32, False)])
 def test_keep_scale_rerotate_vs_oracle(env, r, neox):
     R, torch, dev = env
@@ -51,7 +38,7 @@ def test_keep_scale_rerotate_vs_oracle(env, r, neox):
     ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144, neox=neox)
     cb = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.5, orig_max_pos=262144, neox=neox, rope_type=R.ROPE_LINEAR)
     pos0 = 200003
-    c0, s0 = _seeded_rows(torch, dev, (L, T, Hkv, d), 1200 + r, r, 80)
+    c0, s0 = seeded_int8_rows((L, T, Hkv, d), 1200 + r, r, 80)
     s0[0, 5, 2] = 0.0
     c0[0, 5, 2] = 0
     codes = torch.from_numpy(c0).to(dev)
@@ -86,7 +73,7 @@ def test_hadamard_rerotate_vs_oracle(env, r, neox, d, Hkv):
     ca = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.0, orig_max_pos=262144, neox=neox)
     cb = R.rope_cfg(d, r, rope_theta=5e5, yarn_factor=1.625, orig_max_pos=262144, neox=neox)
     pos0 = 300007
-    c0, s0 = _seeded_rows(torch, dev, (L, T, Hkv, d), 1300 + r + d, r, 127)
+    c0, s0 = seeded_int8_rows((L, T, Hkv, d), 1300 + r + d, r, 127)
     s0[1, 7, Hkv - 1] = 0.0  # an all-zero row stays all zero with scale 0
     c0[1, 7, Hkv - 1] = 0
     codes = torch.from_numpy(c0).to(dev)
