@@ -272,7 +272,7 @@ def visible_positions(p: int, sinks: int, window: int) -> list[int]:
 
 # --------------------------------------------------------------------------
 # Quantisers   ([DYN] "What it does": cached K is dequantised, turned and
-# requantised; config 4 keeps one fp32 scale per row)
+# requantised; the 64-layer re-rotated caches keep one fp32 scale per row)
 # --------------------------------------------------------------------------
 
 
@@ -309,7 +309,7 @@ def _quotients32(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
 def quant_int8_rows(x: np.ndarray):
     """Per-row symmetric int8: scale = max|x| / 127, code = clamp(rne(x / scale), -127, 127).
 
-    One scale per row of d dims (config 4: per-row fp32 scale).  The scale is
+    One scale per row of d dims (a per-row fp32 scale, as the re-rotated int8 caches keep).  The scale is
     max|x| / 127 rounded to float32, the precision it is stored in; each code
     rounds (to nearest, ties to even) the quotient x / scale taken against that
     stored scale and rounded to float32: the code whose multiple of the stored

@@ -131,7 +131,7 @@ def test_paged_decode_b64_ctx32768(env):
 
 
 def test_paged_decode_b64_ctx32768_learned_sinks(env):
-    # the learned-sink decode row's launch: the config-2 decode with one sink logit per query head,
+    # the learned-sink decode row's launch: the batch-64 x 32768 paged decode with one sink logit per query head,
     # after a step; needles score about 16, and the sink logits run from 14 (a few per cent of the
     # needles' weight) to 22 (most of it), so the oracle without them fails the same tolerance
     R, torch, dev, WL = env
