@@ -238,8 +238,9 @@ def main():
                     help="only run a plain 2 GiB device copy 5 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
-              "see the sharding note in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs): there is no multi-GPU path; the "
+              "decode shards by sequence or KV head with no exchange, so one GPU's rate is the per-GPU figure",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
