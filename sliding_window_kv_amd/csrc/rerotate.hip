@@ -1341,10 +1341,10 @@ __device__ __forceinline__ void fmac_partner8(float (&o)[8], const float *x, con
 // workgroup's layers; every 8 lanes move one whole 128-byte row (full cache lines, streamed) in
 // and out.  The first layer's rows come by direct global -> LDS loads; each later layer's rows
 // are loaded into registers two layers ahead and written into the stage once the layer before
-// has left it.  The pass runs at the rate of its memory traffic, not of its arithmetic (on the
-// 64-layer switch: no arithmetic 13.1 ms, arithmetic with no loads or stores 8.7 ms, the whole
-// pass 13.0-13.5 ms); the two-layer lead takes about 2 % off, one layer or a second LDS stage
-// about 1 %.  Rows sit 144 bytes apart in the stage (9 slots of 16 bytes, the ninth unused), so that 8
+// has left it.  Memory traffic and vector issue limit the pass together (on the 64-layer switch:
+// no arithmetic 13.1 ms, arithmetic with no loads or stores 8.7 ms, the whole pass 13.0-13.5 ms,
+// during which the chip holds about 1.9 GHz and the VALU issues at about its fp32 rate); the
+// two-layer lead takes about 2 % off, one layer or a second LDS stage about 1 %.  Rows sit 144 bytes apart in the stage (9 slots of 16 bytes, the ninth unused), so that 8
 // consecutive rows start in 8 distinct 16-byte bank groups and each lane reads its half row at
 // fixed offsets from one address (the two lanes of a row read chunks 2 slots apart, which
 // overlaps in banks two ways within 16 lanes).  Reading the rows in place (32 bytes of a row per
