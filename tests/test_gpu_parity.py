@@ -301,13 +301,15 @@ def test_append_head_shapes(env, layout, dtype_name, d, r, neox, Hq, Hkv, unalig
 
 # ------------------------------------------------------------------ paged append + freeing + decode
 
-def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
+def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed, bs=16):
+    """Mixed rounds of chunk appends and single-token steps into a paged cache of bs-token blocks:
+    integer state, freed ids and cache contents against the oracle after every round, and (for the
+    16-token blocks the decode takes) the decode of every sequence."""
     R, torch, dev = env
     dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
     act = {"f32": R.F32, "bf16": R.BF16}[dtype_name]
     rng = synth.rng(seed)
     max_len = 200
-    bs = 16
     max_blocks = max_len // bs + 1
     num_blocks = B * max_blocks + 7
     table = synth.block_table_permutation(B, max_blocks, num_blocks, seed + 1)
@@ -315,7 +317,7 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
     ocfg = oracle_cfg(cfg)
     gtab = _table(R, torch, dev, cfg, max_len)
     otab = O.build_table(ocfg, max_len)
-    cache = DevPaged(R, torch, dev, dtype, B, Hkv, d, S, W, table, num_blocks)
+    cache = DevPaged(R, torch, dev, dtype, B, Hkv, d, S, W, table, num_blocks, bs=bs)
     otable = [list(map(int, row)) for row in table]
     qall = synth.normal((B, max_len, Hq, d), seed + 2)
     kall = synth.normal((B, max_len, Hkv, d), seed + 3)
@@ -329,7 +331,8 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
     n = [0] * B
     freed_dev = torch.full((B * max_blocks,), -7, dtype=torch.int32, device=dev)
     nfreed = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    if bs == 16:
+        ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
     for _ in range(rounds):
         # a mixed step: some sequences prefill a chunk, some decode one token, some idle
         toks, poss, seqs, oracle_freed = [], [], [], []
@@ -373,6 +376,8 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
                 else:
                     assert_bf16_rounded(got_k, krot[b, p])
                 assert np.array_equal(vc[bid, :, p % bs], vall[b, p])
+        if bs != 16:
+            continue
         # decode for every sequence with its latest query
         qd = torch.from_numpy(np.stack([qrot[b, max(n[b] - 1, 0)] for b in range(B)])).to(dev, dtype)
         out = torch.empty(B, Hq, d, dtype=dtype, device=dev)
@@ -391,6 +396,13 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed):
                 assert rowwise(got[b], O.decode_attention(*args)) <= 1e-5
             else:
                 bf16_attention_ref(got[b], O.decode_attention, *args)
+
+
+@pytest.mark.parametrize("bs,S,W", [(1, 2, 5), (8, 4, 20), (32, 3, 40), (5, 0, 17)])
+def test_paged_append_block_sizes(env, bs, S, W):
+    # the append's slot rule, window edge and null-block freeing with blocks other than 16 tokens
+    # (one token per block, a block smaller than the sinks' span, larger ones, an odd size)
+    _paged_end_to_end(env, "bf16", S, W, B=5, Hq=8, Hkv=2, d=64, rounds=8, seed=2400 + bs, bs=bs)
 
 
 @pytest.mark.parametrize("S,W", [(4, 12), (0, 20), (4, 0), (3, 33), (2, 1), (0, 1)])
