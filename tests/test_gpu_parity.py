@@ -207,6 +207,23 @@ def test_ring_window_of_one(env, S, dtype_name):
     _ring_end_to_end(env, True, dtype_name, [5, 1, 1, 3, 1, 2], S=S, W=1)
 
 
+def _random_ring_case(seed):
+    """(neox, dtype, S, W, chunks): a seeded ring geometry and a chunk sequence that fills the sinks
+    in pieces, wraps the ring several times, and appends chunks shorter than, equal to and longer
+    than the window into a non-empty ring."""
+    rng = synth.rng(seed)
+    S = int(rng.integers(0, 6))
+    W = int(rng.choice([1, 2, int(rng.integers(3, 41))]))
+    lens = [int(rng.choice([1, 1, 2, W, W + 1, int(rng.integers(1, 3 * W + 2))])) for _ in range(10)]
+    return bool(seed % 2), ("bf16" if seed % 3 == 0 else "f32"), S, W, lens
+
+
+@pytest.mark.parametrize("seed", [2501, 2502, 2503, 2504, 2505, 2506])
+def test_ring_random_chunk_sequences(env, seed):
+    neox, dtype_name, S, W, chunks = _random_ring_case(seed)
+    _ring_end_to_end(env, neox, dtype_name, chunks, S=S, W=W)
+
+
 # ------------------------------------------------------------------ rope + append over head shapes
 
 APPEND_SHAPES = [
