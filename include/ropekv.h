@@ -265,8 +265,10 @@ int ropekv_prefill_attn(const void *q, const void *k, const void *v, int32_t T, 
  * max|y| / 127, codes rne(y * (127 / max|y|)) with the reciprocal correctly
  * rounded and the product rounded once (within one fp32 rounding of y / scale);
  * a row the turn leaves unchanged keeps its codes and scale bit for bit.
- * cache: CONTIG, kv_dtype F16 / BF16 / F32 / I8, n_layers layers back to back
- * (FP8: ROPEKV_EDTYPE).
+ * cache: CONTIG, kv_dtype F16 / BF16 / F32 / I8, n_layers >= 1 layers back to back
+ * (FP8: ROPEKV_EDTYPE).  I8 keys need head_dim = 16 * 2^k (16 to 512) and rotary_dim
+ * a multiple of 32 (NeoX) or 16 (GPT-J); Hadamard-rotated NeoX keys rotary_dim = 2^k
+ * >= 64; otherwise ROPEKV_ERANGE.
  * The angle p (w_to,i - w_from,i) and its reduction modulo 2 pi in fp64; cos and sin of the
  * reduced angle, and the rotation, in fp32 (cos and sin within a few 1e-7 of the exact values).
  * from / to must agree on head_dim, rotary_dim and neox. */
