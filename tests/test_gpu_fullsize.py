@@ -441,6 +441,50 @@ def test_rope_append_prefill_t8192(env):
         assert np.array_equal(vc[i], v_raw[row[t]])
 
 
+def test_mixed_step_two_streams(env):
+    # the mixed-step row's launches: the 8192-token prefill chunk on one stream and the 256-sequence
+    # windowed decode on another, running at once, give bit for bit the outputs each gives on one
+    # stream (three repetitions, outputs cleared to NaN before each); sampled rows of both against
+    # the oracle (the needle tests of the same launches carry the visible-set power)
+    R, torch, dev, WL = env
+    pf = WL.Prefill(R, torch, dev)
+    wd = WL.WindowedPagedDecode(R, torch, dev)
+    pf.run()
+    wd.decode()
+    torch.cuda.synchronize()
+    assert pf.int_state[3].item() == 0 and wd.err.item() == 0
+    ref_pf, ref_wd = pf.out.clone(), wd.out.clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        pf.out.fill_(float("nan"))
+        wd.out.fill_(float("nan"))
+        cur = torch.cuda.current_stream()
+        s1.wait_stream(cur)
+        s2.wait_stream(cur)
+        pf.run(stream=s1)
+        wd.decode(stream=s2)
+        cur.wait_stream(s1)
+        cur.wait_stream(s2)
+        torch.cuda.synchronize()
+        assert pf.int_state[3].item() == 0 and wd.err.item() == 0
+        assert torch.equal(pf.out, ref_pf), f"prefill differs on two streams (repetition {rep})"
+        assert torch.equal(wd.out, ref_wd), f"decode differs on two streams (repetition {rep})"
+    q, k, v, out = to_np64(pf.q), to_np64(pf.k), to_np64(pf.v), to_np64(ref_pf)
+    for t in (100, pf.T - 1):
+        bf16_attention_ref(out[t], O.decode_attention, q[t], lambda j: k[j], lambda j: v[j], t + 1, pf.S, pf.W,
+                           pf.Hkv)
+    dq, dout = to_np64(wd.q), to_np64(ref_wd)
+    for b in (0, wd.B - 1):
+        n = int(wd.lens[b])
+        row = wd.table_host[b]
+        live = sorted({int(x) for x in row if x >= 0})
+        idx = torch.tensor(live, dtype=torch.long, device=wd.k.device)
+        kb = dict(zip(live, to_np64(wd.k[idx])))
+        vb = dict(zip(live, to_np64(wd.v[idx])))
+        bf16_attention_ref(dout[b], O.decode_attention, dq[b], lambda j: kb[int(row[j // 16])][:, j % 16],
+                           lambda j: vb[int(row[j // 16])][:, j % 16], n, wd.S, wd.W, wd.Hkv)
+
+
 @pytest.mark.parametrize("kind", ["f16", "i8", "i8_keep", "i8_hadamard"])
 def test_rerotate_l64_t524288_sampled_rows(env, kind):
     R, torch, dev, WL = env
