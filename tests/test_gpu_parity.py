@@ -350,6 +350,9 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed, bs=16)
     nfreed = torch.zeros(1, dtype=torch.int32, device=dev)
     if bs == 16:
         ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    vis_p = torch.zeros(max_len + 8, dtype=torch.int32, device=dev)
+    vis_o = torch.zeros(max_len + 8, dtype=torch.int64, device=dev)
+    vis_n = torch.zeros(1, dtype=torch.int32, device=dev)
     for _ in range(rounds):
         # a mixed step: some sequences prefill a chunk, some decode one token, some idle
         toks, poss, seqs, oracle_freed = [], [], [], []
@@ -393,6 +396,18 @@ def _paged_end_to_end(env, dtype_name, S, W, B, Hq, Hkv, d, rounds, seed, bs=16)
                 else:
                     assert_bf16_rounded(got_k, krot[b, p])
                 assert np.array_equal(vc[bid, :, p % bs], vall[b, p])
+        # visible positions of each sequence's next query, chronological, with the element offset of
+        # each key row (head 0) through the oracle's block table; no visible key sits in a freed block
+        for b in range(B):
+            vis_n.zero_()
+            R.visible_slots(cache.desc, b, vis_p, vis_o, vis_p.numel(), vis_n)
+            torch.cuda.synchronize()
+            nv = vis_n.item()
+            want = O.visible_positions(n[b] - 1, S, W) if n[b] > 0 else []
+            assert vis_p[:nv].cpu().tolist() == want
+            offs = [((otable[b][j // bs] * Hkv) * bs + j % bs) * d for j in want]
+            assert all(otable[b][j // bs] >= 0 for j in want)
+            assert vis_o[:nv].cpu().tolist() == offs
         if bs != 16:
             continue
         # decode for every sequence with its latest query
