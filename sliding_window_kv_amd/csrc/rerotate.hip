@@ -1600,7 +1600,8 @@ __global__ __launch_bounds__(256) void shift_kernel(ShiftArgs a) {
 template <typename T>
 hipError_t launch_shift_t(const ShiftArgs &a, hipStream_t s) {
   const int half = a.p.rotary_dim / 2;
-  const bool wide = half % (16 / (int)sizeof(T)) == 0;
+  // 16-byte vectors only where every row starts on a 16-byte boundary
+  const bool wide = half % (16 / (int)sizeof(T)) == 0 && (a.D * (int)sizeof(T)) % 16 == 0;
   const long items = a.rows * (wide ? half / (16 / (int)sizeof(T)) : half);
   const long blocks = (items + 255) / 256;
   if (blocks < 1) return hipSuccess;
@@ -1682,7 +1683,8 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
     if (c.kv_dtype == ROPEKV_F16 || c.kv_dtype == ROPEKV_BF16 || c.kv_dtype == ROPEKV_F32) {
       const int eb = c.kv_dtype == ROPEKV_F32 ? 4 : 2;
       const int R = to.rotary_dim * eb / 16;
-      if ((to.rotary_dim * eb) % 16 == 0 && pow2(R) && R >= 2 && R <= 32) {
+      // 16-byte chunks need rows that start on 16-byte boundaries (head_dim * eb a multiple of 16)
+      if ((to.rotary_dim * eb) % 16 == 0 && (c.head_dim * eb) % 16 == 0 && pow2(R) && R >= 2 && R <= 32) {
         a.lg = 1;
         const dim3 g1 = one_shot(kFloatChunks * kChunkThreads / R, shm1);
         auto go = [&](auto tag, auto rtag) {
@@ -1745,6 +1747,8 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
       }
     }
   }
+  // the vector variants below move 16 bytes at a time: rows must start on 16-byte boundaries
+  const bool rows16 = (c.head_dim * (c.kv_dtype == ROPEKV_F32 ? 4 : 2)) % 16 == 0;
   switch (c.kv_dtype) {
     case ROPEKV_I8: {
       if (c.k_int8_mode & ROPEKV_I8_HADAMARD) {
@@ -1792,7 +1796,7 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
       break;
     }
     case ROPEKV_F16:
-      if (half % 8 == 0) {
+      if (half % 8 == 0 && rows16) {
         const dim3 g1 = one_shot(256 / (half / 8), shm1);
         hipLaunchKernelGGL((rerotate_float_kernel<f16_t, 8>), g1, dim3(256), shm1, s, a);
       } else {
@@ -1801,7 +1805,7 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
       }
       break;
     case ROPEKV_BF16:
-      if (half % 8 == 0) {
+      if (half % 8 == 0 && rows16) {
         const dim3 g1 = one_shot(256 / (half / 8), shm1);
         hipLaunchKernelGGL((rerotate_float_kernel<bf16_t, 8>), g1, dim3(256), shm1, s, a);
       } else {
@@ -1810,7 +1814,7 @@ hipError_t launch_rerotate(const RopeParams &from, const RopeParams &to, const r
       }
       break;
     case ROPEKV_F32:
-      if (half % 4 == 0) {
+      if (half % 4 == 0 && rows16) {
         const dim3 g1 = one_shot(256 / (half / 4), shm1);
         hipLaunchKernelGGL((rerotate_float_kernel<float, 4>), g1, dim3(256), shm1, s, a);
       } else {

@@ -44,6 +44,9 @@ FLOAT_SHAPES = [
     ("f16", 128, 36, True),     # half 18: one pair per thread
     ("f32", 34, 18, False),     # half 9, odd head dim
     ("f32", 2, 2, True),        # a single pair
+    ("f16", 36, 16, True),      # 72-byte rows: not on 16-byte boundaries, so element by element
+    ("f32", 34, 16, False),     # 136-byte rows, likewise
+    ("bf16", 100, 64, True),    # 200-byte rows, likewise
 ]
 
 
@@ -121,3 +124,36 @@ def test_rerotate_int8_head_shapes(env, d, r, neox, keep):
     if keep:
         assert n_keep > 10 and n_over > 10  # both branches taken
     assert s1[0, 3, 1] == 0 and np.all(c1[0, 3, 1] == 0)
+
+
+SHIFT_SHAPES = [
+    # dtype, d, r, neox, delta
+    ("f16", 128, 64, True, -1),   # 16-byte vectors (8 pairs per thread)
+    ("f32", 512, 512, False, 3),  # 16-byte vectors (4 pairs), the largest head
+    ("bf16", 96, 24, True, -2),   # r / 2 = 12: one pair per thread
+    ("f32", 34, 16, True, 5),     # 136-byte rows: element by element
+    ("bf16", 100, 64, False, -1), # 200-byte rows: element by element
+]
+
+
+@pytest.mark.parametrize("dtype_name,d,r,neox,delta", SHIFT_SHAPES)
+def test_shift_keys_contig_head_shapes(env, dtype_name, d, r, neox, delta):
+    # a contiguous cache of 3 layers: every row turns by delta positions ([SINK] "RoPE: absolute
+    # positions and local rerotation", R_a R_b = R_{a+b}), one rounding of the oracle's shift, the
+    # tail bit for bit
+    R, torch, dev = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype_name]
+    kvdt = {"f32": R.F32, "bf16": R.BF16, "f16": R.F16}[dtype_name]
+    L, T, Hkv = 3, 24, 2
+    cfg = R.rope_cfg(d, r, rope_theta=1e4, neox=neox)
+    k = torch.from_numpy(synth.normal((L, T, Hkv, d), 900 + d + r)).to(dev, dtype)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    desc = R.kv_cache(R.CONTIG, kvdt, Hkv, d, k, capacity=T, err_word=err)
+    before = to_np64(k)
+    R.shift_keys(cfg, desc, delta, L)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    got = to_np64(k)
+    want = O.shift_keys(before.reshape(-1, d), delta, oracle_cfg(cfg)).reshape(before.shape)
+    assert_rounded_once(got, want, dtype_name)
+    assert np.array_equal(got[..., r:], before[..., r:])
