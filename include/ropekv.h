@@ -248,7 +248,9 @@ int ropekv_decode_attn_noalloc(const void *q, int32_t batch, int32_t n_q_heads,
  * >= pos0 come from the chunk's own k, v ([T, Hkv, d], rotated); keys below
  * pos0 from the cache (RING or PAGED) of sequence seq_id.  For RING the
  * prefix must still be in the ring (call before appending the chunk, or keep
- * pos0 + T <= C); a missing key sets ROPEKV_DEV_PREFIX_LOST.
+ * pos0 + T <= C); a missing key (not in the ring, or in a null PAGED block) sets
+ * ROPEKV_DEV_PREFIX_LOST, and the output rows of the queries that see it are then
+ * unspecified (the other rows stay exact; nothing is read out of bounds).
  *   q [T, n_q_heads, d], out same; dtype = kv_dtype (F32 or BF16), d 64 or 128,
  *   n_rep = n_q_heads / Hkv in {1, 2, 4, 8}; seq_id only read when pos0 > 0;
  *   sink_logits as for ropekv_decode_attn; q, k, v and out 16-byte aligned.

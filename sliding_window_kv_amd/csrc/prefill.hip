@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       long off = key_row(a, j, g, D, &chunk);
       const bool needed = j <= qp_hi && (W == 0 || j < S || j > qp_lo - W);
       if (off < 0 && needed && j < a.pos0) lost = true;
-      if (off < 0) {  // beyond the chunk or not in the cache: an in-bounds row, never visible
+      if (off < 0) {  // beyond the chunk (never visible) or a lost prefix key (flagged): an in-bounds row
         off = (long)g * D;
         chunk = true;
       }

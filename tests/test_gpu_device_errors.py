@@ -9,7 +9,8 @@ import pytest
 
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
-from tests.gpu_util import DevPaged, DevRing, attend_set, oracle_cfg, rowwise, to_np64, torch_dev
+from tests.gpu_util import (DevPaged, DevRing, attend_set, bf16_attention_ref, decode_int8, oracle_cfg, rowwise, to_np64,
+                            torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +152,84 @@ def test_decode_skips_a_null_block_it_must_read(env):
     K1, V1 = rows(1)
     kept = [j for j in range(n) if not 16 <= j < 32]
     assert rowwise(got[1], attend_set(qq[1], K1, V1, kept, HKV)) <= 1e-5
+
+
+def _att_over(n, idx):
+    """The oracle's attention over keys 0..n-1 restricted to the rows idx (keys a kernel skipped are
+    left out), as a callable of (q, key-by-position, value-by-position)."""
+    def att(q, kf, vf):
+        Ks = np.stack([kf(j) for j in range(n)])
+        Vs = np.stack([vf(j) for j in range(n)])
+        return attend_set(q, Ks, Vs, idx, HKV)
+    return att
+
+
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
+def test_prefill_prefix_in_a_null_block(env, dtype_name):
+    # an 8-token chunk at pos0 40 over a paged window-12 prefix whose blocks 0 (out of every query's
+    # window) and 1 (keys 16..31) are null: queries 40..42 see keys 29..31, so the call sets
+    # PREFIX_LOST and their rows are unspecified; queries 43..47 see no lost key and match the oracle
+    # (fp32 kernel and bf16 MFMA kernel)
+    R, torch, dev, cfg, table = env
+    dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype_name]
+    pos0, T, W = 40, 8, 12
+    tab = np.array([[-1, -1, 2, 3]], dtype=np.int32)
+    c = DevPaged(R, torch, dev, dtype, 1, HKV, D, 0, W, tab, 4)
+    c.k.copy_(torch.from_numpy(synth.normal(tuple(c.k.shape), 3800)).to(dtype))
+    c.v.copy_(torch.from_numpy(synth.normal(tuple(c.v.shape), 3801)).to(dtype))
+    c.seq_len.fill_(pos0)
+    q = torch.from_numpy(synth.normal((T, HQ, D), 3802)).to(dev, dtype)
+    k = torch.from_numpy(synth.normal((T, HKV, D), 3803)).to(dev, dtype)
+    v = torch.from_numpy(synth.normal((T, HKV, D), 3804)).to(dev, dtype)
+    out = torch.empty_like(q)
+    R.prefill_attn(q, k, v, T, pos0, HQ, c.desc, 0, 0.0, out)
+    torch.cuda.synchronize()
+    assert c.err.item() == R.DEV_PREFIX_LOST
+    kp, vp, qq, got = to_np64(c.k), to_np64(c.v), to_np64(q), to_np64(out)
+    kk, vv = to_np64(k), to_np64(v)
+
+    def kf(j):
+        return kk[j - pos0] if j >= pos0 else kp[tab[0, j // 16], :, j % 16]
+
+    def vf(j):
+        return vv[j - pos0] if j >= pos0 else vp[tab[0, j // 16], :, j % 16]
+
+    for t in range(3, T):  # queries 43..47: window 32..47 at most, all keys present
+        assert min(O.visible_positions(pos0 + t, 0, W)) >= 32
+        args = (qq[t], kf, vf, pos0 + t + 1, 0, W, HKV)
+        if dtype_name == "f32":
+            assert rowwise(got[t], O.decode_attention(*args)) <= 1e-5
+        else:
+            bf16_attention_ref(got[t], O.decode_attention, *args)
+
+
+def test_int8_decode_skips_a_null_block(env):
+    # the 8-bit decode kernel, int8 codes with row scales: sequence 1's second block is null; the
+    # bit is set, that tile skipped, sequence 0 matches the oracle over every key
+    R, torch, dev, cfg, table = env
+    n = 40
+    tab = np.array([[0, 1, 2], [3, -1, 5]], dtype=np.int32)
+    c = DevPaged(R, torch, dev, torch.int8, 2, HKV, D, 0, 0, tab, 6)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3900)
+    for buf, sc in ((c.k, c.k_scale), (c.v, c.v_scale)):
+        buf.copy_(torch.randint(-127, 128, tuple(buf.shape), dtype=torch.int8, device=dev, generator=g))
+        sc.copy_(torch.rand(tuple(sc.shape), device=dev, generator=g) * 0.02 + 0.01)
+    c.seq_len.fill_(n)
+    q = torch.from_numpy(synth.normal((2, HQ, D), 3901)).to(dev, torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(2, HQ, c.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, 2, HQ, c.desc, 0.0, out, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert c.err.item() == R.DEV_NULL_BLOCK
+    kd = decode_int8(c.k.cpu().numpy(), c.k_scale.cpu().numpy())
+    vd = decode_int8(c.v.cpu().numpy(), c.v_scale.cpu().numpy())
+    qq, got = to_np64(q), to_np64(out)
+    for b, idx in ((0, list(range(n))), (1, [j for j in range(n) if not 16 <= j < 32])):
+        def kf(j, b=b):
+            return kd[tab[b, j // 16], :, j % 16] if tab[b, j // 16] >= 0 else np.zeros((HKV, D))
+
+        def vf(j, b=b):
+            return vd[tab[b, j // 16], :, j % 16] if tab[b, j // 16] >= 0 else np.zeros((HKV, D))
+
+        bf16_attention_ref(got[b], _att_over(n, idx), qq[b], kf, vf)
