@@ -233,3 +233,26 @@ def test_int8_decode_skips_a_null_block(env):
             return vd[tab[b, j // 16], :, j % 16] if tab[b, j // 16] >= 0 else np.zeros((HKV, D))
 
         bf16_attention_ref(got[b], _att_over(n, idx), qq[b], kf, vf)
+
+
+def test_decode_sequence_longer_than_its_block_table(env):
+    # full-attention paged decode, fp32, two table columns (32 keys): sequence 1 claims 40 tokens; the
+    # bit is set, the 8 keys no block covers are skipped (its output is the attention over keys
+    # 0..31), sequence 0 (32 tokens) exact
+    R, torch, dev, cfg, table = env
+    tab = np.array([[0, 1], [2, 3]], dtype=np.int32)
+    c = DevPaged(R, torch, dev, torch.float32, 2, HKV, D, 0, 0, tab, 4)
+    c.k.copy_(torch.from_numpy(synth.normal(tuple(c.k.shape), 4000)))
+    c.v.copy_(torch.from_numpy(synth.normal(tuple(c.v.shape), 4001)))
+    c.seq_len.copy_(torch.tensor([32, 40], dtype=torch.int32))
+    q = torch.from_numpy(synth.normal((2, HQ, D), 4002)).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(2, HQ, c.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, 2, HQ, c.desc, 0.0, out, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert c.err.item() == R.DEV_BLOCK_RANGE
+    kp, vp, qq, got = to_np64(c.k), to_np64(c.v), to_np64(q), to_np64(out)
+    for b in (0, 1):
+        K = np.stack([kp[tab[b, j // 16], :, j % 16] for j in range(32)])
+        V = np.stack([vp[tab[b, j // 16], :, j % 16] for j in range(32)])
+        assert rowwise(got[b], attend_set(qq[b], K, V, np.arange(32), HKV)) <= 1e-5
