@@ -26,7 +26,14 @@
  *     table, a non-consecutive position, a null block where a key must be
  *     written or read) are reported by OR-ing ROPEKV_DEV_* bits into the
  *     cache's err_word; the offending token / tile is skipped, never read or
- *     written out of bounds.
+ *     written out of bounds.  In the append, a token whose position lies
+ *     outside the table is left untouched; any other flagged token still has
+ *     its q and k rotated in place, but nothing of it is written to the cache;
+ *     a token flagged for its sequence or position leaves the sequence's state
+ *     as it was, one flagged for its block (null, or past max_blocks) still
+ *     advances it.  The decode leaves a
+ *     skipped tile's keys out of the softmax; the prefill's rule for a lost
+ *     prefix key is given with ropekv_prefill_attn.
  */
 #ifndef ROPEKV_H
 #define ROPEKV_H

@@ -89,6 +89,7 @@ def test_null_block_and_block_range_in_the_append(env):
     c.seq_len.copy_(torch.tensor([0, 0, 32], dtype=torch.int32))
     raw_k, k, v = _append(env, c.desc, [0, 0, 32], [0, 1, 2], 3400)
     assert c.err.item() == R.DEV_NULL_BLOCK | R.DEV_BLOCK_RANGE
+    assert c.seq_len.cpu().tolist() == [1, 1, 33]  # block errors still advance the state
     assert torch.equal(c.v[0, :, 0], v[0])  # sequence 0, block 0, slot 0
     assert not c.k[1:].any() and not c.v[1:].any()  # nothing else written anywhere in the pool
     assert rowwise(to_np64(c.k[0, :, 0]), _rotated(env, raw_k[0], 0)) <= 1e-6
