@@ -1033,3 +1033,71 @@ def test_rerotate_across_schemes(env):
         torch.cuda.synchronize()
         cur = O.rerotate_rows(cur, pos, oracle_cfg(a_), oracle_cfg(b_))
         assert rowwise(to_np64(k[0]), cur) <= 1e-5
+
+
+# ------------------------------------------------------------------ an explicit softmax scale
+
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16", "i8"])
+def test_decode_and_prefill_explicit_scale(env, dtype_name):
+    # scale != 0 replaces 1/sqrt(d) in the decode (fp32, bf16 and int8 caches) and the prefill (fp32,
+    # bf16): a sharper 0.3 and a flatter 0.02 against the oracle at the same scale
+    R, torch, dev = env
+    B, Hkv, n_rep, d, S, W = 3, 2, 4, 64, 4, 40
+    Hq = Hkv * n_rep
+    lens = [5, 60, 130]
+    table = synth.block_table_permutation(B, 16, B * 16, 170)
+    store = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[dtype_name]
+    cache = DevPaged(R, torch, dev, store, B, Hkv, d, S, W, table, B * 16)
+    if dtype_name == "i8":
+        g = torch.Generator(device=dev)
+        g.manual_seed(171)
+        for buf, sc in ((cache.k, cache.k_scale), (cache.v, cache.v_scale)):
+            buf.copy_(torch.randint(-127, 128, tuple(buf.shape), dtype=torch.int8, device=dev, generator=g))
+            sc.copy_(torch.rand(tuple(sc.shape), device=dev, generator=g) * 0.02 + 0.01)
+        kp = decode_int8(cache.k.cpu().numpy(), cache.k_scale.cpu().numpy())
+        vp = decode_int8(cache.v.cpu().numpy(), cache.v_scale.cpu().numpy())
+        qdt = torch.bfloat16
+    else:
+        _fill(torch, cache.k, 172)
+        _fill(torch, cache.v, 173)
+        kp, vp = to_np64(cache.k), to_np64(cache.v)
+        qdt = store
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=qdt, device=dev), 174)
+    qq = to_np64(q)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    for scale in (0.3, 0.02):
+        R.decode_attn(q, B, Hq, cache.desc, scale, out, ws, ws.numel() * 4)
+        torch.cuda.synchronize()
+        assert cache.err.item() == 0
+        got = to_np64(out)
+        for b, n in enumerate(lens):
+            args = (qq[b], lambda j, b=b: kp[table[b, j // 16], :, j % 16], lambda j, b=b: vp[table[b, j // 16], :, j % 16],
+                    n, S, W, Hkv)
+            if dtype_name == "f32":
+                assert rowwise(got[b], O.decode_attention(*args, scale=scale)) <= 1e-5
+            else:
+                bf16_attention_ref(got[b], O.decode_attention, *args, scale=scale)
+    if dtype_name == "i8":
+        return
+    # the prefill of a 20-token chunk from position 0 (no prefix), same scales
+    T = 20
+    pq = _fill(torch, torch.empty(T, Hq, d, dtype=store, device=dev), 175)
+    pk = _fill(torch, torch.empty(T, Hkv, d, dtype=store, device=dev), 176)
+    pv = _fill(torch, torch.empty(T, Hkv, d, dtype=store, device=dev), 177)
+    po = torch.empty_like(pq)
+    Q, K, V = to_np64(pq), to_np64(pk), to_np64(pv)
+    for scale in (0.3, 0.02):
+        R.prefill_attn(pq, pk, pv, T, 0, Hq, cache.desc, 0, scale, po)
+        torch.cuda.synchronize()
+        assert cache.err.item() == 0
+        got = to_np64(po)
+        args = (Q, lambda j: K[j], lambda j: V[j], 0, S, W, Hkv)
+        want = O.prefill_attention(*args, scale=scale)
+        if dtype_name == "f32":
+            assert rowwise(got, want) <= 1e-5
+        else:
+            for t in range(T):
+                bf16_attention_ref(got[t], O.decode_attention, Q[t], lambda j: K[j], lambda j: V[j], t + 1, S, W, Hkv,
+                                   scale=scale)
