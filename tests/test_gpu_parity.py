@@ -635,26 +635,30 @@ def test_prefill_chunk_from_zero(env, T, S, W, n_rep, d):
     ref = bf16_attention_ref(to_np64(out), O.prefill_attention, qq, lambda j: kk[j], lambda j: vv[j], 0, S, W, Hkv)
 
 
-def test_prefill_with_paged_prefix_equals_one_shot(env):
-    # chunked prefill into a cached prefix == the same rows of one-shot prefill
+@pytest.mark.parametrize("seq_id", [0, 2])
+def test_prefill_with_paged_prefix_equals_one_shot(env, seq_id):
+    # chunked prefill into a cached prefix == the same rows of one-shot prefill; the prefix belongs to
+    # sequence seq_id of three, the other sequences' blocks hold different (decoy) rows
     R, torch, dev = env
     Hkv, n_rep, d, S, W = 8, 8, 128, 4, 100
     Hq = Hkv * n_rep
-    T_all, pos0 = 400, 230
+    B, T_all, pos0 = 3, 400, 230
     max_blocks = T_all // 16 + 1
-    table = synth.block_table_permutation(1, max_blocks, max_blocks + 3, 81)
-    cache = DevPaged(R, torch, dev, torch.bfloat16, 1, Hkv, d, S, W, table, max_blocks + 3)
+    table = synth.block_table_permutation(B, max_blocks, B * max_blocks + 3, 81)
+    cache = DevPaged(R, torch, dev, torch.bfloat16, B, Hkv, d, S, W, table, B * max_blocks + 3)
+    _fill(torch, cache.k, 85)
+    _fill(torch, cache.v, 86)
     q = _fill(torch, torch.empty(T_all, Hq, d, dtype=torch.bfloat16, device=dev), 82)
     k = _fill(torch, torch.empty(T_all, Hkv, d, dtype=torch.bfloat16, device=dev), 83)
     v = _fill(torch, torch.empty(T_all, Hkv, d, dtype=torch.bfloat16, device=dev), 84)
     # place the prefix keys / values in their blocks (plumbing: a torch copy, no kernel of ours)
     for p in range(pos0):
-        cache.k[table[0, p // 16], :, p % 16] = k[p]
-        cache.v[table[0, p // 16], :, p % 16] = v[p]
+        cache.k[table[seq_id, p // 16], :, p % 16] = k[p]
+        cache.v[table[seq_id, p // 16], :, p % 16] = v[p]
     cache.seq_len.fill_(pos0)
     T = T_all - pos0
     out = torch.empty(T, Hq, d, dtype=torch.bfloat16, device=dev)
-    R.prefill_attn(q[pos0:], k[pos0:], v[pos0:], T, pos0, Hq, cache.desc, 0, 0.0, out)
+    R.prefill_attn(q[pos0:], k[pos0:], v[pos0:], T, pos0, Hq, cache.desc, seq_id, 0.0, out)
     torch.cuda.synchronize()
     assert cache.err.item() == 0
     qq, kk, vv = to_np64(q), to_np64(k), to_np64(v)
@@ -1101,3 +1105,27 @@ def test_decode_and_prefill_explicit_scale(env, dtype_name):
             for t in range(T):
                 bf16_attention_ref(got[t], O.decode_attention, Q[t], lambda j: K[j], lambda j: V[j], t + 1, S, W, Hkv,
                                    scale=scale)
+
+
+def test_decode_first_sequences_of_a_larger_cache(env):
+    # batch 2 over a cache of 3 sequences: rows 0 and 1 of q / out only, against the oracle
+    R, torch, dev = env
+    Bc, B, Hkv, n_rep, d, S, W = 3, 2, 2, 4, 128, 4, 50
+    Hq = Hkv * n_rep
+    table = synth.block_table_permutation(Bc, 8, Bc * 8, 180)
+    cache = DevPaged(R, torch, dev, torch.float32, Bc, Hkv, d, S, W, table, Bc * 8)
+    _fill(torch, cache.k, 181)
+    _fill(torch, cache.v, 182)
+    lens = [70, 33, 100]
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+    q = _fill(torch, torch.empty(B, Hq, d, dtype=torch.float32, device=dev), 183)
+    out = torch.empty_like(q)
+    ws = torch.empty(R.decode_workspace_size(B, Hq, cache.desc) // 4 + 1, dtype=torch.float32, device=dev)
+    R.decode_attn(q, B, Hq, cache.desc, 0.0, out, ws, ws.numel() * 4)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    kp, vp, qq, got = to_np64(cache.k), to_np64(cache.v), to_np64(q), to_np64(out)
+    for b in range(B):
+        want = O.decode_attention(qq[b], lambda j: kp[table[b, j // 16], :, j % 16],
+                                  lambda j: vp[table[b, j // 16], :, j % 16], lens[b], S, W, Hkv)
+        assert rowwise(got[b], want) <= 1e-5
