@@ -16,7 +16,7 @@ import pytest
 from oracle import ropekv_oracle as O
 from sliding_window_kv_amd import synth
 from tests.gpu_util import (bf16_attention_ref, bf16_round, EPS_TURN_I8, DevPaged, DevRing, assert_bf16_close, assert_bf16_rounded, assert_int8_codes_valid, assert_rounded_once, attend_set,
-                            decode_int8, excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
+                            decode_e4m3, decode_int8, excess, int8_turn_quotients, needle_dirs, needle_kv, normwise, oracle_cfg,
                             oracle_written, plant_queries_, rowwise, to_np64, torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -1041,7 +1041,7 @@ def test_rerotate_across_schemes(env):
 
 # ------------------------------------------------------------------ an explicit softmax scale
 
-@pytest.mark.parametrize("dtype_name", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16", "i8", "fp8"])
 def test_decode_and_prefill_explicit_scale(env, dtype_name):
     # scale != 0 replaces 1/sqrt(d) in the decode (fp32, bf16 and int8 caches) and the prefill (fp32,
     # bf16): a sharper 0.3 and a flatter 0.02 against the oracle at the same scale
@@ -1050,9 +1050,21 @@ def test_decode_and_prefill_explicit_scale(env, dtype_name):
     Hq = Hkv * n_rep
     lens = [5, 60, 130]
     table = synth.block_table_permutation(B, 16, B * 16, 170)
-    store = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[dtype_name]
+    store = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": "fp8"}[dtype_name]
     cache = DevPaged(R, torch, dev, store, B, Hkv, d, S, W, table, B * 16)
-    if dtype_name == "i8":
+    if dtype_name == "fp8":
+        # finite E4M3 bytes (the two NaN codes 0x7f / 0xff replaced by 0), row scales U(2/448, 3.5/448)
+        g = torch.Generator(device=dev)
+        g.manual_seed(171)
+        for buf, sc in ((cache.k, cache.k_scale), (cache.v, cache.v_scale)):
+            codes = torch.randint(0, 256, tuple(buf.shape), dtype=torch.int32, device=dev, generator=g)
+            codes[(codes & 0x7F) == 0x7F] = 0
+            buf.copy_(codes.to(torch.uint8))
+            sc.copy_(torch.rand(tuple(sc.shape), device=dev, generator=g) * (1.5 / 448) + 2.0 / 448)
+        kp = decode_e4m3(cache.k.cpu().numpy()) * cache.k_scale.cpu().numpy().astype(np.float64)[..., None]
+        vp = decode_e4m3(cache.v.cpu().numpy()) * cache.v_scale.cpu().numpy().astype(np.float64)[..., None]
+        qdt = torch.bfloat16
+    elif dtype_name == "i8":
         g = torch.Generator(device=dev)
         g.manual_seed(171)
         for buf, sc in ((cache.k, cache.k_scale), (cache.v, cache.v_scale)):
@@ -1083,7 +1095,7 @@ def test_decode_and_prefill_explicit_scale(env, dtype_name):
                 assert rowwise(got[b], O.decode_attention(*args, scale=scale)) <= 1e-5
             else:
                 bf16_attention_ref(got[b], O.decode_attention, *args, scale=scale)
-    if dtype_name == "i8":
+    if dtype_name in ("i8", "fp8"):
         return
     # the prefill of a 20-token chunk from position 0 (no prefix), same scales
     T = 20
@@ -1129,3 +1141,43 @@ def test_decode_first_sequences_of_a_larger_cache(env):
         want = O.decode_attention(qq[b], lambda j: kp[table[b, j // 16], :, j % 16],
                                   lambda j: vp[table[b, j // 16], :, j % 16], lens[b], S, W, Hkv)
         assert rowwise(got[b], want) <= 1e-5
+
+
+def test_prefill_ring_prefix_of_sequence_one(env):
+    # a 6-token chunk at pos0 30 over the ring prefix of sequence 1 of two (sinks 2, window 20, head at
+    # 7, full ring): the ring rows are placed where the oracle's ring model puts each position, the
+    # other sequence holds decoys; fp32, against the oracle
+    R, torch, dev = env
+    B, Hkv, n_rep, d, S, W = 2, 2, 4, 64, 2, 20
+    Hq = Hkv * n_rep
+    pos0, T, head = 30, 6, 7
+    cache = DevRing(R, torch, dev, torch.float32, B, Hkv, d, S, W)
+    _fill(torch, cache.k, 190)
+    _fill(torch, cache.v, 191)
+    prefix_k = synth.normal((pos0, Hkv, d), 192)
+    prefix_v = synth.normal((pos0, Hkv, d), 193)
+    ring = O.RingSeq(sinks=S, window=W, head=head, count=W, seq_len=pos0)
+    slot_of = dict(zip(O.visible_positions(pos0 - 1, S, W), ring.chronological_slots()))
+    for p, slot in slot_of.items():  # plumbing: torch copies into sequence 1's slots
+        cache.k[1, :, slot] = torch.from_numpy(prefix_k[p]).to(dev)
+        cache.v[1, :, slot] = torch.from_numpy(prefix_v[p]).to(dev)
+    cache.head.copy_(torch.tensor([0, head], dtype=torch.int32))
+    cache.count.copy_(torch.tensor([W, W], dtype=torch.int32))
+    cache.seq_len.copy_(torch.tensor([pos0, pos0], dtype=torch.int32))
+    q = _fill(torch, torch.empty(T, Hq, d, dtype=torch.float32, device=dev), 194)
+    k = _fill(torch, torch.empty(T, Hkv, d, dtype=torch.float32, device=dev), 195)
+    v = _fill(torch, torch.empty(T, Hkv, d, dtype=torch.float32, device=dev), 196)
+    out = torch.empty_like(q)
+    R.prefill_attn(q, k, v, T, pos0, Hq, cache.desc, 1, 0.0, out)
+    torch.cuda.synchronize()
+    assert cache.err.item() == 0
+    kk, vv = to_np64(k), to_np64(v)
+
+    def kf(j):
+        return kk[j - pos0] if j >= pos0 else prefix_k[j].astype(np.float64)
+
+    def vf(j):
+        return vv[j - pos0] if j >= pos0 else prefix_v[j].astype(np.float64)
+
+    want = O.prefill_attention(to_np64(q), kf, vf, pos0, S, W, Hkv)
+    assert rowwise(to_np64(out), want) <= 1e-5
